@@ -1,0 +1,280 @@
+"""Throughput of the MoE re-routing operator (MoeReRoutingV2) on one MI355X.
+
+A step is one whole call of the operator (offsets kernel + gather kernel) on
+one batch of synthetic input already resident in HBM. The default workload is
+the shape of the pages' single-operator example: A=16384 tokens of H=7168 int8
+values, N=E=16, one huge segment, [A] fp32 scales (see
+moe_token_re_amd/workloads.py for the recipe).
+
+Calls rotate over several identical buffer sets whose total footprint is at
+least 1 GiB, so the 256 MB Infinity Cache cannot hold the working set between
+calls. Prints ONE JSON line:
+  value       re-route GB/s = algorithmic bytes per call / wall time per call
+  roofline    the gather kernel alone: algorithmic bytes per launch / its mean
+              duration (HIP events on the launch stream) against 8 TB/s HBM;
+              traffic from rocprofv3 FETCH_SIZE/WRITE_SIZE counters when the
+              committed counter summary matches the current kernel source
+  cpu_baseline the CPU oracle on the same workload, one host thread
+plus the measured copy ceiling (hipMemcpyAsync device-to-device and a plain
+16-byte non-temporal copy kernel moving the same token bytes).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--no-cpu] [--no-ceiling]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import re
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+METRIC = "re-route GB/s (bytes read+written) and % of HBM peak; µs/call A=16384 H=7168"
+PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "mrr_gather_pages_shape_counters.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "moe_token_re_amd", "csrc", f)
+                  for f in ("mrr_kernels.hip", "mrr_internal.h", "mrr_validate.cpp")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def gather_bytes_per_launch(w) -> int:
+    """Algorithmic bytes of one gather launch: per row, the token row and the
+    scale row read and written, the weight read and written, the index written."""
+    per_row = 2 * w.token_row_bytes + 2 * w.scale_row_bytes + (8 if w.weight is not None else 0) + 4
+    return per_row * w.A
+
+
+def traffic_from_profile(w):
+    """HBM bytes per gather launch from the committed counter summary, scaled by
+    the copy kernel's counter reading for a known byte count; None when the
+    summary is missing, for another workload, or the kernel has changed."""
+    if not os.path.exists(PROFILE_SUMMARY):
+        return None
+    text = open(PROFILE_SUMMARY).read()
+    fields = dict(re.findall(r"^(\w+):\s*(\S+)\s*$", text, flags=re.M))
+    try:
+        if fields.get("source_hash") != kernel_source_hash() or fields.get("workload") != w.name:
+            return None
+        fetch = float(fields["gather_FETCH_SIZE_KiB"]) * float(fields["fetch_scale"])
+        write = float(fields["gather_WRITE_SIZE_KiB"]) * float(fields["write_scale"])
+    except (KeyError, ValueError):
+        return None
+    return int(round((fetch + write) * 1024))
+
+
+def time_oracle(w, budget_s=10.0, max_runs=7):
+    """The CPU oracle on the full workload, single-threaded, outputs preallocated
+    and pre-faulted; median over runs that fit the time budget."""
+    from oracle import oracle
+
+    outs = oracle.allocate_outputs(w.tokens, w.counts, w.scales, w.weight)
+    for o in outs:
+        if o is not None:
+            o.fill(0)
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < max_runs:
+        t0 = time.perf_counter()
+        oracle.reroute(w.tokens, w.counts, w.scales, w.weight, w.etn_type, w.idx_type, out=outs)
+        times.append(time.perf_counter() - t0)
+        if time.perf_counter() - t_start > budget_s and len(times) >= 3:
+            break
+    return statistics.median(times), len(times)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="pages_shape")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the copy-ceiling measurement")
+    opt = ap.parse_args()
+
+    if opt.gpus != 1:
+        print(f"bench.py measures one GPU only (the operator is per-device and has no collectives); "
+              f"--gpus {opt.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np  # noqa: F401
+    import torch
+
+    from moe_token_re_amd import _lib, api, workloads
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = workloads.make(opt.workload)
+    alg_bytes = w.algorithmic_bytes()
+    print(f"[bench] workload {w.name}: A={w.A} H={w.H} N={w.N} E={w.E} tokens={w.tokens_dtype} "
+          f"algorithmic bytes/call={alg_bytes}", file=sys.stderr, flush=True)
+
+    base = workloads.torch_inputs(w, dev)
+    stream = torch.cuda.current_stream(dev)
+    footprint = 2 * (w.A * (w.token_row_bytes + w.scale_row_bytes + 4 + (8 if w.weight is not None else 0)))
+    n_sets = max(3, math.ceil((1 << 30) / max(footprint, 1)))
+    calls = []
+    for k in range(n_sets):
+        t = base if k == 0 else {key: (v.clone() if isinstance(v, torch.Tensor) else v) for key, v in base.items()}
+        call, _ = api.make_call(t["tokens"], t["counts"], per_token_scales=t["scales"],
+                                expert_topk_weight=t["weight"], expert_token_num_type=w.etn_type,
+                                idx_type=w.idx_type, tokens_dtype=t["tokens_dtype"], stream=stream)
+        calls.append(call)
+    torch.cuda.synchronize()
+
+    # warmup
+    for i in range(opt.warmup):
+        calls[i % n_sets].run()
+    torch.cuda.synchronize()
+    for c in calls:
+        c.run()
+    torch.cuda.synchronize()
+    st = calls[0].device_status()
+    if st != _lib.SUCCESS:
+        raise SystemExit(f"device status {_lib.status_string(st)}")
+
+    # timed: exactly K whole calls, synchronized on both sides
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(opt.steps):
+        calls[i % n_sets].run()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t0
+    ev_ms = ev0.elapsed_time(ev1)
+    ms_per_step = wall_s * 1e3 / opt.steps
+    value = alg_bytes / (ms_per_step * 1e-3) / 1e9
+    print(f"[bench] {opt.steps} calls: wall {ms_per_step * 1e3:.2f} us/call, events "
+          f"{ev_ms * 1e3 / opt.steps:.2f} us/call, {value:.1f} GB/s", file=sys.stderr, flush=True)
+
+    # per-kernel: events around each launch, on the launch stream
+    n_k = max(opt.steps, 50)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_k)]
+    for i in range(n_k):
+        c = calls[i % n_sets]
+        evs[i][0].record(stream)
+        c.run_offsets()
+        evs[i][1].record(stream)
+        c.run_gather()
+        evs[i][2].record(stream)
+    torch.cuda.synchronize()
+    off_us = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
+    gat_us = [e[1].elapsed_time(e[2]) * 1e3 for e in evs]
+    gather_mean_us = statistics.mean(gat_us)
+    gbytes = gather_bytes_per_launch(w)
+    achieved = gbytes / (gather_mean_us * 1e-6) / 1e9
+    print(f"[bench] per kernel: offsets mean {statistics.mean(off_us):.2f} us, gather mean {gather_mean_us:.2f} us "
+          f"(median {statistics.median(gat_us):.2f}), gather {achieved:.1f} GB/s", file=sys.stderr, flush=True)
+
+    # hot (same buffers every call), labelled as such
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(opt.steps):
+        calls[0].run()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    hot_us = ev0.elapsed_time(ev1) * 1e3 / opt.steps
+
+    # copy ceiling over the same token bytes, same rotation
+    ceiling = None
+    if not opt.no_ceiling:
+        nbytes16 = (w.A * w.token_row_bytes) // 16 * 16
+        srcs = [c.args.tokens for c in calls]
+        dsts = [torch.empty(nbytes16, dtype=torch.uint8, device=dev) for _ in range(n_sets)]
+        bench_lib = ctypes.CDLL(os.path.join(ROOT, "moe_token_re_amd", "libmrr_bench_copy.so"))
+        bench_lib.mrr_bench_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+        bench_lib.mrr_bench_copy.restype = ctypes.c_int
+        hip = ctypes.CDLL("libamdhip64.so")
+        hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                       ctypes.c_void_p]
+        hip.hipMemcpyAsync.restype = ctypes.c_int
+        hip_d2d = 3  # hipMemcpyDeviceToDevice
+        s_ptr = stream.cuda_stream
+        for i in range(10):
+            assert bench_lib.mrr_bench_copy(dsts[i % n_sets].data_ptr(), srcs[i % n_sets], nbytes16, s_ptr) == 0
+            assert hip.hipMemcpyAsync(dsts[i % n_sets].data_ptr(), srcs[i % n_sets], nbytes16, hip_d2d, s_ptr) == 0
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(opt.steps):
+            bench_lib.mrr_bench_copy(dsts[i % n_sets].data_ptr(), srcs[i % n_sets], nbytes16, s_ptr)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        kern_us = ev0.elapsed_time(ev1) * 1e3 / opt.steps
+        ev0.record(stream)
+        for i in range(opt.steps):
+            hip.hipMemcpyAsync(dsts[i % n_sets].data_ptr(), srcs[i % n_sets], nbytes16, hip_d2d, s_ptr)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        memcpy_us = ev0.elapsed_time(ev1) * 1e3 / opt.steps
+        ceil_gbps = max(2 * nbytes16 / (kern_us * 1e-6) / 1e9, 2 * nbytes16 / (memcpy_us * 1e-6) / 1e9)
+        ceiling = {"copy_kernel_us": round(kern_us, 2), "memcpy_d2d_us": round(memcpy_us, 2),
+                   "bytes_read_plus_written": 2 * nbytes16, "ceiling_GBps": round(ceil_gbps, 1),
+                   "gather_frac_of_ceiling": round(achieved / ceil_gbps, 4),
+                   "call_frac_of_ceiling": round(value / ceil_gbps, 4)}
+        print(f"[bench] copy ceiling: kernel {kern_us:.2f} us, hipMemcpyAsync {memcpy_us:.2f} us, "
+              f"{ceil_gbps:.1f} GB/s", file=sys.stderr, flush=True)
+        del dsts
+
+    cpu = None
+    if not opt.no_cpu:
+        med_s, runs = time_oracle(w)
+        cpu = {"value": round(alg_bytes / med_s / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"the full {w.name} workload (one whole call), median of {runs} runs, "
+                         f"{med_s * 1e3:.1f} ms/call; host has {os.cpu_count()} logical CPUs"}
+        print(f"[bench] oracle: {med_s * 1e3:.1f} ms/call on 1 thread", file=sys.stderr, flush=True)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": opt.steps,
+        "warmup": opt.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u8",
+        "data": "synthetic",
+        "config": {"workload": w.name, "A": w.A, "H": w.H, "N": w.N, "E": w.E,
+                   "tokens_dtype": w.tokens_dtype, "counts_dtype": str(w.counts.dtype),
+                   "scales": None if w.scales is None else f"{w.scales_dtype}{list(w.scales.shape)}",
+                   "topk_weight": w.weight is not None, "expert_token_num_type": w.etn_type,
+                   "idx_type": w.idx_type, "buffer_sets": n_sets, "parallelism": "single GPU"},
+        "us_per_call": round(ms_per_step * 1e3, 2),
+        "us_per_call_events": round(ev_ms * 1e3 / opt.steps, 2),
+        "us_per_call_hot_same_buffers": round(hot_us, 2),
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "algorithmic_bytes_per_call": alg_bytes,
+        "offsets_kernel_us_mean": round(statistics.mean(off_us), 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_from_profile(w),
+                     "kernel": "gather_kernel", "bytes_per_launch": gbytes,
+                     "launch_us_mean": round(gather_mean_us, 2)},
+        "copy_ceiling": ceiling,
+        "cpu_baseline": cpu,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

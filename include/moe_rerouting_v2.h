@@ -1,0 +1,192 @@
+/*
+ * moe_rerouting_v2.h -- C ABI of the MoE re-routing operator (MoeReRoutingV2)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What the operator computes (page "CANN ops-transformer MoeReRoutingV2",
+ * nlpx.cn article, sections "功能说明", "计算公式" and "参数说明"):
+ * after the expert-parallel all-to-all a device holds tokens[A, H] ordered by
+ * source rank, and within a rank by local expert. The count matrix
+ * expert_token_num_per_rank[N, E] says how many of those rows came from rank
+ * i for expert j. The operator reorders the rows by expert, and within an
+ * expert by rank:
+ *     permute_tokens[DstOffset(i,j) + k] = tokens[SrcOffset(i,j) + k],
+ *     0 <= k < counts[i][j],
+ * where SrcOffset(i,j) is the number of rows in the cells before (i,j) in
+ * row-major (rank, expert) order and DstOffset(i,j) the number of rows in the
+ * cells before (i,j) in column-major (expert, rank) order. per_token_scales
+ * and expert_topk_weight rows move by the same offsets. The operator also
+ * writes permute_token_idx (gather or scatter form) and expert_token_num (per
+ * expert counts, or their running sum).
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a caller-owned DEVICE pointer on the current HIP
+ *     device; the library never frees, keeps or allocates caller memory, and
+ *     never allocates device memory of its own on the call path.
+ *   - Tensors are dense, row-major, with no padding between rows.
+ *   - Host-detectable errors are returned before anything is launched, and
+ *     then no output is touched.
+ *   - The launching calls are asynchronous and ordered on `stream` (a
+ *     hipStream_t; NULL is the default stream). Errors found on the device
+ *     (bad count values) are recorded in the workspace, the kernels then
+ *     write no output, and mrr_get_device_status() reports them.
+ *   - In-place operation is not supported: inputs, outputs and the workspace
+ *     must not overlap.
+ *   - Calls sharing one workspace must be ordered on one stream; distinct
+ *     workspaces may be used concurrently from several threads.
+ */
+#ifndef MOE_REROUTING_V2_H
+#define MOE_REROUTING_V2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t; /* a hipStream_t is a struct ihipStream_t* */
+
+/* Return codes. */
+typedef enum mrr_status {
+  MRR_SUCCESS = 0,
+  MRR_ERROR_INVALID_VALUE = 1,      /* NULL where a pointer is required, attribute not 0/1,
+                                       weight input/output not paired, overlapping buffers */
+  MRR_ERROR_INVALID_SHAPE = 2,      /* A, H, N, E or a scale shape outside the contract */
+  MRR_ERROR_UNSUPPORTED_DTYPE = 3,  /* a dtype code not allowed for that tensor */
+  MRR_ERROR_MISALIGNED = 4,         /* a typed pointer not aligned to its element size,
+                                       or a workspace not aligned to 16 bytes */
+  MRR_ERROR_WORKSPACE_TOO_SMALL = 5,
+  MRR_ERROR_BAD_COUNTS = 6,         /* found on the device: a negative count, a count above
+                                       INT32_MAX, or counts not summing to A */
+  MRR_ERROR_HIP = 7                 /* a HIP runtime call failed */
+} mrr_status;
+
+/* Element types. Token types follow the operator's prototype (REG_OP section
+ * of the article); only the element width matters to the operator, which
+ * moves bytes: 16 bits (F16, BF16), 8 bits (I8, F8_E5M2, F8_E4M3FN, HIF8) or
+ * 4 bits (F4_E2M1, F4_E1M2, two per byte, low nibble first as stored). */
+typedef enum mrr_dtype {
+  MRR_F16 = 0,
+  MRR_BF16 = 1,
+  MRR_I8 = 2,
+  MRR_F8_E5M2 = 3,
+  MRR_F8_E4M3FN = 4,
+  MRR_HIF8 = 5,
+  MRR_F4_E2M1 = 6,
+  MRR_F4_E1M2 = 7,
+  MRR_I32 = 8,
+  MRR_I64 = 9,
+  MRR_F32 = 10,
+  MRR_F8_E8M0 = 11
+} mrr_dtype;
+
+/*
+ * Arguments of one call, in the order of the operator's prototype: four
+ * inputs, five outputs, two attributes (REG_OP(MoeReRoutingV2) section and
+ * the parameter table "参数说明" of the article).
+ */
+typedef struct mrr_args {
+  /* tokens [A, H]: row r occupies H*bits/8 bytes (fp4: H even, H/2 bytes). */
+  const void* tokens;
+  int32_t tokens_dtype;            /* MRR_F16 .. MRR_F4_E1M2 */
+  int64_t A;                       /* rows; 0 <= A <= INT32_MAX (the index is int32) */
+  int64_t H;                       /* logical elements per row; 0 < H < 16384 */
+
+  /* expert_token_num_per_rank [N, E]: counts[i*E + j] = rows from rank i for
+   * local expert j. Values must be >= 0 (0 = empty segment) and sum to A;
+   * this is checked on the device. N, E >= 0; N*E == 0 requires A == 0. */
+  const void* expert_token_num_per_rank;
+  int32_t counts_dtype;            /* MRR_I32 or MRR_I64 */
+  int64_t N;
+  int64_t E;
+
+  /* per_token_scales, optional (NULL = absent). Shapes:
+   *   MRR_F32,     ndim 1: [A]
+   *   MRR_F32,     ndim 2: [A, S], S >= 1
+   *   MRR_F8_E8M0, ndim 3: [A, ceil(H/64), 2]  (MX block scales of the tokens) */
+  const void* per_token_scales;
+  int32_t scales_dtype;
+  int32_t scales_ndim;
+  int64_t scales_dims[3];
+
+  /* expert_topk_weight [A, 1] fp32, optional (NULL = absent). */
+  const float* expert_topk_weight;
+
+  /* Outputs. */
+  void* permute_tokens;            /* [A, H], tokens' dtype */
+  void* permute_per_token_scales;  /* scales' shape and dtype; may be NULL when the scales
+                                      are absent (the output then has no meaning and is
+                                      never written) */
+  int32_t* permute_token_idx;      /* [A] int32 */
+  void* expert_token_num;          /* [E], counts' dtype */
+  float* permute_topk_weight;      /* [A, 1] fp32; must be NULL exactly when
+                                      expert_topk_weight is NULL */
+
+  /* Attributes. */
+  int64_t expert_token_num_type;   /* 1 (default): rows per expert; 0: inclusive running
+                                      sum of rows per expert (last entry = A) */
+  int64_t idx_type;                /* 0 (default): gather, tokens[idx[d]] lands at row d;
+                                      1: scatter, tokens[s] lands at row idx[s] */
+} mrr_args;
+
+/*
+ * Bytes of device workspace a call with an N x E count matrix needs: a
+ * 256-byte header (validity status of the counts) and two int32 tables of
+ * the per-cell offsets. Returns 0 when N or E is negative or N*E is too
+ * large for 32-bit cell indices. The caller allocates it (no zeroing needed);
+ * it may be reused by calls ordered on one stream.
+ */
+size_t mrr_workspace_size(int64_t N, int64_t E);
+
+/*
+ * The exact checks the launching calls make before they launch anything,
+ * on the host only: no HIP call is made, so this runs without a GPU. The
+ * pointers are compared and tested for alignment, never dereferenced.
+ * Returns MRR_SUCCESS or the first error found.
+ */
+mrr_status mrr_validate(const mrr_args* args, const void* workspace, size_t workspace_bytes);
+
+/*
+ * The whole operator: moe_rerouting_v2_offsets() then moe_rerouting_v2_gather()
+ * on `stream`. Asynchronous. Host-detectable errors are returned before any
+ * launch; count errors are found on the device (see mrr_get_device_status).
+ */
+mrr_status moe_rerouting_v2(const mrr_args* args, void* workspace, size_t workspace_bytes,
+                            struct ihipStream_t* stream);
+
+/*
+ * First phase alone (article, "计算公式": the two double sums): one
+ * workgroup scans the count matrix and writes the SrcOffset and DstOffset
+ * tables and the validity status into the workspace, and expert_token_num
+ * into args->expert_token_num (only when the counts are valid).
+ */
+mrr_status moe_rerouting_v2_offsets(const mrr_args* args, void* workspace, size_t workspace_bytes,
+                                    struct ihipStream_t* stream);
+
+/*
+ * Second phase alone (article, "计算公式": the three moves, and "参数说明":
+ * permute_token_idx): moves the token rows, scale rows and weights and writes
+ * permute_token_idx, from the tables a preceding moe_rerouting_v2_offsets()
+ * call with the same A, N and E wrote into `workspace` on the same stream.
+ * If that call found bad counts, or the workspace holds no tables for this A,
+ * N and E, nothing is written.
+ */
+mrr_status moe_rerouting_v2_gather(const mrr_args* args, void* workspace, size_t workspace_bytes,
+                                   struct ihipStream_t* stream);
+
+/*
+ * Waits for `stream`, then reads the status the last offsets phase left in
+ * `workspace`: MRR_SUCCESS (the counts were valid), MRR_ERROR_BAD_COUNTS,
+ * MRR_ERROR_INVALID_VALUE if the workspace holds no status (no offsets phase
+ * ran on it), or MRR_ERROR_HIP if the copy or the wait fails.
+ * Synchronizing: not for use inside a hot loop.
+ */
+mrr_status mrr_get_device_status(const void* workspace, struct ihipStream_t* stream);
+
+/* A static, human-readable name of a status code. */
+const char* mrr_status_string(mrr_status status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_REROUTING_V2_H */

@@ -1,0 +1,92 @@
+"""ctypes view of the C ABI in include/moe_rerouting_v2.h.
+
+Loads the in-tree libmoe_rerouting_v2.so. There is no fallback: if the library
+has not been built, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe_rerouting_v2.so")
+
+# mrr_status
+SUCCESS = 0
+ERROR_INVALID_VALUE = 1
+ERROR_INVALID_SHAPE = 2
+ERROR_UNSUPPORTED_DTYPE = 3
+ERROR_MISALIGNED = 4
+ERROR_WORKSPACE_TOO_SMALL = 5
+ERROR_BAD_COUNTS = 6
+ERROR_HIP = 7
+
+# mrr_dtype
+F16, BF16, I8, F8_E5M2, F8_E4M3FN, HIF8, F4_E2M1, F4_E1M2, I32, I64, F32, F8_E8M0 = range(12)
+
+EXPORTS = ("mrr_workspace_size", "mrr_validate", "moe_rerouting_v2", "moe_rerouting_v2_offsets",
+           "moe_rerouting_v2_gather", "mrr_get_device_status", "mrr_status_string")
+
+
+class MrrArgs(ctypes.Structure):
+    """struct mrr_args, field for field."""
+
+    _fields_ = [
+        ("tokens", ctypes.c_void_p),
+        ("tokens_dtype", ctypes.c_int32),
+        ("A", ctypes.c_int64),
+        ("H", ctypes.c_int64),
+        ("expert_token_num_per_rank", ctypes.c_void_p),
+        ("counts_dtype", ctypes.c_int32),
+        ("N", ctypes.c_int64),
+        ("E", ctypes.c_int64),
+        ("per_token_scales", ctypes.c_void_p),
+        ("scales_dtype", ctypes.c_int32),
+        ("scales_ndim", ctypes.c_int32),
+        ("scales_dims", ctypes.c_int64 * 3),
+        ("expert_topk_weight", ctypes.c_void_p),
+        ("permute_tokens", ctypes.c_void_p),
+        ("permute_per_token_scales", ctypes.c_void_p),
+        ("permute_token_idx", ctypes.c_void_p),
+        ("expert_token_num", ctypes.c_void_p),
+        ("permute_topk_weight", ctypes.c_void_p),
+        ("expert_token_num_type", ctypes.c_int64),
+        ("idx_type", ctypes.c_int64),
+    ]
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """The loaded library; raises RuntimeError if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                raise RuntimeError(
+                    f"{LIB_PATH} is missing: build it with `python -m moe_token_re_amd.build` "
+                    "(there is no CPU fallback)")
+            lib = ctypes.CDLL(LIB_PATH)
+            P = ctypes.POINTER(MrrArgs)
+            vp, sz = ctypes.c_void_p, ctypes.c_size_t
+            lib.mrr_workspace_size.argtypes = [ctypes.c_int64, ctypes.c_int64]
+            lib.mrr_workspace_size.restype = sz
+            lib.mrr_validate.argtypes = [P, vp, sz]
+            lib.mrr_validate.restype = ctypes.c_int
+            for name in ("moe_rerouting_v2", "moe_rerouting_v2_offsets", "moe_rerouting_v2_gather"):
+                fn = getattr(lib, name)
+                fn.argtypes = [P, vp, sz, vp]
+                fn.restype = ctypes.c_int
+            lib.mrr_get_device_status.argtypes = [vp, vp]
+            lib.mrr_get_device_status.restype = ctypes.c_int
+            lib.mrr_status_string.argtypes = [ctypes.c_int]
+            lib.mrr_status_string.restype = ctypes.c_char_p
+            _lib = lib
+        return _lib
+
+
+def status_string(code: int) -> str:
+    return load().mrr_status_string(code).decode()

@@ -1,0 +1,235 @@
+// mrr_validate.cpp -- host-side argument checks, workspace sizing and launch
+// planning of the MoE re-routing operator. This file includes no HIP header
+// and makes no HIP call, so every check runs (and is tested) without a GPU.
+//
+// The contract checked here is the operator's (page "CANN ops-transformer
+// MoeReRoutingV2", nlpx.cn article): the parameter table "参数说明" (dtypes,
+// shapes, optional inputs, the pairing of expert_topk_weight and
+// permute_topk_weight), "约束说明" (0 < H < 16384, Sum(counts) == A, the
+// attributes) and the InferShape rules (output shapes follow the inputs).
+// Count values live on the device and are checked there by the offsets kernel.
+#include <stdio.h>
+#include <stdlib.h>
+
+#include <algorithm>
+
+#include "mrr_internal.h"
+
+namespace {
+
+using mrr::round_up;
+
+constexpr int64_t kMaxCells = int64_t(1) << 30;
+constexpr int64_t kMaxH = 16384;  // exclusive bound of the contract
+
+int token_bits(int32_t dt) {
+  switch (dt) {
+    case MRR_F16:
+    case MRR_BF16:
+      return 16;
+    case MRR_I8:
+    case MRR_F8_E5M2:
+    case MRR_F8_E4M3FN:
+    case MRR_HIF8:
+      return 8;
+    case MRR_F4_E2M1:
+    case MRR_F4_E1M2:
+      return 4;
+    default:
+      return 0;
+  }
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+  bool is_output;
+};
+
+bool overlaps(const Range& x, const Range& y) { return x.lo < y.hi && y.lo < x.hi; }
+
+int env_int(const char* name, int fallback) {
+  const char* s = getenv(name);
+  if (s == nullptr || *s == '\0') return fallback;
+  return atoi(s);
+}
+
+// Tuning overrides, read once per process. They change the launch shape only,
+// never a result.
+struct Tuning {
+  int rows_per_wg;  // 0 = automatic
+  bool log;
+  Tuning() : rows_per_wg(env_int("MRR_ROWS_PER_WG", 0)), log(env_int("MRR_LOG", 0) != 0) {}
+};
+
+const Tuning& tuning() {
+  static const Tuning t;
+  return t;
+}
+
+int widest_vec(int64_t bytes, const void* a, const void* b) {
+  for (int v = 16; v > 1; v /= 2)
+    if (bytes % v == 0 && aligned(a, v) && aligned(b, v)) return v;
+  return 1;
+}
+
+}  // namespace
+
+extern "C" size_t mrr_workspace_size(int64_t N, int64_t E) {
+  if (N < 0 || E < 0) return 0;
+  if (N != 0 && E > kMaxCells / N) return 0;
+  const size_t M = static_cast<size_t>(N * E);
+  return mrr::kHeaderBytes + round_up(4 * (M + 1), 256) + round_up(4 * M, 256);
+}
+
+extern "C" const char* mrr_status_string(mrr_status s) {
+  switch (s) {
+    case MRR_SUCCESS: return "MRR_SUCCESS";
+    case MRR_ERROR_INVALID_VALUE: return "MRR_ERROR_INVALID_VALUE";
+    case MRR_ERROR_INVALID_SHAPE: return "MRR_ERROR_INVALID_SHAPE";
+    case MRR_ERROR_UNSUPPORTED_DTYPE: return "MRR_ERROR_UNSUPPORTED_DTYPE";
+    case MRR_ERROR_MISALIGNED: return "MRR_ERROR_MISALIGNED";
+    case MRR_ERROR_WORKSPACE_TOO_SMALL: return "MRR_ERROR_WORKSPACE_TOO_SMALL";
+    case MRR_ERROR_BAD_COUNTS: return "MRR_ERROR_BAD_COUNTS";
+    case MRR_ERROR_HIP: return "MRR_ERROR_HIP";
+  }
+  return "MRR_ERROR_UNKNOWN";
+}
+
+namespace mrr {
+
+mrr_status make_plan(const mrr_args* a, const void* ws, size_t ws_bytes, Plan* p) {
+  if (a == nullptr || p == nullptr) return MRR_ERROR_INVALID_VALUE;
+
+  // dtypes (parameter table and the REG_OP prototype)
+  const int bits = token_bits(a->tokens_dtype);
+  if (bits == 0) return MRR_ERROR_UNSUPPORTED_DTYPE;
+  if (a->counts_dtype != MRR_I32 && a->counts_dtype != MRR_I64) return MRR_ERROR_UNSUPPORTED_DTYPE;
+  const int cb = a->counts_dtype == MRR_I64 ? 8 : 4;
+
+  // attributes
+  if (a->expert_token_num_type != 0 && a->expert_token_num_type != 1) return MRR_ERROR_INVALID_VALUE;
+  if (a->idx_type != 0 && a->idx_type != 1) return MRR_ERROR_INVALID_VALUE;
+
+  // shapes ("约束说明": 0 < H < 16384; Sum(counts) == A, with int32 indices)
+  if (a->A < 0 || a->A > INT32_MAX) return MRR_ERROR_INVALID_SHAPE;
+  if (a->H <= 0 || a->H >= kMaxH) return MRR_ERROR_INVALID_SHAPE;
+  if (bits == 4 && (a->H % 2) != 0) return MRR_ERROR_INVALID_SHAPE;
+  if (a->N < 0 || a->E < 0) return MRR_ERROR_INVALID_SHAPE;
+  if (a->N != 0 && a->E > kMaxCells / a->N) return MRR_ERROR_INVALID_SHAPE;
+  const int64_t M = a->N * a->E;
+  if (M == 0 && a->A != 0) return MRR_ERROR_INVALID_SHAPE;
+  const int64_t R = a->H * bits / 8;
+
+  // optional scales: [A] f32, [A, S] f32, or [A, ceil(H/64), 2] e8m0
+  int64_t Rs = 0;
+  if (a->per_token_scales != nullptr) {
+    if (a->scales_dtype == MRR_F32) {
+      if (a->scales_ndim == 1) {
+        if (a->scales_dims[0] != a->A) return MRR_ERROR_INVALID_SHAPE;
+        Rs = 4;
+      } else if (a->scales_ndim == 2) {
+        if (a->scales_dims[0] != a->A || a->scales_dims[1] < 1 || a->scales_dims[1] > (1 << 24))
+          return MRR_ERROR_INVALID_SHAPE;
+        Rs = 4 * a->scales_dims[1];
+      } else {
+        return MRR_ERROR_INVALID_SHAPE;
+      }
+    } else if (a->scales_dtype == MRR_F8_E8M0) {
+      if (a->scales_ndim != 3 || a->scales_dims[0] != a->A || a->scales_dims[1] != (a->H + 63) / 64 ||
+          a->scales_dims[2] != 2)
+        return MRR_ERROR_INVALID_SHAPE;
+      Rs = 2 * a->scales_dims[1];
+    } else {
+      return MRR_ERROR_UNSUPPORTED_DTYPE;
+    }
+    if (a->A > 0 && a->permute_per_token_scales == nullptr) return MRR_ERROR_INVALID_VALUE;
+  }
+
+  // expert_topk_weight and permute_topk_weight come together or not at all
+  const bool has_w = a->expert_topk_weight != nullptr;
+  if (has_w != (a->permute_topk_weight != nullptr)) return MRR_ERROR_INVALID_VALUE;
+
+  // required pointers
+  if (ws == nullptr) return MRR_ERROR_INVALID_VALUE;
+  if (a->A > 0 && (a->tokens == nullptr || a->permute_tokens == nullptr || a->permute_token_idx == nullptr))
+    return MRR_ERROR_INVALID_VALUE;
+  if (M > 0 && a->expert_token_num_per_rank == nullptr) return MRR_ERROR_INVALID_VALUE;
+  if (a->E > 0 && a->expert_token_num == nullptr) return MRR_ERROR_INVALID_VALUE;
+
+  // alignment of typed elements
+  if (!aligned(ws, 16)) return MRR_ERROR_MISALIGNED;
+  if (!aligned(a->expert_token_num_per_rank, cb) || !aligned(a->expert_token_num, cb)) return MRR_ERROR_MISALIGNED;
+  if (!aligned(a->permute_token_idx, 4)) return MRR_ERROR_MISALIGNED;
+  if (has_w && (!aligned(a->expert_topk_weight, 4) || !aligned(a->permute_topk_weight, 4)))
+    return MRR_ERROR_MISALIGNED;
+  if (Rs > 0 && a->scales_dtype == MRR_F32 &&
+      (!aligned(a->per_token_scales, 4) || !aligned(a->permute_per_token_scales, 4)))
+    return MRR_ERROR_MISALIGNED;
+
+  // workspace size
+  const size_t need = mrr_workspace_size(a->N, a->E);
+  if (need == 0 || ws_bytes < need) return MRR_ERROR_WORKSPACE_TOO_SMALL;
+
+  // no output may overlap any other buffer
+  Range r[10];
+  int nr = 0;
+  auto add = [&](const void* ptr, int64_t bytes, bool out) {
+    if (ptr != nullptr && bytes > 0) {
+      uintptr_t lo = reinterpret_cast<uintptr_t>(ptr);
+      r[nr++] = Range{lo, lo + static_cast<uintptr_t>(bytes), out};
+    }
+  };
+  add(a->tokens, a->A * R, false);
+  add(a->expert_token_num_per_rank, M * cb, false);
+  if (Rs > 0) add(a->per_token_scales, a->A * Rs, false);
+  if (has_w) add(a->expert_topk_weight, a->A * 4, false);
+  add(a->permute_tokens, a->A * R, true);
+  if (Rs > 0) add(a->permute_per_token_scales, a->A * Rs, true);
+  add(a->permute_token_idx, a->A * 4, true);
+  add(a->expert_token_num, a->E * cb, true);
+  if (has_w) add(a->permute_topk_weight, a->A * 4, true);
+  add(ws, static_cast<int64_t>(need), true);
+  for (int x = 0; x < nr; ++x)
+    for (int y = x + 1; y < nr; ++y)
+      if ((r[x].is_output || r[y].is_output) && overlaps(r[x], r[y])) return MRR_ERROR_INVALID_VALUE;
+
+  // the launch plan
+  Plan q{};
+  q.A = a->A;
+  q.N = a->N;
+  q.E = a->E;
+  q.M = M;
+  q.row_bytes = R;
+  q.token_vec = widest_vec(R, a->tokens, a->permute_tokens);
+  q.vecs_per_row = R / q.token_vec;
+  q.scale_row_bytes = Rs;
+  q.scale_vec = Rs > 0 ? widest_vec(Rs, a->per_token_scales, a->permute_per_token_scales) : 1;
+  q.count_bytes = cb;
+  q.has_weight = has_w;
+  q.scatter = a->idx_type == 1;
+  q.cumsum = a->expert_token_num_type == 0;
+  int64_t rows = int64_t(kGatherThreads) * kGatherUnroll / q.vecs_per_row;
+  if (tuning().rows_per_wg > 0) rows = tuning().rows_per_wg;
+  q.rows_per_wg = static_cast<int>(std::min<int64_t>(std::max<int64_t>(rows, 1), kMaxRowsPerWg));
+  q.grid = (q.A + q.rows_per_wg - 1) / q.rows_per_wg;
+  q.dst_off_bytes = kHeaderBytes;
+  q.src_off_bytes = kHeaderBytes + round_up(4 * (static_cast<size_t>(M) + 1), 256);
+  *p = q;
+
+  if (tuning().log)
+    fprintf(stderr,
+            "[mrr] A=%lld N=%lld E=%lld R=%lld vec=%d rows/wg=%d grid=%lld Rs=%lld svec=%d w=%d scatter=%d\n",
+            (long long)q.A, (long long)q.N, (long long)q.E, (long long)q.row_bytes, q.token_vec,
+            q.rows_per_wg, (long long)q.grid, (long long)q.scale_row_bytes, q.scale_vec,
+            (int)q.has_weight, (int)q.scatter);
+  return MRR_SUCCESS;
+}
+
+}  // namespace mrr
+
+extern "C" mrr_status mrr_validate(const mrr_args* args, const void* workspace, size_t workspace_bytes) {
+  mrr::Plan plan;
+  return mrr::make_plan(args, workspace, workspace_bytes, &plan);
+}

@@ -1,0 +1,211 @@
+"""The C-ABI library on the host, without a GPU: it loads, exports every
+function include/moe_rerouting_v2.h declares, and its host checks
+(mrr_validate, the same checks every launching call makes first) accept the
+operator's contract and reject everything outside it with the right code.
+
+Pointers here are fake addresses: mrr_validate compares them and tests their
+alignment but never dereferences them, and makes no HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from moe_token_re_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+INCLUDE = os.path.join(ROOT, "include")
+HEADER = os.path.join(INCLUDE, "moe_rerouting_v2.h")
+# header -> the library that must export what it declares
+LIBRARIES = {"moe_rerouting_v2.h": _lib.LIB_PATH,
+             "mrr_bench_copy.h": os.path.join(os.path.dirname(_lib.LIB_PATH), "libmrr_bench_copy.so")}
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="library not built")
+
+
+def declared_functions(header=HEADER):
+    text = open(header).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+
+
+def test_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS), names
+    headers = sorted(f for f in os.listdir(INCLUDE) if f.endswith(".h"))
+    assert headers == sorted(LIBRARIES), headers
+    for h in headers:
+        lib = ctypes.CDLL(LIBRARIES[h])
+        for n in declared_functions(os.path.join(INCLUDE, h)):
+            assert hasattr(lib, n), (h, n)
+
+
+def test_status_strings():
+    for code, name in [(0, "MRR_SUCCESS"), (1, "MRR_ERROR_INVALID_VALUE"), (2, "MRR_ERROR_INVALID_SHAPE"),
+                       (3, "MRR_ERROR_UNSUPPORTED_DTYPE"), (4, "MRR_ERROR_MISALIGNED"),
+                       (5, "MRR_ERROR_WORKSPACE_TOO_SMALL"), (6, "MRR_ERROR_BAD_COUNTS"), (7, "MRR_ERROR_HIP")]:
+        assert _lib.status_string(code) == name
+
+
+def test_workspace_size():
+    L = _lib.load()
+    # 256-byte header + round_up(4*(M+1), 256) + round_up(4*M, 256)
+    assert L.mrr_workspace_size(16, 16) == 256 + 1280 + 1024
+    assert L.mrr_workspace_size(256, 64) == 256 + 65792 + 65536
+    assert L.mrr_workspace_size(0, 5) == 256 + 256 + 0
+    assert L.mrr_workspace_size(-1, 4) == 0
+    assert L.mrr_workspace_size(1 << 20, 1 << 20) == 0
+
+
+# Fake device addresses, far apart so that no two buffers overlap.
+BASE = {"tokens": 0x1000000000, "counts": 0x2000000000, "scales": 0x3000000000, "weight": 0x4000000000,
+        "p_tokens": 0x5000000000, "p_scales": 0x6000000000, "idx": 0x7000000000, "etn": 0x8000000000,
+        "p_weight": 0x9000000000, "ws": 0xA000000000}
+
+
+def valid_args(A=64, H=128, N=2, E=4, tok=_lib.F16, cnt=_lib.I32, scales="f32", weight=True):
+    a = _lib.MrrArgs()
+    a.tokens, a.tokens_dtype, a.A, a.H = BASE["tokens"], tok, A, H
+    a.expert_token_num_per_rank, a.counts_dtype, a.N, a.E = BASE["counts"], cnt, N, E
+    if scales == "f32":
+        a.per_token_scales, a.scales_dtype, a.scales_ndim = BASE["scales"], _lib.F32, 1
+        a.scales_dims[0] = A
+    elif scales == "e8m0":
+        a.per_token_scales, a.scales_dtype, a.scales_ndim = BASE["scales"], _lib.F8_E8M0, 3
+        a.scales_dims[0], a.scales_dims[1], a.scales_dims[2] = A, (H + 63) // 64, 2
+    if scales:
+        a.permute_per_token_scales = BASE["p_scales"]
+    if weight:
+        a.expert_topk_weight, a.permute_topk_weight = BASE["weight"], BASE["p_weight"]
+    a.permute_tokens, a.permute_token_idx, a.expert_token_num = BASE["p_tokens"], BASE["idx"], BASE["etn"]
+    a.expert_token_num_type, a.idx_type = 1, 0
+    return a
+
+
+def validate(a, ws=BASE["ws"], ws_bytes=None):
+    L = _lib.load()
+    if ws_bytes is None:
+        ws_bytes = L.mrr_workspace_size(max(a.N, 0), max(a.E, 0))
+    return L.mrr_validate(ctypes.byref(a), ws, ws_bytes)
+
+
+def test_valid_configurations():
+    assert validate(valid_args()) == _lib.SUCCESS
+    assert validate(valid_args(scales=None, weight=False)) == _lib.SUCCESS
+    assert validate(valid_args(A=16384, H=7168, N=16, E=16, tok=_lib.I8)) == _lib.SUCCESS
+    assert validate(valid_args(A=32768, H=7168, N=32, E=8, tok=_lib.F8_E4M3FN, scales="e8m0")) == _lib.SUCCESS
+    assert validate(valid_args(A=65536, H=2048, N=256, E=64, tok=_lib.F4_E2M1)) == _lib.SUCCESS
+    assert validate(valid_args(H=79, scales="e8m0")) == _lib.SUCCESS   # odd rows, 2 scale pairs
+    assert validate(valid_args(H=16383, tok=_lib.I8)) == _lib.SUCCESS
+    a = valid_args(A=0, N=3, E=2)
+    assert validate(a) == _lib.SUCCESS                                 # empty input
+    a = valid_args(A=0, N=0, E=3)
+    assert validate(a) == _lib.SUCCESS
+    a = valid_args(A=0, N=0, E=0)
+    a.expert_token_num = None
+    assert validate(a) == _lib.SUCCESS
+    for t in range(_lib.F16, _lib.F4_E1M2 + 1):
+        assert validate(valid_args(tok=t)) == _lib.SUCCESS
+    a = valid_args()
+    a.scales_ndim, a.scales_dims[1] = 2, 32
+    assert validate(a) == _lib.SUCCESS
+    a = valid_args(scales=None)
+    a.permute_per_token_scales = None                                  # absent scales: output unused
+    assert validate(a) == _lib.SUCCESS
+    a = valid_args(scales=None)
+    a.permute_per_token_scales = BASE["p_scales"]
+    assert validate(a) == _lib.SUCCESS
+    a = valid_args(tok=_lib.I8, H=33)
+    a.tokens += 1                                                      # byte rows: any alignment
+    a.permute_tokens += 3
+    assert validate(a) == _lib.SUCCESS
+
+
+def _with(f, **kw):
+    a = valid_args(**kw)
+    f(a)
+    return a
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda a: setattr(a, "tokens_dtype", _lib.I32), _lib.ERROR_UNSUPPORTED_DTYPE),
+    (lambda a: setattr(a, "tokens_dtype", 99), _lib.ERROR_UNSUPPORTED_DTYPE),
+    (lambda a: setattr(a, "counts_dtype", _lib.F32), _lib.ERROR_UNSUPPORTED_DTYPE),
+    (lambda a: setattr(a, "scales_dtype", _lib.F16), _lib.ERROR_UNSUPPORTED_DTYPE),
+    (lambda a: setattr(a, "expert_token_num_type", 2), _lib.ERROR_INVALID_VALUE),
+    (lambda a: setattr(a, "idx_type", -1), _lib.ERROR_INVALID_VALUE),
+    (lambda a: setattr(a, "H", 0), _lib.ERROR_INVALID_SHAPE),
+    (lambda a: setattr(a, "H", 16384), _lib.ERROR_INVALID_SHAPE),
+    (lambda a: setattr(a, "A", -1), _lib.ERROR_INVALID_SHAPE),
+    (lambda a: setattr(a, "A", 1 << 31), _lib.ERROR_INVALID_SHAPE),
+    (lambda a: setattr(a, "N", -2), _lib.ERROR_INVALID_SHAPE),
+    (lambda a: (setattr(a, "N", 0)), _lib.ERROR_INVALID_SHAPE),          # no cells but A > 0
+    (lambda a: setattr(a, "scales_ndim", 4), _lib.ERROR_INVALID_SHAPE),
+    (lambda a: a.scales_dims.__setitem__(0, 63), _lib.ERROR_INVALID_SHAPE),
+    (lambda a: (setattr(a, "scales_ndim", 2), a.scales_dims.__setitem__(1, 0)), _lib.ERROR_INVALID_SHAPE),
+    (lambda a: setattr(a, "permute_topk_weight", None), _lib.ERROR_INVALID_VALUE),
+    (lambda a: setattr(a, "expert_topk_weight", None), _lib.ERROR_INVALID_VALUE),
+    (lambda a: setattr(a, "permute_per_token_scales", None), _lib.ERROR_INVALID_VALUE),
+    (lambda a: setattr(a, "tokens", None), _lib.ERROR_INVALID_VALUE),
+    (lambda a: setattr(a, "permute_tokens", None), _lib.ERROR_INVALID_VALUE),
+    (lambda a: setattr(a, "permute_token_idx", None), _lib.ERROR_INVALID_VALUE),
+    (lambda a: setattr(a, "expert_token_num", None), _lib.ERROR_INVALID_VALUE),
+    (lambda a: setattr(a, "expert_token_num_per_rank", None), _lib.ERROR_INVALID_VALUE),
+    (lambda a: setattr(a, "permute_token_idx", BASE["idx"] + 2), _lib.ERROR_MISALIGNED),
+    (lambda a: setattr(a, "expert_token_num_per_rank", BASE["counts"] + 2), _lib.ERROR_MISALIGNED),
+    (lambda a: setattr(a, "expert_token_num", BASE["etn"] + 1), _lib.ERROR_MISALIGNED),
+    (lambda a: setattr(a, "expert_topk_weight", BASE["weight"] + 2), _lib.ERROR_MISALIGNED),
+    (lambda a: setattr(a, "permute_per_token_scales", BASE["p_scales"] + 1), _lib.ERROR_MISALIGNED),
+    # overlaps: an output over an input, over another output, over the workspace
+    (lambda a: setattr(a, "permute_tokens", BASE["tokens"] + 64), _lib.ERROR_INVALID_VALUE),
+    (lambda a: setattr(a, "permute_token_idx", BASE["p_tokens"] + 1024), _lib.ERROR_INVALID_VALUE),
+    (lambda a: setattr(a, "expert_token_num", BASE["ws"] + 16), _lib.ERROR_INVALID_VALUE),
+    (lambda a: setattr(a, "permute_topk_weight", BASE["counts"]), _lib.ERROR_INVALID_VALUE),
+])
+def test_rejections(mutate, code):
+    a = valid_args()
+    mutate(a)
+    assert validate(a) == code
+
+
+def test_int64_counts_alignment():
+    a = valid_args(cnt=_lib.I64)
+    assert validate(a) == _lib.SUCCESS
+    a.expert_token_num_per_rank = BASE["counts"] + 4
+    assert validate(a) == _lib.ERROR_MISALIGNED
+
+
+def test_fp4_needs_even_h():
+    assert validate(valid_args(tok=_lib.F4_E2M1, H=77)) == _lib.ERROR_INVALID_SHAPE
+    assert validate(valid_args(tok=_lib.F4_E1M2, H=78)) == _lib.SUCCESS
+
+
+def test_e8m0_shape_follows_h():
+    a = valid_args(H=128, scales="e8m0")
+    a.scales_dims[1] = 3
+    assert validate(a) == _lib.ERROR_INVALID_SHAPE
+    a = valid_args(H=128, scales="e8m0")
+    a.scales_dims[2] = 1
+    assert validate(a) == _lib.ERROR_INVALID_SHAPE
+
+
+def test_workspace_checks():
+    a = valid_args()
+    need = _lib.load().mrr_workspace_size(2, 4)
+    assert validate(a, ws_bytes=need - 1) == _lib.ERROR_WORKSPACE_TOO_SMALL
+    assert validate(a, ws=None) == _lib.ERROR_INVALID_VALUE
+    assert validate(a, ws=BASE["ws"] + 8) == _lib.ERROR_MISALIGNED
+    assert validate(a, ws=BASE["tokens"] + 128) == _lib.ERROR_INVALID_VALUE   # overlaps tokens
+
+
+def test_launch_entry_points_reject_before_launch():
+    """The launching calls run the same checks first: with bad arguments they
+    return the error without touching the GPU (none is present here)."""
+    L = _lib.load()
+    a = valid_args()
+    a.idx_type = 5
+    ws = BASE["ws"]
+    nb = L.mrr_workspace_size(2, 4)
+    for fn in (L.moe_rerouting_v2, L.moe_rerouting_v2_offsets, L.moe_rerouting_v2_gather):
+        assert fn(ctypes.byref(a), ws, nb, None) == _lib.ERROR_INVALID_VALUE
+    assert L.mrr_get_device_status(None, None) == _lib.ERROR_INVALID_VALUE

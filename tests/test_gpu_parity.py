@@ -1,0 +1,283 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, byte for byte.
+
+Every output the operator defines is compared raw-byte-exact (tolerance 0: the
+operator only moves bytes and computes integer offsets), on seeded inputs:
+  * the five named workloads at their full sizes, in the launch configuration
+    the benchmark times;
+  * a seeded fuzz over the contract: token widths 16/8/4 bits, int32/int64
+    counts, scale layouts [A] / [A,S] / e8m0, weights on/off, both index forms,
+    both expert_token_num modes, empty segments, odd row sizes and unaligned
+    rows, the (N, E) pairs and (A, H) shapes the article's tests name;
+  * edge cases: A = 0, N = 0, one rank, one expert, count tables too large
+    for LDS, long runs of empty cells;
+  * device-detected count errors: outputs are left untouched.
+permute_per_token_scales is not compared when no scales are given: the
+operator defines no value for it then."""
+import numpy as np
+import pytest
+import torch
+
+from moe_token_re_amd import _lib, api, workloads
+from oracle import oracle
+
+pytestmark = pytest.mark.gpu
+
+SENTINEL = 0xA5
+
+
+def _dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def _bytes(t):
+    return t.contiguous().view(-1).view(torch.uint8).cpu().numpy()
+
+
+def _np_bytes(a):
+    return np.ascontiguousarray(a).view(np.uint8).reshape(-1)
+
+
+def run_hip(w: workloads.Workload, dev, phases=False):
+    """Runs the HIP path on a workload with outputs pre-filled with a sentinel.
+    Returns (outputs on the host as raw bytes, the device status code)."""
+    print(f"[hip] {w.name} A={w.A} H={w.H} N={w.N} E={w.E} tok={w.tokens_dtype} "
+          f"scales={w.scales_dtype} w={w.weight is not None} etn={w.etn_type} idx={w.idx_type}", flush=True)
+    t = workloads.torch_inputs(w, dev)
+    args, outs = api.prepare(t["tokens"], t["counts"], per_token_scales=t["scales"],
+                             expert_topk_weight=t["weight"], expert_token_num_type=w.etn_type,
+                             idx_type=w.idx_type, tokens_dtype=t["tokens_dtype"])
+    for o in outs:
+        if o.numel():
+            o.view(-1).view(torch.uint8).fill_(SENTINEL)
+    call, outs = api.make_call(t["tokens"], t["counts"], per_token_scales=t["scales"],
+                               expert_topk_weight=t["weight"], expert_token_num_type=w.etn_type,
+                               idx_type=w.idx_type, tokens_dtype=t["tokens_dtype"], out=outs)
+    if phases:
+        call.run_offsets()
+        call.run_gather()
+    else:
+        call.run()
+    status = call.device_status()
+    torch.cuda.synchronize()
+    return [_bytes(o) for o in outs], status
+
+
+def run_oracle(w: workloads.Workload):
+    return oracle.reroute(w.tokens, w.counts, w.scales, w.weight, w.etn_type, w.idx_type)
+
+
+def assert_parity(w, hip_out, ref):
+    p_tok, p_sc, p_idx, p_etn, p_w = hip_out
+    r_tok, r_sc, r_idx, r_etn, r_w = ref
+    assert np.array_equal(p_tok, _np_bytes(r_tok)), f"{w.name}: permute_tokens differ"
+    assert np.array_equal(p_idx.view(np.int32), r_idx), f"{w.name}: permute_token_idx differ"
+    assert np.array_equal(p_etn, _np_bytes(r_etn)), f"{w.name}: expert_token_num differ"
+    if w.scales is not None:
+        assert np.array_equal(p_sc, _np_bytes(r_sc)), f"{w.name}: permute_per_token_scales differ"
+    if w.weight is not None:
+        assert np.array_equal(p_w, _np_bytes(r_w)), f"{w.name}: permute_topk_weight differ"
+    else:
+        assert p_w.size == 0
+
+
+def check(w, phases=False):
+    dev = _dev()
+    hip_out, status = run_hip(w, dev, phases)
+    assert status == _lib.SUCCESS, _lib.status_string(status)
+    assert_parity(w, hip_out, run_oracle(w))
+
+
+# --- the five named workloads, full size ---------------------------------
+
+@pytest.mark.parametrize("name", list(workloads.CONFIGS))
+def test_named_workload_full_size(name):
+    check(workloads.make(name))
+
+
+def test_two_phases_equal_whole_call():
+    check(workloads.make("tiny_segments"), phases=True)
+
+
+# --- seeded fuzz over the contract ----------------------------------------
+
+TOKEN_KINDS = ["float16", "bfloat16", "int8", "float8_e5m2", "float8_e4m3fn", "hifloat8",
+               "float4_e2m1fn_x2", "float4_e1m2fn_x2"]
+
+
+def fuzz_cases():
+    rng = np.random.default_rng(2024)
+    cases = []
+    ne_pairs = [(4, 2), (23, 2), (14, 1), (2, 4), (16, 16), (7, 13), (1, 9), (33, 5)]
+    for k in range(48):
+        n, e = ne_pairs[k % len(ne_pairs)]
+        tok = TOKEN_KINDS[k % len(TOKEN_KINDS)]
+        h = int(rng.choice([2, 8, 64, 79, 128, 130, 1000, 2048, 7168, 16382]))
+        if tok.startswith("float4") and h % 2:
+            h += 1
+        scales = [None, "a", "as", "e8m0"][k % 4]
+        cases.append(dict(seed=1000 + k, N=n, E=e, H=h, tokens_dtype=tok,
+                          counts_dtype=np.int64 if k % 3 == 0 else np.int32,
+                          count_range=(0, 9) if k % 2 else (1, 40), scales=scales,
+                          S=int(rng.integers(1, 40)), weight=bool(k % 5 != 0),
+                          etn_type=int(k % 7 == 0) ^ 1, idx_type=int(k % 2 == 1)))
+    return cases
+
+
+@pytest.mark.parametrize("case", fuzz_cases(), ids=lambda c: f"s{c['seed']}")
+def test_fuzz(case):
+    check(workloads.random_case(**case))
+
+
+# Shapes named by the article's tests ("测试与验证"): (52, 21), (35, 15267),
+# (28, 6057), read both ways as (A, H); (N, E) in {(4,2), (23,2), (14,1)}.
+@pytest.mark.parametrize("a,h", [(52, 21), (21, 52), (35, 15267), (15267, 35), (28, 6057), (6057, 28)])
+@pytest.mark.parametrize("ne", [(4, 2), (23, 2), (14, 1)])
+def test_article_test_shapes(a, h, ne):
+    n, e = ne
+    rng = np.random.default_rng(a * 7 + h)
+    # counts >= 0 summing to a: a multinomial over the n*e cells
+    counts = rng.multinomial(a, [1.0 / (n * e)] * (n * e)).reshape(n, e).astype(np.int32)
+    raw = rng.integers(0, 256, (a, 2 * h), dtype=np.uint8)
+    w = workloads.Workload(f"article_{a}x{h}_{n}x{e}", counts, raw.view(np.float16), "float16", h,
+                           rng.standard_normal(a, dtype=np.float32), "float32",
+                           rng.random((a, 1), dtype=np.float32), 1, (a + h) % 2)
+    check(w)
+
+
+def test_geir_sample_shape():
+    """Graph-mode sample: A=11, H=79, N=11, E=1, S=1 (scales [A, 1] f32)."""
+    rng = np.random.default_rng(11)
+    counts = np.ones((11, 1), np.int32)
+    w = workloads.Workload("geir", counts, rng.standard_normal((11, 79)).astype(np.float16), "float16", 79,
+                           rng.standard_normal((11, 1), dtype=np.float32), "float32",
+                           rng.random((11, 1), dtype=np.float32), 1, 0)
+    check(w)
+
+
+# --- edge cases -----------------------------------------------------------
+
+def test_empty_all_zero_counts():
+    w = workloads.random_case(7, 5, 3, 64, count_range=(0, 1))
+    assert w.A == 0
+    check(w)
+
+
+def test_zero_ranks():
+    w = workloads.Workload("n0", np.zeros((0, 6), np.int64), np.zeros((0, 32), np.float16), "float16", 32,
+                           etn_type=0)
+    check(w)
+
+
+@pytest.mark.parametrize("shape", [(1, 300), (300, 1), (1, 1)])
+def test_single_rank_or_expert(shape):
+    check(workloads.random_case(31, shape[0], shape[1], 256, tokens_dtype="bfloat16", count_range=(0, 7),
+                                scales="as", S=3, weight=True, idx_type=1))
+
+
+def test_large_table_unstaged():
+    """N*E = 131072 cells: more counts than fit in LDS, mostly empty, so the
+    row search runs across long stretches of empty cells."""
+    rng = np.random.default_rng(77)
+    counts = np.zeros((512, 256), np.int32)
+    cells = rng.choice(512 * 256, 900, replace=False)
+    counts.reshape(-1)[cells] = rng.integers(1, 30, 900)
+    a = int(counts.sum())
+    tok = rng.integers(0, 256, (a, 96), dtype=np.uint8)
+    w = workloads.Workload("large_table", counts, tok, "int8", 96, None, None,
+                           rng.random((a, 1), dtype=np.float32), 0, 0)
+    check(w)
+
+
+def test_sparse_cells_window_fallback():
+    """Rows whose cells lie more than 64 cells apart inside one 64-row batch."""
+    counts = np.zeros((40, 100), np.int64)
+    counts[0, 0] = 3
+    counts[39, 99] = 70
+    counts[20, 50] = 1
+    a = int(counts.sum())
+    rng = np.random.default_rng(5)
+    w = workloads.Workload("sparse", counts, rng.integers(0, 256, (a, 16), dtype=np.uint8), "int8", 16,
+                           idx_type=1)
+    check(w)
+
+
+def test_repeat_calls_identical():
+    dev = _dev()
+    w = workloads.random_case(99, 8, 8, 512, tokens_dtype="int8", scales="e8m0", weight=True)
+    first, _ = run_hip(w, dev)
+    second, _ = run_hip(w, dev)
+    for x, y in zip(first, second):
+        assert np.array_equal(x, y)
+
+
+# --- device-detected count errors -------------------------------------------
+
+@pytest.mark.parametrize("kind", ["negative", "sum_low", "sum_high", "too_large"])
+def test_bad_counts_write_nothing(kind):
+    dev = _dev()
+    rng = np.random.default_rng(3)
+    counts = rng.integers(1, 5, (4, 3)).astype(np.int64)
+    a = int(counts.sum())
+    if kind == "negative":
+        counts[1, 1] = -counts[1, 1]
+        counts[2, 2] += 2 * abs(counts[1, 1])    # keep the sum at a
+    elif kind == "sum_low":
+        counts[0, 0] -= 1
+    elif kind == "sum_high":
+        counts[0, 0] += 1
+    else:
+        counts[3, 2] = (1 << 32) + counts[3, 2]  # above INT32_MAX
+    tok = rng.integers(0, 256, (a, 64), dtype=np.uint8)
+    w = workloads.Workload(f"bad_{kind}", counts, tok, "int8", 64,
+                           rng.standard_normal(a, dtype=np.float32), "float32",
+                           rng.random((a, 1), dtype=np.float32), 1, 0)
+    out, status = run_hip(w, dev)
+    assert status == _lib.ERROR_BAD_COUNTS
+    for o in out:
+        assert (o == SENTINEL).all(), kind
+
+
+def test_bad_counts_raise_with_check():
+    dev = _dev()
+    counts = torch.tensor([[2, 1], [1, 1]], dtype=torch.int32, device=dev)
+    tokens = torch.zeros((4, 8), dtype=torch.float16, device=dev)   # sum is 5, A is 4
+    with pytest.raises(ValueError):
+        api.moe_re_routing(tokens, counts, check=True)
+
+
+def test_gather_needs_matching_tables():
+    """A gather phase on a workspace whose tables were built for another
+    (A, N, E) writes nothing."""
+    dev = _dev()
+    w1 = workloads.random_case(1, 3, 3, 64, tokens_dtype="int8", count_range=(1, 5))
+    t1 = workloads.torch_inputs(w1, dev)
+    call1, _ = api.make_call(t1["tokens"], t1["counts"])
+    call1.run()
+    w2 = workloads.random_case(2, 3, 4, 64, tokens_dtype="int8", count_range=(1, 5))
+    t2 = workloads.torch_inputs(w2, dev)
+    args, outs = api.prepare(t2["tokens"], t2["counts"])
+    for o in outs:
+        if o.numel():
+            o.view(-1).view(torch.uint8).fill_(SENTINEL)
+    call2, outs = api.make_call(t2["tokens"], t2["counts"], out=outs, workspace=call1.workspace)
+    call2.run_gather()
+    torch.cuda.synchronize()
+    for o in (outs[0], outs[2]):
+        assert (_bytes(o) == SENTINEL).all()
+
+
+def test_python_api_shapes():
+    dev = _dev()
+    w = workloads.make("tiny")
+    t = workloads.torch_inputs(w, dev)
+    p_tok, p_sc, p_idx, p_etn, p_w = api.moe_re_routing(t["tokens"], t["counts"], per_token_scales=t["scales"],
+                                                        check=True)
+    assert p_tok.shape == t["tokens"].shape and p_tok.dtype == t["tokens"].dtype
+    assert p_sc.shape == (w.A,) and p_sc.dtype == torch.float32
+    assert p_idx.shape == (w.A,) and p_idx.dtype == torch.int32
+    assert p_etn.shape == (w.E,) and p_etn.dtype == t["counts"].dtype
+    assert p_w.shape == (0,) and p_w.dtype == torch.float32
+    ref = run_oracle(w)
+    assert np.array_equal(p_idx.cpu().numpy(), ref[2])

@@ -2,6 +2,8 @@
 copy on the CPU, and checks that at least one pin (oracle_pins.py) fails for
 every one of them. The pins are only worth something if they catch these."""
 import os
+import subprocess
+import sys
 
 import pytest
 
@@ -66,23 +68,36 @@ def test_source_matches_mutant_sites():
             assert src.count(o) == 1, name
 
 
-def _fails_some_pin(orc):
-    failed = []
-    for name, check in pins.ALL_CHECKS:
-        try:
-            check(orc)
-        except (AssertionError, oracle.OracleError, IndexError, ValueError):
-            failed.append(name)
-    return failed
+_CHILD = r"""
+import sys
+sys.path[:0] = [sys.argv[2], sys.argv[3]]
+from oracle import oracle
+import oracle_pins as pins
+orc = oracle.Oracle(sys.argv[1])
+failed = []
+for name, check in pins.ALL_CHECKS:
+    try:
+        check(orc)
+    except (AssertionError, oracle.OracleError, IndexError, ValueError):
+        failed.append(name)
+print("failed:", failed)
+sys.exit(1 if failed else 0)
+"""
 
 
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_mutant_is_caught(tmp_path, name, old, new):
+    """A planted mistake may also corrupt memory (that is part of the mistake),
+    so the pins run against it in a child process: a pin failure or a crash
+    there both count as caught; only a clean pass of every pin fails the test."""
     src = open(SRC).read()
     for o, n in _sites(old, new):
         src = src.replace(o, n)
     path = tmp_path / "oracle_mutant.c"
     path.write_text(src)
     lib = oracle.build(str(path), str(tmp_path / f"lib_{name}.so"))
-    failed = _fails_some_pin(oracle.Oracle(lib))
-    assert failed, f"mutant {name} passed every pin"
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    here = os.path.dirname(os.path.abspath(__file__))
+    res = subprocess.run([sys.executable, "-c", _CHILD, lib, root, here], capture_output=True, text=True,
+                         timeout=300)
+    assert res.returncode != 0, f"mutant {name} passed every pin: {res.stdout}"
