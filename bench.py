@@ -40,7 +40,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 METRIC = "re-route GB/s (bytes read+written) and % of HBM peak; µs/call A=16384 H=7168"
-PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "mrr_gather_pages_shape_counters.txt")
+PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "pages_shape_counters.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "moe_token_re_amd", "csrc", f)
                   for f in ("mrr_kernels.hip", "mrr_internal.h", "mrr_validate.cpp")]
 
@@ -60,19 +60,21 @@ def gather_bytes_per_launch(w) -> int:
     return per_row * w.A
 
 
-def traffic_from_profile(w):
-    """HBM bytes per gather launch from the committed counter summary, scaled by
-    the copy kernel's counter reading for a known byte count; None when the
-    summary is missing, for another workload, or the kernel has changed."""
+def traffic_from_profile(w, kernel_name):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, scaled by the copy kernel's counter reading for a known byte
+    count; None when the summary is missing, for another workload or kernel,
+    or the kernel source has changed since the counters were taken."""
     if not os.path.exists(PROFILE_SUMMARY):
         return None
     text = open(PROFILE_SUMMARY).read()
     fields = dict(re.findall(r"^(\w+):\s*(\S+)\s*$", text, flags=re.M))
     try:
-        if fields.get("source_hash") != kernel_source_hash() or fields.get("workload") != w.name:
+        if (fields.get("source_hash") != kernel_source_hash() or fields.get("workload") != w.name
+                or fields.get("kernel") != kernel_name):
             return None
-        fetch = float(fields["gather_FETCH_SIZE_KiB"]) * float(fields["fetch_scale"])
-        write = float(fields["gather_WRITE_SIZE_KiB"]) * float(fields["write_scale"])
+        fetch = float(fields["FETCH_SIZE_KiB"]) * float(fields["fetch_scale"])
+        write = float(fields["WRITE_SIZE_KiB"]) * float(fields["write_scale"])
     except (KeyError, ValueError):
         return None
     return int(round((fetch + write) * 1024))
@@ -165,24 +167,39 @@ def main():
     print(f"[bench] {opt.steps} calls: wall {ms_per_step * 1e3:.2f} us/call, events "
           f"{ev_ms * 1e3 / opt.steps:.2f} us/call, {value:.1f} GB/s", file=sys.stderr, flush=True)
 
-    # per-kernel: events around each launch, on the launch stream
+    # per-kernel: events around each launch, on the launch stream. When the
+    # call is one fused kernel that kernel is the dominant one; otherwise the
+    # gather kernel is, timed apart from the offsets kernel.
+    plan = calls[0].plan()
     n_k = max(opt.steps, 50)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_k)]
     for i in range(n_k):
         c = calls[i % n_sets]
         evs[i][0].record(stream)
-        c.run_offsets()
-        evs[i][1].record(stream)
-        c.run_gather()
+        if plan["fused"]:
+            c.run()
+            evs[i][1].record(stream)
+        else:
+            c.run_offsets()
+            evs[i][1].record(stream)
+            c.run_gather()
         evs[i][2].record(stream)
     torch.cuda.synchronize()
-    off_us = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
-    gat_us = [e[1].elapsed_time(e[2]) * 1e3 for e in evs]
-    gather_mean_us = statistics.mean(gat_us)
-    gbytes = gather_bytes_per_launch(w)
-    achieved = gbytes / (gather_mean_us * 1e-6) / 1e9
-    print(f"[bench] per kernel: offsets mean {statistics.mean(off_us):.2f} us, gather mean {gather_mean_us:.2f} us "
-          f"(median {statistics.median(gat_us):.2f}), gather {achieved:.1f} GB/s", file=sys.stderr, flush=True)
+    if plan["fused"]:
+        kernel_name = "fused_kernel"
+        off_us = [0.0]
+        kern_us = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
+        kbytes = alg_bytes
+    else:
+        kernel_name = "gather_kernel"
+        off_us = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
+        kern_us = [e[1].elapsed_time(e[2]) * 1e3 for e in evs]
+        kbytes = gather_bytes_per_launch(w)
+    kern_mean_us = statistics.mean(kern_us)
+    achieved = kbytes / (kern_mean_us * 1e-6) / 1e9
+    print(f"[bench] plan {plan}", file=sys.stderr, flush=True)
+    print(f"[bench] per kernel: {kernel_name} mean {kern_mean_us:.2f} us (median {statistics.median(kern_us):.2f}), "
+          f"{achieved:.1f} GB/s; offsets kernel mean {statistics.mean(off_us):.2f} us", file=sys.stderr, flush=True)
 
     # hot (same buffers every call), labelled as such
     torch.cuda.synchronize()
@@ -264,11 +281,12 @@ def main():
         "us_per_call_hot_same_buffers": round(hot_us, 2),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "algorithmic_bytes_per_call": alg_bytes,
-        "offsets_kernel_us_mean": round(statistics.mean(off_us), 2),
+        "launch_path": "fused single kernel" if plan["fused"] else "offsets kernel + gather kernel",
+        "offsets_kernel_us_mean": None if plan["fused"] else round(statistics.mean(off_us), 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_from_profile(w),
-                     "kernel": "gather_kernel", "bytes_per_launch": gbytes,
-                     "launch_us_mean": round(gather_mean_us, 2)},
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_from_profile(w, kernel_name),
+                     "kernel": kernel_name, "bytes_per_launch": kbytes,
+                     "launch_us_mean": round(kern_mean_us, 2)},
         "copy_ceiling": ceiling,
         "cpu_baseline": cpu,
         "kernel_source_hash": kernel_source_hash(),

@@ -146,9 +146,32 @@ size_t mrr_workspace_size(int64_t N, int64_t E);
  */
 mrr_status mrr_validate(const mrr_args* args, const void* workspace, size_t workspace_bytes);
 
+/* How a call with these arguments is launched (filled by mrr_describe_plan). */
+typedef struct mrr_plan_info {
+  int32_t fused;                 /* 1: moe_rerouting_v2 launches one kernel whose workgroups each
+                                    recompute the offsets of the (small) count matrix in LDS;
+                                    0: it launches the offsets kernel, then the gather kernel */
+  int32_t token_vec_bytes;       /* bytes per load/store of the token copy: 16, 8, 4, 2 or 1 */
+  int32_t scale_vec_bytes;       /* the same for scale rows; 0 without scales */
+  int32_t rows_per_workgroup;    /* adjacent output rows per gather workgroup */
+  int32_t threads_per_workgroup;
+  int64_t gather_workgroups;
+  int64_t token_row_bytes;
+  int64_t scale_row_bytes;
+} mrr_plan_info;
+
 /*
- * The whole operator: moe_rerouting_v2_offsets() then moe_rerouting_v2_gather()
- * on `stream`. Asynchronous. Host-detectable errors are returned before any
+ * Runs the same host checks as mrr_validate() and, on success, describes the
+ * launch in *info. Host only, no HIP call.
+ */
+mrr_status mrr_describe_plan(const mrr_args* args, const void* workspace, size_t workspace_bytes,
+                             mrr_plan_info* info);
+
+/*
+ * The whole operator on `stream`, asynchronous. Depending on the size of the
+ * count matrix (see mrr_plan_info.fused) this launches either one fused
+ * kernel, or moe_rerouting_v2_offsets() then moe_rerouting_v2_gather(); the
+ * results are identical. Host-detectable errors are returned before any
  * launch; count errors are found on the device (see mrr_get_device_status).
  */
 mrr_status moe_rerouting_v2(const mrr_args* args, void* workspace, size_t workspace_bytes,
@@ -166,19 +189,20 @@ mrr_status moe_rerouting_v2_offsets(const mrr_args* args, void* workspace, size_
 /*
  * Second phase alone (article, "计算公式": the three moves, and "参数说明":
  * permute_token_idx): moves the token rows, scale rows and weights and writes
- * permute_token_idx, from the tables a preceding moe_rerouting_v2_offsets()
+ * permute_token_idx, from the table a preceding moe_rerouting_v2_offsets()
  * call with the same A, N and E wrote into `workspace` on the same stream.
- * If that call found bad counts, or the workspace holds no tables for this A,
- * N and E, nothing is written.
+ * If that call found bad counts, or the workspace holds no table for this A,
+ * N and E (for instance after a fused moe_rerouting_v2 call, which builds
+ * none), nothing is written.
  */
 mrr_status moe_rerouting_v2_gather(const mrr_args* args, void* workspace, size_t workspace_bytes,
                                    struct ihipStream_t* stream);
 
 /*
- * Waits for `stream`, then reads the status the last offsets phase left in
- * `workspace`: MRR_SUCCESS (the counts were valid), MRR_ERROR_BAD_COUNTS,
- * MRR_ERROR_INVALID_VALUE if the workspace holds no status (no offsets phase
- * ran on it), or MRR_ERROR_HIP if the copy or the wait fails.
+ * Waits for `stream`, then reads the status the last call (whole or offsets
+ * phase) left in `workspace`: MRR_SUCCESS (the counts were valid),
+ * MRR_ERROR_BAD_COUNTS, MRR_ERROR_INVALID_VALUE if the workspace holds no
+ * status (no call ran on it), or MRR_ERROR_HIP if the copy or the wait fails.
  * Synchronizing: not for use inside a hot loop.
  */
 mrr_status mrr_get_device_status(const void* workspace, struct ihipStream_t* stream);

@@ -25,8 +25,8 @@ ERROR_HIP = 7
 # mrr_dtype
 F16, BF16, I8, F8_E5M2, F8_E4M3FN, HIF8, F4_E2M1, F4_E1M2, I32, I64, F32, F8_E8M0 = range(12)
 
-EXPORTS = ("mrr_workspace_size", "mrr_validate", "moe_rerouting_v2", "moe_rerouting_v2_offsets",
-           "moe_rerouting_v2_gather", "mrr_get_device_status", "mrr_status_string")
+EXPORTS = ("mrr_workspace_size", "mrr_validate", "mrr_describe_plan", "moe_rerouting_v2",
+           "moe_rerouting_v2_offsets", "moe_rerouting_v2_gather", "mrr_get_device_status", "mrr_status_string")
 
 
 class MrrArgs(ctypes.Structure):
@@ -56,6 +56,21 @@ class MrrArgs(ctypes.Structure):
     ]
 
 
+class MrrPlanInfo(ctypes.Structure):
+    """struct mrr_plan_info, field for field."""
+
+    _fields_ = [
+        ("fused", ctypes.c_int32),
+        ("token_vec_bytes", ctypes.c_int32),
+        ("scale_vec_bytes", ctypes.c_int32),
+        ("rows_per_workgroup", ctypes.c_int32),
+        ("threads_per_workgroup", ctypes.c_int32),
+        ("gather_workgroups", ctypes.c_int64),
+        ("token_row_bytes", ctypes.c_int64),
+        ("scale_row_bytes", ctypes.c_int64),
+    ]
+
+
 _lock = threading.Lock()
 _lib = None
 
@@ -76,6 +91,8 @@ def load() -> ctypes.CDLL:
             lib.mrr_workspace_size.restype = sz
             lib.mrr_validate.argtypes = [P, vp, sz]
             lib.mrr_validate.restype = ctypes.c_int
+            lib.mrr_describe_plan.argtypes = [P, vp, sz, ctypes.POINTER(MrrPlanInfo)]
+            lib.mrr_describe_plan.restype = ctypes.c_int
             for name in ("moe_rerouting_v2", "moe_rerouting_v2_offsets", "moe_rerouting_v2_gather"):
                 fn = getattr(lib, name)
                 fn.argtypes = [P, vp, sz, vp]

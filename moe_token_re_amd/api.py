@@ -187,6 +187,14 @@ class PreparedCall:
     def validate(self) -> int:
         return self._lib.mrr_validate(self._pargs, self._ws, self._wsb)
 
+    def plan(self) -> dict:
+        """How moe_rerouting_v2 launches this call (mrr_describe_plan)."""
+        info = _lib.MrrPlanInfo()
+        st = self._lib.mrr_describe_plan(self._pargs, self._ws, self._wsb, ctypes.byref(info))
+        if st != _lib.SUCCESS:
+            _raise(st, "mrr_describe_plan")
+        return {name: getattr(info, name) for name, _ in info._fields_}
+
     def run(self):
         st = self._lib.moe_rerouting_v2(self._pargs, self._ws, self._wsb, self._s)
         if st != _lib.SUCCESS:

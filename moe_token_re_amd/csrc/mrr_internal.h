@@ -11,13 +11,14 @@
 namespace mrr {
 
 // Workspace layout (all offsets from the workspace base):
-//   [0, 256)                 WsHeader: validity of the counts the tables were built from
-//   [256, 256 + T1)          dst_off[M + 1] int32, cells in column-major (expert, rank)
-//                            order m = j*N + i; dst_off[M] = A
-//   [256 + T1, 256 + T1+T2)  src_off[M] int32, same cell order
-// with M = N*E, T1 = round_up(4*(M+1), 256), T2 = round_up(4*M, 256).
+//   [0, 256)              WsHeader: validity of the counts the table was built from
+//   [256, 256 + T)        table[M + 1] of int32 pairs (dst_off, src_off), cells in
+//                         column-major (expert j, rank i) order m = j*N + i, so that
+//                         dst_off is non-decreasing in m; table[M] = (A, A)
+// with M = N*E and T = round_up(8*(M+1), 256).
 constexpr size_t kHeaderBytes = 256;
-constexpr uint32_t kTablesValid = 0x4D525256u;  // "VRRM": tables valid for (A, N, E)
+constexpr uint32_t kTablesValid = 0x4D525256u;  // "VRRM": counts valid, table built for (A, N, E)
+constexpr uint32_t kCountsValid = 0x4D525243u;  // "CRRM": counts valid, no table (single-kernel path)
 constexpr uint32_t kTablesBad = 0x4D525242u;    // "BRRM": the counts were rejected
 
 // Flags the offsets kernel sets when it rejects the counts.
@@ -36,11 +37,36 @@ struct WsHeader {
 
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Threads of the gather kernel's workgroup and the number of 16-byte (or
-// narrower) vectors each thread keeps in flight.
-constexpr int kGatherThreads = 256;
-constexpr int kGatherUnroll = 8;
+// Shape of the gather kernel's workgroups: threads, and vectors (16 bytes or
+// narrower) each thread keeps in flight. A workgroup owns
+// rows_per_wg = max(1, threads * unroll / vectors_per_row) adjacent output rows.
+#ifndef MRR_GATHER_THREADS
+#define MRR_GATHER_THREADS 256
+#endif
+#ifndef MRR_GATHER_UNROLL
+#define MRR_GATHER_UNROLL 8
+#endif
+constexpr int kGatherThreads = MRR_GATHER_THREADS;
+constexpr int kGatherUnroll = MRR_GATHER_UNROLL;
 constexpr int kMaxRowsPerWg = 256;
+
+// LDS row stride of the staged count matrix: E plus at least one spare slot,
+// and odd, so that lanes walking cells in chunks of odd length start in
+// distinct LDS banks.
+inline int64_t lds_row_stride(int64_t E) { return (E % 2 == 0) ? E + 1 : E + 2; }
+
+// Dynamic LDS of the offsets computed in a workgroup's LDS: the counts /
+// source-offset matrix [N][ES] and the expert starts [E + 1] (int32), plus,
+// when `with_table`, the (dst_off, src_off) pair table [M + 1] placed first.
+inline int64_t lds_offsets_bytes(int64_t N, int64_t E, bool with_table) {
+  const int64_t tab = with_table ? 8 * (N * E + 1) : 0;
+  return tab + 4 * (N * lds_row_stride(E) + E + 1);
+}
+
+// The whole call runs as one kernel (each gather workgroup recomputes the
+// offsets in LDS) when that LDS stays this small, so that it does not limit
+// how many workgroups a CU holds.
+constexpr int64_t kFusedMaxLds = 8192;
 
 // Everything the launchers need, derived on the host from mrr_args.
 struct Plan {
@@ -54,10 +80,10 @@ struct Plan {
   bool has_weight;
   bool scatter;             // idx_type == 1
   bool cumsum;              // expert_token_num_type == 0
+  bool fused;               // moe_rerouting_v2 runs the single fused kernel
   int rows_per_wg;
   int64_t grid;             // gather workgroups
-  size_t dst_off_bytes;     // offset of dst_off in the workspace
-  size_t src_off_bytes;     // offset of src_off in the workspace
+  size_t table_bytes;       // offset of the (dst_off, src_off) table in the workspace
 };
 
 // Host-only: fills `plan` from validated arguments. Returns MRR_SUCCESS or an error.

@@ -2,31 +2,40 @@
 // (MoeReRoutingV2) for MI355X (gfx950, CDNA4: 64-lane waves, 256 CUs).
 //
 // Page: "CANN ops-transformer MoeReRoutingV2" (nlpx.cn article).
-//   offsets_kernel  -- section "计算公式", the two double sums: SrcOffset is the
-//                      exclusive prefix of the count matrix in row-major (rank,
-//                      expert) order, DstOffset in column-major (expert, rank)
-//                      order; plus expert_token_num ("参数说明") and the
-//                      Sum(counts) == A constraint ("约束说明").
-//   gather_kernel   -- section "计算公式", the moves
-//                      permute_X[DstOffset + k] = X[SrcOffset + k] for tokens,
-//                      per_token_scales and expert_topk_weight, and
-//                      permute_token_idx ("参数说明"; gather or scatter form).
+//   offsets          -- section "计算公式", the two double sums: SrcOffset is the
+//                       exclusive prefix of the count matrix in row-major (rank,
+//                       expert) order, DstOffset in column-major (expert, rank)
+//                       order; plus expert_token_num ("参数说明") and the
+//                       Sum(counts) == A constraint ("约束说明").
+//   row moves        -- section "计算公式", the moves
+//                       permute_X[DstOffset + k] = X[SrcOffset + k] for tokens,
+//                       per_token_scales and expert_topk_weight, and
+//                       permute_token_idx ("参数说明"; gather or scatter form).
 //
-// Design (not the Ascend tiling of the article, which targets another chip):
-//   * One workgroup of 1024 threads scans the counts twice (row-major, then
-//     column-major) with wave shuffles and LDS, and writes per-cell tables
-//     ordered by destination: dst_off[m], src_off[m] for m = j*N + i.
-//   * The gather kernel works in destination order. Each workgroup owns a
-//     contiguous run of output rows; every wave maps 64 of those rows to their
-//     source rows with a cooperative 64-way search over dst_off (ballot over
-//     64 pivots per round, then a 6-step shuffle search inside a 64-cell
-//     window), and moves the 4-byte per-row items (index, weight) with one
-//     lane per row. Then the whole workgroup streams the token bytes: the
-//     (row, 16-byte vector) space of its rows is flattened, every thread keeps
-//     8 vector loads in flight, and the stores are non-temporal and fully
-//     contiguous, since the workgroup's output rows are adjacent.
-//   * No atomics anywhere; every output element is written exactly once, so
-//     results are deterministic.
+// Kernels (the design is ours, not the Ascend tiling the article sketches):
+//   * offsets_staged_kernel: one workgroup of 1024 threads stages the counts
+//     in LDS, scans them row-major then column-major, and writes a table of
+//     int32 pairs (dst_off, src_off) in destination order, cell m = j*N + i.
+//     offsets_global_kernel does the same through global memory for count
+//     matrices too large for LDS.
+//   * gather_kernel: works in destination order. Each workgroup owns a few
+//     adjacent output rows. Every wave maps 64 of them to their source rows
+//     with a cooperative 64-way search over the table (a ballot over 64
+//     pivots per round, then a 6-step shuffle search in a 64-cell window whose
+//     pairs also carry the source offsets). Then the workgroup moves the
+//     4-byte per-row items (index, weight) with one lane per row, and streams
+//     the row bytes: the (row, 16-byte vector) space of its rows is flattened,
+//     each thread issues all its loads before any store, the loads are
+//     branch-free (clamped addresses; only stores are predicated, since a
+//     predicated load makes the compiler wait for it before issuing the next)
+//     and loads and stores are non-temporal. A workgroup's output rows are
+//     adjacent, so its stores are contiguous.
+//   * fused_kernel: for small count matrices, the whole call in one launch:
+//     every gather workgroup recomputes the offsets in its own LDS (a few KiB,
+//     read from L2) and maps its rows from there; workgroup 0 also writes
+//     expert_token_num and the status.
+// No atomics on global memory; every output element is written exactly once,
+// so results are deterministic.
 #include <hip/hip_runtime.h>
 
 #include <limits.h>
@@ -39,14 +48,16 @@
 namespace mrr {
 namespace {
 
-// ---------------------------------------------------------------------------
-// Offsets
-// ---------------------------------------------------------------------------
+using pair_t = int32_t __attribute__((ext_vector_type(2)));  // (dst_off, src_off)
 
 constexpr int kOffsetThreads = 1024;
-constexpr int kOffsetItems = 4;  // counts per thread per tile
-constexpr int64_t kOffsetTile = int64_t(kOffsetThreads) * kOffsetItems;
-constexpr int kWaves = kOffsetThreads / 64;
+constexpr int kOffsetItems = 4;  // counts per thread per tile (global path)
+constexpr int kOffsetTile = kOffsetThreads * kOffsetItems;
+constexpr int kStageUnroll = 8;  // count loads in flight per thread while staging
+
+// ---------------------------------------------------------------------------
+// Workgroup scans
+// ---------------------------------------------------------------------------
 
 __device__ __forceinline__ int64_t wave_inclusive_scan(int64_t v) {
   const int lane = threadIdx.x & 63;
@@ -59,24 +70,33 @@ __device__ __forceinline__ int64_t wave_inclusive_scan(int64_t v) {
 }
 
 // Exclusive prefix of `v` over the workgroup (thread order), and the total.
-// s holds 2*kWaves + 1 entries.
+// s holds 2 * kThreads / 64 + 1 entries.
+template <int kThreads>
 __device__ __forceinline__ int64_t block_exclusive_scan(int64_t v, int64_t* s, int64_t* total) {
+  constexpr int kW = kThreads / 64;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int64_t inc = wave_inclusive_scan(v);
   if (lane == 63) s[wave] = inc;
   __syncthreads();
   if (wave == 0) {
-    const int64_t w = lane < kWaves ? s[lane] : 0;
+    const int64_t w = lane < kW ? s[lane] : 0;
     const int64_t wi = wave_inclusive_scan(w);
-    if (lane < kWaves) s[kWaves + lane] = wi - w;
-    if (lane == kWaves - 1) s[2 * kWaves] = wi;
+    if (lane < kW) s[kW + lane] = wi - w;
+    if (lane == kW - 1) s[2 * kW] = wi;
   }
   __syncthreads();
-  const int64_t res = s[kWaves + wave] + inc - v;
-  *total = s[2 * kWaves];
+  const int64_t res = s[kW + wave] + inc - v;
+  *total = s[2 * kW];
   __syncthreads();  // s is reused by the next call
   return res;
+}
+
+// OR of `flags` over the workgroup (every thread gets the result).
+__device__ __forceinline__ uint32_t block_or(uint32_t flags, uint32_t* s_flags) {
+  if (flags != 0) atomicOr(s_flags, flags);
+  __syncthreads();
+  return *s_flags;
 }
 
 template <typename CountT>
@@ -93,116 +113,266 @@ __device__ __forceinline__ int32_t clamp_count(CountT raw, uint32_t* flags) {
   return static_cast<int32_t>(v);
 }
 
-// One workgroup. counts[N*E] row-major. Writes src_off/dst_off (cells in
-// column-major order), expert_token_num and the workspace header. When
-// `staged`, the clamped counts are kept in dynamic LDS between the passes.
-template <typename CountT>
-__global__ __launch_bounds__(kOffsetThreads) void offsets_kernel(
-    const CountT* __restrict__ counts, int64_t N, int64_t E, int64_t A, int cumsum,
-    CountT* __restrict__ etn, WsHeader* __restrict__ hdr, int32_t* __restrict__ dst_off,
-    int32_t* __restrict__ src_off, int staged) {
-  extern __shared__ int32_t s_counts[];
-  __shared__ int64_t s_scan[2 * kWaves + 1];
-  __shared__ uint32_t s_flags;
-  const int tid = threadIdx.x;
-  const int64_t M = N * E;
-  if (tid == 0) s_flags = 0;
-  uint32_t flags = 0;
-
-  // Pass 1: SrcOffset = exclusive prefix in row-major (rank i, expert j) order.
-  int64_t carry = 0;
-  for (int64_t base = 0; base < M; base += kOffsetTile) {
-    int32_t c[kOffsetItems];
-    int64_t local = 0;
-#pragma unroll
-    for (int k = 0; k < kOffsetItems; ++k) {
-      const int64_t m = base + int64_t(tid) * kOffsetItems + k;
-      c[k] = m < M ? clamp_count(counts[m], &flags) : 0;
-      if (staged && m < M) s_counts[m] = c[k];
-      local += c[k];
-    }
-    int64_t tile_total;
-    int64_t run = carry + block_exclusive_scan(local, s_scan, &tile_total);
-#pragma unroll
-    for (int k = 0; k < kOffsetItems; ++k) {
-      const int64_t m = base + int64_t(tid) * kOffsetItems + k;
-      if (m < M) {
-        const int64_t i = m / E;
-        const int64_t j = m - i * E;
-        src_off[j * N + i] = static_cast<int32_t>(run);
-      }
-      run += c[k];
-    }
-    carry += tile_total;
-  }
-
-  if (flags != 0) atomicOr(&s_flags, flags);
-  __syncthreads();
-  flags = s_flags;
-  if (carry != A) flags |= kFlagSumMismatch;
-  if (flags != 0) {
-    if (tid == 0) {
-      hdr->A = A;
-      hdr->N = N;
-      hdr->E = E;
-      hdr->total = carry;
-      hdr->flags = flags;
-      hdr->status = kTablesBad;
-    }
-    return;  // uniform: every thread sees the same flags
-  }
-
-  // Pass 2: DstOffset = exclusive prefix in column-major (expert j, rank i) order.
-  carry = 0;
-  for (int64_t base = 0; base < M; base += kOffsetTile) {
-    int32_t c[kOffsetItems];
-    int64_t local = 0;
-#pragma unroll
-    for (int k = 0; k < kOffsetItems; ++k) {
-      const int64_t mc = base + int64_t(tid) * kOffsetItems + k;
-      int32_t v = 0;
-      if (mc < M) {
-        const int64_t j = mc / N;
-        const int64_t i = mc - j * N;
-        v = staged ? s_counts[i * E + j] : clamp_count(counts[i * E + j], &flags);
-      }
-      c[k] = v;
-      local += v;
-    }
-    int64_t tile_total;
-    int64_t run = carry + block_exclusive_scan(local, s_scan, &tile_total);
-#pragma unroll
-    for (int k = 0; k < kOffsetItems; ++k) {
-      const int64_t mc = base + int64_t(tid) * kOffsetItems + k;
-      if (mc < M) dst_off[mc] = static_cast<int32_t>(run);
-      run += c[k];
-    }
-    carry += tile_total;
-  }
-  if (tid == 0) dst_off[M] = static_cast<int32_t>(A);
-  __threadfence_block();
-  __syncthreads();
-
-  // expert_token_num: column j covers cells [j*N, (j+1)*N) of the column-major
-  // table, so its rows are dst_off[(j+1)*N] - dst_off[j*N]; the cumsum form is
-  // the inclusive running total dst_off[(j+1)*N].
-  for (int64_t j = tid; j < E; j += kOffsetThreads) {
-    const int64_t end = dst_off[(j + 1) * N];
-    const int64_t start = dst_off[j * N];
-    etn[j] = static_cast<CountT>(cumsum ? end : end - start);
-  }
-  if (tid == 0) {
-    hdr->A = A;
-    hdr->N = N;
-    hdr->E = E;
-    hdr->total = carry;
-    hdr->flags = 0;
-    hdr->status = kTablesValid;
-  }
+__device__ __forceinline__ void write_header(WsHeader* hdr, int64_t A, int64_t N, int64_t E, int64_t total,
+                                             uint32_t flags, uint32_t valid_status) {
+  hdr->A = A;
+  hdr->N = N;
+  hdr->E = E;
+  hdr->total = total;
+  hdr->flags = flags;
+  hdr->status = flags == 0 ? valid_status : kTablesBad;
 }
 
 // ---------------------------------------------------------------------------
-// Gather
+// Offsets in a workgroup's LDS
+// ---------------------------------------------------------------------------
+
+// Computes both offset tables of counts[N][E] in LDS with kThreads threads.
+// q is an [N][ES] int32 LDS array (ES = lds_row_stride(E), odd): it first
+// holds the clamped counts, then, in place, the row-major exclusive prefix
+// q[i][j] = SrcOffset(i, j), with q[i][E] = SrcOffset(i+1, 0) (the prefix at
+// the end of row i), so that a count is q[i][j+1] - q[i][j]. Each thread owns
+// a contiguous chunk of C cells (C odd) of one order at a time; with both C
+// and ES odd, the 64 lanes of a wave start their chunks in distinct LDS banks.
+// Writes tab[m] = (DstOffset, SrcOffset) for m = j*N + i and tab[M] = (A, A)
+// (tab in LDS or global memory), and col[j] = DstOffset(0, j), col[E] = A.
+// Returns 0, or the rejection flags (the same in every thread; then tab and
+// col are not written).
+template <int kThreads, typename CountT>
+__device__ uint32_t lds_offsets(const CountT* __restrict__ counts, int N, int E, int ES, int64_t A, int32_t* q,
+                                int32_t* col, pair_t* tab, int64_t* s_scan, uint32_t* s_flags, int64_t* total_out) {
+  const int tid = threadIdx.x;
+  const int M = N * E;
+  int C = (M + kThreads - 1) / kThreads;
+  C |= 1;
+  if (tid == 0) *s_flags = 0;
+  for (int j = tid; j <= E; j += kThreads) col[j] = 0;
+
+  // Stage the counts: coalesced, branch-free loads, kStageUnroll in flight.
+  uint32_t flags = 0;
+  for (int base = 0; base < M; base += kThreads * kStageUnroll) {
+    CountT v[kStageUnroll];
+#pragma unroll
+    for (int u = 0; u < kStageUnroll; ++u) {
+      const int m = base + tid + u * kThreads;
+      v[u] = counts[m < M ? m : M - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < kStageUnroll; ++u) {
+      const int m = base + tid + u * kThreads;
+      if (m < M) {
+        const int i = m / E;
+        q[i * ES + (m - i * E)] = clamp_count(v[u], &flags);
+      }
+    }
+  }
+  __syncthreads();
+
+  // Pass 1: SrcOffset, the exclusive prefix in row-major (rank i, expert j) order.
+  const int m0 = tid * C;
+  const int m1 = min(m0 + C, M);
+  int64_t sum = 0;
+  if (m0 < m1) {
+    int i = m0 / E, j = m0 - (m0 / E) * E;
+    for (int m = m0; m < m1; ++m) {
+      sum += q[i * ES + j];
+      if (++j == E) {
+        j = 0;
+        ++i;
+      }
+    }
+  }
+  int64_t total;
+  int64_t run = block_exclusive_scan<kThreads>(sum, s_scan, &total);
+  if (m0 < m1) {
+    int i = m0 / E, j = m0 - (m0 / E) * E;
+    for (int m = m0; m < m1; ++m) {
+      const int32_t c = q[i * ES + j];
+      q[i * ES + j] = static_cast<int32_t>(run);
+      run += c;
+      if (j == E - 1) q[i * ES + E] = static_cast<int32_t>(run);
+      if (++j == E) {
+        j = 0;
+        ++i;
+      }
+    }
+  }
+  *total_out = total;
+  flags = block_or(flags, s_flags);
+  if (total != A) flags |= kFlagSumMismatch;
+  if (flags != 0) return flags;
+
+  // Pass 2: DstOffset, the exclusive prefix in column-major (expert j, rank i)
+  // order; each cell's pair is written once, in destination order.
+  sum = 0;
+  if (m0 < m1) {
+    int j = m0 / N, i = m0 - (m0 / N) * N;
+    for (int mc = m0; mc < m1; ++mc) {
+      sum += q[i * ES + j + 1] - q[i * ES + j];
+      if (++i == N) {
+        i = 0;
+        ++j;
+      }
+    }
+  }
+  run = block_exclusive_scan<kThreads>(sum, s_scan, &total);
+  if (m0 < m1) {
+    int j = m0 / N, i = m0 - (m0 / N) * N;
+    for (int mc = m0; mc < m1; ++mc) {
+      const int32_t src = q[i * ES + j];
+      const int32_t c = q[i * ES + j + 1] - src;
+      pair_t t;
+      t.x = static_cast<int32_t>(run);
+      t.y = src;
+      tab[mc] = t;
+      if (i == 0) col[j] = static_cast<int32_t>(run);
+      run += c;
+      if (++i == N) {
+        i = 0;
+        ++j;
+      }
+    }
+  }
+  if (tid == 0) {
+    pair_t t;
+    t.x = static_cast<int32_t>(A);
+    t.y = static_cast<int32_t>(A);
+    tab[M] = t;
+    col[E] = static_cast<int32_t>(A);
+  }
+  __syncthreads();
+  return 0;
+}
+
+// expert_token_num from the expert starts col[0..E]: expert j's rows are
+// [col[j], col[j+1]); the cumsum form is the inclusive total col[j+1].
+template <int kThreads, typename CountT>
+__device__ __forceinline__ void write_etn(const int32_t* col, int E, int cumsum, CountT* __restrict__ etn) {
+  for (int j = threadIdx.x; j < E; j += kThreads)
+    etn[j] = static_cast<CountT>(cumsum ? col[j + 1] : col[j + 1] - col[j]);
+}
+
+// ---------------------------------------------------------------------------
+// Offsets kernels
+// ---------------------------------------------------------------------------
+
+template <typename CountT>
+__global__ __launch_bounds__(kOffsetThreads) void offsets_staged_kernel(
+    const CountT* __restrict__ counts, int32_t N, int32_t E, int32_t ES, int64_t A, int cumsum,
+    CountT* __restrict__ etn, WsHeader* __restrict__ hdr, pair_t* __restrict__ table) {
+  extern __shared__ int32_t s_dyn[];
+  __shared__ int64_t s_scan[2 * kOffsetThreads / 64 + 1];
+  __shared__ uint32_t s_flags;
+  int32_t* q = s_dyn;             // [N][ES]
+  int32_t* col = s_dyn + N * ES;  // [E + 1]
+  int64_t total = 0;
+  const uint32_t flags =
+      lds_offsets<kOffsetThreads>(counts, N, E, ES, A, q, col, table, s_scan, &s_flags, &total);
+  if (flags == 0) write_etn<kOffsetThreads>(col, E, cumsum, etn);
+  if (threadIdx.x == 0) write_header(hdr, A, N, E, total, flags, kTablesValid);
+}
+
+// For count matrices too large for LDS: the same two scans in tiles of
+// kOffsetTile cells, reading the counts from global memory (the column-major
+// pass reads them transposed) and writing the source offsets of the first
+// pass straight into the table.
+template <typename CountT>
+__global__ __launch_bounds__(kOffsetThreads) void offsets_global_kernel(
+    const CountT* __restrict__ counts, int32_t N, int32_t E, int64_t A, int cumsum, CountT* __restrict__ etn,
+    WsHeader* __restrict__ hdr, int32_t* __restrict__ table) {
+  __shared__ int64_t s_scan[2 * kOffsetThreads / 64 + 1];
+  __shared__ uint32_t s_flags;
+  const int tid = threadIdx.x;
+  const int M = N * E;
+  if (tid == 0) s_flags = 0;
+  uint32_t flags = 0;
+
+  // Pass 1: SrcOffset (row-major), stored in the second slot of cell (i, j)'s
+  // column-major pair.
+  int64_t carry = 0;
+  for (int base = 0; base < M; base += kOffsetTile) {
+    CountT raw[kOffsetItems];
+#pragma unroll
+    for (int k = 0; k < kOffsetItems; ++k) {
+      const int m = base + tid * kOffsetItems + k;
+      raw[k] = counts[m < M ? m : M - 1];
+    }
+    int32_t c[kOffsetItems];
+    int64_t local = 0;
+#pragma unroll
+    for (int k = 0; k < kOffsetItems; ++k) {
+      const int m = base + tid * kOffsetItems + k;
+      c[k] = m < M ? clamp_count(raw[k], &flags) : 0;
+      local += c[k];
+    }
+    int64_t tile_total;
+    int64_t run = carry + block_exclusive_scan<kOffsetThreads>(local, s_scan, &tile_total);
+#pragma unroll
+    for (int k = 0; k < kOffsetItems; ++k) {
+      const int m = base + tid * kOffsetItems + k;
+      if (m < M) {
+        const int i = m / E;
+        const int j = m - i * E;
+        table[2 * (j * N + i) + 1] = static_cast<int32_t>(run);
+      }
+      run += c[k];
+    }
+    carry += tile_total;
+  }
+  flags = block_or(flags, &s_flags);
+  if (carry != A) flags |= kFlagSumMismatch;
+  if (flags != 0) {
+    if (tid == 0) write_header(hdr, A, N, E, carry, flags, kTablesValid);
+    return;
+  }
+
+  // Pass 2: DstOffset (column-major).
+  carry = 0;
+  for (int base = 0; base < M; base += kOffsetTile) {
+    CountT raw[kOffsetItems];
+#pragma unroll
+    for (int k = 0; k < kOffsetItems; ++k) {
+      const int mc = base + tid * kOffsetItems + k;
+      const int mcc = mc < M ? mc : M - 1;
+      const int j = mcc / N;
+      raw[k] = counts[(mcc - j * N) * E + j];
+    }
+    int32_t c[kOffsetItems];
+    int64_t local = 0;
+#pragma unroll
+    for (int k = 0; k < kOffsetItems; ++k) {
+      const int mc = base + tid * kOffsetItems + k;
+      c[k] = mc < M ? clamp_count(raw[k], &flags) : 0;
+      local += c[k];
+    }
+    int64_t tile_total;
+    int64_t run = carry + block_exclusive_scan<kOffsetThreads>(local, s_scan, &tile_total);
+#pragma unroll
+    for (int k = 0; k < kOffsetItems; ++k) {
+      const int mc = base + tid * kOffsetItems + k;
+      if (mc < M) table[2 * mc] = static_cast<int32_t>(run);
+      run += c[k];
+    }
+    carry += tile_total;
+  }
+  if (tid == 0) {
+    table[2 * M] = static_cast<int32_t>(A);
+    table[2 * M + 1] = static_cast<int32_t>(A);
+  }
+  __threadfence_block();
+  __syncthreads();
+
+  // expert_token_num from the expert starts dst_off[j*N] in the table.
+  for (int j = tid; j < E; j += kOffsetThreads) {
+    const int64_t end = table[2 * ((j + 1) * N)];
+    const int64_t start = table[2 * (j * N)];
+    etn[j] = static_cast<CountT>(cumsum ? end : end - start);
+  }
+  if (tid == 0) write_header(hdr, A, N, E, carry, 0, kTablesValid);
+}
+
+// ---------------------------------------------------------------------------
+// Row moves
 // ---------------------------------------------------------------------------
 
 template <int V>
@@ -236,9 +406,8 @@ struct GatherArgs {
   const uint32_t* weight;  // fp32 weights moved as raw 4-byte words
   uint32_t* out_weight;
   int32_t* idx;
-  const int32_t* dst_off;
-  const int32_t* src_off;
-  const WsHeader* hdr;
+  const pair_t* table;     // in the workspace (gather_kernel)
+  WsHeader* hdr;
   int64_t row_bytes;
   int64_t scale_row_bytes;
   int64_t N;
@@ -251,58 +420,77 @@ struct GatherArgs {
   int32_t rows_per_wg;
 };
 
-// The cell (in column-major order) holding output row d: the largest m with
-// dst_off[m] <= d. All 64 lanes call it together; their rows d lie in
-// [d_lo, d_lo + 63]. Returns m and dst_off[m].
-__device__ __forceinline__ void locate(const int32_t* __restrict__ dst_off, int M, int d_lo, int d,
-                                       int* m_out, int* dm_out) {
+// Source row of output row d, from a (dst_off, src_off) table of M + 1 pairs
+// in LDS or global memory. All 64 lanes of a wave call it together, with
+// their rows d in [d_lo, d_lo + 63]; d_lo is the same for the whole wave.
+// Whatever the table holds, every read stays inside its M + 1 entries.
+__device__ __forceinline__ int32_t source_row(const pair_t* table, int M, int d_lo, int d) {
   const int lane = threadIdx.x & 63;
-  // 64-way search for the cell of d_lo; invariant: dst_off[lo] <= d_lo and
-  // that cell lies in [lo, hi).
+  // 64-way search for the cell of d_lo: the largest m with dst_off[m] <= d_lo.
+  // Invariant: dst_off[lo] <= d_lo and that cell lies in [lo, hi).
   int lo = 0;
   int hi = M;
   while (hi - lo > 64) {
     const int stride = (hi - lo + 63) >> 6;
     const int pos = lo + lane * stride;
-    const int v = pos < hi ? dst_off[pos] : INT_MAX;
+    const int v = pos < hi ? table[pos].x : INT_MAX;
     const uint64_t below = __ballot(v <= d_lo);  // a prefix of the lanes
     const int k = max(__popcll(below) - 1, 0);
     lo += k * stride;
     hi = min(hi, lo + stride);
   }
-  // The 64-cell window [lo, lo + 64): a shuffle binary search per lane.
-  const int piv = (lo + lane <= M) ? dst_off[lo + lane] : INT_MAX;
+  // The 64-cell window [lo, lo + 64) with both offsets of each cell: a
+  // shuffle binary search per lane for the largest l with dst_off <= d.
+  pair_t w;
+  w.x = INT_MAX;
+  w.y = 0;
+  if (lo + lane <= M) w = table[lo + lane];
   int l = 0;
 #pragma unroll
   for (int step = 32; step > 0; step >>= 1) {
     const int cand = l + step;
-    const int pv = __shfl(piv, cand, 64);
-    if (pv <= d) l = cand;
+    if (__shfl(w.x, cand, 64) <= d) l = cand;
   }
-  int m = lo + l;
-  int dm = __shfl(piv, l, 64);
+  int dm = __shfl(w.x, l, 64);
+  int sm = __shfl(w.y, l, 64);
   if (l == 63 && lo + 63 < M) {
     // d lies past the window (many empty cells in between): finish alone.
     int a = lo + 63;
     int b = M;  // dst_off[a] <= d < dst_off[b] == A
     while (b - a > 1) {
       const int mid = (a + b) >> 1;
-      if (dst_off[mid] <= d)
+      if (table[mid].x <= d)
         a = mid;
       else
         b = mid;
     }
-    m = a;
-    dm = dst_off[a];
+    const pair_t t = table[a];
+    dm = t.x;
+    sm = t.y;
   }
-  *m_out = min(m, M - 1);  // a no-op on tables the offsets kernel wrote
-  *dm_out = dm;
+  return sm + (d - dm);
+}
+
+// Fills s_src[0, rows) with the source rows of output rows row0 + [0, rows),
+// or -1 for a row whose mapped source lies outside [0, A).
+__device__ __forceinline__ void map_rows(const pair_t* table, int M, int A, int row0, int rows, int32_t* s_src) {
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  for (int b = wave * 64; b < rows; b += kGatherThreads) {
+    const int lr = b + lane;
+    const bool mine = lr < rows;
+    const int d_lo = row0 + b;
+    const int d = mine ? row0 + lr : d_lo;
+    const int32_t s = source_row(table, M, d_lo, d);
+    const bool ok = mine && static_cast<unsigned>(s) < static_cast<unsigned>(A);
+    if (mine) s_src[lr] = ok ? s : -1;
+  }
 }
 
 // Copies `rows` rows of row_bytes = vpr * V bytes: source row s_src[r] to the
 // r-th row of dst_chunk (rows adjacent). Rows with s_src[r] < 0 are skipped.
 // The (row, vector) space is flattened and walked in steps of the workgroup
-// size, kGatherUnroll loads in flight per thread before their stores.
+// size; each thread issues kGatherUnroll loads before their stores.
 template <int V>
 __device__ __forceinline__ void copy_rows(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst_chunk,
                                           int64_t row_bytes, int vpr, int rows,
@@ -320,15 +508,13 @@ __device__ __forceinline__ void copy_rows(const uint8_t* __restrict__ src, uint8
 #pragma unroll
     for (int k = 0; k < kGatherUnroll; ++k) {
       const int e = e0 + tid + k * kGatherThreads;
-      ok[k] = false;
-      if (e < total) {
-        const int32_t srow = s_src[r];
-        if (srow >= 0) {
-          ok[k] = true;
-          v[k] = __builtin_nontemporal_load(
-              reinterpret_cast<const T*>(src + int64_t(srow) * row_bytes + int64_t(c) * V));
-        }
-      }
+      const bool in = e < total;
+      const int32_t srow = s_src[in ? r : 0];
+      ok[k] = in && srow >= 0;
+      // Branch-free load: items out of range read row 0, column 0 (always
+      // valid, since A > 0 here) and are not stored.
+      const int64_t off = ok[k] ? int64_t(srow) * row_bytes + int64_t(c) * V : 0;
+      v[k] = __builtin_nontemporal_load(reinterpret_cast<const T*>(src + off));
       r += dr;
       c += dc;
       if (c >= vpr) {
@@ -344,41 +530,23 @@ __device__ __forceinline__ void copy_rows(const uint8_t* __restrict__ src, uint8
   }
 }
 
+// Everything a workgroup writes for its output rows row0 + [0, rows), once
+// s_src holds their source rows: the index and weight (one lane per row), the
+// token rows and the scale rows.
 template <int V, bool kScatter, bool kWeight>
-__global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs p) {
-  __shared__ int32_t s_src[kMaxRowsPerWg];
-  const WsHeader* h = p.hdr;
-  if (h->status != kTablesValid || h->A != p.A || h->N != p.N || h->E != p.E) return;
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int row0 = blockIdx.x * p.rows_per_wg;
-  const int rows = min(p.rows_per_wg, p.A - row0);
-
-  // Map this workgroup's output rows to source rows; move the per-row words.
-  for (int b = wave * 64; b < rows; b += kGatherThreads) {
-    const int lr = b + lane;
-    const bool valid = lr < rows;
-    const int d_lo = row0 + b;
-    const int d = valid ? row0 + lr : d_lo;
-    int m, dm;
-    locate(p.dst_off, p.M, d_lo, d, &m, &dm);
-    const int s = p.src_off[m] + (d - dm);
-    const bool ok = valid && static_cast<unsigned>(s) < static_cast<unsigned>(p.A);
-    if (valid) s_src[lr] = ok ? s : -1;
-    if (ok) {
-      if (kScatter)
-        p.idx[s] = d;
-      else
-        p.idx[d] = s;
-      if (kWeight) p.out_weight[d] = p.weight[s];
-    }
+__device__ __forceinline__ void move_rows(const GatherArgs& p, int row0, int rows, const int32_t* s_src) {
+  for (int lr = threadIdx.x; lr < rows; lr += kGatherThreads) {
+    const int32_t s = s_src[lr];
+    if (s < 0) continue;
+    const int d = row0 + lr;
+    if (kScatter)
+      p.idx[s] = d;
+    else
+      p.idx[d] = s;
+    if (kWeight) p.out_weight[d] = p.weight[s];
   }
-  __syncthreads();
 
-  copy_rows<V>(p.tokens, p.out_tokens + int64_t(row0) * p.row_bytes, p.row_bytes, p.vecs_per_row, rows,
-               s_src);
+  copy_rows<V>(p.tokens, p.out_tokens + int64_t(row0) * p.row_bytes, p.row_bytes, p.vecs_per_row, rows, s_src);
 
   if (p.scale_row_bytes > 0) {
     uint8_t* out = p.out_scales + int64_t(row0) * p.scale_row_bytes;
@@ -392,30 +560,93 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs p) {
   }
 }
 
+template <int V, bool kScatter, bool kWeight>
+__global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs p) {
+  __shared__ int32_t s_src[kMaxRowsPerWg];
+  const int row0 = blockIdx.x * p.rows_per_wg;
+  const int rows = min(p.rows_per_wg, p.A - row0);
+  // The table is searched before the header is checked, so that the two
+  // reads overlap; nothing is written unless the header says the table was
+  // built from valid counts for this (A, N, E).
+  const WsHeader* h = p.hdr;
+  const bool valid_table = h->status == kTablesValid && h->A == p.A && h->N == p.N && h->E == p.E;
+  map_rows(p.table, p.M, p.A, row0, rows, s_src);
+  if (!valid_table) return;  // uniform over the workgroup
+  __syncthreads();
+  move_rows<V, kScatter, kWeight>(p, row0, rows, s_src);
+}
+
+struct FusedArgs {
+  const void* counts;
+  void* etn;
+  int32_t ES;
+  int32_t cumsum;
+};
+
+template <int V, bool kScatter, bool kWeight, typename CountT>
+__global__ __launch_bounds__(kGatherThreads) void fused_kernel(GatherArgs p, FusedArgs f) {
+  extern __shared__ int32_t s_dyn[];
+  __shared__ int32_t s_src[kMaxRowsPerWg];
+  __shared__ int64_t s_scan[2 * kGatherThreads / 64 + 1];
+  __shared__ uint32_t s_flags;
+  const int N = static_cast<int>(p.N);
+  const int E = static_cast<int>(p.E);
+  auto* tab = reinterpret_cast<pair_t*>(s_dyn);  // [M + 1], first: 8-byte aligned
+  int32_t* q = s_dyn + 2 * (p.M + 1);            // [N][ES]
+  int32_t* col = q + N * f.ES;                   // [E + 1]
+  int64_t total = 0;
+  const uint32_t flags = lds_offsets<kGatherThreads>(static_cast<const CountT*>(f.counts), N, E, f.ES, p.A, q, col,
+                                                     tab, s_scan, &s_flags, &total);
+  if (blockIdx.x == 0) {
+    if (flags == 0) write_etn<kGatherThreads>(col, E, f.cumsum, static_cast<CountT*>(f.etn));
+    if (threadIdx.x == 0) write_header(p.hdr, p.A, p.N, p.E, total, flags, kCountsValid);
+  }
+  if (flags != 0) return;  // uniform: nothing is written for rejected counts
+
+  const int row0 = blockIdx.x * p.rows_per_wg;
+  const int rows = min(p.rows_per_wg, p.A - row0);
+  map_rows(tab, p.M, p.A, row0, rows, s_src);
+  __syncthreads();
+  move_rows<V, kScatter, kWeight>(p, row0, rows, s_src);
+}
+
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
 
 // Per-device facts, read once per device.
 struct DeviceInfo {
-  int max_lds_per_block = 0;
+  int lds_limit = 0;  // dynamic LDS the staged offsets kernel may take
 };
 
 constexpr int kMaxDevices = 64;
+constexpr int kStaticLdsReserve = 1024;  // the offsets kernels' own static LDS, rounded up
 std::once_flag g_dev_once[kMaxDevices];
 DeviceInfo g_dev[kMaxDevices];
 
 mrr_status device_info(const DeviceInfo** out) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MRR_ERROR_HIP;
-  mrr_status st = MRR_SUCCESS;
   std::call_once(g_dev_once[dev], [&] {
-    int lds = 0;
-    if (hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) lds = 0;
-    g_dev[dev].max_lds_per_block = lds;
+    // Up to 64 KiB needs no opt-in; gfx950 lets one workgroup opt in to up
+    // to 160 KiB.
+    int optin = 0;
+    if (hipDeviceGetAttribute(&optin, hipDeviceAttributeSharedMemPerBlockOptin, dev) != hipSuccess) optin = 0;
+    int plain = 0;
+    if (hipDeviceGetAttribute(&plain, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) plain = 0;
+    int limit = (plain < 65536 ? plain : 65536) - kStaticLdsReserve;
+    const int want = optin - kStaticLdsReserve;
+    if (want > limit &&
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&offsets_staged_kernel<int32_t>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, want) == hipSuccess &&
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&offsets_staged_kernel<int64_t>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, want) == hipSuccess)
+      limit = want;
+    (void)hipGetLastError();  // a refused opt-in only keeps the smaller limit
+    g_dev[dev].lds_limit = limit > 0 ? limit : 0;
   });
   *out = &g_dev[dev];
-  return st;
+  return MRR_SUCCESS;
 }
 
 template <typename CountT>
@@ -423,18 +654,20 @@ mrr_status launch_offsets_t(const Plan& pl, const mrr_args* a, void* ws, hipStre
   const DeviceInfo* di = nullptr;
   if (device_info(&di) != MRR_SUCCESS) return MRR_ERROR_HIP;
   auto* base = static_cast<uint8_t*>(ws);
-  // Keep the counts in LDS between the two passes when they fit in the
-  // 64 KiB a launch may take without opting in to more (leaving room for the
-  // kernel's static LDS).
-  const int64_t stage_bytes = pl.M * 4;
-  const int64_t lds_limit = di->max_lds_per_block < 65536 ? di->max_lds_per_block : 65536;
-  const bool staged = pl.M > 0 && stage_bytes + 1024 <= lds_limit;
-  hipLaunchKernelGGL((offsets_kernel<CountT>), dim3(1), dim3(kOffsetThreads),
-                     staged ? static_cast<size_t>(stage_bytes) : 0, stream,
-                     static_cast<const CountT*>(a->expert_token_num_per_rank), pl.N, pl.E, pl.A,
-                     pl.cumsum ? 1 : 0, static_cast<CountT*>(a->expert_token_num),
-                     reinterpret_cast<WsHeader*>(base), reinterpret_cast<int32_t*>(base + pl.dst_off_bytes),
-                     reinterpret_cast<int32_t*>(base + pl.src_off_bytes), staged ? 1 : 0);
+  const auto* counts = static_cast<const CountT*>(a->expert_token_num_per_rank);
+  auto* etn = static_cast<CountT*>(a->expert_token_num);
+  auto* hdr = reinterpret_cast<WsHeader*>(base);
+  const int32_t N = static_cast<int32_t>(pl.N);
+  const int32_t E = static_cast<int32_t>(pl.E);
+  const int64_t lds = lds_offsets_bytes(pl.N, pl.E, false);
+  if (lds <= di->lds_limit) {
+    hipLaunchKernelGGL((offsets_staged_kernel<CountT>), dim3(1), dim3(kOffsetThreads), static_cast<size_t>(lds),
+                       stream, counts, N, E, static_cast<int32_t>(lds_row_stride(E)), pl.A, pl.cumsum ? 1 : 0, etn,
+                       hdr, reinterpret_cast<pair_t*>(base + pl.table_bytes));
+  } else {
+    hipLaunchKernelGGL((offsets_global_kernel<CountT>), dim3(1), dim3(kOffsetThreads), 0, stream, counts, N, E,
+                       pl.A, pl.cumsum ? 1 : 0, etn, hdr, reinterpret_cast<int32_t*>(base + pl.table_bytes));
+  }
   return hipGetLastError() == hipSuccess ? MRR_SUCCESS : MRR_ERROR_HIP;
 }
 
@@ -443,29 +676,7 @@ mrr_status launch_offsets(const Plan& pl, const mrr_args* a, void* ws, hipStream
                              : launch_offsets_t<int32_t>(pl, a, ws, stream);
 }
 
-template <int V, bool kScatter, bool kWeight>
-void launch_gather_vsw(const Plan& pl, const GatherArgs& g, hipStream_t stream) {
-  hipLaunchKernelGGL((gather_kernel<V, kScatter, kWeight>), dim3(static_cast<unsigned>(pl.grid)),
-                     dim3(kGatherThreads), 0, stream, g);
-}
-
-template <int V>
-void launch_gather_v(const Plan& pl, const GatherArgs& g, hipStream_t stream) {
-  if (pl.scatter) {
-    if (pl.has_weight)
-      launch_gather_vsw<V, true, true>(pl, g, stream);
-    else
-      launch_gather_vsw<V, true, false>(pl, g, stream);
-  } else {
-    if (pl.has_weight)
-      launch_gather_vsw<V, false, true>(pl, g, stream);
-    else
-      launch_gather_vsw<V, false, false>(pl, g, stream);
-  }
-}
-
-mrr_status launch_gather(const Plan& pl, const mrr_args* a, void* ws, hipStream_t stream) {
-  if (pl.A == 0) return MRR_SUCCESS;
+GatherArgs gather_args(const Plan& pl, const mrr_args* a, void* ws) {
   auto* base = static_cast<uint8_t*>(ws);
   GatherArgs g{};
   g.tokens = static_cast<const uint8_t*>(a->tokens);
@@ -475,9 +686,8 @@ mrr_status launch_gather(const Plan& pl, const mrr_args* a, void* ws, hipStream_
   g.weight = reinterpret_cast<const uint32_t*>(a->expert_topk_weight);
   g.out_weight = reinterpret_cast<uint32_t*>(a->permute_topk_weight);
   g.idx = a->permute_token_idx;
-  g.dst_off = reinterpret_cast<const int32_t*>(base + pl.dst_off_bytes);
-  g.src_off = reinterpret_cast<const int32_t*>(base + pl.src_off_bytes);
-  g.hdr = reinterpret_cast<const WsHeader*>(base);
+  g.table = reinterpret_cast<const pair_t*>(base + pl.table_bytes);
+  g.hdr = reinterpret_cast<WsHeader*>(base);
   g.row_bytes = pl.row_bytes;
   g.scale_row_bytes = pl.scale_row_bytes;
   g.N = pl.N;
@@ -488,13 +698,73 @@ mrr_status launch_gather(const Plan& pl, const mrr_args* a, void* ws, hipStream_
   g.A = static_cast<int32_t>(pl.A);
   g.M = static_cast<int32_t>(pl.M);
   g.rows_per_wg = pl.rows_per_wg;
+  return g;
+}
+
+// Launches kernel K<V, scatter, weight> (gather or fused) for the plan's
+// vector width and flags; `launch` receives a pointer to the instance.
+template <template <int, bool, bool> class K, typename Launch>
+void dispatch(const Plan& pl, Launch&& launch) {
+  auto pick = [&](auto vtag) {
+    constexpr int V = decltype(vtag)::value;
+    if (pl.scatter) {
+      if (pl.has_weight)
+        launch(K<V, true, true>::fn());
+      else
+        launch(K<V, true, false>::fn());
+    } else {
+      if (pl.has_weight)
+        launch(K<V, false, true>::fn());
+      else
+        launch(K<V, false, false>::fn());
+    }
+  };
   switch (pl.token_vec) {
-    case 16: launch_gather_v<16>(pl, g, stream); break;
-    case 8: launch_gather_v<8>(pl, g, stream); break;
-    case 4: launch_gather_v<4>(pl, g, stream); break;
-    case 2: launch_gather_v<2>(pl, g, stream); break;
-    default: launch_gather_v<1>(pl, g, stream); break;
+    case 16: pick(std::integral_constant<int, 16>{}); break;
+    case 8: pick(std::integral_constant<int, 8>{}); break;
+    case 4: pick(std::integral_constant<int, 4>{}); break;
+    case 2: pick(std::integral_constant<int, 2>{}); break;
+    default: pick(std::integral_constant<int, 1>{}); break;
   }
+}
+
+template <int V, bool S, bool W>
+struct GatherK {
+  static auto fn() { return &gather_kernel<V, S, W>; }
+};
+template <int V, bool S, bool W>
+struct FusedK32 {
+  static auto fn() { return &fused_kernel<V, S, W, int32_t>; }
+};
+template <int V, bool S, bool W>
+struct FusedK64 {
+  static auto fn() { return &fused_kernel<V, S, W, int64_t>; }
+};
+
+mrr_status launch_gather(const Plan& pl, const mrr_args* a, void* ws, hipStream_t stream) {
+  if (pl.A == 0) return MRR_SUCCESS;
+  const GatherArgs g = gather_args(pl, a, ws);
+  dispatch<GatherK>(pl, [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(pl.grid)), dim3(kGatherThreads), 0, stream, g);
+  });
+  return hipGetLastError() == hipSuccess ? MRR_SUCCESS : MRR_ERROR_HIP;
+}
+
+mrr_status launch_fused(const Plan& pl, const mrr_args* a, void* ws, hipStream_t stream) {
+  const GatherArgs g = gather_args(pl, a, ws);
+  FusedArgs f{};
+  f.counts = a->expert_token_num_per_rank;
+  f.etn = a->expert_token_num;
+  f.ES = static_cast<int32_t>(lds_row_stride(pl.E));
+  f.cumsum = pl.cumsum ? 1 : 0;
+  const size_t lds = static_cast<size_t>(lds_offsets_bytes(pl.N, pl.E, true));
+  auto launch = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(pl.grid)), dim3(kGatherThreads), lds, stream, g, f);
+  };
+  if (pl.count_bytes == 8)
+    dispatch<FusedK64>(pl, launch);
+  else
+    dispatch<FusedK32>(pl, launch);
   return hipGetLastError() == hipSuccess ? MRR_SUCCESS : MRR_ERROR_HIP;
 }
 
@@ -522,6 +792,7 @@ extern "C" mrr_status moe_rerouting_v2(const mrr_args* args, void* workspace, si
   mrr::Plan plan;
   mrr_status st = mrr::make_plan(args, workspace, workspace_bytes, &plan);
   if (st != MRR_SUCCESS) return st;
+  if (plan.fused) return mrr::launch_fused(plan, args, workspace, stream);
   st = mrr::launch_offsets(plan, args, workspace, stream);
   if (st != MRR_SUCCESS) return st;
   return mrr::launch_gather(plan, args, workspace, stream);
@@ -532,7 +803,7 @@ extern "C" mrr_status mrr_get_device_status(const void* workspace, struct ihipSt
   mrr::WsHeader h{};
   if (hipMemcpyAsync(&h, workspace, sizeof(h), hipMemcpyDeviceToHost, stream) != hipSuccess) return MRR_ERROR_HIP;
   if (hipStreamSynchronize(stream) != hipSuccess) return MRR_ERROR_HIP;
-  if (h.status == mrr::kTablesValid) return MRR_SUCCESS;
+  if (h.status == mrr::kTablesValid || h.status == mrr::kCountsValid) return MRR_SUCCESS;
   if (h.status == mrr::kTablesBad) return MRR_ERROR_BAD_COUNTS;
   return MRR_ERROR_INVALID_VALUE;
 }

@@ -59,8 +59,12 @@ int env_int(const char* name, int fallback) {
 // never a result.
 struct Tuning {
   int rows_per_wg;  // 0 = automatic
+  bool fused;       // allow the single-kernel path (MRR_FUSED=0 turns it off)
   bool log;
-  Tuning() : rows_per_wg(env_int("MRR_ROWS_PER_WG", 0)), log(env_int("MRR_LOG", 0) != 0) {}
+  Tuning()
+      : rows_per_wg(env_int("MRR_ROWS_PER_WG", 0)),
+        fused(env_int("MRR_FUSED", 1) != 0),
+        log(env_int("MRR_LOG", 0) != 0) {}
 };
 
 const Tuning& tuning() {
@@ -80,7 +84,7 @@ extern "C" size_t mrr_workspace_size(int64_t N, int64_t E) {
   if (N < 0 || E < 0) return 0;
   if (N != 0 && E > kMaxCells / N) return 0;
   const size_t M = static_cast<size_t>(N * E);
-  return mrr::kHeaderBytes + round_up(4 * (M + 1), 256) + round_up(4 * M, 256);
+  return mrr::kHeaderBytes + round_up(8 * (M + 1), 256);
 }
 
 extern "C" const char* mrr_status_string(mrr_status s) {
@@ -214,16 +218,17 @@ mrr_status make_plan(const mrr_args* a, const void* ws, size_t ws_bytes, Plan* p
   if (tuning().rows_per_wg > 0) rows = tuning().rows_per_wg;
   q.rows_per_wg = static_cast<int>(std::min<int64_t>(std::max<int64_t>(rows, 1), kMaxRowsPerWg));
   q.grid = (q.A + q.rows_per_wg - 1) / q.rows_per_wg;
-  q.dst_off_bytes = kHeaderBytes;
-  q.src_off_bytes = kHeaderBytes + round_up(4 * (static_cast<size_t>(M) + 1), 256);
+  q.fused = tuning().fused && q.A > 0 && lds_offsets_bytes(q.N, q.E, true) <= kFusedMaxLds;
+  q.table_bytes = kHeaderBytes;
   *p = q;
 
   if (tuning().log)
     fprintf(stderr,
-            "[mrr] A=%lld N=%lld E=%lld R=%lld vec=%d rows/wg=%d grid=%lld Rs=%lld svec=%d w=%d scatter=%d\n",
+            "[mrr] A=%lld N=%lld E=%lld R=%lld vec=%d rows/wg=%d grid=%lld Rs=%lld svec=%d w=%d scatter=%d "
+            "fused=%d\n",
             (long long)q.A, (long long)q.N, (long long)q.E, (long long)q.row_bytes, q.token_vec,
             q.rows_per_wg, (long long)q.grid, (long long)q.scale_row_bytes, q.scale_vec,
-            (int)q.has_weight, (int)q.scatter);
+            (int)q.has_weight, (int)q.scatter, (int)q.fused);
   return MRR_SUCCESS;
 }
 
@@ -232,4 +237,21 @@ mrr_status make_plan(const mrr_args* a, const void* ws, size_t ws_bytes, Plan* p
 extern "C" mrr_status mrr_validate(const mrr_args* args, const void* workspace, size_t workspace_bytes) {
   mrr::Plan plan;
   return mrr::make_plan(args, workspace, workspace_bytes, &plan);
+}
+
+extern "C" mrr_status mrr_describe_plan(const mrr_args* args, const void* workspace, size_t workspace_bytes,
+                                        mrr_plan_info* info) {
+  if (info == nullptr) return MRR_ERROR_INVALID_VALUE;
+  mrr::Plan plan;
+  const mrr_status st = mrr::make_plan(args, workspace, workspace_bytes, &plan);
+  if (st != MRR_SUCCESS) return st;
+  info->fused = plan.fused ? 1 : 0;
+  info->token_vec_bytes = plan.token_vec;
+  info->scale_vec_bytes = plan.scale_row_bytes > 0 ? plan.scale_vec : 0;
+  info->rows_per_workgroup = plan.rows_per_wg;
+  info->threads_per_workgroup = mrr::kGatherThreads;
+  info->gather_workgroups = plan.grid;
+  info->token_row_bytes = plan.row_bytes;
+  info->scale_row_bytes = plan.scale_row_bytes;
+  return MRR_SUCCESS;
 }

@@ -49,7 +49,7 @@ def test_status_strings():
 
 def test_workspace_size():
     L = _lib.load()
-    # 256-byte header + round_up(4*(M+1), 256) + round_up(4*M, 256)
+    # 256-byte header + round_up(8*(M+1), 256) for the (dst, src) pair table
     assert L.mrr_workspace_size(16, 16) == 256 + 1280 + 1024
     assert L.mrr_workspace_size(256, 64) == 256 + 65792 + 65536
     assert L.mrr_workspace_size(0, 5) == 256 + 256 + 0
@@ -166,6 +166,40 @@ def test_rejections(mutate, code):
     a = valid_args()
     mutate(a)
     assert validate(a) == code
+
+
+def describe(a, ws=BASE["ws"]):
+    L = _lib.load()
+    info = _lib.MrrPlanInfo()
+    st = L.mrr_describe_plan(ctypes.byref(a), ws, L.mrr_workspace_size(a.N, a.E), ctypes.byref(info))
+    return st, info
+
+
+def test_describe_plan():
+    # pages' shape: 7168-byte rows in 16-byte vectors; 16x16 counts take the single-kernel path
+    st, info = describe(valid_args(A=16384, H=7168, N=16, E=16, tok=_lib.I8))
+    assert st == _lib.SUCCESS
+    assert info.fused == 1 and info.token_vec_bytes == 16 and info.token_row_bytes == 7168
+    assert info.scale_row_bytes == 4 and info.scale_vec_bytes == 4
+    rows = max(1, info.threads_per_workgroup * 8 // 448)
+    assert info.rows_per_workgroup == min(rows, 256)
+    assert info.gather_workgroups == -(-16384 // info.rows_per_workgroup)
+    # 256x64 counts are too many to recompute per workgroup: two kernels
+    st, info = describe(valid_args(A=65536, H=2048, N=256, E=64, tok=_lib.F4_E2M1))
+    assert st == _lib.SUCCESS and info.fused == 0 and info.token_row_bytes == 1024
+    # odd rows fall back to narrower vectors
+    a = valid_args(tok=_lib.F16, H=79)
+    st, info = describe(a)
+    assert st == _lib.SUCCESS and info.token_vec_bytes == 2 and info.token_row_bytes == 158
+    # empty input: nothing to gather, never the single-kernel path
+    st, info = describe(valid_args(A=0, N=3, E=2))
+    assert st == _lib.SUCCESS and info.fused == 0 and info.gather_workgroups == 0
+    # describe runs the same checks
+    a = valid_args()
+    a.idx_type = 3
+    assert describe(a)[0] == _lib.ERROR_INVALID_VALUE
+    assert _lib.load().mrr_describe_plan(ctypes.byref(valid_args()), BASE["ws"], 1 << 20, None) == \
+        _lib.ERROR_INVALID_VALUE
 
 
 def test_int64_counts_alignment():

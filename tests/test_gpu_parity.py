@@ -96,8 +96,30 @@ def test_named_workload_full_size(name):
     check(workloads.make(name))
 
 
-def test_two_phases_equal_whole_call():
-    check(workloads.make("tiny_segments"), phases=True)
+@pytest.mark.parametrize("name", list(workloads.CONFIGS))
+def test_two_phases_equal_oracle(name):
+    """The offsets kernel then the gather kernel, called separately (the
+    two-kernel path, also for count matrices small enough for the fused one)."""
+    check(workloads.make(name), phases=True)
+
+
+@pytest.mark.parametrize("seed,n,e", [(1, 2, 4), (2, 16, 16), (3, 1, 40), (4, 33, 3), (5, 9, 1)])
+def test_fused_equals_two_phase(seed, n, e):
+    """Small count matrices: the single-kernel whole call and the two-kernel
+    phases give the same bytes (and both match the oracle)."""
+    dev = _dev()
+    w = workloads.random_case(seed, n, e, 96, tokens_dtype="bfloat16", count_range=(0, 12), scales="as", S=5,
+                              weight=True, idx_type=seed % 2, etn_type=seed % 2)
+    t = workloads.torch_inputs(w, dev)
+    call, _ = api.make_call(t["tokens"], t["counts"], per_token_scales=t["scales"], expert_topk_weight=t["weight"],
+                            expert_token_num_type=w.etn_type, idx_type=w.idx_type)
+    assert call.plan()["fused"] == 1
+    whole, st1 = run_hip(w, dev)
+    parts, st2 = run_hip(w, dev, phases=True)
+    assert st1 == st2 == _lib.SUCCESS
+    for x, y in zip(whole, parts):
+        assert np.array_equal(x, y)
+    assert_parity(w, whole, run_oracle(w))
 
 
 # --- seeded fuzz over the contract ----------------------------------------
@@ -214,8 +236,9 @@ def test_repeat_calls_identical():
 
 # --- device-detected count errors -------------------------------------------
 
+@pytest.mark.parametrize("phases", [False, True], ids=["whole", "phases"])
 @pytest.mark.parametrize("kind", ["negative", "sum_low", "sum_high", "too_large"])
-def test_bad_counts_write_nothing(kind):
+def test_bad_counts_write_nothing(kind, phases):
     dev = _dev()
     rng = np.random.default_rng(3)
     counts = rng.integers(1, 5, (4, 3)).astype(np.int64)
@@ -233,10 +256,24 @@ def test_bad_counts_write_nothing(kind):
     w = workloads.Workload(f"bad_{kind}", counts, tok, "int8", 64,
                            rng.standard_normal(a, dtype=np.float32), "float32",
                            rng.random((a, 1), dtype=np.float32), 1, 0)
-    out, status = run_hip(w, dev)
+    out, status = run_hip(w, dev, phases=phases)
     assert status == _lib.ERROR_BAD_COUNTS
     for o in out:
         assert (o == SENTINEL).all(), kind
+
+
+def test_bad_counts_large_table():
+    """A count matrix too large for the single-kernel path, with a bad sum."""
+    dev = _dev()
+    rng = np.random.default_rng(9)
+    counts = rng.integers(0, 3, (256, 64)).astype(np.int32)
+    a = int(counts.sum())
+    counts[100, 7] += 1
+    w = workloads.Workload("bad_large", counts, rng.integers(0, 256, (a, 32), dtype=np.uint8), "int8", 32)
+    out, status = run_hip(w, dev)
+    assert status == _lib.ERROR_BAD_COUNTS
+    for o in out:
+        assert (o == SENTINEL).all()
 
 
 def test_bad_counts_raise_with_check():
@@ -247,15 +284,22 @@ def test_bad_counts_raise_with_check():
         api.moe_re_routing(tokens, counts, check=True)
 
 
-def test_gather_needs_matching_tables():
-    """A gather phase on a workspace whose tables were built for another
-    (A, N, E) writes nothing."""
+@pytest.mark.parametrize("first", ["offsets", "fused_call"])
+def test_gather_needs_matching_tables(first):
+    """A gather phase on a workspace whose table was built for another
+    (A, N, E), or that holds no table (a fused whole call builds none),
+    writes nothing."""
     dev = _dev()
     w1 = workloads.random_case(1, 3, 3, 64, tokens_dtype="int8", count_range=(1, 5))
     t1 = workloads.torch_inputs(w1, dev)
     call1, _ = api.make_call(t1["tokens"], t1["counts"])
-    call1.run()
-    w2 = workloads.random_case(2, 3, 4, 64, tokens_dtype="int8", count_range=(1, 5))
+    if first == "offsets":
+        call1.run_offsets()
+    else:
+        assert call1.plan()["fused"] == 1
+        call1.run()
+    w2 = (workloads.random_case(2, 3, 4, 64, tokens_dtype="int8", count_range=(1, 5)) if first == "offsets"
+          else w1)
     t2 = workloads.torch_inputs(w2, dev)
     args, outs = api.prepare(t2["tokens"], t2["counts"])
     for o in outs:
