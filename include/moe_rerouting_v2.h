@@ -158,6 +158,8 @@ typedef struct mrr_plan_info {
   int64_t gather_workgroups;
   int64_t token_row_bytes;
   int64_t scale_row_bytes;
+  int32_t scale_inline_bytes;    /* 16 or 4: scale rows move in pieces of that size together with
+                                    the token rows; 0: in a separate pass after them */
 } mrr_plan_info;
 
 /*

@@ -68,6 +68,7 @@ class MrrPlanInfo(ctypes.Structure):
         ("gather_workgroups", ctypes.c_int64),
         ("token_row_bytes", ctypes.c_int64),
         ("scale_row_bytes", ctypes.c_int64),
+        ("scale_inline_bytes", ctypes.c_int32),
     ]
 
 

@@ -50,23 +50,29 @@ constexpr int kGatherThreads = MRR_GATHER_THREADS;
 constexpr int kGatherUnroll = MRR_GATHER_UNROLL;
 constexpr int kMaxRowsPerWg = 256;
 
-// LDS row stride of the staged count matrix: E plus at least one spare slot,
-// and odd, so that lanes walking cells in chunks of odd length start in
-// distinct LDS banks.
-inline int64_t lds_row_stride(int64_t E) { return (E % 2 == 0) ? E + 1 : E + 2; }
-
-// Dynamic LDS of the offsets computed in a workgroup's LDS: the counts /
-// source-offset matrix [N][ES] and the expert starts [E + 1] (int32), plus,
-// when `with_table`, the (dst_off, src_off) pair table [M + 1] placed first.
-inline int64_t lds_offsets_bytes(int64_t N, int64_t E, bool with_table) {
-  const int64_t tab = with_table ? 8 * (N * E + 1) : 0;
-  return tab + 4 * (N * lds_row_stride(E) + E + 1);
+// Offsets computed in one workgroup's LDS (the single-workgroup offsets
+// kernel, and every workgroup of the fused kernel) use one of two layouts:
+//  * one cell per thread (M <= threads): counts and source offsets in
+//    column-major cell order, [M] int32 each;
+//  * chunks of cells per thread (M > threads): counts (overwritten by the
+//    destination offsets) and source offsets as [E][NS] int32 matrices, the
+//    column stride NS = N rounded up to odd so that lanes walking odd-length
+//    chunks hit distinct LDS banks;
+// plus the expert starts [E + 1]. 16 bytes of slack keep the first-cell reads
+// of an empty matrix inside the allocation.
+inline int64_t lds_col_stride(int64_t N) { return N | 1; }
+inline int64_t offsets_lds_bytes(int64_t N, int64_t E, int64_t threads) {
+  const int64_t M = N * E;
+  const int64_t mats = M <= threads ? 2 * M : 2 * E * lds_col_stride(N);
+  return 4 * (mats + E + 1) + 16;
 }
 
 // The whole call runs as one kernel (each gather workgroup recomputes the
-// offsets in LDS) when that LDS stays this small, so that it does not limit
-// how many workgroups a CU holds.
-constexpr int64_t kFusedMaxLds = 8192;
+// offsets in LDS, one cell per thread) when the count matrix has at most as
+// many cells as a gather workgroup has threads.
+inline int64_t fused_lds_bytes(int64_t N, int64_t E) {
+  return 8 * (N * E + 1) + offsets_lds_bytes(N, E, MRR_GATHER_THREADS);
+}
 
 // Everything the launchers need, derived on the host from mrr_args.
 struct Plan {
@@ -76,6 +82,9 @@ struct Plan {
   int64_t vecs_per_row;     // R / token_vec
   int64_t scale_row_bytes;  // Rs, 0 when there is nothing to move
   int scale_vec;            // bytes per access of the scale copy
+  int scale_inline;         // 16 or 4: scale rows moved in pieces of that many bytes, at most one
+                            // piece per thread, loaded together with the token rows; 0: a
+                            // separate pass after the token rows
   int count_bytes;          // 4 or 8
   bool has_weight;
   bool scatter;             // idx_type == 1

@@ -55,6 +55,7 @@ constexpr int kOffsetItems = 4;  // counts per thread per tile (global path)
 constexpr int kOffsetTile = kOffsetThreads * kOffsetItems;
 constexpr int kStageUnroll = 8;  // count loads in flight per thread while staging
 
+
 // ---------------------------------------------------------------------------
 // Workgroup scans
 // ---------------------------------------------------------------------------
@@ -99,6 +100,61 @@ __device__ __forceinline__ uint32_t block_or(uint32_t flags, uint32_t* s_flags) 
   return *s_flags;
 }
 
+// Inclusive scan over the 64 lanes of a wave (wrapping 32-bit adds), with no
+// LDS traffic: DPP row shifts by 1, 2, 4 and 8 scan each row of 16 lanes, then
+// the row totals (read with readlane) are added to the later rows. Every lane
+// of the wave must be active.
+__device__ __forceinline__ uint32_t wave_scan_u32(uint32_t v) {
+  constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kRowShr1, 0xf, 0xf, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kRowShr2, 0xf, 0xf, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kRowShr4, 0xf, 0xf, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kRowShr8, 0xf, 0xf, false));
+  const uint32_t r0 = __builtin_amdgcn_readlane(v, 15);
+  const uint32_t r1 = __builtin_amdgcn_readlane(v, 31);
+  const uint32_t r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return v + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+}
+
+// Exact sum over the 64 lanes of a wave of values below 2^36, without LDS:
+// the low 16 and the high 20 bits are summed apart with the DPP scan (each sum
+// fits in 32 bits) and recombined.
+__device__ __forceinline__ uint64_t wave_sum_u36(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readlane(wave_scan_u32(static_cast<uint32_t>(v & 0xffffu)), 63);
+  const uint32_t hi = __builtin_amdgcn_readlane(wave_scan_u32(static_cast<uint32_t>(v >> 16)), 63);
+  return (uint64_t(hi) << 16) + lo;
+}
+
+// Exclusive scan of v over the workgroup (thread order) with wrapping 32-bit
+// adds. With kExact, also the exact workgroup sum of `exact` (each < 2^36)
+// in *total: a caller that finds *total == A (<= INT32_MAX) with every term
+// >= 0 knows that no partial sum wrapped. s_w and s_t hold kThreads / 64
+// entries each and must not be reused before a later barrier.
+template <int kThreads, bool kExact>
+__device__ __forceinline__ uint32_t block_scan_u32(uint32_t v, uint64_t exact, uint32_t* s_w, uint64_t* s_t,
+                                                   uint64_t* total) {
+  constexpr int kW = kThreads / 64;
+  const int wave = threadIdx.x >> 6;
+  const uint32_t incl = wave_scan_u32(v);
+  uint64_t wsum = 0;
+  if (kExact) wsum = wave_sum_u36(exact);
+  if ((threadIdx.x & 63) == 63) {
+    s_w[wave] = incl;
+    if (kExact) s_t[wave] = wsum;
+  }
+  __syncthreads();
+  uint32_t base = 0;
+  uint64_t tot = 0;
+#pragma unroll
+  for (int k = 0; k < kW; ++k) {
+    if (kExact) tot += s_t[k];
+    if (k < wave) base += s_w[k];
+  }
+  if (kExact) *total = tot;
+  return base + incl - v;
+}
+
 template <typename CountT>
 __device__ __forceinline__ int32_t clamp_count(CountT raw, uint32_t* flags) {
   const int64_t v = static_cast<int64_t>(raw);
@@ -127,113 +183,17 @@ __device__ __forceinline__ void write_header(WsHeader* hdr, int64_t A, int64_t N
 // Offsets in a workgroup's LDS
 // ---------------------------------------------------------------------------
 
-// Computes both offset tables of counts[N][E] in LDS with kThreads threads.
-// q is an [N][ES] int32 LDS array (ES = lds_row_stride(E), odd): it first
-// holds the clamped counts, then, in place, the row-major exclusive prefix
-// q[i][j] = SrcOffset(i, j), with q[i][E] = SrcOffset(i+1, 0) (the prefix at
-// the end of row i), so that a count is q[i][j+1] - q[i][j]. Each thread owns
-// a contiguous chunk of C cells (C odd) of one order at a time; with both C
-// and ES odd, the 64 lanes of a wave start their chunks in distinct LDS banks.
-// Writes tab[m] = (DstOffset, SrcOffset) for m = j*N + i and tab[M] = (A, A)
-// (tab in LDS or global memory), and col[j] = DstOffset(0, j), col[E] = A.
-// Returns 0, or the rejection flags (the same in every thread; then tab and
-// col are not written).
-template <int kThreads, typename CountT>
-__device__ uint32_t lds_offsets(const CountT* __restrict__ counts, int N, int E, int ES, int64_t A, int32_t* q,
-                                int32_t* col, pair_t* tab, int64_t* s_scan, uint32_t* s_flags, int64_t* total_out) {
-  const int tid = threadIdx.x;
-  const int M = N * E;
-  int C = (M + kThreads - 1) / kThreads;
-  C |= 1;
-  if (tid == 0) *s_flags = 0;
-  for (int j = tid; j <= E; j += kThreads) col[j] = 0;
+// Scratch a workgroup needs to exchange wave results while computing offsets.
+template <int kThreads>
+struct ScanShared {
+  uint32_t w[2][kThreads / 64];
+  uint64_t t[2][kThreads / 64];
+  uint32_t flags;
+};
 
-  // Stage the counts: coalesced, branch-free loads, kStageUnroll in flight.
-  uint32_t flags = 0;
-  for (int base = 0; base < M; base += kThreads * kStageUnroll) {
-    CountT v[kStageUnroll];
-#pragma unroll
-    for (int u = 0; u < kStageUnroll; ++u) {
-      const int m = base + tid + u * kThreads;
-      v[u] = counts[m < M ? m : M - 1];
-    }
-#pragma unroll
-    for (int u = 0; u < kStageUnroll; ++u) {
-      const int m = base + tid + u * kThreads;
-      if (m < M) {
-        const int i = m / E;
-        q[i * ES + (m - i * E)] = clamp_count(v[u], &flags);
-      }
-    }
-  }
-  __syncthreads();
-
-  // Pass 1: SrcOffset, the exclusive prefix in row-major (rank i, expert j) order.
-  const int m0 = tid * C;
-  const int m1 = min(m0 + C, M);
-  int64_t sum = 0;
-  if (m0 < m1) {
-    int i = m0 / E, j = m0 - (m0 / E) * E;
-    for (int m = m0; m < m1; ++m) {
-      sum += q[i * ES + j];
-      if (++j == E) {
-        j = 0;
-        ++i;
-      }
-    }
-  }
-  int64_t total;
-  int64_t run = block_exclusive_scan<kThreads>(sum, s_scan, &total);
-  if (m0 < m1) {
-    int i = m0 / E, j = m0 - (m0 / E) * E;
-    for (int m = m0; m < m1; ++m) {
-      const int32_t c = q[i * ES + j];
-      q[i * ES + j] = static_cast<int32_t>(run);
-      run += c;
-      if (j == E - 1) q[i * ES + E] = static_cast<int32_t>(run);
-      if (++j == E) {
-        j = 0;
-        ++i;
-      }
-    }
-  }
-  *total_out = total;
-  flags = block_or(flags, s_flags);
-  if (total != A) flags |= kFlagSumMismatch;
-  if (flags != 0) return flags;
-
-  // Pass 2: DstOffset, the exclusive prefix in column-major (expert j, rank i)
-  // order; each cell's pair is written once, in destination order.
-  sum = 0;
-  if (m0 < m1) {
-    int j = m0 / N, i = m0 - (m0 / N) * N;
-    for (int mc = m0; mc < m1; ++mc) {
-      sum += q[i * ES + j + 1] - q[i * ES + j];
-      if (++i == N) {
-        i = 0;
-        ++j;
-      }
-    }
-  }
-  run = block_exclusive_scan<kThreads>(sum, s_scan, &total);
-  if (m0 < m1) {
-    int j = m0 / N, i = m0 - (m0 / N) * N;
-    for (int mc = m0; mc < m1; ++mc) {
-      const int32_t src = q[i * ES + j];
-      const int32_t c = q[i * ES + j + 1] - src;
-      pair_t t;
-      t.x = static_cast<int32_t>(run);
-      t.y = src;
-      tab[mc] = t;
-      if (i == 0) col[j] = static_cast<int32_t>(run);
-      run += c;
-      if (++i == N) {
-        i = 0;
-        ++j;
-      }
-    }
-  }
-  if (tid == 0) {
+// Writes the end-of-table entries and finishes: tab[M] = (A, A), col[E] = A.
+__device__ __forceinline__ void finish_offsets(pair_t* tab, int32_t* col, int M, int E, int64_t A) {
+  if (threadIdx.x == 0) {
     pair_t t;
     t.x = static_cast<int32_t>(A);
     t.y = static_cast<int32_t>(A);
@@ -241,6 +201,187 @@ __device__ uint32_t lds_offsets(const CountT* __restrict__ counts, int N, int E,
     col[E] = static_cast<int32_t>(A);
   }
   __syncthreads();
+}
+
+// Both offset tables of counts[N][E] with one cell per thread (M <= kThreads),
+// in a workgroup's LDS. lds holds the counts and the source offsets in
+// column-major cell order ([M] int32 each). Writes tab[m] = (DstOffset,
+// SrcOffset) for m = j*N + i (tab in LDS or global memory; coalesced), tab[M]
+// = (A, A), and the expert starts col[j] = DstOffset(0, j), col[E] = A.
+// Returns 0, or the rejection flags (the same in every thread; then tab and
+// col are not written).
+template <int kThreads, typename CountT>
+__device__ uint32_t offsets_cells(const CountT* __restrict__ counts, int N, int E, int64_t A, int32_t* lds,
+                                  int32_t* col, pair_t* tab, ScanShared<kThreads>* sh, int64_t* total_out) {
+  const int tid = threadIdx.x;
+  const int M = N * E;
+  int32_t* s_c = lds;      // counts, column-major
+  int32_t* s_s = lds + M;  // SrcOffset, column-major
+  if (tid == 0) sh->flags = 0;
+  for (int j = tid; j <= E; j += kThreads) col[j] = 0;
+  uint32_t flags = 0;
+  // Thread t holds cell t in row-major (rank i, expert j) order.
+  const bool in = tid < M;
+  uint32_t c = 0;
+  if (in) c = static_cast<uint32_t>(clamp_count(counts[tid], &flags));
+  uint64_t total;
+  const uint32_t src = block_scan_u32<kThreads, true>(c, c, sh->w[0], sh->t[0], &total);
+  if (in) {
+    const int i = tid / E;
+    const int j = tid - i * E;
+    s_c[j * N + i] = static_cast<int32_t>(c);
+    s_s[j * N + i] = static_cast<int32_t>(src);
+  }
+  *total_out = static_cast<int64_t>(total);
+  flags = block_or(flags, &sh->flags);  // also orders the writes above before the reads below
+  if (total != static_cast<uint64_t>(A)) flags |= kFlagSumMismatch;
+  if (flags != 0) return flags;
+  // Thread u now holds cell u in column-major (expert j, rank i) order.
+  const uint32_t c2 = in ? static_cast<uint32_t>(s_c[tid]) : 0u;
+  uint64_t unused;
+  const uint32_t dst = block_scan_u32<kThreads, false>(c2, 0, sh->w[1], sh->t[1], &unused);
+  if (in) {
+    pair_t t;
+    t.x = static_cast<int32_t>(dst);
+    t.y = s_s[tid];
+    tab[tid] = t;
+    if (tid % N == 0) col[tid / N] = static_cast<int32_t>(dst);
+  }
+  finish_offsets(tab, col, M, E, A);
+  return 0;
+}
+
+// The same for larger matrices (kThreads < M <= kThreads * kC), with chunks of
+// kC consecutive cells per thread (kC odd). lds holds two [E][NS] int32
+// matrices, NS = N rounded up to odd: the counts (overwritten by DstOffset)
+// and SrcOffset. Chunk loops are unrolled, so a thread's loads are all in
+// flight together; a chunk walk along a column touches consecutive LDS words,
+// and with kC and NS both odd the 64 lanes of a wave start in distinct banks.
+template <int kThreads, int kC, typename CountT>
+__device__ uint32_t offsets_chunks(const CountT* __restrict__ counts, int N, int E, int64_t A, int32_t* lds,
+                                   int32_t* col, pair_t* tab, ScanShared<kThreads>* sh, int64_t* total_out) {
+  const int tid = threadIdx.x;
+  const int M = N * E;
+  const int NS = N | 1;
+  int32_t* s_c = lds;           // [E][NS]: counts, then DstOffset
+  int32_t* s_s = lds + E * NS;  // [E][NS]: SrcOffset
+  if (tid == 0) sh->flags = 0;
+  for (int j = tid; j <= E; j += kThreads) col[j] = 0;
+  uint32_t flags = 0;
+  const int m0 = tid * kC;
+
+  // Stage the counts with coalesced loads, all in flight: cell m = i*E + j
+  // (m = tid + k * kThreads) goes to s_c[j][i].
+  {
+    CountT raw[kC];
+#pragma unroll
+    for (int k = 0; k < kC; ++k) {
+      const int m = tid + k * kThreads;
+      raw[k] = counts[m < M ? m : M - 1];
+    }
+    int i = tid / E, j = tid - (tid / E) * E;
+    const int di = kThreads / E, dj = kThreads - (kThreads / E) * E;
+#pragma unroll
+    for (int k = 0; k < kC; ++k) {
+      if (tid + k * kThreads < M) s_c[j * NS + i] = clamp_count(raw[k], &flags);
+      i += di;
+      j += dj;
+      const bool wrap = j >= E;
+      j = wrap ? j - E : j;
+      i += wrap ? 1 : 0;
+    }
+  }
+  __syncthreads();
+
+  // Pass 1: SrcOffset over my row-major chunk [m0, m0 + kC).
+  uint64_t total;
+  {
+    int addr[kC];
+    int i = m0 / E, j = m0 - (m0 / E) * E;
+#pragma unroll
+    for (int k = 0; k < kC; ++k) {
+      addr[k] = m0 + k < M ? j * NS + i : 0;
+      ++j;
+      const bool wrap = j == E;
+      j = wrap ? 0 : j;
+      i += wrap ? 1 : 0;
+    }
+    uint32_t c[kC];
+    uint32_t local = 0;
+    uint64_t exact = 0;
+#pragma unroll
+    for (int k = 0; k < kC; ++k) {
+      c[k] = m0 + k < M ? static_cast<uint32_t>(s_c[addr[k]]) : 0u;
+      local += c[k];
+      exact += c[k];
+    }
+    uint32_t run = block_scan_u32<kThreads, true>(local, exact, sh->w[0], sh->t[0], &total);
+#pragma unroll
+    for (int k = 0; k < kC; ++k) {
+      if (m0 + k < M) s_s[addr[k]] = static_cast<int32_t>(run);
+      run += c[k];
+    }
+  }
+  *total_out = static_cast<int64_t>(total);
+  flags = block_or(flags, &sh->flags);  // also orders pass 1's writes before pass 2's reads
+  if (total != static_cast<uint64_t>(A)) flags |= kFlagSumMismatch;
+  if (flags != 0) return flags;
+
+  // Pass 2: DstOffset over my column-major chunk, in place of the counts.
+  {
+    int addr[kC];
+    uint32_t c[kC];
+    uint32_t top = 0;  // bit k: the chunk's k-th cell is rank 0 of its expert
+    int j = m0 / N, i = m0 - (m0 / N) * N;
+#pragma unroll
+    for (int k = 0; k < kC; ++k) {
+      addr[k] = m0 + k < M ? j * NS + i : 0;
+      top |= (m0 + k < M && i == 0 ? 1u : 0u) << k;
+      ++i;
+      const bool wrap = i == N;
+      i = wrap ? 0 : i;
+      j += wrap ? 1 : 0;
+    }
+    uint32_t local = 0;
+#pragma unroll
+    for (int k = 0; k < kC; ++k) {
+      c[k] = m0 + k < M ? static_cast<uint32_t>(s_c[addr[k]]) : 0u;
+      local += c[k];
+    }
+    uint64_t unused;
+    uint32_t run = block_scan_u32<kThreads, false>(local, 0, sh->w[1], sh->t[1], &unused);
+#pragma unroll
+    for (int k = 0; k < kC; ++k) {
+      if (m0 + k < M) {
+        s_c[addr[k]] = static_cast<int32_t>(run);
+        if ((top >> k) & 1u) col[(m0 + k) / N] = static_cast<int32_t>(run);
+      }
+      run += c[k];
+    }
+  }
+  __syncthreads();
+
+  // The table, with coalesced stores: cell m = j*N + i.
+  {
+    int j = tid / N, i = tid - (tid / N) * N;
+    const int dj = kThreads / N, di = kThreads - (kThreads / N) * N;
+#pragma unroll
+    for (int k = 0; k < kC; ++k) {
+      const int m = tid + k * kThreads;
+      if (m < M) {
+        pair_t t;
+        t.x = s_c[j * NS + i];
+        t.y = s_s[j * NS + i];
+        tab[m] = t;
+      }
+      i += di;
+      j += dj;
+      const bool wrap = i >= N;
+      i = wrap ? i - N : i;
+      j += wrap ? 1 : 0;
+    }
+  }
+  finish_offsets(tab, col, M, E, A);
   return 0;
 }
 
@@ -256,18 +397,20 @@ __device__ __forceinline__ void write_etn(const int32_t* col, int E, int cumsum,
 // Offsets kernels
 // ---------------------------------------------------------------------------
 
-template <typename CountT>
+// kC == 1: one cell per thread (M <= kOffsetThreads); otherwise chunks of kC.
+template <typename CountT, int kC>
 __global__ __launch_bounds__(kOffsetThreads) void offsets_staged_kernel(
-    const CountT* __restrict__ counts, int32_t N, int32_t E, int32_t ES, int64_t A, int cumsum,
-    CountT* __restrict__ etn, WsHeader* __restrict__ hdr, pair_t* __restrict__ table) {
+    const CountT* __restrict__ counts, int32_t N, int32_t E, int64_t A, int cumsum, CountT* __restrict__ etn,
+    WsHeader* __restrict__ hdr, pair_t* __restrict__ table, int32_t mats_ints) {
   extern __shared__ int32_t s_dyn[];
-  __shared__ int64_t s_scan[2 * kOffsetThreads / 64 + 1];
-  __shared__ uint32_t s_flags;
-  int32_t* q = s_dyn;             // [N][ES]
-  int32_t* col = s_dyn + N * ES;  // [E + 1]
+  __shared__ ScanShared<kOffsetThreads> sh;
+  int32_t* col = s_dyn + mats_ints;  // [E + 1], after the offset matrices
   int64_t total = 0;
-  const uint32_t flags =
-      lds_offsets<kOffsetThreads>(counts, N, E, ES, A, q, col, table, s_scan, &s_flags, &total);
+  uint32_t flags;
+  if (kC == 1)
+    flags = offsets_cells<kOffsetThreads>(counts, N, E, A, s_dyn, col, table, &sh, &total);
+  else
+    flags = offsets_chunks<kOffsetThreads, kC>(counts, N, E, A, s_dyn, col, table, &sh, &total);
   if (flags == 0) write_etn<kOffsetThreads>(col, E, cumsum, etn);
   if (threadIdx.x == 0) write_header(hdr, A, N, E, total, flags, kTablesValid);
 }
@@ -503,18 +646,15 @@ __device__ __forceinline__ void copy_rows(const uint8_t* __restrict__ src, uint8
   const int dr = kGatherThreads / vpr;
   const int dc = kGatherThreads - dr * vpr;
   for (int e0 = 0; e0 < total; e0 += kGatherThreads * kGatherUnroll) {
-    T v[kGatherUnroll];
-    bool ok[kGatherUnroll];
+    // First every item's (row, column) and source row (LDS reads, all issued
+    // together), then all the loads, then all the stores.
+    int32_t srow[kGatherUnroll];
+    int col[kGatherUnroll];
 #pragma unroll
     for (int k = 0; k < kGatherUnroll; ++k) {
-      const int e = e0 + tid + k * kGatherThreads;
-      const bool in = e < total;
-      const int32_t srow = s_src[in ? r : 0];
-      ok[k] = in && srow >= 0;
-      // Branch-free load: items out of range read row 0, column 0 (always
-      // valid, since A > 0 here) and are not stored.
-      const int64_t off = ok[k] ? int64_t(srow) * row_bytes + int64_t(c) * V : 0;
-      v[k] = __builtin_nontemporal_load(reinterpret_cast<const T*>(src + off));
+      const bool in = e0 + tid + k * kGatherThreads < total;
+      srow[k] = s_src[in ? r : 0];
+      col[k] = in ? c : -1;
       r += dr;
       c += dc;
       if (c >= vpr) {
@@ -522,45 +662,83 @@ __device__ __forceinline__ void copy_rows(const uint8_t* __restrict__ src, uint8
         ++r;
       }
     }
+    T v[kGatherUnroll];
+#pragma unroll
+    for (int k = 0; k < kGatherUnroll; ++k) {
+      // Branch-free load: items out of range read row 0, column 0 (always
+      // valid, since A > 0 here) and are not stored.
+      const bool ok = col[k] >= 0 && srow[k] >= 0;
+      const int64_t off = ok ? int64_t(srow[k]) * row_bytes + int64_t(col[k]) * V : 0;
+      v[k] = __builtin_nontemporal_load(reinterpret_cast<const T*>(src + off));
+    }
 #pragma unroll
     for (int k = 0; k < kGatherUnroll; ++k) {
       const int e = e0 + tid + k * kGatherThreads;
-      if (ok[k]) __builtin_nontemporal_store(v[k], reinterpret_cast<T*>(dst_chunk + int64_t(e) * V));
+      if (col[k] >= 0 && srow[k] >= 0)
+        __builtin_nontemporal_store(v[k], reinterpret_cast<T*>(dst_chunk + int64_t(e) * V));
     }
   }
 }
 
 // Everything a workgroup writes for its output rows row0 + [0, rows), once
 // s_src holds their source rows: the index and weight (one lane per row), the
-// token rows and the scale rows.
-template <int V, bool kScatter, bool kWeight>
+// token rows and the scale rows. The small loads (the weight, and with kSV > 0
+// this thread's kSV-byte piece of the scale rows) are issued before the token
+// copy so that they are in flight with it, and stored after it; with kSV == 0
+// the scale rows take a separate pass after the token rows.
+template <int V, int kSV, bool kScatter, bool kWeight>
 __device__ __forceinline__ void move_rows(const GatherArgs& p, int row0, int rows, const int32_t* s_src) {
-  for (int lr = threadIdx.x; lr < rows; lr += kGatherThreads) {
-    const int32_t s = s_src[lr];
+  const int tid = threadIdx.x;
+  const int64_t Rs = p.scale_row_bytes;
+
+  // This thread's row for the per-row words (first round; more rows than
+  // threads only happen for tiny rows and are handled below).
+  const int32_t my_s = tid < rows ? s_src[tid] : -1;
+  uint32_t wv = 0;
+  if (kWeight) wv = p.weight[my_s >= 0 ? my_s : 0];  // branch-free: row 0 when unused
+
+  using ST = typename VecT<(kSV > 0 ? kSV : 4)>::type;
+  ST piece{};
+  int32_t sc_src = -1;
+  int sc_row = 0, sc_off = 0;
+  if (kSV > 0) {
+    const int spr = static_cast<int>(Rs / kSV);  // pieces per scale row
+    sc_row = tid / spr;
+    sc_off = (tid - sc_row * spr) * kSV;
+    sc_src = tid < rows * spr ? s_src[sc_row] : -1;
+    const int64_t off = sc_src >= 0 ? int64_t(sc_src) * Rs + sc_off : 0;  // branch-free
+    piece = __builtin_nontemporal_load(reinterpret_cast<const ST*>(p.scales + off));
+  }
+
+  copy_rows<V>(p.tokens, p.out_tokens + int64_t(row0) * p.row_bytes, p.row_bytes, p.vecs_per_row, rows, s_src);
+
+  if (kSV > 0 && sc_src >= 0)
+    __builtin_nontemporal_store(piece, reinterpret_cast<ST*>(p.out_scales + int64_t(row0 + sc_row) * Rs + sc_off));
+  for (int lr = tid; lr < rows; lr += kGatherThreads) {
+    const int32_t s = lr == tid ? my_s : s_src[lr];
     if (s < 0) continue;
     const int d = row0 + lr;
     if (kScatter)
       p.idx[s] = d;
     else
       p.idx[d] = s;
-    if (kWeight) p.out_weight[d] = p.weight[s];
+    if (kWeight) p.out_weight[d] = lr == tid ? wv : p.weight[s];
   }
 
-  copy_rows<V>(p.tokens, p.out_tokens + int64_t(row0) * p.row_bytes, p.row_bytes, p.vecs_per_row, rows, s_src);
-
-  if (p.scale_row_bytes > 0) {
-    uint8_t* out = p.out_scales + int64_t(row0) * p.scale_row_bytes;
+  if (kSV == 0 && Rs > 0) {
+    uint8_t* out = p.out_scales + int64_t(row0) * Rs;
+    const int spr = p.scale_vecs_per_row;
     switch (p.scale_vec) {
-      case 16: copy_rows<16>(p.scales, out, p.scale_row_bytes, p.scale_vecs_per_row, rows, s_src); break;
-      case 8: copy_rows<8>(p.scales, out, p.scale_row_bytes, p.scale_vecs_per_row, rows, s_src); break;
-      case 4: copy_rows<4>(p.scales, out, p.scale_row_bytes, p.scale_vecs_per_row, rows, s_src); break;
-      case 2: copy_rows<2>(p.scales, out, p.scale_row_bytes, p.scale_vecs_per_row, rows, s_src); break;
-      default: copy_rows<1>(p.scales, out, p.scale_row_bytes, p.scale_vecs_per_row, rows, s_src); break;
+      case 16: copy_rows<16>(p.scales, out, Rs, spr, rows, s_src); break;
+      case 8: copy_rows<8>(p.scales, out, Rs, spr, rows, s_src); break;
+      case 4: copy_rows<4>(p.scales, out, Rs, spr, rows, s_src); break;
+      case 2: copy_rows<2>(p.scales, out, Rs, spr, rows, s_src); break;
+      default: copy_rows<1>(p.scales, out, Rs, spr, rows, s_src); break;
     }
   }
 }
 
-template <int V, bool kScatter, bool kWeight>
+template <int V, int kSV, bool kScatter, bool kWeight>
 __global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs p) {
   __shared__ int32_t s_src[kMaxRowsPerWg];
   const int row0 = blockIdx.x * p.rows_per_wg;
@@ -573,30 +751,28 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs p) {
   map_rows(p.table, p.M, p.A, row0, rows, s_src);
   if (!valid_table) return;  // uniform over the workgroup
   __syncthreads();
-  move_rows<V, kScatter, kWeight>(p, row0, rows, s_src);
+  move_rows<V, kSV, kScatter, kWeight>(p, row0, rows, s_src);
 }
 
 struct FusedArgs {
   const void* counts;
   void* etn;
-  int32_t ES;
   int32_t cumsum;
 };
 
-template <int V, bool kScatter, bool kWeight, typename CountT>
+template <int V, int kSV, bool kScatter, bool kWeight, typename CountT>
 __global__ __launch_bounds__(kGatherThreads) void fused_kernel(GatherArgs p, FusedArgs f) {
   extern __shared__ int32_t s_dyn[];
   __shared__ int32_t s_src[kMaxRowsPerWg];
-  __shared__ int64_t s_scan[2 * kGatherThreads / 64 + 1];
-  __shared__ uint32_t s_flags;
+  __shared__ ScanShared<kGatherThreads> sh;
   const int N = static_cast<int>(p.N);
   const int E = static_cast<int>(p.E);
   auto* tab = reinterpret_cast<pair_t*>(s_dyn);  // [M + 1], first: 8-byte aligned
-  int32_t* q = s_dyn + 2 * (p.M + 1);            // [N][ES]
-  int32_t* col = q + N * f.ES;                   // [E + 1]
+  int32_t* mats = s_dyn + 2 * (p.M + 1);         // counts and source offsets, [M] each
+  int32_t* col = mats + 2 * p.M;                 // [E + 1]
   int64_t total = 0;
-  const uint32_t flags = lds_offsets<kGatherThreads>(static_cast<const CountT*>(f.counts), N, E, f.ES, p.A, q, col,
-                                                     tab, s_scan, &s_flags, &total);
+  const uint32_t flags =
+      offsets_cells<kGatherThreads>(static_cast<const CountT*>(f.counts), N, E, p.A, mats, col, tab, &sh, &total);
   if (blockIdx.x == 0) {
     if (flags == 0) write_etn<kGatherThreads>(col, E, f.cumsum, static_cast<CountT*>(f.etn));
     if (threadIdx.x == 0) write_header(p.hdr, p.A, p.N, p.E, total, flags, kCountsValid);
@@ -607,12 +783,27 @@ __global__ __launch_bounds__(kGatherThreads) void fused_kernel(GatherArgs p, Fus
   const int rows = min(p.rows_per_wg, p.A - row0);
   map_rows(tab, p.M, p.A, row0, rows, s_src);
   __syncthreads();
-  move_rows<V, kScatter, kWeight>(p, row0, rows, s_src);
+  move_rows<V, kSV, kScatter, kWeight>(p, row0, rows, s_src);
 }
 
 // ---------------------------------------------------------------------------
 // Host side
 // ---------------------------------------------------------------------------
+
+// Chunk lengths of the single-workgroup offsets kernel (1: one cell per
+// thread); the launcher takes the smallest that covers the count matrix.
+constexpr int kChunkSizes[] = {1, 3, 5, 9, 17};
+
+template <typename CountT>
+const void* staged_kernel_fn(int kc) {
+  switch (kc) {
+    case 1: return reinterpret_cast<const void*>(&offsets_staged_kernel<CountT, 1>);
+    case 3: return reinterpret_cast<const void*>(&offsets_staged_kernel<CountT, 3>);
+    case 5: return reinterpret_cast<const void*>(&offsets_staged_kernel<CountT, 5>);
+    case 9: return reinterpret_cast<const void*>(&offsets_staged_kernel<CountT, 9>);
+    default: return reinterpret_cast<const void*>(&offsets_staged_kernel<CountT, 17>);
+  }
+}
 
 // Per-device facts, read once per device.
 struct DeviceInfo {
@@ -636,12 +827,16 @@ mrr_status device_info(const DeviceInfo** out) {
     if (hipDeviceGetAttribute(&plain, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) plain = 0;
     int limit = (plain < 65536 ? plain : 65536) - kStaticLdsReserve;
     const int want = optin - kStaticLdsReserve;
-    if (want > limit &&
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&offsets_staged_kernel<int32_t>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, want) == hipSuccess &&
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&offsets_staged_kernel<int64_t>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, want) == hipSuccess)
-      limit = want;
+    if (want > limit) {
+      bool ok = true;
+      for (int kc : kChunkSizes) {
+        ok = ok && hipFuncSetAttribute(staged_kernel_fn<int32_t>(kc), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       want) == hipSuccess;
+        ok = ok && hipFuncSetAttribute(staged_kernel_fn<int64_t>(kc), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       want) == hipSuccess;
+      }
+      if (ok) limit = want;
+    }
     (void)hipGetLastError();  // a refused opt-in only keeps the smaller limit
     g_dev[dev].lds_limit = limit > 0 ? limit : 0;
   });
@@ -649,24 +844,38 @@ mrr_status device_info(const DeviceInfo** out) {
   return MRR_SUCCESS;
 }
 
+template <typename CountT, int kC>
+void launch_staged(const Plan& pl, const mrr_args* a, uint8_t* base, size_t lds, hipStream_t stream) {
+  const int32_t mats = static_cast<int32_t>((static_cast<int64_t>(lds) - 16) / 4 - (pl.E + 1));
+  hipLaunchKernelGGL((offsets_staged_kernel<CountT, kC>), dim3(1), dim3(kOffsetThreads), lds, stream,
+                     static_cast<const CountT*>(a->expert_token_num_per_rank), static_cast<int32_t>(pl.N),
+                     static_cast<int32_t>(pl.E), pl.A, pl.cumsum ? 1 : 0, static_cast<CountT*>(a->expert_token_num),
+                     reinterpret_cast<WsHeader*>(base), reinterpret_cast<pair_t*>(base + pl.table_bytes), mats);
+}
+
 template <typename CountT>
 mrr_status launch_offsets_t(const Plan& pl, const mrr_args* a, void* ws, hipStream_t stream) {
   const DeviceInfo* di = nullptr;
   if (device_info(&di) != MRR_SUCCESS) return MRR_ERROR_HIP;
   auto* base = static_cast<uint8_t*>(ws);
-  const auto* counts = static_cast<const CountT*>(a->expert_token_num_per_rank);
-  auto* etn = static_cast<CountT*>(a->expert_token_num);
-  auto* hdr = reinterpret_cast<WsHeader*>(base);
-  const int32_t N = static_cast<int32_t>(pl.N);
-  const int32_t E = static_cast<int32_t>(pl.E);
-  const int64_t lds = lds_offsets_bytes(pl.N, pl.E, false);
-  if (lds <= di->lds_limit) {
-    hipLaunchKernelGGL((offsets_staged_kernel<CountT>), dim3(1), dim3(kOffsetThreads), static_cast<size_t>(lds),
-                       stream, counts, N, E, static_cast<int32_t>(lds_row_stride(E)), pl.A, pl.cumsum ? 1 : 0, etn,
-                       hdr, reinterpret_cast<pair_t*>(base + pl.table_bytes));
+  const int64_t lds = offsets_lds_bytes(pl.N, pl.E, kOffsetThreads);
+  int kc = 0;
+  for (int c : kChunkSizes)
+    if (kc == 0 && int64_t(kOffsetThreads) * c >= pl.M) kc = c;
+  if (kc != 0 && lds <= di->lds_limit) {
+    const size_t l = static_cast<size_t>(lds);
+    switch (kc) {
+      case 1: launch_staged<CountT, 1>(pl, a, base, l, stream); break;
+      case 3: launch_staged<CountT, 3>(pl, a, base, l, stream); break;
+      case 5: launch_staged<CountT, 5>(pl, a, base, l, stream); break;
+      case 9: launch_staged<CountT, 9>(pl, a, base, l, stream); break;
+      default: launch_staged<CountT, 17>(pl, a, base, l, stream); break;
+    }
   } else {
-    hipLaunchKernelGGL((offsets_global_kernel<CountT>), dim3(1), dim3(kOffsetThreads), 0, stream, counts, N, E,
-                       pl.A, pl.cumsum ? 1 : 0, etn, hdr, reinterpret_cast<int32_t*>(base + pl.table_bytes));
+    hipLaunchKernelGGL((offsets_global_kernel<CountT>), dim3(1), dim3(kOffsetThreads), 0, stream,
+                       static_cast<const CountT*>(a->expert_token_num_per_rank), static_cast<int32_t>(pl.N),
+                       static_cast<int32_t>(pl.E), pl.A, pl.cumsum ? 1 : 0, static_cast<CountT*>(a->expert_token_num),
+                       reinterpret_cast<WsHeader*>(base), reinterpret_cast<int32_t*>(base + pl.table_bytes));
   }
   return hipGetLastError() == hipSuccess ? MRR_SUCCESS : MRR_ERROR_HIP;
 }
@@ -701,44 +910,56 @@ GatherArgs gather_args(const Plan& pl, const mrr_args* a, void* ws) {
   return g;
 }
 
-// Launches kernel K<V, scatter, weight> (gather or fused) for the plan's
-// vector width and flags; `launch` receives a pointer to the instance.
-template <template <int, bool, bool> class K, typename Launch>
+// Launches kernel K<V, SV, scatter, weight> (gather or fused) for the plan's
+// token vector width, inline scale piece width and flags; `launch` receives a
+// pointer to the instance. Inline scale pieces are only planned with 16-byte
+// token vectors.
+template <template <int, int, bool, bool> class K, typename Launch>
 void dispatch(const Plan& pl, Launch&& launch) {
-  auto pick = [&](auto vtag) {
+  auto flags = [&](auto vtag, auto stag) {
     constexpr int V = decltype(vtag)::value;
+    constexpr int SV = decltype(stag)::value;
     if (pl.scatter) {
       if (pl.has_weight)
-        launch(K<V, true, true>::fn());
+        launch(K<V, SV, true, true>::fn());
       else
-        launch(K<V, true, false>::fn());
+        launch(K<V, SV, true, false>::fn());
     } else {
       if (pl.has_weight)
-        launch(K<V, false, true>::fn());
+        launch(K<V, SV, false, true>::fn());
       else
-        launch(K<V, false, false>::fn());
+        launch(K<V, SV, false, false>::fn());
     }
   };
+  using I16 = std::integral_constant<int, 16>;
+  using I0 = std::integral_constant<int, 0>;
   switch (pl.token_vec) {
-    case 16: pick(std::integral_constant<int, 16>{}); break;
-    case 8: pick(std::integral_constant<int, 8>{}); break;
-    case 4: pick(std::integral_constant<int, 4>{}); break;
-    case 2: pick(std::integral_constant<int, 2>{}); break;
-    default: pick(std::integral_constant<int, 1>{}); break;
+    case 16:
+      if (pl.scale_inline == 16)
+        flags(I16{}, I16{});
+      else if (pl.scale_inline == 4)
+        flags(I16{}, std::integral_constant<int, 4>{});
+      else
+        flags(I16{}, I0{});
+      break;
+    case 8: flags(std::integral_constant<int, 8>{}, I0{}); break;
+    case 4: flags(std::integral_constant<int, 4>{}, I0{}); break;
+    case 2: flags(std::integral_constant<int, 2>{}, I0{}); break;
+    default: flags(std::integral_constant<int, 1>{}, I0{}); break;
   }
 }
 
-template <int V, bool S, bool W>
+template <int V, int SV, bool S, bool W>
 struct GatherK {
-  static auto fn() { return &gather_kernel<V, S, W>; }
+  static auto fn() { return &gather_kernel<V, SV, S, W>; }
 };
-template <int V, bool S, bool W>
+template <int V, int SV, bool S, bool W>
 struct FusedK32 {
-  static auto fn() { return &fused_kernel<V, S, W, int32_t>; }
+  static auto fn() { return &fused_kernel<V, SV, S, W, int32_t>; }
 };
-template <int V, bool S, bool W>
+template <int V, int SV, bool S, bool W>
 struct FusedK64 {
-  static auto fn() { return &fused_kernel<V, S, W, int64_t>; }
+  static auto fn() { return &fused_kernel<V, SV, S, W, int64_t>; }
 };
 
 mrr_status launch_gather(const Plan& pl, const mrr_args* a, void* ws, hipStream_t stream) {
@@ -755,9 +976,8 @@ mrr_status launch_fused(const Plan& pl, const mrr_args* a, void* ws, hipStream_t
   FusedArgs f{};
   f.counts = a->expert_token_num_per_rank;
   f.etn = a->expert_token_num;
-  f.ES = static_cast<int32_t>(lds_row_stride(pl.E));
   f.cumsum = pl.cumsum ? 1 : 0;
-  const size_t lds = static_cast<size_t>(lds_offsets_bytes(pl.N, pl.E, true));
+  const size_t lds = static_cast<size_t>(fused_lds_bytes(pl.N, pl.E));
   auto launch = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(pl.grid)), dim3(kGatherThreads), lds, stream, g, f);
   };

@@ -218,7 +218,14 @@ mrr_status make_plan(const mrr_args* a, const void* ws, size_t ws_bytes, Plan* p
   if (tuning().rows_per_wg > 0) rows = tuning().rows_per_wg;
   q.rows_per_wg = static_cast<int>(std::min<int64_t>(std::max<int64_t>(rows, 1), kMaxRowsPerWg));
   q.grid = (q.A + q.rows_per_wg - 1) / q.rows_per_wg;
-  q.fused = tuning().fused && q.A > 0 && lds_offsets_bytes(q.N, q.E, true) <= kFusedMaxLds;
+  q.scale_inline = 0;
+  if (Rs > 0 && q.token_vec == 16) {
+    if (q.scale_vec == 16 && q.rows_per_wg * (Rs / 16) <= kGatherThreads)
+      q.scale_inline = 16;
+    else if (q.scale_vec >= 4 && q.rows_per_wg * (Rs / 4) <= kGatherThreads)
+      q.scale_inline = 4;
+  }
+  q.fused = tuning().fused && q.A > 0 && M <= kGatherThreads;
   q.table_bytes = kHeaderBytes;
   *p = q;
 
@@ -253,5 +260,6 @@ extern "C" mrr_status mrr_describe_plan(const mrr_args* args, const void* worksp
   info->gather_workgroups = plan.grid;
   info->token_row_bytes = plan.row_bytes;
   info->scale_row_bytes = plan.scale_row_bytes;
+  info->scale_inline_bytes = plan.scale_inline;
   return MRR_SUCCESS;
 }

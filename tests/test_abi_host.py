@@ -181,12 +181,21 @@ def test_describe_plan():
     assert st == _lib.SUCCESS
     assert info.fused == 1 and info.token_vec_bytes == 16 and info.token_row_bytes == 7168
     assert info.scale_row_bytes == 4 and info.scale_vec_bytes == 4
+    assert info.scale_inline_bytes == 4            # one 4-byte piece per row, loaded with the tokens
     rows = max(1, info.threads_per_workgroup * 8 // 448)
     assert info.rows_per_workgroup == min(rows, 256)
     assert info.gather_workgroups == -(-16384 // info.rows_per_workgroup)
     # 256x64 counts are too many to recompute per workgroup: two kernels
     st, info = describe(valid_args(A=65536, H=2048, N=256, E=64, tok=_lib.F4_E2M1))
     assert st == _lib.SUCCESS and info.fused == 0 and info.token_row_bytes == 1024
+    # e8m0 scales [A, 112, 2] of H=7168 fp8 tokens: 224-byte scale rows in 16-byte pieces
+    st, info = describe(valid_args(A=32768, H=7168, N=32, E=8, tok=_lib.F8_E4M3FN, scales="e8m0"))
+    assert st == _lib.SUCCESS and info.scale_row_bytes == 224 and info.scale_inline_bytes == 16
+    # more scale pieces than threads: a separate scale pass
+    a = valid_args(A=4096, H=64, tok=_lib.F16)
+    a.scales_ndim, a.scales_dims[1] = 2, 5
+    st, info = describe(a)
+    assert st == _lib.SUCCESS and info.rows_per_workgroup == 256 and info.scale_inline_bytes == 0
     # odd rows fall back to narrower vectors
     a = valid_args(tok=_lib.F16, H=79)
     st, info = describe(a)

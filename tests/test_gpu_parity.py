@@ -212,6 +212,53 @@ def test_large_table_unstaged():
     check(w)
 
 
+# Count matrices of every size class of the single-workgroup offsets kernel:
+# one cell per thread (<= 1024 cells), chunks of 3, 5, 9 and 17 cells per
+# thread (each class's lower and upper edge), and beyond 17408 cells the
+# path through global memory.
+@pytest.mark.parametrize("n,e", [(32, 32), (32, 33), (64, 48), (64, 49), (100, 51), (128, 41), (96, 96), (97, 96),
+                                 (136, 128), (137, 128), (5000, 1), (1, 3000), (3, 1700)])
+def test_offsets_size_classes(n, e):
+    w = workloads.random_case(n * 7 + e, n, e, 40, tokens_dtype="int8", count_range=(0, 4), weight=True,
+                              idx_type=(n + e) % 2, etn_type=(n * e) % 2)
+    check(w)
+    check(w, phases=True)
+
+
+@pytest.mark.parametrize("n,e", [(64, 49), (97, 96)])
+def test_bad_counts_chunked(n, e):
+    dev = _dev()
+    rng = np.random.default_rng(n + e)
+    counts = rng.integers(0, 4, (n, e)).astype(np.int64)
+    a = int(counts.sum())
+    counts[n // 2, e // 3] = -1  # a negative count (the sum no longer matches either)
+    w = workloads.Workload(f"bad_chunk_{n}x{e}", counts, rng.integers(0, 256, (a, 8), dtype=np.uint8), "int8", 8)
+    out, status = run_hip(w, dev)
+    assert status == _lib.ERROR_BAD_COUNTS
+    for o in out:
+        assert (o == SENTINEL).all()
+
+
+@pytest.mark.parametrize("h,tok,scales,S,inline", [
+    (64, "float16", "as", 5, 0),       # 256 rows x 5 pieces > threads: separate scale pass
+    (64, "float16", "a", 1, 4),        # [A] f32: one 4-byte piece per row
+    (7168, "int8", "e8m0", 1, 16),     # 224-byte e8m0 rows: 16-byte pieces
+    (2048, "bfloat16", "as", 32, 16),  # 128-byte rows: 16-byte pieces
+    (2048, "bfloat16", "as", 3, 4),    # 12-byte rows: 4-byte pieces
+    (79, "float16", "e8m0", 1, 0),     # odd rows (2-byte token vectors): separate pass
+])
+def test_scale_paths(h, tok, scales, S, inline):
+    dev = _dev()
+    w = workloads.random_case(h + S, 6, 5, h, tokens_dtype=tok, count_range=(0, 40), scales=scales, S=S,
+                              weight=True, idx_type=h % 2)
+    t = workloads.torch_inputs(w, dev)
+    call, _ = api.make_call(t["tokens"], t["counts"], per_token_scales=t["scales"], expert_topk_weight=t["weight"],
+                            idx_type=w.idx_type, tokens_dtype=t["tokens_dtype"])
+    assert call.plan()["scale_inline_bytes"] == inline
+    check(w)
+    check(w, phases=True)
+
+
 def test_sparse_cells_window_fallback():
     """Rows whose cells lie more than 64 cells apart inside one 64-row batch."""
     counts = np.zeros((40, 100), np.int64)
