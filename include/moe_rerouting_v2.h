@@ -160,6 +160,10 @@ typedef struct mrr_plan_info {
   int64_t scale_row_bytes;
   int32_t scale_inline_bytes;    /* 16 or 4: scale rows move in pieces of that size together with
                                     the token rows; 0: in a separate pass after them */
+  int64_t offsets_workgroups;    /* workgroups of moe_rerouting_v2_offsets(): 1 for the
+                                    single-workgroup kernel, more when each workgroup computes
+                                    the offsets of a band of ranks (larger count matrices);
+                                    0 when there are no cells */
 } mrr_plan_info;
 
 /*
@@ -180,10 +184,12 @@ mrr_status moe_rerouting_v2(const mrr_args* args, void* workspace, size_t worksp
                             struct ihipStream_t* stream);
 
 /*
- * First phase alone (article, "计算公式": the two double sums): one
- * workgroup scans the count matrix and writes the SrcOffset and DstOffset
- * tables and the validity status into the workspace, and expert_token_num
- * into args->expert_token_num (only when the counts are valid).
+ * First phase alone (article, "计算公式": the two double sums): scans the
+ * count matrix (one workgroup, or one per band of ranks for larger
+ * matrices; see mrr_plan_info.offsets_workgroups) and writes the SrcOffset
+ * and DstOffset tables and the validity status into the workspace, and
+ * expert_token_num into args->expert_token_num (only when the counts are
+ * valid).
  */
 mrr_status moe_rerouting_v2_offsets(const mrr_args* args, void* workspace, size_t workspace_bytes,
                                     struct ihipStream_t* stream);

@@ -69,6 +69,7 @@ class MrrPlanInfo(ctypes.Structure):
         ("token_row_bytes", ctypes.c_int64),
         ("scale_row_bytes", ctypes.c_int64),
         ("scale_inline_bytes", ctypes.c_int32),
+        ("offsets_workgroups", ctypes.c_int64),
     ]
 
 

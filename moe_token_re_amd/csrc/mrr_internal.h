@@ -47,8 +47,17 @@ inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 #define MRR_GATHER_UNROLL 8
 #endif
 constexpr int kGatherThreads = MRR_GATHER_THREADS;
+
 constexpr int kGatherUnroll = MRR_GATHER_UNROLL;
 constexpr int kMaxRowsPerWg = 256;
+
+// The offsets kernels run workgroups of kOffsetThreads threads. Count
+// matrices with kOffsetThreads < M <= kBandMaxCells and E <= kOffsetThreads
+// take the banded kernel: one workgroup per band of band_rows ranks, each of
+// which reads the whole matrix once (so its L2 reads grow as M^2 /
+// kOffsetThreads); the others take one workgroup.
+constexpr int kOffsetThreads = 1024;
+constexpr int64_t kBandMaxCells = int64_t(1) << 17;
 
 // Offsets computed in one workgroup's LDS (the single-workgroup offsets
 // kernel, and every workgroup of the fused kernel) use one of two layouts:
@@ -92,6 +101,9 @@ struct Plan {
   bool fused;               // moe_rerouting_v2 runs the single fused kernel
   int rows_per_wg;
   int64_t grid;             // gather workgroups
+  int64_t band_grid;        // banded offsets kernel: workgroups (bands); 0 = single-workgroup kernel
+  int band_rows;            // ranks per band: min(N, kOffsetThreads / E)
+  int band_lanes;           // threads per column in the banded kernel's first step (a power of two)
   size_t table_bytes;       // offset of the (dst_off, src_off) table in the workspace
 };
 

@@ -50,10 +50,8 @@ namespace {
 
 using pair_t = int32_t __attribute__((ext_vector_type(2)));  // (dst_off, src_off)
 
-constexpr int kOffsetThreads = 1024;
 constexpr int kOffsetItems = 4;  // counts per thread per tile (global path)
 constexpr int kOffsetTile = kOffsetThreads * kOffsetItems;
-constexpr int kStageUnroll = 8;  // count loads in flight per thread while staging
 
 
 // ---------------------------------------------------------------------------
@@ -514,6 +512,148 @@ __global__ __launch_bounds__(kOffsetThreads) void offsets_global_kernel(
   if (tid == 0) write_header(hdr, A, N, E, carry, 0, kTablesValid);
 }
 
+// Banded offsets for larger count matrices (kOffsetThreads < M, E <=
+// kOffsetThreads): workgroup b owns the band of rows [i0, i0 + band_rows) and
+// writes the table entries of its cells; no workgroup waits for another.
+//  1. Every workgroup reads the whole count matrix (from L2 after the first
+//     reader) to get, per expert column j, the total T_j over all ranks and
+//     the part B_j above its band. Thread t takes column t % E and every
+//     lanes-th row from row t / E (lanes * E <= kOffsetThreads, a power of
+//     two); an LDS tree adds the lanes' partial sums. Reading every cell also
+//     tells each workgroup whether the counts are valid.
+//  2. Expert j's rows start at DstOffset(0, j) = sum of T_j' over j' < j (a
+//     scan over the columns); the band's first source offset is sum_j B_j.
+//  3. Within the band: a row-major scan of its cells gives SrcOffset, a
+//     column-major scan (within each column, added to DstOffset(0, j) + B_j)
+//     gives DstOffset. A column's band entries are adjacent in the table.
+// The L2 reads grow as M * (number of bands), so this path is for count
+// matrices up to a bound the planner sets; beyond it the single-workgroup
+// kernels run.
+constexpr int kBandUnroll = 8;  // count loads in flight per thread in step 1
+
+struct BandShared {
+  uint64_t tot[kOffsetThreads];      // per-lane column totals, then the tree sums
+  uint32_t bef[kOffsetThreads];      // per-lane sums of the rows above the band
+  int32_t band[2 * kOffsetThreads];  // the band's counts, [rows][E | 1]
+  int32_t src[kOffsetThreads];       // the band's SrcOffset, row-major
+  int32_t col[kOffsetThreads + 1];   // DstOffset(0, j), col[E] = A
+  uint32_t above[kOffsetThreads];    // B_j
+  uint32_t cstart[kOffsetThreads];   // column-major scan value at each column's first band cell
+  ScanShared<kOffsetThreads> sh;
+};
+
+template <typename CountT>
+__global__ __launch_bounds__(kOffsetThreads) void offsets_banded_kernel(
+    const CountT* __restrict__ counts, int32_t N, int32_t E, int32_t band_rows, int32_t lanes, int64_t A,
+    int cumsum, CountT* __restrict__ etn, WsHeader* __restrict__ hdr, pair_t* __restrict__ table) {
+  __shared__ BandShared s;
+  const int tid = threadIdx.x;
+  const int i0 = blockIdx.x * band_rows;
+  const int rows = min(band_rows, N - i0);  // rows in this band
+  const int ES = E | 1;                     // LDS row stride of the band's counts
+  if (tid == 0) s.sh.flags = 0;
+  uint32_t flags = 0;
+
+  // Step 1: column totals and the rows above the band.
+  {
+    const int r = tid / E;
+    const int j = tid - r * E;
+    uint64_t tot = 0;
+    uint32_t bef = 0;
+    if (r < lanes) {
+      for (int ib = r; ib < N; ib += lanes * kBandUnroll) {
+        CountT raw[kBandUnroll];
+#pragma unroll
+        for (int k = 0; k < kBandUnroll; ++k) {
+          const int i = ib + k * lanes;
+          raw[k] = counts[(i < N ? i : N - 1) * E + j];
+        }
+#pragma unroll
+        for (int k = 0; k < kBandUnroll; ++k) {
+          const int i = ib + k * lanes;
+          if (i < N) {
+            const uint32_t c = static_cast<uint32_t>(clamp_count(raw[k], &flags));
+            tot += c;
+            bef += i < i0 ? c : 0u;
+            if (i >= i0 && i < i0 + rows) s.band[(i - i0) * ES + j] = static_cast<int32_t>(c);
+          }
+        }
+      }
+      s.tot[tid] = tot;
+      s.bef[tid] = bef;
+    }
+    __syncthreads();
+    for (int half = lanes >> 1; half >= 1; half >>= 1) {
+      if (r < half) {
+        s.tot[tid] += s.tot[tid + half * E];
+        s.bef[tid] += s.bef[tid + half * E];
+      }
+      __syncthreads();
+    }
+  }
+
+  // Step 2: expert starts, the band's first source offset, validity.
+  const bool is_col = tid < E;
+  const uint64_t tot_j = is_col ? s.tot[tid] : 0;
+  const uint32_t bef_j = is_col ? s.bef[tid] : 0u;
+  uint64_t grand, above_all;
+  // A column total at or above 2^32 already rules the counts out; clamping it
+  // keeps the exact sum's terms below 2^36.
+  const uint64_t tot_c = tot_j < (uint64_t(1) << 32) ? tot_j : (uint64_t(1) << 32);
+  const uint32_t start_j =
+      block_scan_u32<kOffsetThreads, true>(static_cast<uint32_t>(tot_j), tot_c, s.sh.w[0], s.sh.t[0], &grand);
+  block_scan_u32<kOffsetThreads, true>(0u, bef_j, s.sh.w[1], s.sh.t[1], &above_all);
+  flags = block_or(flags, &s.sh.flags);  // also a barrier: the scans' LDS may be reused after it
+  if (grand != static_cast<uint64_t>(A)) flags |= kFlagSumMismatch;
+  if (flags != 0) {  // uniform: every workgroup saw every count
+    if (blockIdx.x == 0 && tid == 0) write_header(hdr, A, N, E, static_cast<int64_t>(grand), flags, kTablesValid);
+    return;
+  }
+  if (is_col) {
+    s.col[tid] = static_cast<int32_t>(start_j);
+    s.above[tid] = bef_j;
+  }
+  if (tid == 0) s.col[E] = static_cast<int32_t>(A);
+
+  // Step 3a: SrcOffset of the band's cells, row-major (thread q = ii * E + j).
+  const int cells = rows * E;
+  {
+    const int ii = tid / E;
+    const int j = tid - ii * E;
+    const uint32_t c = tid < cells ? static_cast<uint32_t>(s.band[ii * ES + j]) : 0u;
+    uint64_t unused;
+    const uint32_t ex = block_scan_u32<kOffsetThreads, false>(c, 0, s.sh.w[0], s.sh.t[0], &unused);
+    if (tid < cells) s.src[tid] = static_cast<int32_t>(static_cast<uint32_t>(above_all) + ex);
+  }
+  // Step 3b: DstOffset, column-major within the band (thread u = j * rows + ii).
+  {
+    const int j = tid / rows;
+    const int ii = tid - j * rows;
+    const bool in = tid < cells;
+    const uint32_t c = in ? static_cast<uint32_t>(s.band[ii * ES + j]) : 0u;
+    uint64_t unused;
+    const uint32_t ex = block_scan_u32<kOffsetThreads, false>(c, 0, s.sh.w[1], s.sh.t[1], &unused);
+    if (in && ii == 0) s.cstart[j] = ex;
+    __syncthreads();  // also publishes s.src, s.col and s.above
+    if (in) {
+      pair_t t;
+      t.x = static_cast<int32_t>(static_cast<uint32_t>(s.col[j]) + s.above[j] + (ex - s.cstart[j]));
+      t.y = s.src[ii * E + j];
+      table[j * N + i0 + ii] = t;
+    }
+  }
+  if (blockIdx.x == 0) {
+    write_etn<kOffsetThreads>(s.col, E, cumsum, etn);
+    if (tid == 0) {
+      pair_t t;
+      t.x = static_cast<int32_t>(A);
+      t.y = static_cast<int32_t>(A);
+      table[N * E] = t;
+      write_header(hdr, A, N, E, static_cast<int64_t>(grand), 0, kTablesValid);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Row moves
 // ---------------------------------------------------------------------------
@@ -855,9 +995,17 @@ void launch_staged(const Plan& pl, const mrr_args* a, uint8_t* base, size_t lds,
 
 template <typename CountT>
 mrr_status launch_offsets_t(const Plan& pl, const mrr_args* a, void* ws, hipStream_t stream) {
+  auto* base = static_cast<uint8_t*>(ws);
+  if (pl.band_grid > 0) {
+    hipLaunchKernelGGL((offsets_banded_kernel<CountT>), dim3(static_cast<unsigned>(pl.band_grid)),
+                       dim3(kOffsetThreads), 0, stream, static_cast<const CountT*>(a->expert_token_num_per_rank),
+                       static_cast<int32_t>(pl.N), static_cast<int32_t>(pl.E), pl.band_rows, pl.band_lanes, pl.A,
+                       pl.cumsum ? 1 : 0, static_cast<CountT*>(a->expert_token_num),
+                       reinterpret_cast<WsHeader*>(base), reinterpret_cast<pair_t*>(base + pl.table_bytes));
+    return hipGetLastError() == hipSuccess ? MRR_SUCCESS : MRR_ERROR_HIP;
+  }
   const DeviceInfo* di = nullptr;
   if (device_info(&di) != MRR_SUCCESS) return MRR_ERROR_HIP;
-  auto* base = static_cast<uint8_t*>(ws);
   const int64_t lds = offsets_lds_bytes(pl.N, pl.E, kOffsetThreads);
   int kc = 0;
   for (int c : kChunkSizes)

@@ -59,10 +59,12 @@ int env_int(const char* name, int fallback) {
 // never a result.
 struct Tuning {
   int rows_per_wg;  // 0 = automatic
+  int offsets;      // 0 = automatic, 1 = single-workgroup offsets kernel, 2 = banded where it applies
   bool fused;       // allow the single-kernel path (MRR_FUSED=0 turns it off)
   bool log;
   Tuning()
       : rows_per_wg(env_int("MRR_ROWS_PER_WG", 0)),
+        offsets(env_int("MRR_OFFSETS", 0)),
         fused(env_int("MRR_FUSED", 1) != 0),
         log(env_int("MRR_LOG", 0) != 0) {}
 };
@@ -226,16 +228,27 @@ mrr_status make_plan(const mrr_args* a, const void* ws, size_t ws_bytes, Plan* p
       q.scale_inline = 4;
   }
   q.fused = tuning().fused && q.A > 0 && M <= kGatherThreads;
+  q.band_grid = 0;
+  q.band_rows = 0;
+  q.band_lanes = 0;
+  const bool band_fits = M > 0 && q.E <= kOffsetThreads && M <= kBandMaxCells;
+  if (band_fits && (tuning().offsets == 2 || (tuning().offsets == 0 && M > kOffsetThreads))) {
+    q.band_rows = static_cast<int>(std::min<int64_t>(q.N, kOffsetThreads / q.E));
+    int lanes = 1;
+    while (lanes * 2 * q.E <= kOffsetThreads) lanes *= 2;
+    q.band_lanes = lanes;
+    q.band_grid = (q.N + q.band_rows - 1) / q.band_rows;
+  }
   q.table_bytes = kHeaderBytes;
   *p = q;
 
   if (tuning().log)
     fprintf(stderr,
             "[mrr] A=%lld N=%lld E=%lld R=%lld vec=%d rows/wg=%d grid=%lld Rs=%lld svec=%d w=%d scatter=%d "
-            "fused=%d\n",
+            "fused=%d bands=%lld\n",
             (long long)q.A, (long long)q.N, (long long)q.E, (long long)q.row_bytes, q.token_vec,
             q.rows_per_wg, (long long)q.grid, (long long)q.scale_row_bytes, q.scale_vec,
-            (int)q.has_weight, (int)q.scatter, (int)q.fused);
+            (int)q.has_weight, (int)q.scatter, (int)q.fused, (long long)q.band_grid);
   return MRR_SUCCESS;
 }
 
@@ -261,5 +274,6 @@ extern "C" mrr_status mrr_describe_plan(const mrr_args* args, const void* worksp
   info->token_row_bytes = plan.row_bytes;
   info->scale_row_bytes = plan.scale_row_bytes;
   info->scale_inline_bytes = plan.scale_inline;
+  info->offsets_workgroups = plan.band_grid > 0 ? plan.band_grid : (plan.M > 0 ? 1 : 0);
   return MRR_SUCCESS;
 }

@@ -182,12 +182,19 @@ def test_describe_plan():
     assert info.fused == 1 and info.token_vec_bytes == 16 and info.token_row_bytes == 7168
     assert info.scale_row_bytes == 4 and info.scale_vec_bytes == 4
     assert info.scale_inline_bytes == 4            # one 4-byte piece per row, loaded with the tokens
+    assert info.offsets_workgroups == 1
     rows = max(1, info.threads_per_workgroup * 8 // 448)
     assert info.rows_per_workgroup == min(rows, 256)
     assert info.gather_workgroups == -(-16384 // info.rows_per_workgroup)
     # 256x64 counts are too many to recompute per workgroup: two kernels
     st, info = describe(valid_args(A=65536, H=2048, N=256, E=64, tok=_lib.F4_E2M1))
     assert st == _lib.SUCCESS and info.fused == 0 and info.token_row_bytes == 1024
+    assert info.offsets_workgroups == 16           # bands of 1024 // 64 = 16 ranks
+    # the banded offsets kernel: more than 1024 cells, at most 1024 experts and 2^17 cells
+    for n, e, wgs in [(1, 1024, 1), (2, 1024, 2), (33, 32, 2), (7, 513, 7), (5000, 1, 5), (512, 256, 128),
+                      (2, 1025, 1), (520, 256, 1)]:
+        st, info = describe(valid_args(A=0, N=n, E=e))
+        assert st == _lib.SUCCESS and info.offsets_workgroups == wgs, (n, e)
     # e8m0 scales [A, 112, 2] of H=7168 fp8 tokens: 224-byte scale rows in 16-byte pieces
     st, info = describe(valid_args(A=32768, H=7168, N=32, E=8, tok=_lib.F8_E4M3FN, scales="e8m0"))
     assert st == _lib.SUCCESS and info.scale_row_bytes == 224 and info.scale_inline_bytes == 16
@@ -203,6 +210,9 @@ def test_describe_plan():
     # empty input: nothing to gather, never the single-kernel path
     st, info = describe(valid_args(A=0, N=3, E=2))
     assert st == _lib.SUCCESS and info.fused == 0 and info.gather_workgroups == 0
+    assert info.offsets_workgroups == 1
+    st, info = describe(valid_args(A=0, N=0, E=2))
+    assert st == _lib.SUCCESS and info.offsets_workgroups == 0
     # describe runs the same checks
     a = valid_args()
     a.idx_type = 3

@@ -199,8 +199,9 @@ def test_single_rank_or_expert(shape):
 
 
 def test_large_table_unstaged():
-    """N*E = 131072 cells: more counts than fit in LDS, mostly empty, so the
-    row search runs across long stretches of empty cells."""
+    """N*E = 131072 cells (the largest matrix the banded offsets kernel
+    takes), mostly empty, so the row search runs across long stretches of
+    empty cells."""
     rng = np.random.default_rng(77)
     counts = np.zeros((512, 256), np.int32)
     cells = rng.choice(512 * 256, 900, replace=False)
@@ -212,31 +213,76 @@ def test_large_table_unstaged():
     check(w)
 
 
-# Count matrices of every size class of the single-workgroup offsets kernel:
-# one cell per thread (<= 1024 cells), chunks of 3, 5, 9 and 17 cells per
-# thread (each class's lower and upper edge), and beyond 17408 cells the
-# path through global memory.
-@pytest.mark.parametrize("n,e", [(32, 32), (32, 33), (64, 48), (64, 49), (100, 51), (128, 41), (96, 96), (97, 96),
-                                 (136, 128), (137, 128), (5000, 1), (1, 3000), (3, 1700)])
-def test_offsets_size_classes(n, e):
+def _offsets_workgroups(w, dev):
+    t = workloads.torch_inputs(w, dev)
+    call, _ = api.make_call(t["tokens"], t["counts"], per_token_scales=t["scales"], expert_topk_weight=t["weight"],
+                            expert_token_num_type=w.etn_type, idx_type=w.idx_type, tokens_dtype=t["tokens_dtype"])
+    return call.plan()["offsets_workgroups"]
+
+
+# Count matrices of every size class of the single-workgroup offsets kernel
+# (taken when the banded kernel does not apply: at most 1024 cells, more than
+# 1024 experts, or more than 2^17 cells): one cell per thread, chunks of 3, 5,
+# 9 and 17 cells per thread (each class's lower and upper edge), and beyond
+# 17408 cells the path through global memory.
+@pytest.mark.parametrize("n,e", [(32, 32), (1, 1024), (2, 1025), (1, 3000), (4, 1280), (3, 1700), (5, 1100),
+                                 (8, 1152), (9, 1100), (16, 1088), (17, 1025), (130, 1040), (520, 256)])
+def test_offsets_single_workgroup(n, e):
     w = workloads.random_case(n * 7 + e, n, e, 40, tokens_dtype="int8", count_range=(0, 4), weight=True,
                               idx_type=(n + e) % 2, etn_type=(n * e) % 2)
+    assert _offsets_workgroups(w, _dev()) == 1
     check(w)
     check(w, phases=True)
 
 
-@pytest.mark.parametrize("n,e", [(64, 49), (97, 96)])
-def test_bad_counts_chunked(n, e):
+# The banded offsets kernel (1024 < N*E <= 2^17 cells, E <= 1024): one
+# workgroup per band of min(N, 1024 // E) ranks, ragged last bands, one rank
+# per band (E > 512), one expert, and the largest matrix it takes.
+@pytest.mark.parametrize("n,e", [(32, 33), (33, 32), (64, 48), (64, 49), (100, 51), (128, 41), (96, 96),
+                                 (97, 96), (136, 128), (137, 128), (256, 64), (5000, 1), (1100, 1), (2, 1024),
+                                 (7, 513), (5, 300), (64, 17), (130, 1008), (512, 256)])
+def test_offsets_banded(n, e):
+    w = workloads.random_case(n * 5 + e, n, e, 40, tokens_dtype="int8", count_range=(0, 4), weight=True,
+                              idx_type=(n * e) % 2, etn_type=(n + e) % 2)
+    band_rows = min(n, 1024 // e)
+    assert _offsets_workgroups(w, _dev()) == -(-n // band_rows)
+    check(w)
+    check(w, phases=True)
+
+
+def test_offsets_banded_int64_cumsum():
+    w = workloads.random_case(4242, 300, 20, 24, tokens_dtype="float16", counts_dtype="int64", count_range=(0, 6),
+                              scales="a", weight=True, idx_type=1, etn_type=0)
+    assert _offsets_workgroups(w, _dev()) > 1
+    check(w)
+    check(w, phases=True)
+
+
+# Rejected counts are seen by every workgroup of the banded kernel (each
+# reads the whole matrix); the bad cell sits in a band other than the first.
+@pytest.mark.parametrize("n,e,kind", [(64, 49, "negative"), (97, 96, "negative"), (256, 64, "too_large"),
+                                      (256, 64, "sum_high"), (130, 1008, "sum_low"), (2, 1500, "negative"),
+                                      (9, 1100, "negative"), (520, 256, "sum_high")])
+def test_bad_counts_large(n, e, kind):
     dev = _dev()
     rng = np.random.default_rng(n + e)
     counts = rng.integers(0, 4, (n, e)).astype(np.int64)
+    counts[n - 1, e - 1] += 2
     a = int(counts.sum())
-    counts[n // 2, e // 3] = -1  # a negative count (the sum no longer matches either)
-    w = workloads.Workload(f"bad_chunk_{n}x{e}", counts, rng.integers(0, 256, (a, 8), dtype=np.uint8), "int8", 8)
-    out, status = run_hip(w, dev)
-    assert status == _lib.ERROR_BAD_COUNTS
-    for o in out:
-        assert (o == SENTINEL).all()
+    if kind == "negative":
+        counts[n // 2, e // 3] = -1  # the sum no longer matches either
+    elif kind == "too_large":
+        counts[n - 1, e // 2] += 1 << 32  # the sum's low 32 bits still equal a
+    elif kind == "sum_high":
+        counts[n - 1, 0] += 1
+    else:
+        counts[n - 1, e - 1] -= 1
+    w = workloads.Workload(f"bad_{kind}_{n}x{e}", counts, rng.integers(0, 256, (a, 8), dtype=np.uint8), "int8", 8)
+    for phases in (False, True):
+        out, status = run_hip(w, dev, phases=phases)
+        assert status == _lib.ERROR_BAD_COUNTS
+        for o in out:
+            assert (o == SENTINEL).all()
 
 
 @pytest.mark.parametrize("h,tok,scales,S,inline", [
