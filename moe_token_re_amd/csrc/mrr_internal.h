@@ -32,7 +32,7 @@ struct WsHeader {
   int64_t A;
   int64_t N;
   int64_t E;
-  int64_t total;    // sum of the counts, each clamped to [0, INT32_MAX]
+  int64_t total;    // sum of the counts (diagnostic only when the counts are rejected)
 };
 
 inline size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }

@@ -124,6 +124,50 @@ __device__ __forceinline__ uint64_t wave_sum_u36(uint64_t v) {
   return (uint64_t(hi) << 16) + lo;
 }
 
+// Exact sum over the 64 lanes of a wave of values below 2^42 (the low 16 and
+// the high 26 bits summed apart, each sum fitting in 32 bits).
+__device__ __forceinline__ uint64_t wave_sum_u42(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readlane(wave_scan_u32(static_cast<uint32_t>(v & 0xffffu)), 63);
+  const uint32_t hi = __builtin_amdgcn_readlane(wave_scan_u32(static_cast<uint32_t>(v >> 16)), 63);
+  return (uint64_t(hi) << 16) + lo;
+}
+
+// kK exclusive scans over the workgroup (thread order, wrapping 32-bit adds)
+// behind one barrier; for each k in kExactMask also the exact workgroup sum of
+// exact[k] (each term < 2^36) in tot[k]. Each wave scans its lanes with DPP and
+// publishes its total; after the barrier every wave reads the kThreads / 64
+// wave totals one per lane and scans them the same way. LDS the caller writes
+// before the call is visible to every thread after it. s_w and s_t must not
+// be reused before a later barrier.
+template <int kThreads, int kK, unsigned kExactMask>
+__device__ __forceinline__ void block_scan_k(const uint32_t (&v)[kK], const uint64_t (&exact)[kK],
+                                             uint32_t (&out)[kK], uint64_t (&tot)[kK],
+                                             uint32_t (*s_w)[kThreads / 64], uint64_t (*s_t)[kThreads / 64]) {
+  constexpr int kW = kThreads / 64;
+  static_assert(kW <= 64, "one lane per wave total");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  uint32_t incl[kK];
+#pragma unroll
+  for (int k = 0; k < kK; ++k) {
+    incl[k] = wave_scan_u32(v[k]);
+    if (lane == 63) s_w[k][wave] = incl[k];
+    if ((kExactMask >> k) & 1u) {
+      const uint64_t ws = wave_sum_u36(exact[k]);
+      if (lane == 63) s_t[k][wave] = ws;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kK; ++k) {
+    const uint32_t wi = wave_scan_u32(lane < kW ? s_w[k][lane] : 0u);
+    const uint32_t base = wave > 0 ? __builtin_amdgcn_readlane(wi, wave - 1) : 0u;
+    out[k] = base + incl[k] - v[k];
+    tot[k] = 0;
+    if ((kExactMask >> k) & 1u) tot[k] = wave_sum_u42(lane < kW ? s_t[k][lane] : 0);
+  }
+}
+
 // Exclusive scan of v over the workgroup (thread order) with wrapping 32-bit
 // adds. With kExact, also the exact workgroup sum of `exact` (each < 2^36)
 // in *total: a caller that finds *total == A (<= INT32_MAX) with every term
@@ -132,25 +176,13 @@ __device__ __forceinline__ uint64_t wave_sum_u36(uint64_t v) {
 template <int kThreads, bool kExact>
 __device__ __forceinline__ uint32_t block_scan_u32(uint32_t v, uint64_t exact, uint32_t* s_w, uint64_t* s_t,
                                                    uint64_t* total) {
-  constexpr int kW = kThreads / 64;
-  const int wave = threadIdx.x >> 6;
-  const uint32_t incl = wave_scan_u32(v);
-  uint64_t wsum = 0;
-  if (kExact) wsum = wave_sum_u36(exact);
-  if ((threadIdx.x & 63) == 63) {
-    s_w[wave] = incl;
-    if (kExact) s_t[wave] = wsum;
-  }
-  __syncthreads();
-  uint32_t base = 0;
-  uint64_t tot = 0;
-#pragma unroll
-  for (int k = 0; k < kW; ++k) {
-    if (kExact) tot += s_t[k];
-    if (k < wave) base += s_w[k];
-  }
-  if (kExact) *total = tot;
-  return base + incl - v;
+  uint32_t out[1];
+  uint64_t tot[1];
+  block_scan_k<kThreads, 1, kExact ? 1u : 0u>({v}, {exact}, out, tot,
+                                              reinterpret_cast<uint32_t(*)[kThreads / 64]>(s_w),
+                                              reinterpret_cast<uint64_t(*)[kThreads / 64]>(s_t));
+  if (kExact) *total = tot[0];
+  return out[0];
 }
 
 template <typename CountT>
@@ -513,33 +545,75 @@ __global__ __launch_bounds__(kOffsetThreads) void offsets_global_kernel(
 }
 
 // Banded offsets for larger count matrices (kOffsetThreads < M, E <=
-// kOffsetThreads): workgroup b owns the band of rows [i0, i0 + band_rows) and
+// kOffsetThreads): workgroup b owns the band of ranks [i0, i0 + band_rows) and
 // writes the table entries of its cells; no workgroup waits for another.
 //  1. Every workgroup reads the whole count matrix (from L2 after the first
-//     reader) to get, per expert column j, the total T_j over all ranks and
-//     the part B_j above its band. Thread t takes column t % E and every
-//     lanes-th row from row t / E (lanes * E <= kOffsetThreads, a power of
-//     two); an LDS tree adds the lanes' partial sums. Reading every cell also
-//     tells each workgroup whether the counts are valid.
-//  2. Expert j's rows start at DstOffset(0, j) = sum of T_j' over j' < j (a
-//     scan over the columns); the band's first source offset is sum_j B_j.
-//  3. Within the band: a row-major scan of its cells gives SrcOffset, a
-//     column-major scan (within each column, added to DstOffset(0, j) + B_j)
-//     gives DstOffset. A column's band entries are adjacent in the table.
-// The L2 reads grow as M * (number of bands), so this path is for count
-// matrices up to a bound the planner sets; beyond it the single-workgroup
-// kernels run.
-constexpr int kBandUnroll = 8;  // count loads in flight per thread in step 1
+//     reader): thread t takes expert column j = t % E and every lanes-th rank
+//     from t / E (lanes * E <= kOffsetThreads, a power of two), with all its
+//     loads in flight together, and sums the column over all ranks (T_j) and
+//     over the ranks above the band (B_j); the thread of column j then adds up
+//     the lanes' sums from LDS. Reading every cell also tells each workgroup
+//     whether the counts are valid. The band's own cells come from one more
+//     load per thread, issued first.
+//  2. Column scans: expert j's rows start at DstOffset(0, j) = sum of T_j'
+//     over j' < j, and the band's first source offset is sum_j B_j. With at
+//     most 64 experts, wave 0 alone does this.
+//  3. The band's cells are scanned in row-major order for SrcOffset (after
+//     sum_j B_j) and in column-major order for DstOffset: a cell of column j
+//     gets DstOffset(0, j) + B_j plus the band's counts above it in its
+//     column (the column-major scan minus its value at the column's first
+//     band cell). Each order's threads write their half of the cell's
+//     (DstOffset, SrcOffset) pair.
+// Every workgroup repeats step 1 over all M cells, which is why the per-cell
+// work is kept to a few instructions, and why the L2 reads grow as
+// M * (number of bands); the planner bounds M for this path.
+constexpr int kBandUnroll = 16;  // count loads in flight per thread in step 1
+constexpr int kBandFanIn = 16;   // lanes' sums a column's thread adds up; more take a first LDS pass
 
 struct BandShared {
-  uint64_t tot[kOffsetThreads];      // per-lane column totals, then the tree sums
-  uint32_t bef[kOffsetThreads];      // per-lane sums of the rows above the band
+  uint64_t tot[kOffsetThreads];      // per-lane sums over all ranks,
+  uint32_t bef[kOffsetThreads];      // and over the ranks above the band
   int32_t band[2 * kOffsetThreads];  // the band's counts, [rows][E | 1]
-  int32_t src[kOffsetThreads];       // the band's SrcOffset, row-major
   int32_t col[kOffsetThreads + 1];   // DstOffset(0, j), col[E] = A
   uint32_t above[kOffsetThreads];    // B_j
-  uint32_t cstart[kOffsetThreads];   // column-major scan value at each column's first band cell
-  ScanShared<kOffsetThreads> sh;
+  uint32_t cstart[kOffsetThreads];   // column-major band scan at each column's first band cell
+  uint32_t w[4][kOffsetThreads / 64];
+  uint64_t t[4][kOffsetThreads / 64];
+  uint32_t flags;
+  uint32_t above_all;
+  uint64_t grand;
+};
+
+// floor(t / d) for 0 <= t < 2^12 and 1 <= d <= 2^12, with inv = 1.0f / d:
+// (t + 1/2) / d lies at least 1 / (2d) from an integer, far more than the
+// float error of the product.
+__device__ __forceinline__ int div_small(int t, float inv) {
+  return static_cast<int>((static_cast<float>(t) + 0.5f) * inv);
+}
+
+// One count of the main sweep: the running sums, and what validity needs.
+// int32 counts: the OR of the raw words keeps the sign bits (a negative
+// count), and the 64-bit sum is exact. int64 counts are checked one by one.
+template <typename CountT>
+struct CountAcc {
+  uint64_t tot = 0;
+  uint32_t bef = 0;
+  uint32_t orv = 0;
+  uint32_t flags = 0;
+  __device__ __forceinline__ void add(CountT raw, bool above) {
+    uint32_t c;
+    if (sizeof(CountT) == 4) {
+      c = static_cast<uint32_t>(raw);
+      orv |= c;
+    } else {
+      c = static_cast<uint32_t>(clamp_count(raw, &flags));
+    }
+    tot += c;
+    bef += above ? c : 0u;
+  }
+  __device__ __forceinline__ uint32_t final_flags() const {
+    return flags | ((orv >> 31) != 0 ? kFlagNegative : 0u);
+  }
 };
 
 template <typename CountT>
@@ -549,98 +623,138 @@ __global__ __launch_bounds__(kOffsetThreads) void offsets_banded_kernel(
   __shared__ BandShared s;
   const int tid = threadIdx.x;
   const int i0 = blockIdx.x * band_rows;
-  const int rows = min(band_rows, N - i0);  // rows in this band
+  const int rows = min(band_rows, N - i0);  // ranks in this band
+  const int cells = rows * E;               // <= kOffsetThreads
   const int ES = E | 1;                     // LDS row stride of the band's counts
-  if (tid == 0) s.sh.flags = 0;
-  uint32_t flags = 0;
+  const float inv_e = 1.0f / static_cast<float>(E);
+  const float inv_rows = 1.0f / static_cast<float>(rows);
+  if (tid == 0) s.flags = 0;
 
-  // Step 1: column totals and the rows above the band.
+  // Step 1: per-lane column sums, and the band's counts.
+  const int qi = div_small(tid, inv_e);  // row-major band cell q = tid: (qi, qj)
+  const int qj = tid - qi * E;
+  const CountT band_raw = counts[i0 * E + (tid < cells ? tid : cells - 1)];  // row-major: cell q of the band
+  CountAcc<CountT> acc;
   {
-    const int r = tid / E;
-    const int j = tid - r * E;
-    uint64_t tot = 0;
-    uint32_t bef = 0;
+    const int r = qi;  // lane r of column j = qj
+    const int j = qj;
     if (r < lanes) {
-      for (int ib = r; ib < N; ib += lanes * kBandUnroll) {
+      const CountT* p = counts + j;
+      int ib = r;
+      for (; ib + (kBandUnroll - 1) * lanes < N; ib += kBandUnroll * lanes) {
+        CountT raw[kBandUnroll];
+#pragma unroll
+        for (int k = 0; k < kBandUnroll; ++k) raw[k] = p[(ib + k * lanes) * E];
+#pragma unroll
+        for (int k = 0; k < kBandUnroll; ++k) acc.add(raw[k], ib + k * lanes < i0);
+      }
+      if (ib < N) {  // the last, partial chunk: clamped loads, predicated sums
         CountT raw[kBandUnroll];
 #pragma unroll
         for (int k = 0; k < kBandUnroll; ++k) {
           const int i = ib + k * lanes;
-          raw[k] = counts[(i < N ? i : N - 1) * E + j];
+          raw[k] = p[(i < N ? i : N - 1) * E];
         }
 #pragma unroll
-        for (int k = 0; k < kBandUnroll; ++k) {
-          const int i = ib + k * lanes;
-          if (i < N) {
-            const uint32_t c = static_cast<uint32_t>(clamp_count(raw[k], &flags));
-            tot += c;
-            bef += i < i0 ? c : 0u;
-            if (i >= i0 && i < i0 + rows) s.band[(i - i0) * ES + j] = static_cast<int32_t>(c);
-          }
-        }
+        for (int k = 0; k < kBandUnroll; ++k)
+          if (ib + k * lanes < N) acc.add(raw[k], ib + k * lanes < i0);
       }
-      s.tot[tid] = tot;
-      s.bef[tid] = bef;
+      s.tot[tid] = acc.tot;
+      s.bef[tid] = acc.bef;
     }
+    uint32_t f = acc.final_flags();
+    if (tid < cells) s.band[qi * ES + qj] = clamp_count(band_raw, &f);
+    if (f != 0) atomicOr(&s.flags, f);
     __syncthreads();
-    for (int half = lanes >> 1; half >= 1; half >>= 1) {
-      if (r < half) {
-        s.tot[tid] += s.tot[tid + half * E];
-        s.bef[tid] += s.bef[tid + half * E];
+    if (lanes > kBandFanIn) {  // uniform: fold lanes r + 16k into lane r < 16
+      if (r < kBandFanIn) {
+        uint64_t tot = s.tot[tid];
+        uint32_t bef = s.bef[tid];
+        for (int k = r + kBandFanIn; k < lanes; k += kBandFanIn) {
+          tot += s.tot[k * E + j];
+          bef += s.bef[k * E + j];
+        }
+        s.tot[tid] = tot;
+        s.bef[tid] = bef;
       }
       __syncthreads();
     }
   }
 
-  // Step 2: expert starts, the band's first source offset, validity.
+  // Step 2: column scans and validity. A column total at or above 2^32
+  // already rules the counts out; otherwise the 32-bit running sum over the
+  // columns is exact unless it wraps, which shows as an inclusive value
+  // below the exclusive one.
   const bool is_col = tid < E;
-  const uint64_t tot_j = is_col ? s.tot[tid] : 0;
-  const uint32_t bef_j = is_col ? s.bef[tid] : 0u;
-  uint64_t grand, above_all;
-  // A column total at or above 2^32 already rules the counts out; clamping it
-  // keeps the exact sum's terms below 2^36.
-  const uint64_t tot_c = tot_j < (uint64_t(1) << 32) ? tot_j : (uint64_t(1) << 32);
-  const uint32_t start_j =
-      block_scan_u32<kOffsetThreads, true>(static_cast<uint32_t>(tot_j), tot_c, s.sh.w[0], s.sh.t[0], &grand);
-  block_scan_u32<kOffsetThreads, true>(0u, bef_j, s.sh.w[1], s.sh.t[1], &above_all);
-  flags = block_or(flags, &s.sh.flags);  // also a barrier: the scans' LDS may be reused after it
-  if (grand != static_cast<uint64_t>(A)) flags |= kFlagSumMismatch;
+  uint64_t tot_j = 0;
+  uint32_t bef_j = 0;
+  if (is_col) {
+    const int fan = lanes < kBandFanIn ? lanes : kBandFanIn;
+    for (int k = 0; k < fan; ++k) {
+      tot_j += s.tot[k * E + tid];
+      bef_j += s.bef[k * E + tid];
+    }
+  }
+  const uint32_t t32 = static_cast<uint32_t>(tot_j);
+  if (E <= 64) {  // uniform: wave 0 holds every column
+    if (tid < 64) {
+      const uint32_t incl = wave_scan_u32(t32);
+      const uint32_t excl = incl - t32;
+      const bool bad = (tot_j >> 32) != 0 || incl < excl;
+      const uint32_t above_all = __builtin_amdgcn_readlane(wave_scan_u32(bef_j), 63);
+      const uint32_t grand = __builtin_amdgcn_readlane(incl, 63);
+      const bool any_bad = __builtin_amdgcn_ballot_w64(bad) != 0;
+      if (is_col) {
+        s.col[tid] = static_cast<int32_t>(excl);
+        s.above[tid] = bef_j;
+      }
+      if (tid == 0) {
+        if (any_bad || grand != static_cast<uint64_t>(A)) s.flags |= kFlagSumMismatch;
+        s.col[E] = static_cast<int32_t>(A);
+        s.above_all = above_all;
+        s.grand = grand;
+      }
+    }
+  } else {
+    const uint64_t tot_c = tot_j < (uint64_t(1) << 32) ? tot_j : (uint64_t(1) << 32);
+    uint32_t ex2[2];
+    uint64_t sum2[2];
+    block_scan_k<kOffsetThreads, 2, 3u>({t32, 0u}, {tot_c, bef_j}, ex2, sum2, s.w, s.t);
+    if (is_col) {
+      s.col[tid] = static_cast<int32_t>(ex2[0]);
+      s.above[tid] = bef_j;
+    }
+    if (tid == 0) {
+      s.col[E] = static_cast<int32_t>(A);
+      s.above_all = static_cast<uint32_t>(sum2[1]);
+      s.grand = sum2[0];
+      if (sum2[0] != static_cast<uint64_t>(A)) atomicOr(&s.flags, kFlagSumMismatch);
+    }
+  }
+  __syncthreads();
+  const uint32_t flags = s.flags;
   if (flags != 0) {  // uniform: every workgroup saw every count
-    if (blockIdx.x == 0 && tid == 0) write_header(hdr, A, N, E, static_cast<int64_t>(grand), flags, kTablesValid);
+    if (blockIdx.x == 0 && tid == 0) write_header(hdr, A, N, E, static_cast<int64_t>(s.grand), flags, kTablesValid);
     return;
   }
-  if (is_col) {
-    s.col[tid] = static_cast<int32_t>(start_j);
-    s.above[tid] = bef_j;
-  }
-  if (tid == 0) s.col[E] = static_cast<int32_t>(A);
 
-  // Step 3a: SrcOffset of the band's cells, row-major (thread q = ii * E + j).
-  const int cells = rows * E;
-  {
-    const int ii = tid / E;
-    const int j = tid - ii * E;
-    const uint32_t c = tid < cells ? static_cast<uint32_t>(s.band[ii * ES + j]) : 0u;
-    uint64_t unused;
-    const uint32_t ex = block_scan_u32<kOffsetThreads, false>(c, 0, s.sh.w[0], s.sh.t[0], &unused);
-    if (tid < cells) s.src[tid] = static_cast<int32_t>(static_cast<uint32_t>(above_all) + ex);
-  }
-  // Step 3b: DstOffset, column-major within the band (thread u = j * rows + ii).
-  {
-    const int j = tid / rows;
-    const int ii = tid - j * rows;
-    const bool in = tid < cells;
-    const uint32_t c = in ? static_cast<uint32_t>(s.band[ii * ES + j]) : 0u;
-    uint64_t unused;
-    const uint32_t ex = block_scan_u32<kOffsetThreads, false>(c, 0, s.sh.w[1], s.sh.t[1], &unused);
-    if (in && ii == 0) s.cstart[j] = ex;
-    __syncthreads();  // also publishes s.src, s.col and s.above
-    if (in) {
-      pair_t t;
-      t.x = static_cast<int32_t>(static_cast<uint32_t>(s.col[j]) + s.above[j] + (ex - s.cstart[j]));
-      t.y = s.src[ii * E + j];
-      table[j * N + i0 + ii] = t;
-    }
+  // Step 3: the band's cells in row-major (q = qi * E + qj) and column-major
+  // (u = uj * rows + ui) order.
+  const int uj = div_small(tid, inv_rows);
+  const int ui = tid - uj * rows;
+  const bool in = tid < cells;
+  const uint32_t cq = in ? static_cast<uint32_t>(s.band[qi * ES + qj]) : 0u;
+  const uint32_t cu = in ? static_cast<uint32_t>(s.band[ui * ES + uj]) : 0u;
+  uint32_t ex3[2];
+  uint64_t unused[2];
+  block_scan_k<kOffsetThreads, 2, 0u>({cq, cu}, {0, 0}, ex3, unused, s.w + 2, s.t + 2);
+  if (in && ui == 0) s.cstart[uj] = ex3[1];
+  __syncthreads();
+  int32_t* words = reinterpret_cast<int32_t*>(table);
+  if (in) {
+    words[2 * (qj * N + i0 + qi) + 1] = static_cast<int32_t>(s.above_all + ex3[0]);
+    words[2 * (uj * N + i0 + ui)] =
+        static_cast<int32_t>(static_cast<uint32_t>(s.col[uj]) + s.above[uj] + (ex3[1] - s.cstart[uj]));
   }
   if (blockIdx.x == 0) {
     write_etn<kOffsetThreads>(s.col, E, cumsum, etn);
@@ -649,7 +763,7 @@ __global__ __launch_bounds__(kOffsetThreads) void offsets_banded_kernel(
       t.x = static_cast<int32_t>(A);
       t.y = static_cast<int32_t>(A);
       table[N * E] = t;
-      write_header(hdr, A, N, E, static_cast<int64_t>(grand), 0, kTablesValid);
+      write_header(hdr, A, N, E, static_cast<int64_t>(s.grand), 0, kTablesValid);
     }
   }
 }
