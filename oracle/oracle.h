@@ -69,6 +69,24 @@ int oracle_reroute(const uint8_t* tokens, int64_t A, int64_t token_row_bytes,
                    uint8_t* out_tokens, uint8_t* out_scales, int32_t* out_idx,
                    void* out_etn, float* out_weight);
 
+/*
+ * The inverse re-route (not on the page; the "计算公式" moves read
+ * backwards): rows [A][row_bytes] in expert-major order, as the operator
+ * outputs them, return to rank-major order:
+ *   out_rows[SrcOffset + k] = rows[DstOffset + k]   (and scales, weight)
+ * for every cell and 0 <= k < its count. idx_type 0: out_idx[s] = the input
+ * (expert-major) row of output row s; 1: out_idx[d] = the output row of input
+ * row d. out_etn is the forward operator's expert_token_num. Same arguments,
+ * checks and return codes as oracle_reroute.
+ */
+int oracle_reroute_inverse(const uint8_t* rows, int64_t A, int64_t row_bytes,
+                           const void* counts, int counts_is_i64, int64_t N, int64_t E,
+                           const uint8_t* scales, int64_t scale_row_bytes,
+                           const float* weight,
+                           int64_t etn_type, int64_t idx_type,
+                           uint8_t* out_rows, uint8_t* out_scales, int32_t* out_idx,
+                           void* out_etn, float* out_weight);
+
 #ifdef __cplusplus
 }
 #endif

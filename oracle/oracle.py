@@ -82,6 +82,8 @@ class Oracle:
         lib.oracle_reroute.argtypes = [vp, i64, i64, vp, i32, i64, i64, vp, i64, vp,
                                        i64, i64, vp, vp, vp, vp, vp]
         lib.oracle_reroute.restype = i32
+        lib.oracle_reroute_inverse.argtypes = lib.oracle_reroute.argtypes
+        lib.oracle_reroute_inverse.restype = i32
         self.lib = lib
         self.path = lib_path
 
@@ -103,6 +105,16 @@ class Oracle:
         permute_token_idx int32 [A], expert_token_num [E] in the counts' dtype,
         permute_weight or None). `out` may hold preallocated arrays from
         allocate_outputs(), which are then filled and returned."""
+        return self._call(self.lib.oracle_reroute, tokens, counts, scales, weight, etn_type, idx_type, out)
+
+    def reroute_inverse(self, rows, counts, scales=None, weight=None, etn_type=1, idx_type=0, out=None):
+        """The inverse re-route: expert-major rows (the operator's output
+        layout) back to rank-major order. Same arguments and results as
+        reroute()."""
+        return self._call(self.lib.oracle_reroute_inverse, rows, counts, scales, weight, etn_type, idx_type, out)
+
+    @staticmethod
+    def _call(fn, tokens, counts, scales, weight, etn_type, idx_type, out):
         tokens = np.ascontiguousarray(tokens)
         counts = np.ascontiguousarray(counts)
         if counts.ndim != 2:
@@ -121,21 +133,21 @@ class Oracle:
                 raise ValueError("weight must be float32 with A elements")
         outs = allocate_outputs(tokens, counts, scales, weight) if out is None else out
         o_tok, o_sc, o_idx, o_etn, o_w = outs
-        rc = self.lib.oracle_reroute(
-            _ptr(tokens), a, row, _ptr(counts), _counts_kind(counts), counts.shape[0],
-            counts.shape[1], _ptr(scales), srow, _ptr(weight), int(etn_type), int(idx_type),
-            _ptr(o_tok), _ptr(o_sc), _ptr(o_idx), _ptr(o_etn), _ptr(o_w))
+        rc = fn(_ptr(tokens), a, row, _ptr(counts), _counts_kind(counts), counts.shape[0],
+                counts.shape[1], _ptr(scales), srow, _ptr(weight), int(etn_type), int(idx_type),
+                _ptr(o_tok), _ptr(o_sc), _ptr(o_idx), _ptr(o_etn), _ptr(o_w))
         if rc != OK:
             raise OracleError(rc)
         return outs
 
 
 def load() -> Oracle:
-    """The oracle built from oracle.c, compiling it first only when no build exists."""
+    """The oracle built from oracle.c, compiling it first when no build exists
+    or the source is newer than the build."""
     global _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(_LIB_PATH):
+            if not os.path.exists(_LIB_PATH) or os.path.getmtime(_SRC) > os.path.getmtime(_LIB_PATH):
                 build()
             _lib = Oracle(_LIB_PATH)
         return _lib
@@ -147,3 +159,7 @@ def offsets(counts):
 
 def reroute(tokens, counts, scales=None, weight=None, etn_type=1, idx_type=0, out=None):
     return load().reroute(tokens, counts, scales, weight, etn_type, idx_type, out)
+
+
+def reroute_inverse(rows, counts, scales=None, weight=None, etn_type=1, idx_type=0, out=None):
+    return load().reroute_inverse(rows, counts, scales, weight, etn_type, idx_type, out)

@@ -22,6 +22,15 @@ What pins what (page: "CANN ops-transformer MoeReRoutingV2", nlpx.cn):
   * invariants: the index is a permutation, gather and scatter forms are
     inverse, scales and weights move with the token rows byte for byte,
     expert_token_num equals the per-expert histogram of the moved rows.
+The inverse re-route (expert-major rows back to rank-major order; the page
+gives only the forward moves, the inverse reads them backwards) is pinned by:
+  * the golden fixtures read backwards: input row d goes to output row
+    gather_idx[d], so the inverse's gather index is the fixture's scatter
+    index and its scatter index is the fixture's gather index;
+  * the stable-sort brute force: the inverse permutation of the sort's
+    (numpy argsort of the lexsort order) for every small count matrix;
+  * round trips: forward then inverse, and inverse then forward, give back
+    the input bytes (tokens, scales, weights) for random count matrices.
 """
 from __future__ import annotations
 
@@ -234,6 +243,88 @@ def check_empty(orc):
     assert etn.shape == (0,)
 
 
+def check_inverse_golden(orc, name):
+    g = load_golden(name)
+    counts = g["counts"].astype(np.int32)
+    a = int(g["A"][0])
+    rows = row_coded_tokens(a, 6, seed=3)
+    for idx_type, key in ((0, "scatter_idx"), (1, "gather_idx")):
+        for etn_type, ekey in ((1, "etn_count"), (0, "etn_cumsum")):
+            out, _, idx, etn, _ = orc.reroute_inverse(rows, counts, etn_type=etn_type, idx_type=idx_type)
+            assert np.array_equal(idx, g[key]), (name, "inverse", key, idx)
+            assert np.array_equal(etn, g[ekey]), (name, "inverse", ekey, etn)
+            assert np.array_equal(out, rows[g["scatter_idx"]]), (name, "inverse rows")
+
+
+def check_inverse_case_against_sort(orc, counts, row_bytes=5, seed=0, with_extras=True):
+    """Every output of one inverse case against the inverse of the stable-sort order."""
+    a = int(counts.sum())
+    rows = row_coded_tokens(a, row_bytes, seed)
+    rng = np.random.default_rng(seed + 2)
+    scales = rng.integers(0, 256, (a, 8), dtype=np.uint8) if with_extras else None
+    weight = rng.integers(0, 256, (a, 4), dtype=np.uint8).view(np.float32).reshape(a, 1) if with_extras else None
+    g = stable_sort_gather(counts)  # forward: expert-major row d <- rank-major row g[d]
+    back = np.argsort(g, kind="stable")  # inverse: rank-major row s <- expert-major row back[s]
+    _, expert = labels(counts)
+    per_expert = np.bincount(expert, minlength=counts.shape[1]) if a else np.zeros(counts.shape[1], np.int64)
+    for idx_type in (0, 1):
+        for etn_type in (0, 1):
+            out, o_sc, idx, etn, o_w = orc.reroute_inverse(rows, counts, scales, weight, etn_type, idx_type)
+            assert np.array_equal(out, rows[back]), ("inverse rows", counts)
+            assert np.array_equal(idx, back if idx_type == 0 else g), ("inverse idx", idx_type, counts, idx)
+            if with_extras:
+                assert np.array_equal(o_sc, scales[back]), ("inverse scales", counts)
+                assert np.array_equal(o_w.view(np.uint32), weight.view(np.uint32)[back]), ("inverse weight", counts)
+            want = per_expert if etn_type == 1 else np.cumsum(per_expert)
+            assert np.array_equal(etn.astype(np.int64), want), ("inverse etn", etn_type, counts)
+
+
+def check_inverse_bruteforce(orc, max_n=3, max_e=3, values=(0, 1, 2)):
+    cases = 0
+    for n in range(1, max_n + 1):
+        for e in range(1, max_e + 1):
+            for flat in itertools.product(values, repeat=n * e):
+                counts = np.array(flat, np.int64 if cases % 2 else np.int32).reshape(n, e)
+                check_inverse_case_against_sort(orc, counts, row_bytes=4, with_extras=(cases % 5 == 0))
+                cases += 1
+    return cases
+
+
+def check_roundtrip(orc, seeds=range(5)):
+    """Forward then inverse, and inverse then forward, are the identity."""
+    for seed in seeds:
+        rng = np.random.default_rng(300 + seed)
+        n, e = int(rng.integers(1, 30)), int(rng.integers(1, 30))
+        counts = rng.integers(0, 7, (n, e)).astype(np.int32 if seed % 2 else np.int64)
+        a = int(counts.sum())
+        tok = row_coded_tokens(a, 9, seed)
+        scales = rng.integers(0, 256, (a, 3), dtype=np.uint8)
+        weight = rng.integers(0, 256, (a, 4), dtype=np.uint8).view(np.float32).reshape(a, 1)
+        f_tok, f_sc, f_gidx, _, f_w = orc.reroute(tok, counts, scales, weight, 1, 0)
+        b_tok, b_sc, b_sidx, _, b_w = orc.reroute_inverse(f_tok, counts, f_sc, f_w, 1, 1)
+        assert np.array_equal(b_tok, tok) and np.array_equal(b_sc, scales), ("round trip", seed)
+        assert np.array_equal(b_w.view(np.uint32), weight.view(np.uint32)), ("round trip weight", seed)
+        assert np.array_equal(b_sidx, f_gidx), ("inverse scatter idx = forward gather idx", seed)
+        y = row_coded_tokens(a, 7, seed + 1)
+        assert np.array_equal(orc.reroute(orc.reroute_inverse(y, counts)[0], counts)[0], y), ("inverse then forward",)
+
+
+def check_inverse_errors(orc):
+    from oracle.oracle import BAD_ARGS, BAD_COUNTS, OracleError
+    rows = row_coded_tokens(6, 4)
+    for counts, code, kw in ((np.array([[2, -1], [3, 2]], np.int32), BAD_COUNTS, {}),
+                             (np.array([[2, 1], [3, 1]], np.int64), BAD_COUNTS, {}),
+                             (np.array([[2, 1], [2, 1]], np.int32), BAD_ARGS, {"idx_type": 2})):
+        outs = (np.full_like(rows, 0xAB), None, np.full(6, -7, np.int32), np.full(2, -7, counts.dtype), None)
+        try:
+            orc.reroute_inverse(rows, counts, out=outs, **kw)
+        except OracleError as err:
+            assert err.code == code
+        else:
+            raise AssertionError("inverse accepted bad input")
+        assert (outs[0] == 0xAB).all() and (outs[2] == -7).all() and (outs[3] == -7).all()
+
+
 ALL_CHECKS = [
     ("golden", lambda o: [check_golden(o, f) for f in GOLDEN_FILES]),
     ("bruteforce", lambda o: check_bruteforce(o, 2, 2, (0, 1, 2))),
@@ -243,4 +334,8 @@ ALL_CHECKS = [
     ("random_invariants", check_random_invariants),
     ("errors", check_errors),
     ("empty", check_empty),
+    ("inverse_golden", lambda o: [check_inverse_golden(o, f) for f in GOLDEN_FILES]),
+    ("inverse_bruteforce", lambda o: check_inverse_bruteforce(o, 2, 2, (0, 1, 2))),
+    ("roundtrip", check_roundtrip),
+    ("inverse_errors", check_inverse_errors),
 ]

@@ -47,9 +47,24 @@ MUTANTS = [
     ("etn_row_sums",
      "for (int64_t i = 0; i < N; ++i) per_expert += count_at(counts, counts_is_i64, i * E + j);",
      "for (int64_t i = 0; i < N; ++i) per_expert += count_at(counts, counts_is_i64, j * N + i);"),
+    ("inverse_gather_idx_is_scatter",
+     "out_idx[rank_row] = (int32_t)expert_row;",
+     "out_idx[expert_row] = (int32_t)rank_row;"),
+    ("inverse_scatter_idx_drops_k",
+     "out_idx[expert_row] = (int32_t)rank_row;",
+     "out_idx[expert_row] = (int32_t)src;"),
+    ("inverse_moves_forward",
+     "memcpy(out_rows + rank_row * row_bytes, rows + expert_row * row_bytes",
+     "memcpy(out_rows + expert_row * row_bytes, rows + rank_row * row_bytes"),
+    ("inverse_scales_from_rank_row",
+     "scales + expert_row * scale_row_bytes",
+     "scales + rank_row * scale_row_bytes"),
+    ("inverse_weight_from_rank_row",
+     "weight + expert_row, sizeof(float)",
+     "weight + rank_row, sizeof(float)"),
     ("no_sum_check",
      "  if (total != A) return ORACLE_BAD_COUNTS;\n",
-     ""),
+     "  (void)total;\n  (void)A;\n"),
     ("no_negative_check",
      ("    if (c < 0) return ORACLE_BAD_COUNTS;\n",
       "    if (count_at(counts, counts_is_i64, cell) < 0) return ORACLE_BAD_COUNTS;\n"),

@@ -42,3 +42,20 @@ def test_errors_write_nothing(orc):
 
 def test_empty_inputs(orc):
     pins.check_empty(orc)
+
+
+@pytest.mark.parametrize("name", pins.GOLDEN_FILES)
+def test_inverse_golden(orc, name):
+    pins.check_inverse_golden(orc, name)
+
+
+def test_inverse_bruteforce_all_small_count_matrices(orc):
+    assert pins.check_inverse_bruteforce(orc, 3, 3, (0, 1, 2)) == 21297
+
+
+def test_roundtrip(orc):
+    pins.check_roundtrip(orc)
+
+
+def test_inverse_errors_write_nothing(orc):
+    pins.check_inverse_errors(orc)
