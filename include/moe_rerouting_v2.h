@@ -18,6 +18,15 @@
  * writes permute_token_idx (gather or scatter form) and expert_token_num (per
  * expert counts, or their running sum).
  *
+ * With direction = MRR_INVERSE the same call runs the moves backwards, which
+ * the article does not define but its formulas fix: the rows arrive in
+ * expert-major order (as the forward call writes them, e.g. after the expert
+ * computation) and return to rank-major order before the combine step,
+ *     permute_tokens[SrcOffset(i,j) + k] = tokens[DstOffset(i,j) + k],
+ * with scales and weights alike, permute_token_idx relative to this call's
+ * own input and output (gather: row d of the output came from input row
+ * idx[d]), and the same expert_token_num.
+ *
  * Conventions shared by every entry point:
  *   - Every tensor pointer is a caller-owned DEVICE pointer on the current HIP
  *     device; the library never frees, keeps or allocates caller memory, and
@@ -127,7 +136,12 @@ typedef struct mrr_args {
                                       sum of rows per expert (last entry = A) */
   int64_t idx_type;                /* 0 (default): gather, tokens[idx[d]] lands at row d;
                                       1: scatter, tokens[s] lands at row idx[s] */
+  int64_t direction;               /* MRR_FORWARD (0, default): rank-major -> expert-major;
+                                      MRR_INVERSE (1): expert-major -> rank-major */
 } mrr_args;
+
+/* mrr_args.direction */
+enum { MRR_FORWARD = 0, MRR_INVERSE = 1 };
 
 /*
  * Bytes of device workspace a call with an N x E count matrix needs: a

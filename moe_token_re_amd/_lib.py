@@ -22,6 +22,10 @@ ERROR_WORKSPACE_TOO_SMALL = 5
 ERROR_BAD_COUNTS = 6
 ERROR_HIP = 7
 
+# mrr_args.direction
+FORWARD = 0
+INVERSE = 1
+
 # mrr_dtype
 F16, BF16, I8, F8_E5M2, F8_E4M3FN, HIF8, F4_E2M1, F4_E1M2, I32, I64, F32, F8_E8M0 = range(12)
 
@@ -53,6 +57,7 @@ class MrrArgs(ctypes.Structure):
         ("permute_topk_weight", ctypes.c_void_p),
         ("expert_token_num_type", ctypes.c_int64),
         ("idx_type", ctypes.c_int64),
+        ("direction", ctypes.c_int64),
     ]
 
 

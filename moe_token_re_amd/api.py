@@ -12,6 +12,9 @@ shapes follow its InferShape rules:
   permute_token_idx         [A] int32
   expert_token_num          [E], counts' dtype
   permute_topk_weight       weight's shape; an empty (0,) float32 when absent
+moe_re_routing_inverse() runs the same moves backwards (expert-major rows back
+to rank-major order; the article's formulas read in reverse), with the same
+arguments and output shapes.
 """
 from __future__ import annotations
 
@@ -89,7 +92,7 @@ def _check_tensor(name, t, device):
 
 
 def prepare(tokens, expert_token_num_per_rank, *, per_token_scales=None, expert_topk_weight=None,
-            expert_token_num_type=1, idx_type=0, tokens_dtype=None, out=None):
+            expert_token_num_type=1, idx_type=0, tokens_dtype=None, out=None, direction=_lib.FORWARD):
     """Checks the tensors' dtypes and ranks, allocates the outputs (or takes
     `out`, a 5-tuple like the result) and fills an MrrArgs. Returns (args, outputs)."""
     dev = tokens.device
@@ -166,6 +169,7 @@ def prepare(tokens, expert_token_num_per_rank, *, per_token_scales=None, expert_
     a.permute_topk_weight = _ptr(p_w) if expert_topk_weight is not None else None
     a.expert_token_num_type = int(expert_token_num_type)
     a.idx_type = int(idx_type)
+    a.direction = int(direction)
     return a, out
 
 
@@ -223,11 +227,11 @@ def get_device_status(workspace: torch.Tensor, stream: Optional[torch.cuda.Strea
 
 def make_call(tokens, expert_token_num_per_rank, *, per_token_scales=None, expert_topk_weight=None,
               expert_token_num_type=1, idx_type=0, tokens_dtype=None, out=None, workspace=None,
-              stream=None):
+              stream=None, direction=_lib.FORWARD):
     """Marshals once and returns (PreparedCall, outputs)."""
     args, outs = prepare(tokens, expert_token_num_per_rank, per_token_scales=per_token_scales,
                          expert_topk_weight=expert_topk_weight, expert_token_num_type=expert_token_num_type,
-                         idx_type=idx_type, tokens_dtype=tokens_dtype, out=out)
+                         idx_type=idx_type, tokens_dtype=tokens_dtype, out=out, direction=direction)
     dev = tokens.device
     need = workspace_size(args.N, args.E)
     if need == 0:
@@ -239,6 +243,21 @@ def make_call(tokens, expert_token_num_per_rank, *, per_token_scales=None, exper
             workspace.record_stream(s)
     keep = (tokens, expert_token_num_per_rank, per_token_scales, expert_topk_weight) + tuple(outs)
     return PreparedCall(args, workspace, s, keep), outs
+
+
+def _run(direction, tokens, expert_token_num_per_rank, per_token_scales, expert_topk_weight,
+         expert_token_num_type, idx_type, tokens_dtype, check, workspace, where):
+    with torch.cuda.device(tokens.device):
+        call, outs = make_call(tokens, expert_token_num_per_rank, per_token_scales=per_token_scales,
+                               expert_topk_weight=expert_topk_weight,
+                               expert_token_num_type=expert_token_num_type, idx_type=idx_type,
+                               tokens_dtype=tokens_dtype, workspace=workspace, direction=direction)
+        call.run()
+        if check:
+            st = call.device_status()
+            if st != _lib.SUCCESS:
+                _raise(st, where)
+    return outs
 
 
 def moe_re_routing(tokens: torch.Tensor, expert_token_num_per_rank: torch.Tensor, *,
@@ -254,14 +273,22 @@ def moe_re_routing(tokens: torch.Tensor, expert_token_num_per_rank: torch.Tensor
     Count values are checked on the device; with check=True the call waits
     for the stream and raises MrrValueError when they were invalid (then the
     outputs were not written)."""
-    with torch.cuda.device(tokens.device):
-        call, outs = make_call(tokens, expert_token_num_per_rank, per_token_scales=per_token_scales,
-                               expert_topk_weight=expert_topk_weight,
-                               expert_token_num_type=expert_token_num_type, idx_type=idx_type,
-                               tokens_dtype=tokens_dtype, workspace=workspace)
-        call.run()
-        if check:
-            st = call.device_status()
-            if st != _lib.SUCCESS:
-                _raise(st, "device count check")
-    return outs
+    return _run(_lib.FORWARD, tokens, expert_token_num_per_rank, per_token_scales, expert_topk_weight,
+                expert_token_num_type, idx_type, tokens_dtype, check, workspace, "device count check")
+
+
+def moe_re_routing_inverse(tokens: torch.Tensor, expert_token_num_per_rank: torch.Tensor, *,
+                           per_token_scales: Optional[torch.Tensor] = None,
+                           expert_topk_weight: Optional[torch.Tensor] = None,
+                           expert_token_num_type: int = 1, idx_type: int = 0,
+                           tokens_dtype: Optional[str] = None, check: bool = False,
+                           workspace: Optional[torch.Tensor] = None):
+    """The inverse re-route: `tokens` (and the optional scales and weights)
+    are rows in expert-major order, as moe_re_routing returns them; they come
+    back in rank-major order, row DstOffset(i,j) + k going to row
+    SrcOffset(i,j) + k. Same arguments and result tuple as moe_re_routing;
+    permute_token_idx is relative to this call's input and output (gather:
+    output row s came from input row idx[s]), which makes it the forward
+    call's scatter index and vice versa."""
+    return _run(_lib.INVERSE, tokens, expert_token_num_per_rank, per_token_scales, expert_topk_weight,
+                expert_token_num_type, idx_type, tokens_dtype, check, workspace, "device count check")

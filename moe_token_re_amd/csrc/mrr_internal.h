@@ -12,10 +12,13 @@ namespace mrr {
 
 // Workspace layout (all offsets from the workspace base):
 //   [0, 256)              WsHeader: validity of the counts the table was built from
-//   [256, 256 + T)        table[M + 1] of int32 pairs (dst_off, src_off), cells in
-//                         column-major (expert j, rank i) order m = j*N + i, so that
-//                         dst_off is non-decreasing in m; table[M] = (A, A)
-// with M = N*E and T = round_up(8*(M+1), 256).
+//   [256, 256 + T)        table[M + 1] of int32 pairs (output offset, input offset) in
+//                         output order, so that the first member is non-decreasing in m:
+//                         forward: (DstOffset, SrcOffset) of cell m = j*N + i (column-major);
+//                         inverse: (SrcOffset, DstOffset) of cell m = i*E + j (row-major);
+//                         table[M] = (A, A)
+// with M = N*E and T = round_up(8*(M+1), 256). The gather kernels only see
+// this table, so one kernel serves both directions.
 constexpr size_t kHeaderBytes = 256;
 constexpr uint32_t kTablesValid = 0x4D525256u;  // "VRRM": counts valid, table built for (A, N, E)
 constexpr uint32_t kCountsValid = 0x4D525243u;  // "CRRM": counts valid, no table (single-kernel path)
@@ -29,6 +32,8 @@ constexpr uint32_t kFlagTooLarge = 4u;      // some count > INT32_MAX
 struct WsHeader {
   uint32_t status;  // kTablesValid or kTablesBad; anything else: no tables yet
   uint32_t flags;
+  uint32_t inverse;  // the table's direction (1: inverse)
+  uint32_t pad;
   int64_t A;
   int64_t N;
   int64_t E;
@@ -98,6 +103,7 @@ struct Plan {
   bool has_weight;
   bool scatter;             // idx_type == 1
   bool cumsum;              // expert_token_num_type == 0
+  bool inverse;             // direction == MRR_INVERSE: the table in row-major cell order
   bool fused;               // moe_rerouting_v2 runs the single fused kernel
   int rows_per_wg;
   int64_t grid;             // gather workgroups

@@ -200,7 +200,8 @@ __device__ __forceinline__ int32_t clamp_count(CountT raw, uint32_t* flags) {
 }
 
 __device__ __forceinline__ void write_header(WsHeader* hdr, int64_t A, int64_t N, int64_t E, int64_t total,
-                                             uint32_t flags, uint32_t valid_status) {
+                                             uint32_t flags, uint32_t valid_status, int inverse) {
+  hdr->inverse = static_cast<uint32_t>(inverse);
   hdr->A = A;
   hdr->N = N;
   hdr->E = E;
@@ -235,14 +236,17 @@ __device__ __forceinline__ void finish_offsets(pair_t* tab, int32_t* col, int M,
 
 // Both offset tables of counts[N][E] with one cell per thread (M <= kThreads),
 // in a workgroup's LDS. lds holds the counts and the source offsets in
-// column-major cell order ([M] int32 each). Writes tab[m] = (DstOffset,
-// SrcOffset) for m = j*N + i (tab in LDS or global memory; coalesced), tab[M]
-// = (A, A), and the expert starts col[j] = DstOffset(0, j), col[E] = A.
+// column-major cell order ([M] int32 each). Writes the table (in LDS or
+// global memory) in output order: forward, tab[j*N + i] = (DstOffset,
+// SrcOffset) (coalesced); inverse, tab[i*E + j] = (SrcOffset, DstOffset);
+// then tab[M] = (A, A), and the expert starts col[j] = DstOffset(0, j),
+// col[E] = A.
 // Returns 0, or the rejection flags (the same in every thread; then tab and
 // col are not written).
 template <int kThreads, typename CountT>
-__device__ uint32_t offsets_cells(const CountT* __restrict__ counts, int N, int E, int64_t A, int32_t* lds,
-                                  int32_t* col, pair_t* tab, ScanShared<kThreads>* sh, int64_t* total_out) {
+__device__ uint32_t offsets_cells(const CountT* __restrict__ counts, int N, int E, int64_t A, int inverse,
+                                  int32_t* lds, int32_t* col, pair_t* tab, ScanShared<kThreads>* sh,
+                                  int64_t* total_out) {
   const int tid = threadIdx.x;
   const int M = N * E;
   int32_t* s_c = lds;      // counts, column-major
@@ -271,11 +275,19 @@ __device__ uint32_t offsets_cells(const CountT* __restrict__ counts, int N, int 
   uint64_t unused;
   const uint32_t dst = block_scan_u32<kThreads, false>(c2, 0, sh->w[1], sh->t[1], &unused);
   if (in) {
+    const int j = tid / N;
+    const int i = tid - j * N;
     pair_t t;
-    t.x = static_cast<int32_t>(dst);
-    t.y = s_s[tid];
-    tab[tid] = t;
-    if (tid % N == 0) col[tid / N] = static_cast<int32_t>(dst);
+    if (inverse) {
+      t.x = s_s[tid];
+      t.y = static_cast<int32_t>(dst);
+      tab[i * E + j] = t;
+    } else {
+      t.x = static_cast<int32_t>(dst);
+      t.y = s_s[tid];
+      tab[tid] = t;
+    }
+    if (i == 0) col[j] = static_cast<int32_t>(dst);
   }
   finish_offsets(tab, col, M, E, A);
   return 0;
@@ -288,8 +300,9 @@ __device__ uint32_t offsets_cells(const CountT* __restrict__ counts, int N, int 
 // flight together; a chunk walk along a column touches consecutive LDS words,
 // and with kC and NS both odd the 64 lanes of a wave start in distinct banks.
 template <int kThreads, int kC, typename CountT>
-__device__ uint32_t offsets_chunks(const CountT* __restrict__ counts, int N, int E, int64_t A, int32_t* lds,
-                                   int32_t* col, pair_t* tab, ScanShared<kThreads>* sh, int64_t* total_out) {
+__device__ uint32_t offsets_chunks(const CountT* __restrict__ counts, int N, int E, int64_t A, int inverse,
+                                   int32_t* lds, int32_t* col, pair_t* tab, ScanShared<kThreads>* sh,
+                                   int64_t* total_out) {
   const int tid = threadIdx.x;
   const int M = N * E;
   const int NS = N | 1;
@@ -391,8 +404,27 @@ __device__ uint32_t offsets_chunks(const CountT* __restrict__ counts, int N, int
   }
   __syncthreads();
 
-  // The table, with coalesced stores: cell m = j*N + i.
-  {
+  // The table, with coalesced stores, in output order: forward, cell m =
+  // j*N + i; inverse, cell m = i*E + j with the pair's members swapped.
+  if (inverse) {
+    int i = tid / E, j = tid - (tid / E) * E;
+    const int di = kThreads / E, dj = kThreads - (kThreads / E) * E;
+#pragma unroll
+    for (int k = 0; k < kC; ++k) {
+      const int m = tid + k * kThreads;
+      if (m < M) {
+        pair_t t;
+        t.x = s_s[j * NS + i];
+        t.y = s_c[j * NS + i];
+        tab[m] = t;
+      }
+      i += di;
+      j += dj;
+      const bool wrap = j >= E;
+      j = wrap ? j - E : j;
+      i += wrap ? 1 : 0;
+    }
+  } else {
     int j = tid / N, i = tid - (tid / N) * N;
     const int dj = kThreads / N, di = kThreads - (kThreads / N) * N;
 #pragma unroll
@@ -430,29 +462,29 @@ __device__ __forceinline__ void write_etn(const int32_t* col, int E, int cumsum,
 // kC == 1: one cell per thread (M <= kOffsetThreads); otherwise chunks of kC.
 template <typename CountT, int kC>
 __global__ __launch_bounds__(kOffsetThreads) void offsets_staged_kernel(
-    const CountT* __restrict__ counts, int32_t N, int32_t E, int64_t A, int cumsum, CountT* __restrict__ etn,
-    WsHeader* __restrict__ hdr, pair_t* __restrict__ table, int32_t mats_ints) {
+    const CountT* __restrict__ counts, int32_t N, int32_t E, int64_t A, int cumsum, int inverse,
+    CountT* __restrict__ etn, WsHeader* __restrict__ hdr, pair_t* __restrict__ table, int32_t mats_ints) {
   extern __shared__ int32_t s_dyn[];
   __shared__ ScanShared<kOffsetThreads> sh;
   int32_t* col = s_dyn + mats_ints;  // [E + 1], after the offset matrices
   int64_t total = 0;
   uint32_t flags;
   if (kC == 1)
-    flags = offsets_cells<kOffsetThreads>(counts, N, E, A, s_dyn, col, table, &sh, &total);
+    flags = offsets_cells<kOffsetThreads>(counts, N, E, A, inverse, s_dyn, col, table, &sh, &total);
   else
-    flags = offsets_chunks<kOffsetThreads, kC>(counts, N, E, A, s_dyn, col, table, &sh, &total);
+    flags = offsets_chunks<kOffsetThreads, kC>(counts, N, E, A, inverse, s_dyn, col, table, &sh, &total);
   if (flags == 0) write_etn<kOffsetThreads>(col, E, cumsum, etn);
-  if (threadIdx.x == 0) write_header(hdr, A, N, E, total, flags, kTablesValid);
+  if (threadIdx.x == 0) write_header(hdr, A, N, E, total, flags, kTablesValid, inverse);
 }
 
 // For count matrices too large for LDS: the same two scans in tiles of
 // kOffsetTile cells, reading the counts from global memory (the column-major
-// pass reads them transposed) and writing the source offsets of the first
-// pass straight into the table.
+// pass reads them transposed) and writing each pass's offsets straight into
+// their slot of the table (output order; see the workspace layout).
 template <typename CountT>
 __global__ __launch_bounds__(kOffsetThreads) void offsets_global_kernel(
-    const CountT* __restrict__ counts, int32_t N, int32_t E, int64_t A, int cumsum, CountT* __restrict__ etn,
-    WsHeader* __restrict__ hdr, int32_t* __restrict__ table) {
+    const CountT* __restrict__ counts, int32_t N, int32_t E, int64_t A, int cumsum, int inverse,
+    CountT* __restrict__ etn, WsHeader* __restrict__ hdr, int32_t* __restrict__ table) {
   __shared__ int64_t s_scan[2 * kOffsetThreads / 64 + 1];
   __shared__ uint32_t s_flags;
   const int tid = threadIdx.x;
@@ -460,8 +492,8 @@ __global__ __launch_bounds__(kOffsetThreads) void offsets_global_kernel(
   if (tid == 0) s_flags = 0;
   uint32_t flags = 0;
 
-  // Pass 1: SrcOffset (row-major), stored in the second slot of cell (i, j)'s
-  // column-major pair.
+  // Pass 1: SrcOffset (row-major): forward, the second member of cell (i, j)'s
+  // pair at j*N + i; inverse, the first member at i*E + j.
   int64_t carry = 0;
   for (int base = 0; base < M; base += kOffsetTile) {
     CountT raw[kOffsetItems];
@@ -486,7 +518,7 @@ __global__ __launch_bounds__(kOffsetThreads) void offsets_global_kernel(
       if (m < M) {
         const int i = m / E;
         const int j = m - i * E;
-        table[2 * (j * N + i) + 1] = static_cast<int32_t>(run);
+        table[inverse ? 2 * m : 2 * (j * N + i) + 1] = static_cast<int32_t>(run);
       }
       run += c[k];
     }
@@ -495,11 +527,12 @@ __global__ __launch_bounds__(kOffsetThreads) void offsets_global_kernel(
   flags = block_or(flags, &s_flags);
   if (carry != A) flags |= kFlagSumMismatch;
   if (flags != 0) {
-    if (tid == 0) write_header(hdr, A, N, E, carry, flags, kTablesValid);
+    if (tid == 0) write_header(hdr, A, N, E, carry, flags, kTablesValid, inverse);
     return;
   }
 
-  // Pass 2: DstOffset (column-major).
+  // Pass 2: DstOffset (column-major): forward, the first member at j*N + i;
+  // inverse, the second member at i*E + j.
   carry = 0;
   for (int base = 0; base < M; base += kOffsetTile) {
     CountT raw[kOffsetItems];
@@ -523,7 +556,11 @@ __global__ __launch_bounds__(kOffsetThreads) void offsets_global_kernel(
 #pragma unroll
     for (int k = 0; k < kOffsetItems; ++k) {
       const int mc = base + tid * kOffsetItems + k;
-      if (mc < M) table[2 * mc] = static_cast<int32_t>(run);
+      if (mc < M) {
+        const int j = mc / N;
+        const int i = mc - j * N;
+        table[inverse ? 2 * (i * E + j) + 1 : 2 * mc] = static_cast<int32_t>(run);
+      }
       run += c[k];
     }
     carry += tile_total;
@@ -535,13 +572,19 @@ __global__ __launch_bounds__(kOffsetThreads) void offsets_global_kernel(
   __threadfence_block();
   __syncthreads();
 
-  // expert_token_num from the expert starts dst_off[j*N] in the table.
+  // expert_token_num from the expert starts DstOffset(0, j) in the table.
   for (int j = tid; j < E; j += kOffsetThreads) {
-    const int64_t end = table[2 * ((j + 1) * N)];
-    const int64_t start = table[2 * (j * N)];
+    int64_t start, end;
+    if (inverse) {
+      start = N > 0 ? table[2 * j + 1] : 0;
+      end = N > 0 && j + 1 < E ? table[2 * (j + 1) + 1] : A;
+    } else {
+      start = table[2 * (j * N)];
+      end = table[2 * ((j + 1) * N)];
+    }
     etn[j] = static_cast<CountT>(cumsum ? end : end - start);
   }
-  if (tid == 0) write_header(hdr, A, N, E, carry, 0, kTablesValid);
+  if (tid == 0) write_header(hdr, A, N, E, carry, 0, kTablesValid, inverse);
 }
 
 // Banded offsets for larger count matrices (kOffsetThreads < M, E <=
@@ -619,7 +662,7 @@ struct CountAcc {
 template <typename CountT>
 __global__ __launch_bounds__(kOffsetThreads) void offsets_banded_kernel(
     const CountT* __restrict__ counts, int32_t N, int32_t E, int32_t band_rows, int32_t lanes, int64_t A,
-    int cumsum, CountT* __restrict__ etn, WsHeader* __restrict__ hdr, pair_t* __restrict__ table) {
+    int cumsum, int inverse, CountT* __restrict__ etn, WsHeader* __restrict__ hdr, pair_t* __restrict__ table) {
   __shared__ BandShared s;
   const int tid = threadIdx.x;
   const int i0 = blockIdx.x * band_rows;
@@ -734,7 +777,8 @@ __global__ __launch_bounds__(kOffsetThreads) void offsets_banded_kernel(
   __syncthreads();
   const uint32_t flags = s.flags;
   if (flags != 0) {  // uniform: every workgroup saw every count
-    if (blockIdx.x == 0 && tid == 0) write_header(hdr, A, N, E, static_cast<int64_t>(s.grand), flags, kTablesValid);
+    if (blockIdx.x == 0 && tid == 0)
+      write_header(hdr, A, N, E, static_cast<int64_t>(s.grand), flags, kTablesValid, inverse);
     return;
   }
 
@@ -751,10 +795,17 @@ __global__ __launch_bounds__(kOffsetThreads) void offsets_banded_kernel(
   if (in && ui == 0) s.cstart[uj] = ex3[1];
   __syncthreads();
   int32_t* words = reinterpret_cast<int32_t*>(table);
-  if (in) {
-    words[2 * (qj * N + i0 + qi) + 1] = static_cast<int32_t>(s.above_all + ex3[0]);
-    words[2 * (uj * N + i0 + ui)] =
+  if (in) {  // output order: forward, cell j*N + i as (dst, src); inverse, cell i*E + j as (src, dst)
+    const int32_t src = static_cast<int32_t>(s.above_all + ex3[0]);
+    const int32_t dst =
         static_cast<int32_t>(static_cast<uint32_t>(s.col[uj]) + s.above[uj] + (ex3[1] - s.cstart[uj]));
+    if (inverse) {
+      words[2 * ((i0 + qi) * E + qj)] = src;
+      words[2 * ((i0 + ui) * E + uj) + 1] = dst;
+    } else {
+      words[2 * (qj * N + i0 + qi) + 1] = src;
+      words[2 * (uj * N + i0 + ui)] = dst;
+    }
   }
   if (blockIdx.x == 0) {
     write_etn<kOffsetThreads>(s.col, E, cumsum, etn);
@@ -763,7 +814,7 @@ __global__ __launch_bounds__(kOffsetThreads) void offsets_banded_kernel(
       t.x = static_cast<int32_t>(A);
       t.y = static_cast<int32_t>(A);
       table[N * E] = t;
-      write_header(hdr, A, N, E, static_cast<int64_t>(s.grand), 0, kTablesValid);
+      write_header(hdr, A, N, E, static_cast<int64_t>(s.grand), 0, kTablesValid, inverse);
     }
   }
 }
@@ -815,10 +866,11 @@ struct GatherArgs {
   int32_t A;
   int32_t M;
   int32_t rows_per_wg;
+  int32_t inverse;         // the direction the table must have been built for
 };
 
-// Source row of output row d, from a (dst_off, src_off) table of M + 1 pairs
-// in LDS or global memory. All 64 lanes of a wave call it together, with
+// Source row of output row d, from a table of M + 1 (output offset, input
+// offset) pairs sorted by output offset, in LDS or global memory. All 64 lanes of a wave call it together, with
 // their rows d in [d_lo, d_lo + 63]; d_lo is the same for the whole wave.
 // Whatever the table holds, every read stays inside its M + 1 entries.
 __device__ __forceinline__ int32_t source_row(const pair_t* table, int M, int d_lo, int d) {
@@ -999,9 +1051,10 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs p) {
   const int rows = min(p.rows_per_wg, p.A - row0);
   // The table is searched before the header is checked, so that the two
   // reads overlap; nothing is written unless the header says the table was
-  // built from valid counts for this (A, N, E).
+  // built from valid counts for this (A, N, E) and direction.
   const WsHeader* h = p.hdr;
-  const bool valid_table = h->status == kTablesValid && h->A == p.A && h->N == p.N && h->E == p.E;
+  const bool valid_table = h->status == kTablesValid && h->A == p.A && h->N == p.N && h->E == p.E &&
+                           h->inverse == static_cast<uint32_t>(p.inverse);
   map_rows(p.table, p.M, p.A, row0, rows, s_src);
   if (!valid_table) return;  // uniform over the workgroup
   __syncthreads();
@@ -1026,10 +1079,11 @@ __global__ __launch_bounds__(kGatherThreads) void fused_kernel(GatherArgs p, Fus
   int32_t* col = mats + 2 * p.M;                 // [E + 1]
   int64_t total = 0;
   const uint32_t flags =
-      offsets_cells<kGatherThreads>(static_cast<const CountT*>(f.counts), N, E, p.A, mats, col, tab, &sh, &total);
+      offsets_cells<kGatherThreads>(static_cast<const CountT*>(f.counts), N, E, p.A, p.inverse, mats, col, tab,
+                                    &sh, &total);
   if (blockIdx.x == 0) {
     if (flags == 0) write_etn<kGatherThreads>(col, E, f.cumsum, static_cast<CountT*>(f.etn));
-    if (threadIdx.x == 0) write_header(p.hdr, p.A, p.N, p.E, total, flags, kCountsValid);
+    if (threadIdx.x == 0) write_header(p.hdr, p.A, p.N, p.E, total, flags, kCountsValid, p.inverse);
   }
   if (flags != 0) return;  // uniform: nothing is written for rejected counts
 
@@ -1103,8 +1157,9 @@ void launch_staged(const Plan& pl, const mrr_args* a, uint8_t* base, size_t lds,
   const int32_t mats = static_cast<int32_t>((static_cast<int64_t>(lds) - 16) / 4 - (pl.E + 1));
   hipLaunchKernelGGL((offsets_staged_kernel<CountT, kC>), dim3(1), dim3(kOffsetThreads), lds, stream,
                      static_cast<const CountT*>(a->expert_token_num_per_rank), static_cast<int32_t>(pl.N),
-                     static_cast<int32_t>(pl.E), pl.A, pl.cumsum ? 1 : 0, static_cast<CountT*>(a->expert_token_num),
-                     reinterpret_cast<WsHeader*>(base), reinterpret_cast<pair_t*>(base + pl.table_bytes), mats);
+                     static_cast<int32_t>(pl.E), pl.A, pl.cumsum ? 1 : 0, pl.inverse ? 1 : 0,
+                     static_cast<CountT*>(a->expert_token_num), reinterpret_cast<WsHeader*>(base),
+                     reinterpret_cast<pair_t*>(base + pl.table_bytes), mats);
 }
 
 template <typename CountT>
@@ -1114,7 +1169,7 @@ mrr_status launch_offsets_t(const Plan& pl, const mrr_args* a, void* ws, hipStre
     hipLaunchKernelGGL((offsets_banded_kernel<CountT>), dim3(static_cast<unsigned>(pl.band_grid)),
                        dim3(kOffsetThreads), 0, stream, static_cast<const CountT*>(a->expert_token_num_per_rank),
                        static_cast<int32_t>(pl.N), static_cast<int32_t>(pl.E), pl.band_rows, pl.band_lanes, pl.A,
-                       pl.cumsum ? 1 : 0, static_cast<CountT*>(a->expert_token_num),
+                       pl.cumsum ? 1 : 0, pl.inverse ? 1 : 0, static_cast<CountT*>(a->expert_token_num),
                        reinterpret_cast<WsHeader*>(base), reinterpret_cast<pair_t*>(base + pl.table_bytes));
     return hipGetLastError() == hipSuccess ? MRR_SUCCESS : MRR_ERROR_HIP;
   }
@@ -1136,8 +1191,9 @@ mrr_status launch_offsets_t(const Plan& pl, const mrr_args* a, void* ws, hipStre
   } else {
     hipLaunchKernelGGL((offsets_global_kernel<CountT>), dim3(1), dim3(kOffsetThreads), 0, stream,
                        static_cast<const CountT*>(a->expert_token_num_per_rank), static_cast<int32_t>(pl.N),
-                       static_cast<int32_t>(pl.E), pl.A, pl.cumsum ? 1 : 0, static_cast<CountT*>(a->expert_token_num),
-                       reinterpret_cast<WsHeader*>(base), reinterpret_cast<int32_t*>(base + pl.table_bytes));
+                       static_cast<int32_t>(pl.E), pl.A, pl.cumsum ? 1 : 0, pl.inverse ? 1 : 0,
+                       static_cast<CountT*>(a->expert_token_num), reinterpret_cast<WsHeader*>(base),
+                       reinterpret_cast<int32_t*>(base + pl.table_bytes));
   }
   return hipGetLastError() == hipSuccess ? MRR_SUCCESS : MRR_ERROR_HIP;
 }
@@ -1169,6 +1225,7 @@ GatherArgs gather_args(const Plan& pl, const mrr_args* a, void* ws) {
   g.A = static_cast<int32_t>(pl.A);
   g.M = static_cast<int32_t>(pl.M);
   g.rows_per_wg = pl.rows_per_wg;
+  g.inverse = pl.inverse ? 1 : 0;
   return g;
 }
 

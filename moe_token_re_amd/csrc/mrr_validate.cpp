@@ -117,6 +117,7 @@ mrr_status make_plan(const mrr_args* a, const void* ws, size_t ws_bytes, Plan* p
   // attributes
   if (a->expert_token_num_type != 0 && a->expert_token_num_type != 1) return MRR_ERROR_INVALID_VALUE;
   if (a->idx_type != 0 && a->idx_type != 1) return MRR_ERROR_INVALID_VALUE;
+  if (a->direction != MRR_FORWARD && a->direction != MRR_INVERSE) return MRR_ERROR_INVALID_VALUE;
 
   // shapes ("约束说明": 0 < H < 16384; Sum(counts) == A, with int32 indices)
   if (a->A < 0 || a->A > INT32_MAX) return MRR_ERROR_INVALID_SHAPE;
@@ -215,6 +216,7 @@ mrr_status make_plan(const mrr_args* a, const void* ws, size_t ws_bytes, Plan* p
   q.count_bytes = cb;
   q.has_weight = has_w;
   q.scatter = a->idx_type == 1;
+  q.inverse = a->direction == MRR_INVERSE;
   q.cumsum = a->expert_token_num_type == 0;
   int64_t rows = int64_t(kGatherThreads) * kGatherUnroll / q.vecs_per_row;
   if (tuning().rows_per_wg > 0) rows = tuning().rows_per_wg;

@@ -119,6 +119,9 @@ def test_valid_configurations():
     a.tokens += 1                                                      # byte rows: any alignment
     a.permute_tokens += 3
     assert validate(a) == _lib.SUCCESS
+    a = valid_args(scales="e8m0")
+    a.direction = _lib.INVERSE                                         # the same checks run backwards
+    assert validate(a) == _lib.SUCCESS
 
 
 def _with(f, **kw):
@@ -134,6 +137,8 @@ def _with(f, **kw):
     (lambda a: setattr(a, "scales_dtype", _lib.F16), _lib.ERROR_UNSUPPORTED_DTYPE),
     (lambda a: setattr(a, "expert_token_num_type", 2), _lib.ERROR_INVALID_VALUE),
     (lambda a: setattr(a, "idx_type", -1), _lib.ERROR_INVALID_VALUE),
+    (lambda a: setattr(a, "direction", 2), _lib.ERROR_INVALID_VALUE),
+    (lambda a: setattr(a, "direction", -1), _lib.ERROR_INVALID_VALUE),
     (lambda a: setattr(a, "H", 0), _lib.ERROR_INVALID_SHAPE),
     (lambda a: setattr(a, "H", 16384), _lib.ERROR_INVALID_SHAPE),
     (lambda a: setattr(a, "A", -1), _lib.ERROR_INVALID_SHAPE),
