@@ -10,16 +10,22 @@ Calls rotate over several identical buffer sets whose total footprint is at
 least 1 GiB, so the 256 MB Infinity Cache cannot hold the working set between
 calls. Prints ONE JSON line:
   value       re-route GB/s = algorithmic bytes per call / wall time per call
-  roofline    the gather kernel alone: algorithmic bytes per launch / its mean
-              duration (HIP events on the launch stream) against 8 TB/s HBM;
+  roofline    the dominant kernel alone (the fused kernel, or the gather
+              kernel of the two-kernel path): algorithmic bytes per launch /
+              its mean duration over back-to-back launches (HIP events on
+              the launch stream) against 8 TB/s HBM;
               traffic from rocprofv3 FETCH_SIZE/WRITE_SIZE counters when the
               committed counter summary matches the current kernel source
   cpu_baseline the CPU oracle on the same workload, one host thread
 plus the measured copy ceiling (hipMemcpyAsync device-to-device and a plain
 16-byte non-temporal copy kernel moving the same token bytes).
 
+With --inverse the same workload runs the inverse re-route (its token rows
+taken as expert-major, returned to rank-major order), with the oracle's
+inverse as the CPU baseline.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-cpu] [--no-ceiling]
+                       [--inverse] [--no-cpu] [--no-ceiling]
 """
 from __future__ import annotations
 
@@ -60,18 +66,18 @@ def gather_bytes_per_launch(w) -> int:
     return per_row * w.A
 
 
-def traffic_from_profile(w, kernel_name):
+def traffic_from_profile(w, kernel_name, direction="forward"):
     """HBM bytes per launch of the dominant kernel from the committed counter
     summary, scaled by the copy kernel's counter reading for a known byte
-    count; None when the summary is missing, for another workload or kernel,
-    or the kernel source has changed since the counters were taken."""
+    count; None when the summary is missing, for another workload, kernel or
+    direction, or the kernel source has changed since the counters were taken."""
     if not os.path.exists(PROFILE_SUMMARY):
         return None
     text = open(PROFILE_SUMMARY).read()
     fields = dict(re.findall(r"^(\w+):\s*(\S+)\s*$", text, flags=re.M))
     try:
         if (fields.get("source_hash") != kernel_source_hash() or fields.get("workload") != w.name
-                or fields.get("kernel") != kernel_name):
+                or fields.get("kernel") != kernel_name or fields.get("direction", "forward") != direction):
             return None
         fetch = float(fields["FETCH_SIZE_KiB"]) * float(fields["fetch_scale"])
         write = float(fields["WRITE_SIZE_KiB"]) * float(fields["write_scale"])
@@ -80,10 +86,12 @@ def traffic_from_profile(w, kernel_name):
     return int(round((fetch + write) * 1024))
 
 
-def time_oracle(w, budget_s=10.0, max_runs=7):
+def time_oracle(w, budget_s=10.0, max_runs=7, inverse=False):
     """The CPU oracle on the full workload, single-threaded, outputs preallocated
     and pre-faulted; median over runs that fit the time budget."""
     from oracle import oracle
+
+    fn = oracle.reroute_inverse if inverse else oracle.reroute
 
     outs = oracle.allocate_outputs(w.tokens, w.counts, w.scales, w.weight)
     for o in outs:
@@ -93,7 +101,7 @@ def time_oracle(w, budget_s=10.0, max_runs=7):
     t_start = time.perf_counter()
     while len(times) < max_runs:
         t0 = time.perf_counter()
-        oracle.reroute(w.tokens, w.counts, w.scales, w.weight, w.etn_type, w.idx_type, out=outs)
+        fn(w.tokens, w.counts, w.scales, w.weight, w.etn_type, w.idx_type, out=outs)
         times.append(time.perf_counter() - t0)
         if time.perf_counter() - t_start > budget_s and len(times) >= 3:
             break
@@ -106,6 +114,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="pages_shape")
+    ap.add_argument("--inverse", action="store_true", help="time the inverse re-route (expert-major -> rank-major)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the copy-ceiling measurement")
     opt = ap.parse_args()
@@ -136,7 +145,8 @@ def main():
         t = base if k == 0 else {key: (v.clone() if isinstance(v, torch.Tensor) else v) for key, v in base.items()}
         call, _ = api.make_call(t["tokens"], t["counts"], per_token_scales=t["scales"],
                                 expert_topk_weight=t["weight"], expert_token_num_type=w.etn_type,
-                                idx_type=w.idx_type, tokens_dtype=t["tokens_dtype"], stream=stream)
+                                idx_type=w.idx_type, tokens_dtype=t["tokens_dtype"], stream=stream,
+                                direction=_lib.INVERSE if opt.inverse else _lib.FORWARD)
         calls.append(call)
     torch.cuda.synchronize()
 
@@ -167,39 +177,40 @@ def main():
     print(f"[bench] {opt.steps} calls: wall {ms_per_step * 1e3:.2f} us/call, events "
           f"{ev_ms * 1e3 / opt.steps:.2f} us/call, {value:.1f} GB/s", file=sys.stderr, flush=True)
 
-    # per-kernel: events around each launch, on the launch stream. When the
-    # call is one fused kernel that kernel is the dominant one; otherwise the
-    # gather kernel is, timed apart from the offsets kernel.
+    # per-kernel: K back-to-back launches of one kernel between two events on
+    # the launch stream, rotating over the buffer sets. When the call is one
+    # fused kernel that kernel is the dominant one; otherwise the gather
+    # kernel is, timed on tables its sets' offsets kernels built beforehand.
     plan = calls[0].plan()
     n_k = max(opt.steps, 50)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(n_k)]
-    for i in range(n_k):
-        c = calls[i % n_sets]
-        evs[i][0].record(stream)
-        if plan["fused"]:
-            c.run()
-            evs[i][1].record(stream)
-        else:
-            c.run_offsets()
-            evs[i][1].record(stream)
-            c.run_gather()
-        evs[i][2].record(stream)
-    torch.cuda.synchronize()
+
+    def back_to_back_us(fn):
+        for i in range(min(10, n_k)):
+            fn(calls[i % n_sets])
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(n_k):
+            fn(calls[i % n_sets])
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) * 1e3 / n_k
+
+    off_mean_us = None
     if plan["fused"]:
         kernel_name = "fused_kernel"
-        off_us = [0.0]
-        kern_us = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
+        kern_mean_us = back_to_back_us(lambda c: c.run())
         kbytes = alg_bytes
     else:
         kernel_name = "gather_kernel"
-        off_us = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
-        kern_us = [e[1].elapsed_time(e[2]) * 1e3 for e in evs]
+        off_mean_us = back_to_back_us(lambda c: c.run_offsets())
+        for c in calls:
+            c.run_offsets()
+        kern_mean_us = back_to_back_us(lambda c: c.run_gather())
         kbytes = gather_bytes_per_launch(w)
-    kern_mean_us = statistics.mean(kern_us)
     achieved = kbytes / (kern_mean_us * 1e-6) / 1e9
     print(f"[bench] plan {plan}", file=sys.stderr, flush=True)
-    print(f"[bench] per kernel: {kernel_name} mean {kern_mean_us:.2f} us (median {statistics.median(kern_us):.2f}), "
-          f"{achieved:.1f} GB/s; offsets kernel mean {statistics.mean(off_us):.2f} us", file=sys.stderr, flush=True)
+    print(f"[bench] per kernel ({n_k} back-to-back launches): {kernel_name} {kern_mean_us:.2f} us, "
+          f"{achieved:.1f} GB/s; offsets kernel {off_mean_us} us", file=sys.stderr, flush=True)
 
     # hot (same buffers every call), labelled as such
     torch.cuda.synchronize()
@@ -252,7 +263,7 @@ def main():
 
     cpu = None
     if not opt.no_cpu:
-        med_s, runs = time_oracle(w)
+        med_s, runs = time_oracle(w, inverse=opt.inverse)
         cpu = {"value": round(alg_bytes / med_s / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
                "sample": f"the full {w.name} workload (one whole call), median of {runs} runs, "
                          f"{med_s * 1e3:.1f} ms/call; host has {os.cpu_count()} logical CPUs"}
@@ -275,16 +286,17 @@ def main():
                    "tokens_dtype": w.tokens_dtype, "counts_dtype": str(w.counts.dtype),
                    "scales": None if w.scales is None else f"{w.scales_dtype}{list(w.scales.shape)}",
                    "topk_weight": w.weight is not None, "expert_token_num_type": w.etn_type,
-                   "idx_type": w.idx_type, "buffer_sets": n_sets, "parallelism": "single GPU"},
+                   "idx_type": w.idx_type, "direction": "inverse" if opt.inverse else "forward",
+                   "buffer_sets": n_sets, "parallelism": "single GPU"},
         "us_per_call": round(ms_per_step * 1e3, 2),
         "us_per_call_events": round(ev_ms * 1e3 / opt.steps, 2),
         "us_per_call_hot_same_buffers": round(hot_us, 2),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "algorithmic_bytes_per_call": alg_bytes,
         "launch_path": "fused single kernel" if plan["fused"] else "offsets kernel + gather kernel",
-        "offsets_kernel_us_mean": None if plan["fused"] else round(statistics.mean(off_us), 2),
+        "offsets_kernel_us_mean": None if off_mean_us is None else round(off_mean_us, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_from_profile(w, kernel_name),
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_from_profile(w, kernel_name, "inverse" if opt.inverse else "forward"),
                      "kernel": kernel_name, "bytes_per_launch": kbytes,
                      "launch_us_mean": round(kern_mean_us, 2)},
         "copy_ceiling": ceiling,
