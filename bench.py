@@ -11,7 +11,8 @@ least 1 GiB, so the 256 MB Infinity Cache cannot hold the working set between
 calls. Prints ONE JSON line:
   value       re-route GB/s = algorithmic bytes per call / wall time per call
   roofline    the dominant kernel alone (the fused kernel, or the gather
-              kernel of the two-kernel path): algorithmic bytes per launch /
+              kernel of the two-kernel path; the row map it reads is
+              implementation traffic, not counted): algorithmic bytes per launch /
               its mean duration over back-to-back launches (HIP events on
               the launch stream) against 8 TB/s HBM;
               traffic from rocprofv3 FETCH_SIZE/WRITE_SIZE counters when the
@@ -201,7 +202,7 @@ def main():
         kern_mean_us = back_to_back_us(lambda c: c.run())
         kbytes = alg_bytes
     else:
-        kernel_name = "gather_kernel"
+        kernel_name = "stream_gather_kernel" if plan["gather_kernel"] == 1 else "gather_kernel"
         off_mean_us = back_to_back_us(lambda c: c.run_offsets())
         for c in calls:
             c.run_offsets()

@@ -144,13 +144,15 @@ typedef struct mrr_args {
 enum { MRR_FORWARD = 0, MRR_INVERSE = 1 };
 
 /*
- * Bytes of device workspace a call with an N x E count matrix needs: a
- * 256-byte header (validity status of the counts) and two int32 tables of
- * the per-cell offsets. Returns 0 when N or E is negative or N*E is too
- * large for 32-bit cell indices. The caller allocates it (no zeroing needed);
- * it may be reused by calls ordered on one stream.
+ * Bytes of device workspace a call with A rows and an N x E count matrix
+ * needs: a 256-byte header (validity status of the counts), the per-cell
+ * offsets (two int32 per cell) and the source row of every output row (one
+ * int32 per row), each part rounded up to 256 bytes. Returns 0 when A, N or
+ * E is negative, A > INT32_MAX, or N*E is too large for 32-bit cell indices.
+ * The caller allocates it (no zeroing needed); it may be reused by calls
+ * ordered on one stream.
  */
-size_t mrr_workspace_size(int64_t N, int64_t E);
+size_t mrr_workspace_size(int64_t A, int64_t N, int64_t E);
 
 /*
  * The exact checks the launching calls make before they launch anything,
@@ -174,10 +176,15 @@ typedef struct mrr_plan_info {
   int64_t scale_row_bytes;
   int32_t scale_inline_bytes;    /* 16 or 4: scale rows move in pieces of that size together with
                                     the token rows; 0: in a separate pass after them */
-  int64_t offsets_workgroups;    /* workgroups of moe_rerouting_v2_offsets(): 1 for the
-                                    single-workgroup kernel, more when each workgroup computes
-                                    the offsets of a band of ranks (larger count matrices);
-                                    0 when there are no cells */
+  int64_t offsets_workgroups;    /* workgroups of moe_rerouting_v2_offsets(): several for larger
+                                    count matrices (bands of ranks) or when the row map is
+                                    written (one workgroup per 1024 rows); 1 otherwise; 0 when
+                                    there are no cells */
+  int32_t gather_kernel;         /* what moe_rerouting_v2_gather() launches: 1 = 64-lane
+                                    workgroups, each moving 64 vectors of one output stream
+                                    (token rows, scale rows, per-row items) with the row map
+                                    the offsets phase wrote; 0 = workgroups of whole rows that
+                                    search the offsets table */
 } mrr_plan_info;
 
 /*

@@ -75,6 +75,7 @@ class MrrPlanInfo(ctypes.Structure):
         ("scale_row_bytes", ctypes.c_int64),
         ("scale_inline_bytes", ctypes.c_int32),
         ("offsets_workgroups", ctypes.c_int64),
+        ("gather_kernel", ctypes.c_int32),
     ]
 
 
@@ -94,7 +95,7 @@ def load() -> ctypes.CDLL:
             lib = ctypes.CDLL(LIB_PATH)
             P = ctypes.POINTER(MrrArgs)
             vp, sz = ctypes.c_void_p, ctypes.c_size_t
-            lib.mrr_workspace_size.argtypes = [ctypes.c_int64, ctypes.c_int64]
+            lib.mrr_workspace_size.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
             lib.mrr_workspace_size.restype = sz
             lib.mrr_validate.argtypes = [P, vp, sz]
             lib.mrr_validate.restype = ctypes.c_int

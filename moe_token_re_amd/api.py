@@ -73,9 +73,9 @@ def _raise(status: int, where: str):
     raise MrrValueError(status, where)
 
 
-def workspace_size(N: int, E: int) -> int:
-    """Bytes of workspace a call with an N x E count matrix needs."""
-    return int(_lib.load().mrr_workspace_size(N, E))
+def workspace_size(A: int, N: int, E: int) -> int:
+    """Bytes of workspace a call with A rows and an N x E count matrix needs."""
+    return int(_lib.load().mrr_workspace_size(A, N, E))
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -233,7 +233,7 @@ def make_call(tokens, expert_token_num_per_rank, *, per_token_scales=None, exper
                          expert_topk_weight=expert_topk_weight, expert_token_num_type=expert_token_num_type,
                          idx_type=idx_type, tokens_dtype=tokens_dtype, out=out, direction=direction)
     dev = tokens.device
-    need = workspace_size(args.N, args.E)
+    need = workspace_size(args.A, args.N, args.E)
     if need == 0:
         raise MrrValueError(_lib.ERROR_INVALID_SHAPE, "mrr_workspace_size")
     s = stream if stream is not None else torch.cuda.current_stream(dev)

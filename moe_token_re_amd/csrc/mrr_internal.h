@@ -17,8 +17,11 @@ namespace mrr {
 //                         forward: (DstOffset, SrcOffset) of cell m = j*N + i (column-major);
 //                         inverse: (SrcOffset, DstOffset) of cell m = i*E + j (row-major);
 //                         table[M] = (A, A)
-// with M = N*E and T = round_up(8*(M+1), 256). The gather kernels only see
-// this table, so one kernel serves both directions.
+//   [256 + T, ... + Rm)   rowmap[A] int32: the input row of every output row (written by
+//                         the offsets kernels that can, see Plan::rowmap)
+// with M = N*E, T = round_up(8*(M+1), 256) and Rm = round_up(4*A, 256). The
+// gather kernels only see the table or the row map, so one kernel serves both
+// directions.
 constexpr size_t kHeaderBytes = 256;
 constexpr uint32_t kTablesValid = 0x4D525256u;  // "VRRM": counts valid, table built for (A, N, E)
 constexpr uint32_t kCountsValid = 0x4D525243u;  // "CRRM": counts valid, no table (single-kernel path)
@@ -64,6 +67,15 @@ constexpr int kMaxRowsPerWg = 256;
 constexpr int kOffsetThreads = 1024;
 constexpr int64_t kBandMaxCells = int64_t(1) << 17;
 
+// The stream gather kernel launches one workgroup per chunk; calls with more
+// chunks than this take the row-workgroup gather kernel instead.
+constexpr int64_t kMaxStreamGrid = int64_t(1) << 31;
+
+// Calls whose token rows total at least this many bytes take the two-kernel
+// path (offsets, then the stream gather) even when the single-kernel path
+// could run them.
+constexpr int64_t kFusedMaxTokenBytes = int64_t(64) << 20;
+
 // Offsets computed in one workgroup's LDS (the single-workgroup offsets
 // kernel, and every workgroup of the fused kernel) use one of two layouts:
 //  * one cell per thread (M <= threads): counts and source offsets in
@@ -107,10 +119,16 @@ struct Plan {
   bool fused;               // moe_rerouting_v2 runs the single fused kernel
   int rows_per_wg;
   int64_t grid;             // gather workgroups
+  bool stream;              // the gather kernel is the stream kernel: 64-lane workgroups, one chunk of
+                            // 64 vectors (token or scale rows) or 64 rows (items) each
+  int64_t tok_chunks, sc_chunks, item_chunks;  // the stream kernel's chunks
+  int64_t stream_grid;      // its workgroups: the total number of chunks
   int64_t band_grid;        // banded offsets kernel: workgroups (bands); 0 = single-workgroup kernel
   int band_rows;            // ranks per band: min(N, kOffsetThreads / E)
   int band_lanes;           // threads per column in the banded kernel's first step (a power of two)
+  int band_split;           // workgroups per band (they share the band's row map writes)
   size_t table_bytes;       // offset of the (dst_off, src_off) table in the workspace
+  size_t rowmap_bytes;      // offset of the row map in the workspace
 };
 
 // Host-only: fills `plan` from validated arguments. Returns MRR_SUCCESS or an error.

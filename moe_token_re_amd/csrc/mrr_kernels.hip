@@ -41,6 +41,7 @@
 #include <limits.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "mrr_internal.h"
@@ -222,13 +223,48 @@ struct ScanShared {
   uint32_t flags;
 };
 
+// floor(t / d) for 0 <= t < 2^12 and 1 <= d <= 2^12, with inv = 1.0f / d:
+// (t + 1/2) / d lies at least 1 / (2d) from an integer, far more than the
+// float error of the product.
+__device__ __forceinline__ int div_small(int t, float inv) {
+  return static_cast<int>((static_cast<float>(t) + 0.5f) * inv);
+}
+
+// One entry of the row map, rowmap[d] = the input row of output row d, from
+// the cells' offsets in LDS (dst and src, both indexed by column-major cell
+// j * N + i): a binary search for the last output-order cell whose output
+// offset is <= d (an empty cell shares its offset with the next one).
+// Output order is column-major for the forward call, row-major for the
+// inverse.
+__device__ __forceinline__ int32_t rowmap_entry(const int32_t* s_dst, const int32_t* s_src, int N, int E,
+                                                int inverse, float inv_e, int d) {
+  const int M = N * E;
+  auto cm = [&](int c) {  // output-order cell -> its column-major index
+    if (!inverse) return c;
+    const int i = div_small(c, inv_e);
+    return (c - i * E) * N + i;
+  };
+  const int32_t* s_out = inverse ? s_src : s_dst;
+  const int32_t* s_in = inverse ? s_dst : s_src;
+  int lo = 0, hi = M;  // out(lo) <= d < out(hi) (= A)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_out[cm(mid)] <= d)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  const int c = cm(lo);
+  return s_in[c] + (d - s_out[c]);
+}
+
 // Writes the end-of-table entries and finishes: tab[M] = (A, A), col[E] = A.
 __device__ __forceinline__ void finish_offsets(pair_t* tab, int32_t* col, int M, int E, int64_t A) {
   if (threadIdx.x == 0) {
     pair_t t;
     t.x = static_cast<int32_t>(A);
     t.y = static_cast<int32_t>(A);
-    tab[M] = t;
+    if (tab != nullptr) tab[M] = t;
     col[E] = static_cast<int32_t>(A);
   }
   __syncthreads();
@@ -236,17 +272,19 @@ __device__ __forceinline__ void finish_offsets(pair_t* tab, int32_t* col, int M,
 
 // Both offset tables of counts[N][E] with one cell per thread (M <= kThreads),
 // in a workgroup's LDS. lds holds the counts and the source offsets in
-// column-major cell order ([M] int32 each). Writes the table (in LDS or
-// global memory) in output order: forward, tab[j*N + i] = (DstOffset,
+// column-major cell order ([M] int32 each); the counts are then replaced by
+// the destination offsets. Writes the table (in LDS or global memory; none
+// when tab is null) in output order: forward, tab[j*N + i] = (DstOffset,
 // SrcOffset) (coalesced); inverse, tab[i*E + j] = (SrcOffset, DstOffset);
 // then tab[M] = (A, A), and the expert starts col[j] = DstOffset(0, j),
-// col[E] = A.
+// col[E] = A. With a row map, also rowmap[d] for d = row0 + thread (one row
+// per thread, coalesced).
 // Returns 0, or the rejection flags (the same in every thread; then tab and
 // col are not written).
 template <int kThreads, typename CountT>
 __device__ uint32_t offsets_cells(const CountT* __restrict__ counts, int N, int E, int64_t A, int inverse,
                                   int32_t* lds, int32_t* col, pair_t* tab, ScanShared<kThreads>* sh,
-                                  int64_t* total_out) {
+                                  int64_t* total_out, int32_t* __restrict__ rowmap = nullptr, int row0 = 0) {
   const int tid = threadIdx.x;
   const int M = N * E;
   int32_t* s_c = lds;      // counts, column-major
@@ -281,15 +319,21 @@ __device__ uint32_t offsets_cells(const CountT* __restrict__ counts, int N, int 
     if (inverse) {
       t.x = s_s[tid];
       t.y = static_cast<int32_t>(dst);
-      tab[i * E + j] = t;
+      if (tab != nullptr) tab[i * E + j] = t;
     } else {
       t.x = static_cast<int32_t>(dst);
       t.y = s_s[tid];
-      tab[tid] = t;
+      if (tab != nullptr) tab[tid] = t;
     }
     if (i == 0) col[j] = static_cast<int32_t>(dst);
+    s_c[tid] = static_cast<int32_t>(dst);  // this thread's own count was read before the scan
   }
   finish_offsets(tab, col, M, E, A);
+  if (rowmap != nullptr) {
+    const int d = row0 + tid;
+    if (d < A)
+      rowmap[d] = rowmap_entry(s_c, s_s, N, E, inverse, 1.0f / static_cast<float>(E), d);
+  }
   return 0;
 }
 
@@ -463,16 +507,23 @@ __device__ __forceinline__ void write_etn(const int32_t* col, int E, int cumsum,
 template <typename CountT, int kC>
 __global__ __launch_bounds__(kOffsetThreads) void offsets_staged_kernel(
     const CountT* __restrict__ counts, int32_t N, int32_t E, int64_t A, int cumsum, int inverse,
-    CountT* __restrict__ etn, WsHeader* __restrict__ hdr, pair_t* __restrict__ table, int32_t mats_ints) {
+    CountT* __restrict__ etn, WsHeader* __restrict__ hdr, pair_t* __restrict__ table, int32_t mats_ints,
+    int32_t* __restrict__ rowmap) {
   extern __shared__ int32_t s_dyn[];
   __shared__ ScanShared<kOffsetThreads> sh;
   int32_t* col = s_dyn + mats_ints;  // [E + 1], after the offset matrices
   int64_t total = 0;
   uint32_t flags;
+  // With a row map (one cell per thread only), workgroup b also writes the
+  // row map's rows [1024 b, 1024 b + 1024); workgroup 0 alone writes the
+  // table, expert_token_num and the status.
+  const bool lead = blockIdx.x == 0;
   if (kC == 1)
-    flags = offsets_cells<kOffsetThreads>(counts, N, E, A, inverse, s_dyn, col, table, &sh, &total);
+    flags = offsets_cells<kOffsetThreads>(counts, N, E, A, inverse, s_dyn, col, lead ? table : nullptr, &sh, &total,
+                                          rowmap, static_cast<int>(blockIdx.x) * kOffsetThreads);
   else
     flags = offsets_chunks<kOffsetThreads, kC>(counts, N, E, A, inverse, s_dyn, col, table, &sh, &total);
+  if (!lead) return;
   if (flags == 0) write_etn<kOffsetThreads>(col, E, cumsum, etn);
   if (threadIdx.x == 0) write_header(hdr, A, N, E, total, flags, kTablesValid, inverse);
 }
@@ -620,6 +671,8 @@ struct BandShared {
   int32_t col[kOffsetThreads + 1];   // DstOffset(0, j), col[E] = A
   uint32_t above[kOffsetThreads];    // B_j
   uint32_t cstart[kOffsetThreads];   // column-major band scan at each column's first band cell
+  int32_t src_q[kOffsetThreads + 1]; // the band's cells by row-major index: SrcOffset (+ end),
+  int32_t dst_q[kOffsetThreads];     // and DstOffset (for the row map)
   uint32_t w[4][kOffsetThreads / 64];
   uint64_t t[4][kOffsetThreads / 64];
   uint32_t flags;
@@ -627,12 +680,6 @@ struct BandShared {
   uint64_t grand;
 };
 
-// floor(t / d) for 0 <= t < 2^12 and 1 <= d <= 2^12, with inv = 1.0f / d:
-// (t + 1/2) / d lies at least 1 / (2d) from an integer, far more than the
-// float error of the product.
-__device__ __forceinline__ int div_small(int t, float inv) {
-  return static_cast<int>((static_cast<float>(t) + 0.5f) * inv);
-}
 
 // One count of the main sweep: the running sums, and what validity needs.
 // int32 counts: the OR of the raw words keeps the sign bits (a negative
@@ -662,10 +709,15 @@ struct CountAcc {
 template <typename CountT>
 __global__ __launch_bounds__(kOffsetThreads) void offsets_banded_kernel(
     const CountT* __restrict__ counts, int32_t N, int32_t E, int32_t band_rows, int32_t lanes, int64_t A,
-    int cumsum, int inverse, CountT* __restrict__ etn, WsHeader* __restrict__ hdr, pair_t* __restrict__ table) {
+    int cumsum, int inverse, CountT* __restrict__ etn, WsHeader* __restrict__ hdr, pair_t* __restrict__ table,
+    int32_t* __restrict__ rowmap, int32_t split) {
   __shared__ BandShared s;
   const int tid = threadIdx.x;
-  const int i0 = blockIdx.x * band_rows;
+  // `split` workgroups share a band: each computes its offsets, slice 0
+  // writes its table entries, and each writes 1/split of its rows' row map.
+  const int band = blockIdx.x / split;
+  const int slice = blockIdx.x - band * split;
+  const int i0 = band * band_rows;
   const int rows = min(band_rows, N - i0);  // ranks in this band
   const int cells = rows * E;               // <= kOffsetThreads
   const int ES = E | 1;                     // LDS row stride of the band's counts
@@ -795,7 +847,7 @@ __global__ __launch_bounds__(kOffsetThreads) void offsets_banded_kernel(
   if (in && ui == 0) s.cstart[uj] = ex3[1];
   __syncthreads();
   int32_t* words = reinterpret_cast<int32_t*>(table);
-  if (in) {  // output order: forward, cell j*N + i as (dst, src); inverse, cell i*E + j as (src, dst)
+  if (in && slice == 0) {  // output order: forward, cell j*N + i as (dst, src); inverse, cell i*E + j as (src, dst)
     const int32_t src = static_cast<int32_t>(s.above_all + ex3[0]);
     const int32_t dst =
         static_cast<int32_t>(static_cast<uint32_t>(s.col[uj]) + s.above[uj] + (ex3[1] - s.cstart[uj]));
@@ -805,6 +857,51 @@ __global__ __launch_bounds__(kOffsetThreads) void offsets_banded_kernel(
     } else {
       words[2 * (qj * N + i0 + qi) + 1] = src;
       words[2 * (uj * N + i0 + ui)] = dst;
+    }
+  }
+  if (in) {
+    s.src_q[tid] = static_cast<int32_t>(s.above_all + ex3[0]);
+    s.dst_q[ui * E + uj] =
+        static_cast<int32_t>(static_cast<uint32_t>(s.col[uj]) + s.above[uj] + (ex3[1] - s.cstart[uj]));
+    if (tid == cells - 1) s.src_q[cells] = static_cast<int32_t>(s.above_all + ex3[0] + cq);  // the band's end
+  }
+  if (rowmap != nullptr) {
+    // The row map for the band's rows: they are the source rows [S0, S1) in
+    // row-major cell order; each thread takes a contiguous slice, finds its
+    // first cell by a binary search over src_q and walks forward. Forward:
+    // output row DstOffset + k takes source row SrcOffset + k; inverse: the
+    // reverse (output rows are then the source rows, written contiguously).
+    __syncthreads();
+    const int rows_b = s.src_q[cells] - static_cast<int>(s.above_all);
+    const int per_slice = (rows_b + split - 1) / split;
+    const int S0 = static_cast<int>(s.above_all) + slice * per_slice;
+    const int S1 = static_cast<int>(s.above_all) + min(rows_b, (slice + 1) * per_slice);
+    const int Rt = (per_slice + kOffsetThreads - 1) / kOffsetThreads;
+    const int r0 = S0 + tid * Rt;
+    const int r1 = min(S1, r0 + Rt);
+    if (r0 < r1) {
+      int lo = 0, hi = cells;  // src_q[lo] <= r0 < src_q[hi]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s.src_q[mid] <= r0)
+          lo = mid;
+        else
+          hi = mid;
+      }
+      int q = lo;
+      int sq = s.src_q[q], dq = s.dst_q[q], next = s.src_q[q + 1];
+      for (int r = r0; r < r1; ++r) {
+        while (r >= next) {
+          ++q;
+          sq = next;
+          dq = s.dst_q[q];
+          next = s.src_q[q + 1];
+        }
+        if (inverse)
+          rowmap[r] = dq + (r - sq);
+        else
+          rowmap[dq + (r - sq)] = r;
+      }
     }
   }
   if (blockIdx.x == 0) {
@@ -855,6 +952,7 @@ struct GatherArgs {
   uint32_t* out_weight;
   int32_t* idx;
   const pair_t* table;     // in the workspace (gather_kernel)
+  const int32_t* rowmap;   // in the workspace (stream_gather_kernel): input row of every output row
   WsHeader* hdr;
   int64_t row_bytes;
   int64_t scale_row_bytes;
@@ -884,7 +982,7 @@ __device__ __forceinline__ int32_t source_row(const pair_t* table, int M, int d_
     const int pos = lo + lane * stride;
     const int v = pos < hi ? table[pos].x : INT_MAX;
     const uint64_t below = __ballot(v <= d_lo);  // a prefix of the lanes
-    const int k = max(__popcll(below) - 1, 0);
+    const int k = max(static_cast<int>(__popcll(below)) - 1, 0);
     lo += k * stride;
     hi = min(hi, lo + stride);
   }
@@ -1061,6 +1159,127 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs p) {
   move_rows<V, kSV, kScatter, kWeight>(p, row0, rows, s_src);
 }
 
+// ---------------------------------------------------------------------------
+// Stream gather: one-wave workgroups, one vector per lane
+// ---------------------------------------------------------------------------
+
+// The output of the two-kernel path is three byte streams in output order:
+// the token rows (A * vpr vectors of V bytes), the scale rows (A * svpr
+// vectors of SV bytes) and the per-row items (A rows: index and weight).
+// Each is cut into chunks of 64 consecutive vectors (rows, for the items),
+// and one 64-lane workgroup moves one chunk: every lane finds its vector's
+// output row, looks up that row's source in the offsets table (a 64-way
+// search shared by the wave), and issues one load and one store. Small
+// one-shot workgroups keep the CU's wave slots full while each wave's short
+// search is in flight, which streams closer to the copy ceiling than large
+// workgroups with many loads per lane.
+struct StreamGrid {
+  uint32_t tok_chunks;   // ceil(A * vpr / 64)
+  uint32_t sc_end;       // tok_chunks + ceil(A * svpr / 64) (no scale chunks without scales)
+  uint32_t cpr;          // token chunks per row when whole (vpr % 64 == 0), else 0
+  uint32_t cpr_magic;    // ceil(2^32 / cpr): chunk / cpr by a multiply-high and one correction
+  float inv_vpr;         // 1 / vpr and 1 / svpr, for rows shorter than a chunk
+  float inv_svpr;
+};
+
+// The workspace header's verdict, read through the scalar cache: it was
+// written by an earlier kernel and this kernel does not write it.
+__device__ __forceinline__ bool header_valid(const WsHeader* hdr, const GatherArgs& p) {
+  using CHdr = const WsHeader __attribute__((address_space(4)))*;
+  const CHdr h = reinterpret_cast<CHdr>(reinterpret_cast<uintptr_t>(hdr));
+  // all fields loaded together (no short-circuit between the loads)
+  const uint32_t status = h->status, inverse = h->inverse;
+  const int64_t A = h->A, N = h->N, E = h->E;
+  return (status == kTablesValid) & (A == p.A) & (N == p.N) & (E == p.E) &
+         (inverse == static_cast<uint32_t>(p.inverse));
+}
+
+// A token chunk that lies in one row (the row is a whole number of chunks):
+// chunk c is part c % cpr of row c / cpr.
+template <int V>
+__device__ __forceinline__ void stream_whole_row_chunk(const GatherArgs& p, const StreamGrid& g, uint32_t c,
+                                                       bool valid) {
+  using T = typename VecT<V>::type;
+  uint32_t d = c;
+  if (g.cpr != 1) {  // uniform
+    d = __umulhi(c, g.cpr_magic);
+    d -= d * g.cpr > c ? 1u : 0u;
+  }
+  const int32_t s = p.rowmap[d];  // the same address in every lane
+  const uint32_t col = (c - d * g.cpr) * 64u + (threadIdx.x & 63);  // vector within the row
+  const bool ok = valid && static_cast<unsigned>(s) < static_cast<unsigned>(p.A);
+  const int64_t so = ok ? int64_t(s) * p.row_bytes + int64_t(col) * V : 0;
+  const T v = __builtin_nontemporal_load(reinterpret_cast<const T*>(p.tokens + so));
+  if (ok) __builtin_nontemporal_store(v, reinterpret_cast<T*>(p.out_tokens + int64_t(d) * p.row_bytes + int64_t(col) * V));
+}
+
+// Chunk `chunk` of a row stream: vectors [64 chunk, 64 chunk + 64) of the
+// rows [0, A) of vpr vectors of V bytes each, output row d taken from
+// source row source_row(d).
+template <int V>
+__device__ __forceinline__ void stream_rows(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                            int64_t row_bytes, int vpr, float inv_vpr, int64_t chunk,
+                                            const int32_t* __restrict__ rowmap, int A, bool valid) {
+  using T = typename VecT<V>::type;
+  const int lane = threadIdx.x & 63;
+  const int64_t g0 = chunk * 64;
+  const int64_t total = int64_t(A) * vpr;
+  const int64_t d0 = g0 / vpr;  // the chunk's first row (uniform)
+  const int off = static_cast<int>(g0 - d0 * vpr) + lane;  // < vpr + 64
+  // Row within the chunk: at most one row boundary when vpr >= 64; below
+  // that, a small exact division (off < 128).
+  const int dd = vpr >= 64 ? (off >= vpr ? 1 : 0) : div_small(off, inv_vpr);
+  const int col = off - dd * vpr;
+  const bool in = g0 + lane < total;
+  const int d = static_cast<int>(d0) + (in ? dd : 0);  // in [d0, d0 + 63]
+  const int32_t s = rowmap[d];
+  const bool ok = in && valid && static_cast<unsigned>(s) < static_cast<unsigned>(A);
+  // Branch-free load (row 0, column 0 when not moving: always valid here).
+  const int64_t so = ok ? int64_t(s) * row_bytes + int64_t(col) * V : 0;
+  const T v = __builtin_nontemporal_load(reinterpret_cast<const T*>(src + so));
+  if (ok) __builtin_nontemporal_store(v, reinterpret_cast<T*>(dst + (g0 + lane) * V));
+}
+
+template <int V, bool kScatter, bool kWeight>
+__global__ __launch_bounds__(64) void stream_gather_kernel(GatherArgs p, StreamGrid g) {
+  const bool valid = header_valid(p.hdr, p);
+  const uint32_t b = blockIdx.x;  // one chunk per workgroup; uniform branches below
+  if (b < g.tok_chunks) {
+    if (g.cpr != 0)
+      stream_whole_row_chunk<V>(p, g, b, valid);
+    else
+      stream_rows<V>(p.tokens, p.out_tokens, p.row_bytes, p.vecs_per_row, g.inv_vpr, b, p.rowmap, p.A, valid);
+  } else if (b < g.sc_end) {
+    const int64_t c = b - g.tok_chunks;
+    const int spr = p.scale_vecs_per_row;
+    const int64_t Rs = p.scale_row_bytes;
+    const float inv = g.inv_svpr;
+    switch (p.scale_vec) {
+      case 16: stream_rows<16>(p.scales, p.out_scales, Rs, spr, inv, c, p.rowmap, p.A, valid); break;
+      case 8: stream_rows<8>(p.scales, p.out_scales, Rs, spr, inv, c, p.rowmap, p.A, valid); break;
+      case 4: stream_rows<4>(p.scales, p.out_scales, Rs, spr, inv, c, p.rowmap, p.A, valid); break;
+      case 2: stream_rows<2>(p.scales, p.out_scales, Rs, spr, inv, c, p.rowmap, p.A, valid); break;
+      default: stream_rows<1>(p.scales, p.out_scales, Rs, spr, inv, c, p.rowmap, p.A, valid); break;
+    }
+  } else {
+    const int r0 = static_cast<int>(b - g.sc_end) * 64;
+    const int d = r0 + static_cast<int>(threadIdx.x & 63);
+    const bool in = d < p.A;
+    const int32_t s = p.rowmap[in ? d : r0];
+    const bool ok = in && valid && static_cast<unsigned>(s) < static_cast<unsigned>(p.A);
+    if (kWeight) {
+      const uint32_t wv = p.weight[ok ? s : 0];
+      if (ok) p.out_weight[d] = wv;
+    }
+    if (ok) {
+      if (kScatter)
+        p.idx[s] = d;
+      else
+        p.idx[d] = s;
+    }
+  }
+}
+
 struct FusedArgs {
   const void* counts;
   void* etn;
@@ -1155,22 +1374,27 @@ mrr_status device_info(const DeviceInfo** out) {
 template <typename CountT, int kC>
 void launch_staged(const Plan& pl, const mrr_args* a, uint8_t* base, size_t lds, hipStream_t stream) {
   const int32_t mats = static_cast<int32_t>((static_cast<int64_t>(lds) - 16) / 4 - (pl.E + 1));
-  hipLaunchKernelGGL((offsets_staged_kernel<CountT, kC>), dim3(1), dim3(kOffsetThreads), lds, stream,
+  const unsigned grid =
+      kC == 1 && pl.stream ? static_cast<unsigned>(std::max<int64_t>(1, (pl.A + kOffsetThreads - 1) / kOffsetThreads))
+                           : 1u;
+  hipLaunchKernelGGL((offsets_staged_kernel<CountT, kC>), dim3(grid), dim3(kOffsetThreads), lds, stream,
                      static_cast<const CountT*>(a->expert_token_num_per_rank), static_cast<int32_t>(pl.N),
                      static_cast<int32_t>(pl.E), pl.A, pl.cumsum ? 1 : 0, pl.inverse ? 1 : 0,
                      static_cast<CountT*>(a->expert_token_num), reinterpret_cast<WsHeader*>(base),
-                     reinterpret_cast<pair_t*>(base + pl.table_bytes), mats);
+                     reinterpret_cast<pair_t*>(base + pl.table_bytes), mats,
+                     pl.stream ? reinterpret_cast<int32_t*>(base + pl.rowmap_bytes) : nullptr);
 }
 
 template <typename CountT>
 mrr_status launch_offsets_t(const Plan& pl, const mrr_args* a, void* ws, hipStream_t stream) {
   auto* base = static_cast<uint8_t*>(ws);
   if (pl.band_grid > 0) {
-    hipLaunchKernelGGL((offsets_banded_kernel<CountT>), dim3(static_cast<unsigned>(pl.band_grid)),
+    hipLaunchKernelGGL((offsets_banded_kernel<CountT>), dim3(static_cast<unsigned>(pl.band_grid * pl.band_split)),
                        dim3(kOffsetThreads), 0, stream, static_cast<const CountT*>(a->expert_token_num_per_rank),
                        static_cast<int32_t>(pl.N), static_cast<int32_t>(pl.E), pl.band_rows, pl.band_lanes, pl.A,
                        pl.cumsum ? 1 : 0, pl.inverse ? 1 : 0, static_cast<CountT*>(a->expert_token_num),
-                       reinterpret_cast<WsHeader*>(base), reinterpret_cast<pair_t*>(base + pl.table_bytes));
+                       reinterpret_cast<WsHeader*>(base), reinterpret_cast<pair_t*>(base + pl.table_bytes),
+                       pl.stream ? reinterpret_cast<int32_t*>(base + pl.rowmap_bytes) : nullptr, pl.band_split);
     return hipGetLastError() == hipSuccess ? MRR_SUCCESS : MRR_ERROR_HIP;
   }
   const DeviceInfo* di = nullptr;
@@ -1214,6 +1438,7 @@ GatherArgs gather_args(const Plan& pl, const mrr_args* a, void* ws) {
   g.out_weight = reinterpret_cast<uint32_t*>(a->permute_topk_weight);
   g.idx = a->permute_token_idx;
   g.table = reinterpret_cast<const pair_t*>(base + pl.table_bytes);
+  g.rowmap = reinterpret_cast<const int32_t*>(base + pl.rowmap_bytes);
   g.hdr = reinterpret_cast<WsHeader*>(base);
   g.row_bytes = pl.row_bytes;
   g.scale_row_bytes = pl.scale_row_bytes;
@@ -1281,9 +1506,45 @@ struct FusedK64 {
   static auto fn() { return &fused_kernel<V, SV, S, W, int64_t>; }
 };
 
+StreamGrid stream_grid(const Plan& pl) {
+  StreamGrid sg;
+  sg.tok_chunks = static_cast<uint32_t>(pl.tok_chunks);
+  sg.sc_end = static_cast<uint32_t>(pl.tok_chunks + pl.sc_chunks);
+  sg.inv_vpr = 1.0f / static_cast<float>(pl.vecs_per_row);
+  sg.inv_svpr = pl.scale_row_bytes > 0 ? 1.0f / static_cast<float>(pl.scale_row_bytes / pl.scale_vec) : 0.0f;
+  // cpr_magic = ceil(2^32 / cpr) puts umulhi(c, magic) at c / cpr or one above.
+  sg.cpr = 0;
+  sg.cpr_magic = 0;
+  if (pl.vecs_per_row % 64 == 0) {
+    sg.cpr = static_cast<uint32_t>(pl.vecs_per_row / 64);
+    sg.cpr_magic = sg.cpr == 1 ? 0u : static_cast<uint32_t>(((uint64_t(1) << 32) + sg.cpr - 1) / sg.cpr);
+  }
+  return sg;
+}
+
+template <bool S, bool W>
+void launch_stream_sw(const Plan& pl, const GatherArgs& g, hipStream_t stream) {
+  const StreamGrid sg = stream_grid(pl);
+  const dim3 grid(static_cast<unsigned>(pl.stream_grid)), block(64);
+  switch (pl.token_vec) {
+    case 16: hipLaunchKernelGGL((stream_gather_kernel<16, S, W>), grid, block, 0, stream, g, sg); break;
+    case 8: hipLaunchKernelGGL((stream_gather_kernel<8, S, W>), grid, block, 0, stream, g, sg); break;
+    case 4: hipLaunchKernelGGL((stream_gather_kernel<4, S, W>), grid, block, 0, stream, g, sg); break;
+    case 2: hipLaunchKernelGGL((stream_gather_kernel<2, S, W>), grid, block, 0, stream, g, sg); break;
+    default: hipLaunchKernelGGL((stream_gather_kernel<1, S, W>), grid, block, 0, stream, g, sg); break;
+  }
+}
+
 mrr_status launch_gather(const Plan& pl, const mrr_args* a, void* ws, hipStream_t stream) {
   if (pl.A == 0) return MRR_SUCCESS;
   const GatherArgs g = gather_args(pl, a, ws);
+  if (pl.stream) {
+    if (pl.scatter)
+      pl.has_weight ? launch_stream_sw<true, true>(pl, g, stream) : launch_stream_sw<true, false>(pl, g, stream);
+    else
+      pl.has_weight ? launch_stream_sw<false, true>(pl, g, stream) : launch_stream_sw<false, false>(pl, g, stream);
+    return hipGetLastError() == hipSuccess ? MRR_SUCCESS : MRR_ERROR_HIP;
+  }
   dispatch<GatherK>(pl, [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3(static_cast<unsigned>(pl.grid)), dim3(kGatherThreads), 0, stream, g);
   });

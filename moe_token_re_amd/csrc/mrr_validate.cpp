@@ -60,11 +60,13 @@ int env_int(const char* name, int fallback) {
 struct Tuning {
   int rows_per_wg;  // 0 = automatic
   int offsets;      // 0 = automatic, 1 = single-workgroup offsets kernel, 2 = banded where it applies
+  int stream;       // 1 (default): the stream gather kernel for the two-kernel path; 0: row workgroups
   bool fused;       // allow the single-kernel path (MRR_FUSED=0 turns it off)
   bool log;
   Tuning()
       : rows_per_wg(env_int("MRR_ROWS_PER_WG", 0)),
         offsets(env_int("MRR_OFFSETS", 0)),
+        stream(env_int("MRR_STREAM", 1)),
         fused(env_int("MRR_FUSED", 1) != 0),
         log(env_int("MRR_LOG", 0) != 0) {}
 };
@@ -82,11 +84,11 @@ int widest_vec(int64_t bytes, const void* a, const void* b) {
 
 }  // namespace
 
-extern "C" size_t mrr_workspace_size(int64_t N, int64_t E) {
-  if (N < 0 || E < 0) return 0;
+extern "C" size_t mrr_workspace_size(int64_t A, int64_t N, int64_t E) {
+  if (A < 0 || A > INT32_MAX || N < 0 || E < 0) return 0;
   if (N != 0 && E > kMaxCells / N) return 0;
   const size_t M = static_cast<size_t>(N * E);
-  return mrr::kHeaderBytes + round_up(8 * (M + 1), 256);
+  return mrr::kHeaderBytes + round_up(8 * (M + 1), 256) + round_up(4 * static_cast<size_t>(A), 256);
 }
 
 extern "C" const char* mrr_status_string(mrr_status s) {
@@ -176,7 +178,7 @@ mrr_status make_plan(const mrr_args* a, const void* ws, size_t ws_bytes, Plan* p
     return MRR_ERROR_MISALIGNED;
 
   // workspace size
-  const size_t need = mrr_workspace_size(a->N, a->E);
+  const size_t need = mrr_workspace_size(a->A, a->N, a->E);
   if (need == 0 || ws_bytes < need) return MRR_ERROR_WORKSPACE_TOO_SMALL;
 
   // no output may overlap any other buffer
@@ -233,6 +235,7 @@ mrr_status make_plan(const mrr_args* a, const void* ws, size_t ws_bytes, Plan* p
   q.band_grid = 0;
   q.band_rows = 0;
   q.band_lanes = 0;
+  q.band_split = 1;
   const bool band_fits = M > 0 && q.E <= kOffsetThreads && M <= kBandMaxCells;
   if (band_fits && (tuning().offsets == 2 || (tuning().offsets == 0 && M > kOffsetThreads))) {
     q.band_rows = static_cast<int>(std::min<int64_t>(q.N, kOffsetThreads / q.E));
@@ -241,7 +244,28 @@ mrr_status make_plan(const mrr_args* a, const void* ws, size_t ws_bytes, Plan* p
     q.band_lanes = lanes;
     q.band_grid = (q.N + q.band_rows - 1) / q.band_rows;
   }
+  // The stream gather reads the row map, which the single-workgroup kernel
+  // with one cell per thread and the banded kernel write.
+  q.stream = tuning().stream != 0 && (q.band_grid > 0 || M <= kOffsetThreads);
+  // With the row map, several workgroups per band, so that each writes about
+  // one row per thread.
+  if (q.stream && q.band_grid > 0)
+    q.band_split = static_cast<int>(
+        std::min<int64_t>(16, std::max<int64_t>(1, q.A / (q.band_grid * kOffsetThreads))));
+  q.tok_chunks = q.sc_chunks = q.item_chunks = q.stream_grid = 0;
+  if (q.stream) {
+    q.tok_chunks = (q.A * q.vecs_per_row + 63) / 64;
+    q.sc_chunks = Rs > 0 ? (q.A * (Rs / q.scale_vec) + 63) / 64 : 0;
+    q.item_chunks = (q.A + 63) / 64;
+    q.stream_grid = q.tok_chunks + q.sc_chunks + q.item_chunks;
+    if (q.stream_grid >= kMaxStreamGrid) q.stream = false;  // 32-bit chunk numbers and grid
+  }
+  // The single-kernel path saves a launch; the two-kernel path's stream
+  // gather streams faster. The launch matters less than the rate from a few
+  // tens of MiB of rows on.
+  if (q.fused && q.stream && q.A * q.row_bytes >= kFusedMaxTokenBytes) q.fused = false;
   q.table_bytes = kHeaderBytes;
+  q.rowmap_bytes = kHeaderBytes + round_up(8 * (static_cast<size_t>(M) + 1), 256);
   *p = q;
 
   if (tuning().log)
@@ -271,11 +295,15 @@ extern "C" mrr_status mrr_describe_plan(const mrr_args* args, const void* worksp
   info->token_vec_bytes = plan.token_vec;
   info->scale_vec_bytes = plan.scale_row_bytes > 0 ? plan.scale_vec : 0;
   info->rows_per_workgroup = plan.rows_per_wg;
-  info->threads_per_workgroup = mrr::kGatherThreads;
-  info->gather_workgroups = plan.grid;
+  info->threads_per_workgroup = plan.fused || !plan.stream ? mrr::kGatherThreads : 64;
+  info->gather_workgroups = plan.fused || !plan.stream ? plan.grid : plan.stream_grid;
   info->token_row_bytes = plan.row_bytes;
   info->scale_row_bytes = plan.scale_row_bytes;
   info->scale_inline_bytes = plan.scale_inline;
-  info->offsets_workgroups = plan.band_grid > 0 ? plan.band_grid : (plan.M > 0 ? 1 : 0);
+  info->offsets_workgroups = plan.band_grid > 0 ? plan.band_grid * plan.band_split
+                           : plan.M == 0 ? 0
+                           : plan.stream ? std::max<int64_t>(1, (plan.A + mrr::kOffsetThreads - 1) / mrr::kOffsetThreads)
+                                         : 1;
+  info->gather_kernel = plan.stream ? 1 : 0;
   return MRR_SUCCESS;
 }

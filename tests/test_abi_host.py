@@ -49,12 +49,15 @@ def test_status_strings():
 
 def test_workspace_size():
     L = _lib.load()
-    # 256-byte header + round_up(8*(M+1), 256) for the (dst, src) pair table
-    assert L.mrr_workspace_size(16, 16) == 256 + 1280 + 1024
-    assert L.mrr_workspace_size(256, 64) == 256 + 65792 + 65536
-    assert L.mrr_workspace_size(0, 5) == 256 + 256 + 0
-    assert L.mrr_workspace_size(-1, 4) == 0
-    assert L.mrr_workspace_size(1 << 20, 1 << 20) == 0
+    # 256-byte header + round_up(8*(M+1), 256) for the pair table + round_up(4*A, 256) for the row map
+    assert L.mrr_workspace_size(16384, 16, 16) == 256 + 1280 + 1024 + 65536
+    assert L.mrr_workspace_size(65536, 256, 64) == 256 + 65792 + 65536 + 262144
+    assert L.mrr_workspace_size(42, 2, 4) == 256 + 256 + 256
+    assert L.mrr_workspace_size(0, 0, 5) == 256 + 256 + 0
+    assert L.mrr_workspace_size(0, -1, 4) == 0
+    assert L.mrr_workspace_size(-1, 2, 4) == 0
+    assert L.mrr_workspace_size(1 << 31, 2, 4) == 0
+    assert L.mrr_workspace_size(0, 1 << 20, 1 << 20) == 0
 
 
 # Fake device addresses, far apart so that no two buffers overlap.
@@ -85,7 +88,7 @@ def valid_args(A=64, H=128, N=2, E=4, tok=_lib.F16, cnt=_lib.I32, scales="f32", 
 def validate(a, ws=BASE["ws"], ws_bytes=None):
     L = _lib.load()
     if ws_bytes is None:
-        ws_bytes = L.mrr_workspace_size(max(a.N, 0), max(a.E, 0))
+        ws_bytes = L.mrr_workspace_size(min(max(a.A, 0), (1 << 31) - 1), max(a.N, 0), max(a.E, 0))
     return L.mrr_validate(ctypes.byref(a), ws, ws_bytes)
 
 
@@ -176,25 +179,31 @@ def test_rejections(mutate, code):
 def describe(a, ws=BASE["ws"]):
     L = _lib.load()
     info = _lib.MrrPlanInfo()
-    st = L.mrr_describe_plan(ctypes.byref(a), ws, L.mrr_workspace_size(a.N, a.E), ctypes.byref(info))
+    st = L.mrr_describe_plan(ctypes.byref(a), ws, L.mrr_workspace_size(a.A, a.N, a.E), ctypes.byref(info))
     return st, info
 
 
 def test_describe_plan():
-    # pages' shape: 7168-byte rows in 16-byte vectors; 16x16 counts take the single-kernel path
+    # pages' shape: 7168-byte rows in 16-byte vectors; 112 MiB of token rows take the two-kernel
+    # path with the stream gather: 64-lane workgroups over 64-vector chunks of the token rows
+    # (16384 * 448 / 64), the scale rows (16384 4-byte vectors / 64) and the items (16384 / 64)
     st, info = describe(valid_args(A=16384, H=7168, N=16, E=16, tok=_lib.I8))
     assert st == _lib.SUCCESS
-    assert info.fused == 1 and info.token_vec_bytes == 16 and info.token_row_bytes == 7168
-    assert info.scale_row_bytes == 4 and info.scale_vec_bytes == 4
+    assert info.fused == 0 and info.gather_kernel == 1 and info.token_vec_bytes == 16
+    assert info.token_row_bytes == 7168 and info.scale_row_bytes == 4 and info.scale_vec_bytes == 4
+    assert info.threads_per_workgroup == 64 and info.gather_workgroups == 114688 + 256 + 256
+    assert info.offsets_workgroups == 16           # the row map: one workgroup per 1024 rows
+    # a smaller call with the same counts: one kernel whose workgroups each recompute the offsets
+    st, info = describe(valid_args(A=2048, H=7168, N=16, E=16, tok=_lib.I8))
+    assert st == _lib.SUCCESS and info.fused == 1 and info.threads_per_workgroup == 256
     assert info.scale_inline_bytes == 4            # one 4-byte piece per row, loaded with the tokens
-    assert info.offsets_workgroups == 1
     rows = max(1, info.threads_per_workgroup * 8 // 448)
     assert info.rows_per_workgroup == min(rows, 256)
-    assert info.gather_workgroups == -(-16384 // info.rows_per_workgroup)
+    assert info.gather_workgroups == -(-2048 // info.rows_per_workgroup)
     # 256x64 counts are too many to recompute per workgroup: two kernels
     st, info = describe(valid_args(A=65536, H=2048, N=256, E=64, tok=_lib.F4_E2M1))
     assert st == _lib.SUCCESS and info.fused == 0 and info.token_row_bytes == 1024
-    assert info.offsets_workgroups == 16           # bands of 1024 // 64 = 16 ranks
+    assert info.offsets_workgroups == 16 * 4       # bands of 1024 // 64 = 16 ranks, 4 workgroups each
     # the banded offsets kernel: more than 1024 cells, at most 1024 experts and 2^17 cells
     for n, e, wgs in [(1, 1024, 1), (2, 1024, 2), (33, 32, 2), (7, 513, 7), (5000, 1, 5), (512, 256, 128),
                       (2, 1025, 1), (520, 256, 1)]:
@@ -249,7 +258,7 @@ def test_e8m0_shape_follows_h():
 
 def test_workspace_checks():
     a = valid_args()
-    need = _lib.load().mrr_workspace_size(2, 4)
+    need = _lib.load().mrr_workspace_size(64, 2, 4)
     assert validate(a, ws_bytes=need - 1) == _lib.ERROR_WORKSPACE_TOO_SMALL
     assert validate(a, ws=None) == _lib.ERROR_INVALID_VALUE
     assert validate(a, ws=BASE["ws"] + 8) == _lib.ERROR_MISALIGNED
@@ -263,7 +272,7 @@ def test_launch_entry_points_reject_before_launch():
     a = valid_args()
     a.idx_type = 5
     ws = BASE["ws"]
-    nb = L.mrr_workspace_size(2, 4)
+    nb = L.mrr_workspace_size(64, 2, 4)
     for fn in (L.moe_rerouting_v2, L.moe_rerouting_v2_offsets, L.moe_rerouting_v2_gather):
         assert fn(ctypes.byref(a), ws, nb, None) == _lib.ERROR_INVALID_VALUE
     assert L.mrr_get_device_status(None, None) == _lib.ERROR_INVALID_VALUE
