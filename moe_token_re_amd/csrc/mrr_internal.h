@@ -65,6 +65,9 @@ constexpr int kMaxRowsPerWg = 256;
 // which reads the whole matrix once (so its L2 reads grow as M^2 /
 // kOffsetThreads); the others take one workgroup.
 constexpr int kOffsetThreads = 1024;
+// Matrices of at most this many cells, when the row map is written, take
+// workgroups of this many threads (one per that many rows).
+constexpr int kSmallOffsetCells = 256;
 constexpr int64_t kBandMaxCells = int64_t(1) << 17;
 
 // The stream gather kernel launches one workgroup per chunk; calls with more

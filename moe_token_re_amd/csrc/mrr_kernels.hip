@@ -528,6 +528,30 @@ __global__ __launch_bounds__(kOffsetThreads) void offsets_staged_kernel(
   if (threadIdx.x == 0) write_header(hdr, A, N, E, total, flags, kTablesValid, inverse);
 }
 
+// Offsets and the row map for count matrices of at most kSmallCells cells:
+// the same work as offsets_staged_kernel<CountT, 1> in workgroups of
+// kSmallCells threads (short workgroup scans), one per kSmallCells rows of
+// the row map; workgroup 0 also writes the table, expert_token_num and the
+// status.
+constexpr int kSmallCells = kSmallOffsetCells;
+
+template <typename CountT>
+__global__ __launch_bounds__(kSmallCells) void offsets_small_kernel(
+    const CountT* __restrict__ counts, int32_t N, int32_t E, int64_t A, int cumsum, int inverse,
+    CountT* __restrict__ etn, WsHeader* __restrict__ hdr, pair_t* __restrict__ table, int32_t* __restrict__ rowmap) {
+  __shared__ int32_t s_mats[2 * kSmallCells];
+  __shared__ int32_t s_col[kSmallCells + 1];
+  __shared__ ScanShared<kSmallCells> sh;
+  const bool lead = blockIdx.x == 0;
+  int64_t total = 0;
+  const uint32_t flags =
+      offsets_cells<kSmallCells>(counts, N, E, A, inverse, s_mats, s_col, lead ? table : nullptr, &sh, &total, rowmap,
+                                 static_cast<int>(blockIdx.x) * kSmallCells);
+  if (!lead) return;
+  if (flags == 0) write_etn<kSmallCells>(s_col, E, cumsum, etn);
+  if (threadIdx.x == 0) write_header(hdr, A, N, E, total, flags, kTablesValid, inverse);
+}
+
 // For count matrices too large for LDS: the same two scans in tiles of
 // kOffsetTile cells, reading the counts from global memory (the column-major
 // pass reads them transposed) and writing each pass's offsets straight into
@@ -1395,6 +1419,16 @@ mrr_status launch_offsets_t(const Plan& pl, const mrr_args* a, void* ws, hipStre
                        pl.cumsum ? 1 : 0, pl.inverse ? 1 : 0, static_cast<CountT*>(a->expert_token_num),
                        reinterpret_cast<WsHeader*>(base), reinterpret_cast<pair_t*>(base + pl.table_bytes),
                        pl.stream ? reinterpret_cast<int32_t*>(base + pl.rowmap_bytes) : nullptr, pl.band_split);
+    return hipGetLastError() == hipSuccess ? MRR_SUCCESS : MRR_ERROR_HIP;
+  }
+  if (pl.stream && pl.M <= kSmallCells) {
+    const unsigned grid = static_cast<unsigned>(std::max<int64_t>(1, (pl.A + kSmallCells - 1) / kSmallCells));
+    hipLaunchKernelGGL((offsets_small_kernel<CountT>), dim3(grid), dim3(kSmallCells), 0, stream,
+                       static_cast<const CountT*>(a->expert_token_num_per_rank), static_cast<int32_t>(pl.N),
+                       static_cast<int32_t>(pl.E), pl.A, pl.cumsum ? 1 : 0, pl.inverse ? 1 : 0,
+                       static_cast<CountT*>(a->expert_token_num), reinterpret_cast<WsHeader*>(base),
+                       reinterpret_cast<pair_t*>(base + pl.table_bytes),
+                       reinterpret_cast<int32_t*>(base + pl.rowmap_bytes));
     return hipGetLastError() == hipSuccess ? MRR_SUCCESS : MRR_ERROR_HIP;
   }
   const DeviceInfo* di = nullptr;

@@ -302,8 +302,10 @@ extern "C" mrr_status mrr_describe_plan(const mrr_args* args, const void* worksp
   info->scale_inline_bytes = plan.scale_inline;
   info->offsets_workgroups = plan.band_grid > 0 ? plan.band_grid * plan.band_split
                            : plan.M == 0 ? 0
-                           : plan.stream ? std::max<int64_t>(1, (plan.A + mrr::kOffsetThreads - 1) / mrr::kOffsetThreads)
-                                         : 1;
+                           : !plan.stream ? 1
+                           : plan.M <= mrr::kSmallOffsetCells
+                               ? std::max<int64_t>(1, (plan.A + mrr::kSmallOffsetCells - 1) / mrr::kSmallOffsetCells)
+                               : std::max<int64_t>(1, (plan.A + mrr::kOffsetThreads - 1) / mrr::kOffsetThreads);
   info->gather_kernel = plan.stream ? 1 : 0;
   return MRR_SUCCESS;
 }

@@ -192,7 +192,7 @@ def test_describe_plan():
     assert info.fused == 0 and info.gather_kernel == 1 and info.token_vec_bytes == 16
     assert info.token_row_bytes == 7168 and info.scale_row_bytes == 4 and info.scale_vec_bytes == 4
     assert info.threads_per_workgroup == 64 and info.gather_workgroups == 114688 + 256 + 256
-    assert info.offsets_workgroups == 16           # the row map: one workgroup per 1024 rows
+    assert info.offsets_workgroups == 64           # the row map: one workgroup per 256 rows (<= 256 cells)
     # a smaller call with the same counts: one kernel whose workgroups each recompute the offsets
     st, info = describe(valid_args(A=2048, H=7168, N=16, E=16, tok=_lib.I8))
     assert st == _lib.SUCCESS and info.fused == 1 and info.threads_per_workgroup == 256

@@ -164,8 +164,9 @@ def _offsets_workgroups(w, dev):
 def test_offsets_single_workgroup(n, e):
     w = workloads.random_case(n * 7 + e, n, e, 40, tokens_dtype="int8", count_range=(0, 4), weight=True,
                               idx_type=(n + e) % 2, etn_type=(n * e) % 2)
-    # one workgroup; with the row map (one cell per thread), one per 1024 rows
-    want = max(1, -(-w.A // 1024)) if n * e <= 1024 else 1
+    # one workgroup; with the row map (one cell per thread), one per 256 rows up to 256 cells, else
+    # one per 1024 rows
+    want = 1 if n * e > 1024 else max(1, -(-w.A // (256 if n * e <= 256 else 1024)))
     assert _offsets_workgroups(w, _dev()) == want
     check(w)
     check(w, phases=True)
