@@ -57,7 +57,9 @@ def _fuzz_cases():
 
 @pytest.mark.parametrize("case", _fuzz_cases(), ids=lambda c: f"s{c['seed']}")
 def test_inverse_fuzz(case):
-    check(workloads.random_case(**case), direction=INV)
+    w = workloads.random_case(**case)
+    check(w, direction=INV)
+    check(w, phases=True, direction=INV)
 
 
 @pytest.mark.parametrize("name", ["pages_shape", "mxfp8_skewed", "tiny_segments"])

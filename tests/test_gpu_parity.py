@@ -83,7 +83,9 @@ def fuzz_cases():
 
 @pytest.mark.parametrize("case", fuzz_cases(), ids=lambda c: f"s{c['seed']}")
 def test_fuzz(case):
-    check(workloads.random_case(**case))
+    w = workloads.random_case(**case)
+    check(w)               # small calls: the single fused kernel
+    check(w, phases=True)  # the two phases: the stream gather where the row map is written
 
 
 # Shapes named by the article's tests ("测试与验证"): (52, 21), (35, 15267),
