@@ -165,11 +165,13 @@ mrr_status mrr_validate(const mrr_args* args, const void* workspace, size_t work
 /* How a call with these arguments is launched (filled by mrr_describe_plan). */
 typedef struct mrr_plan_info {
   int32_t fused;                 /* 1: moe_rerouting_v2 launches one kernel whose workgroups each
-                                    recompute the offsets of the (small) count matrix in LDS;
-                                    0: it launches the offsets kernel, then the gather kernel */
+                                    recompute the offsets of the (small) count matrix in LDS
+                                    (small calls); 0: it launches the offsets kernel, then the
+                                    gather kernel */
   int32_t token_vec_bytes;       /* bytes per load/store of the token copy: 16, 8, 4, 2 or 1 */
   int32_t scale_vec_bytes;       /* the same for scale rows; 0 without scales */
-  int32_t rows_per_workgroup;    /* adjacent output rows per gather workgroup */
+  int32_t rows_per_workgroup;    /* adjacent output rows per workgroup of the fused kernel or
+                                    the row-workgroup gather */
   int32_t threads_per_workgroup;
   int64_t gather_workgroups;
   int64_t token_row_bytes;
@@ -178,8 +180,8 @@ typedef struct mrr_plan_info {
                                     the token rows; 0: in a separate pass after them */
   int64_t offsets_workgroups;    /* workgroups of moe_rerouting_v2_offsets(): several for larger
                                     count matrices (bands of ranks) or when the row map is
-                                    written (one workgroup per 1024 rows); 1 otherwise; 0 when
-                                    there are no cells */
+                                    written (one workgroup per 256 or 1024 rows); 1 otherwise;
+                                    0 when there are no cells */
   int32_t gather_kernel;         /* what moe_rerouting_v2_gather() launches: 1 = 64-lane
                                     workgroups, each moving 64 vectors of one output stream
                                     (token rows, scale rows, per-row items) with the row map
@@ -206,9 +208,10 @@ mrr_status moe_rerouting_v2(const mrr_args* args, void* workspace, size_t worksp
 
 /*
  * First phase alone (article, "计算公式": the two double sums): scans the
- * count matrix (one workgroup, or one per band of ranks for larger
- * matrices; see mrr_plan_info.offsets_workgroups) and writes the SrcOffset
- * and DstOffset tables and the validity status into the workspace, and
+ * count matrix (see mrr_plan_info.offsets_workgroups) and writes into the
+ * workspace the SrcOffset and DstOffset table, the validity status and, for
+ * count matrices of at most 1024 cells or up to 2^17 cells with at most 1024
+ * experts, the row map (the input row of every output row); and
  * expert_token_num into args->expert_token_num (only when the counts are
  * valid).
  */
@@ -218,8 +221,9 @@ mrr_status moe_rerouting_v2_offsets(const mrr_args* args, void* workspace, size_
 /*
  * Second phase alone (article, "计算公式": the three moves, and "参数说明":
  * permute_token_idx): moves the token rows, scale rows and weights and writes
- * permute_token_idx, from the table a preceding moe_rerouting_v2_offsets()
- * call with the same A, N and E wrote into `workspace` on the same stream.
+ * permute_token_idx, from the row map or the table (mrr_plan_info.
+ * gather_kernel) that a preceding moe_rerouting_v2_offsets() call with the
+ * same arguments wrote into `workspace` on the same stream.
  * If that call found bad counts, or the workspace holds no table for this A,
  * N and E (for instance after a fused moe_rerouting_v2 call, which builds
  * none), nothing is written.

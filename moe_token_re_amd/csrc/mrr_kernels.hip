@@ -12,27 +12,41 @@
 //                       per_token_scales and expert_topk_weight, and
 //                       permute_token_idx ("参数说明"; gather or scatter form).
 //
-// Kernels (the design is ours, not the Ascend tiling the article sketches):
-//   * offsets_staged_kernel: one workgroup of 1024 threads stages the counts
-//     in LDS, scans them row-major then column-major, and writes a table of
-//     int32 pairs (dst_off, src_off) in destination order, cell m = j*N + i.
-//     offsets_global_kernel does the same through global memory for count
-//     matrices too large for LDS.
-//   * gather_kernel: works in destination order. Each workgroup owns a few
-//     adjacent output rows. Every wave maps 64 of them to their source rows
-//     with a cooperative 64-way search over the table (a ballot over 64
-//     pivots per round, then a 6-step shuffle search in a 64-cell window whose
-//     pairs also carry the source offsets). Then the workgroup moves the
-//     4-byte per-row items (index, weight) with one lane per row, and streams
-//     the row bytes: the (row, 16-byte vector) space of its rows is flattened,
-//     each thread issues all its loads before any store, the loads are
-//     branch-free (clamped addresses; only stores are predicated, since a
-//     predicated load makes the compiler wait for it before issuing the next)
-//     and loads and stores are non-temporal. A workgroup's output rows are
-//     adjacent, so its stores are contiguous.
+// Kernels (the design is ours, not the Ascend tiling the article sketches).
+// Offsets phase: every kernel validates the counts, writes the status header,
+// expert_token_num and a table of int32 pairs in output order (forward: cell
+// j*N + i holds (dst_off, src_off); inverse: cell i*E + j holds (src_off,
+// dst_off)), and, where the plan asks for it, the row map: the input row of
+// every output row, one int32 per row.
+//   * offsets_small_kernel (at most 256 cells) and offsets_staged_kernel (at
+//     most 1024): each workgroup stages the counts in LDS and scans them
+//     row-major then column-major; workgroup 0 writes the table, header and
+//     expert_token_num, and every workgroup writes its slice of the row map,
+//     one row per thread, by a binary search over the cells in LDS.
+//   * offsets_banded_kernel (up to 2^17 cells, E <= 1024): the ranks are cut
+//     into bands; every workgroup sweeps the whole count matrix once for the
+//     validity flags and the column totals, then scans its own band, writes
+//     its rows of the table and, split over a few workgroups per band, walks
+//     contiguous runs of input rows to write the row map.
+//   * offsets_global_kernel: one workgroup scans through global memory, for
+//     count matrices too large for the others (no row map).
+// Gather phase:
+//   * stream_gather_kernel (when a row map exists): one 64-lane wave per
+//     chunk of 64 16-byte vectors of token rows, 64 vectors of scale rows or
+//     64 rows of 4-byte items (index, weight); each lane finds its row's input
+//     row with one row-map load, then copies with non-temporal loads and
+//     stores. A chunk that covers whole rows finds its first row with a
+//     multiply-high by a precomputed reciprocal, so all its lanes share one
+//     row-map word. The grid is the plain copy's, which measures fastest.
+//   * gather_kernel (no row map): each workgroup owns a few adjacent output
+//     rows; every wave maps 64 of them to their input rows with a 64-way
+//     search over the table (a ballot over 64 pivots, then a shuffle search in
+//     a 64-cell window), then the workgroup moves the items, one lane per
+//     row, and streams the row bytes with all loads of a thread issued before
+//     its stores (clamped, branch-free loads; predicated stores).
 //   * fused_kernel: for small count matrices, the whole call in one launch:
-//     every gather workgroup recomputes the offsets in its own LDS (a few KiB,
-//     read from L2) and maps its rows from there; workgroup 0 also writes
+//     every workgroup recomputes the offsets in its own LDS (a few KiB, read
+//     from L2) and maps its rows from there; workgroup 0 also writes
 //     expert_token_num and the status.
 // No atomics on global memory; every output element is written exactly once,
 // so results are deterministic.
