@@ -60,6 +60,38 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def bench_copy_lib():
+    lib = ctypes.CDLL(os.path.join(ROOT, "moe_token_re_amd", "libmrr_bench_copy.so"))
+    lib.mrr_bench_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.mrr_bench_copy.restype = ctypes.c_int
+    lib.mrr_bench_device_facts.argtypes = [ctypes.c_int, ctypes.POINTER(ctypes.c_longlong)]
+    lib.mrr_bench_device_facts.restype = ctypes.c_int
+    return lib
+
+
+def device_facts(torch, dev, lib) -> dict:
+    """The device's compute units, LDS, clocks and caches, as HIP reports them."""
+    props = torch.cuda.get_device_properties(dev)
+    out = {"name": props.name, "arch": getattr(props, "gcnArchName", None), "hbm_bytes": props.total_memory}
+    facts = (ctypes.c_longlong * 7)()
+    if lib.mrr_bench_device_facts(dev.index or 0, facts) == 0:
+        out.update({"compute_units": facts[0], "lds_bytes_per_cu": facts[1], "lds_bytes_per_workgroup_max": facts[2],
+                    "shader_clock_mhz": facts[3] / 1000, "memory_clock_mhz": facts[4] / 1000,
+                    "memory_bus_bits": facts[5], "l2_bytes": facts[6]})
+    return out
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def gather_bytes_per_launch(w) -> int:
     """Algorithmic bytes of one gather launch: per row, the token row and the
     scale row read and written, the weight read and written, the index written."""
@@ -134,6 +166,9 @@ def main():
     torch.cuda.set_device(dev)
     w = workloads.make(opt.workload)
     alg_bytes = w.algorithmic_bytes()
+    bench_lib = bench_copy_lib()
+    device = device_facts(torch, dev, bench_lib)
+    print(f"[bench] device {device}", file=sys.stderr, flush=True)
     print(f"[bench] workload {w.name}: A={w.A} H={w.H} N={w.N} E={w.E} tokens={w.tokens_dtype} "
           f"algorithmic bytes/call={alg_bytes}", file=sys.stderr, flush=True)
 
@@ -177,6 +212,18 @@ def main():
     value = alg_bytes / (ms_per_step * 1e-3) / 1e9
     print(f"[bench] {opt.steps} calls: wall {ms_per_step * 1e3:.2f} us/call, events "
           f"{ev_ms * 1e3 / opt.steps:.2f} us/call, {value:.1f} GB/s", file=sys.stderr, flush=True)
+
+    # the median of per-call event pairs (a separate pass: the events between
+    # calls cost a little)
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(opt.steps)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(pairs):
+        a.record(stream)
+        calls[i % n_sets].run()
+        b.record(stream)
+    torch.cuda.synchronize()
+    per_call_median_us = statistics.median(a.elapsed_time(b) for a, b in pairs) * 1e3
+    del pairs
 
     # per-kernel: K back-to-back launches of one kernel between two events on
     # the launch stream, rotating over the buffer sets. When the call is one
@@ -228,9 +275,6 @@ def main():
         nbytes16 = (w.A * w.token_row_bytes) // 16 * 16
         srcs = [c.args.tokens for c in calls]
         dsts = [torch.empty(nbytes16, dtype=torch.uint8, device=dev) for _ in range(n_sets)]
-        bench_lib = ctypes.CDLL(os.path.join(ROOT, "moe_token_re_amd", "libmrr_bench_copy.so"))
-        bench_lib.mrr_bench_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
-        bench_lib.mrr_bench_copy.restype = ctypes.c_int
         hip = ctypes.CDLL("libamdhip64.so")
         hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
                                        ctypes.c_void_p]
@@ -267,7 +311,8 @@ def main():
         med_s, runs = time_oracle(w, inverse=opt.inverse)
         cpu = {"value": round(alg_bytes / med_s / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
                "sample": f"the full {w.name} workload (one whole call), median of {runs} runs, "
-                         f"{med_s * 1e3:.1f} ms/call; host has {os.cpu_count()} logical CPUs"}
+                         f"{med_s * 1e3:.1f} ms/call; host has {os.cpu_count()} logical CPUs",
+               "cpu_model": cpu_model()}
         print(f"[bench] oracle: {med_s * 1e3:.1f} ms/call on 1 thread", file=sys.stderr, flush=True)
 
     line = {
@@ -291,6 +336,7 @@ def main():
                    "buffer_sets": n_sets, "parallelism": "single GPU"},
         "us_per_call": round(ms_per_step * 1e3, 2),
         "us_per_call_events": round(ev_ms * 1e3 / opt.steps, 2),
+        "us_per_call_event_pair_median": round(per_call_median_us, 2),
         "us_per_call_hot_same_buffers": round(hot_us, 2),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "algorithmic_bytes_per_call": alg_bytes,
@@ -303,6 +349,7 @@ def main():
         "copy_ceiling": ceiling,
         "cpu_baseline": cpu,
         "kernel_source_hash": kernel_source_hash(),
+        "device": device,
     }
     print(json.dumps(line), flush=True)
 

@@ -23,6 +23,15 @@ struct ihipStream_t;
  */
 int mrr_bench_copy(void* dst, const void* src, size_t bytes, struct ihipStream_t* stream);
 
+/*
+ * Facts about device `device` that the benchmark report states beside its
+ * figures, written to out[0..6]: compute units, LDS bytes per compute unit,
+ * largest LDS bytes one workgroup may use, peak shader clock (kHz), memory
+ * clock (kHz), memory bus width (bits), L2 cache bytes. Host-side queries
+ * only. Returns 0, or 2 if a query failed (out is then partly written).
+ */
+int mrr_bench_device_facts(int device, long long out[7]);
+
 #ifdef __cplusplus
 }
 #endif

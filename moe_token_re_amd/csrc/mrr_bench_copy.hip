@@ -37,3 +37,17 @@ extern "C" int mrr_bench_copy(void* dst, const void* src, size_t bytes, struct i
                      static_cast<v4u*>(dst), static_cast<const v4u*>(src), n_vec);
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
+
+extern "C" int mrr_bench_device_facts(int device, long long out[7]) {
+  const hipDeviceAttribute_t attrs[7] = {
+      hipDeviceAttributeMultiprocessorCount,        hipDeviceAttributeMaxSharedMemoryPerMultiprocessor,
+      hipDeviceAttributeSharedMemPerBlockOptin,     hipDeviceAttributeClockRate,
+      hipDeviceAttributeMemoryClockRate,            hipDeviceAttributeMemoryBusWidth,
+      hipDeviceAttributeL2CacheSize};
+  for (int k = 0; k < 7; ++k) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, attrs[k], device) != hipSuccess) return 2;
+    out[k] = v;
+  }
+  return 0;
+}
