@@ -244,32 +244,30 @@ __device__ __forceinline__ int div_small(int t, float inv) {
   return static_cast<int>((static_cast<float>(t) + 0.5f) * inv);
 }
 
-// One entry of the row map, rowmap[d] = the input row of output row d, from
-// the cells' offsets in LDS (dst and src, both indexed by column-major cell
-// j * N + i): a binary search for the last output-order cell whose output
-// offset is <= d (an empty cell shares its offset with the next one).
-// Output order is column-major for the forward call, row-major for the
-// inverse.
-__device__ __forceinline__ int32_t rowmap_entry(const int32_t* s_dst, const int32_t* s_src, int N, int E,
-                                                int inverse, float inv_e, int d) {
-  const int M = N * E;
-  auto cm = [&](int c) {  // output-order cell -> its column-major index
-    if (!inverse) return c;
-    const int i = div_small(c, inv_e);
-    return (c - i * E) * N + i;
-  };
-  const int32_t* s_out = inverse ? s_src : s_dst;
-  const int32_t* s_in = inverse ? s_dst : s_src;
-  int lo = 0, hi = M;  // out(lo) <= d < out(hi) (= A)
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (s_out[cm(mid)] <= d)
-      lo = mid;
-    else
-      hi = mid;
-  }
-  const int c = cm(lo);
-  return s_in[c] + (d - s_out[c]);
+// Inclusive running maximum of v over the workgroup (thread order), for
+// values >= -1: DPP row shifts within each row of 16 lanes, the row maxima of
+// the wave by readlane, then the wave maxima through LDS (s_w holds
+// kThreads / 64 entries) behind one barrier. Every lane must be active.
+template <int kThreads>
+__device__ __forceinline__ int32_t block_max_scan(int32_t v, int32_t* s_w) {
+  constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+  v = max(v, __builtin_amdgcn_update_dpp(-1, v, kRowShr1, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(-1, v, kRowShr2, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(-1, v, kRowShr4, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(-1, v, kRowShr8, 0xf, 0xf, false));
+  const int lane = threadIdx.x & 63;
+  const int row = lane >> 4;
+  const int32_t r0 = __builtin_amdgcn_readlane(v, 15);
+  const int32_t r1 = __builtin_amdgcn_readlane(v, 31);
+  const int32_t r2 = __builtin_amdgcn_readlane(v, 47);
+  v = max(v, row >= 1 ? r0 : -1);
+  v = max(v, row >= 2 ? r1 : -1);
+  v = max(v, row >= 3 ? r2 : -1);
+  const int wave = threadIdx.x >> 6;
+  if (lane == 63) s_w[wave] = v;
+  __syncthreads();
+  for (int k = 0; k < wave; ++k) v = max(v, s_w[k]);
+  return v;
 }
 
 // Writes the end-of-table entries and finishes: tab[M] = (A, A), col[E] = A.
@@ -298,13 +296,15 @@ __device__ __forceinline__ void finish_offsets(pair_t* tab, int32_t* col, int M,
 template <int kThreads, typename CountT>
 __device__ uint32_t offsets_cells(const CountT* __restrict__ counts, int N, int E, int64_t A, int inverse,
                                   int32_t* lds, int32_t* col, pair_t* tab, ScanShared<kThreads>* sh,
-                                  int64_t* total_out, int32_t* __restrict__ rowmap = nullptr, int row0 = 0) {
+                                  int64_t* total_out, int32_t* __restrict__ rowmap = nullptr, int row0 = 0,
+                                  int32_t* s_mark = nullptr) {
   const int tid = threadIdx.x;
   const int M = N * E;
   int32_t* s_c = lds;      // counts, column-major
   int32_t* s_s = lds + M;  // SrcOffset, column-major
   if (tid == 0) sh->flags = 0;
   for (int j = tid; j <= E; j += kThreads) col[j] = 0;
+  if (rowmap != nullptr) s_mark[tid] = -1;
   uint32_t flags = 0;
   // Thread t holds cell t in row-major (rank i, expert j) order.
   const bool in = tid < M;
@@ -341,12 +341,34 @@ __device__ uint32_t offsets_cells(const CountT* __restrict__ counts, int N, int 
     }
     if (i == 0) col[j] = static_cast<int32_t>(dst);
     s_c[tid] = static_cast<int32_t>(dst);  // this thread's own count was read before the scan
+    if (rowmap != nullptr && c2 > 0) {
+      // Mark where this cell's rows start among the workgroup's output rows
+      // [row0, row0 + kThreads), by its output-order index (forward: this
+      // column-major index; inverse: the row-major one), or at 0 if it covers
+      // row0 from before. Output-order indices rise with the output offset,
+      // so a running maximum over the marks gives each row its cell.
+      const int32_t out_off = inverse ? s_s[tid] : static_cast<int32_t>(dst);
+      const int lo = out_off - row0;
+      const int o = inverse ? i * E + j : tid;
+      if (lo >= 0 && lo < kThreads)
+        s_mark[lo] = o;
+      else if (lo < 0 && out_off + static_cast<int32_t>(c2) > row0)
+        s_mark[0] = o;
+    }
   }
   finish_offsets(tab, col, M, E, A);
   if (rowmap != nullptr) {
+    const int o = block_max_scan<kThreads>(s_mark[tid], s_mark + kThreads);
     const int d = row0 + tid;
-    if (d < A)
-      rowmap[d] = rowmap_entry(s_c, s_s, N, E, inverse, 1.0f / static_cast<float>(E), d);
+    if (d < A) {
+      int u = o;  // the cell's column-major index
+      if (inverse) {
+        const int i = div_small(o, 1.0f / static_cast<float>(E));
+        u = (o - i * E) * N + i;
+      }
+      // forward: s_s holds the input (source) offsets, s_c the output ones; inverse: the reverse
+      rowmap[d] = inverse ? s_c[u] + (d - s_s[u]) : s_s[u] + (d - s_c[u]);
+    }
   }
   return 0;
 }
@@ -534,7 +556,8 @@ __global__ __launch_bounds__(kOffsetThreads) void offsets_staged_kernel(
   const bool lead = blockIdx.x == 0;
   if (kC == 1)
     flags = offsets_cells<kOffsetThreads>(counts, N, E, A, inverse, s_dyn, col, lead ? table : nullptr, &sh, &total,
-                                          rowmap, static_cast<int>(blockIdx.x) * kOffsetThreads);
+                                          rowmap, static_cast<int>(blockIdx.x) * kOffsetThreads,
+                                          col + E + 1);  // row marks after col (the launch sizes them)
   else
     flags = offsets_chunks<kOffsetThreads, kC>(counts, N, E, A, inverse, s_dyn, col, table, &sh, &total);
   if (!lead) return;
@@ -556,11 +579,12 @@ __global__ __launch_bounds__(kSmallCells) void offsets_small_kernel(
   __shared__ int32_t s_mats[2 * kSmallCells];
   __shared__ int32_t s_col[kSmallCells + 1];
   __shared__ ScanShared<kSmallCells> sh;
+  __shared__ int32_t s_mark[kSmallCells + kSmallCells / 64];  // row marks, then wave maxima
   const bool lead = blockIdx.x == 0;
   int64_t total = 0;
   const uint32_t flags =
       offsets_cells<kSmallCells>(counts, N, E, A, inverse, s_mats, s_col, lead ? table : nullptr, &sh, &total, rowmap,
-                                 static_cast<int>(blockIdx.x) * kSmallCells);
+                                 static_cast<int>(blockIdx.x) * kSmallCells, s_mark);
   if (!lead) return;
   if (flags == 0) write_etn<kSmallCells>(s_col, E, cumsum, etn);
   if (threadIdx.x == 0) write_header(hdr, A, N, E, total, flags, kTablesValid, inverse);
@@ -1415,7 +1439,9 @@ void launch_staged(const Plan& pl, const mrr_args* a, uint8_t* base, size_t lds,
   const unsigned grid =
       kC == 1 && pl.stream ? static_cast<unsigned>(std::max<int64_t>(1, (pl.A + kOffsetThreads - 1) / kOffsetThreads))
                            : 1u;
-  hipLaunchKernelGGL((offsets_staged_kernel<CountT, kC>), dim3(grid), dim3(kOffsetThreads), lds, stream,
+  // one cell per thread with a row map: the row marks and wave maxima after col
+  const size_t dyn = lds + (kC == 1 && pl.stream ? 4 * static_cast<size_t>(kOffsetThreads + kOffsetThreads / 64) : 0);
+  hipLaunchKernelGGL((offsets_staged_kernel<CountT, kC>), dim3(grid), dim3(kOffsetThreads), dyn, stream,
                      static_cast<const CountT*>(a->expert_token_num_per_rank), static_cast<int32_t>(pl.N),
                      static_cast<int32_t>(pl.E), pl.A, pl.cumsum ? 1 : 0, pl.inverse ? 1 : 0,
                      static_cast<CountT*>(a->expert_token_num), reinterpret_cast<WsHeader*>(base),
