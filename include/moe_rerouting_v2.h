@@ -209,11 +209,11 @@ mrr_status moe_rerouting_v2(const mrr_args* args, void* workspace, size_t worksp
 /*
  * First phase alone (article, "计算公式": the two double sums): scans the
  * count matrix (see mrr_plan_info.offsets_workgroups) and writes into the
- * workspace the SrcOffset and DstOffset table, the validity status and, for
- * count matrices of at most 1024 cells or up to 2^17 cells with at most 1024
- * experts, the row map (the input row of every output row); and
- * expert_token_num into args->expert_token_num (only when the counts are
- * valid).
+ * workspace the validity status and what the second phase reads: for count
+ * matrices of at most 1024 cells or up to 2^17 cells with at most 1024
+ * experts, the row map (the input row of every output row); otherwise the
+ * SrcOffset and DstOffset table. Writes expert_token_num into
+ * args->expert_token_num (only when the counts are valid).
  */
 mrr_status moe_rerouting_v2_offsets(const mrr_args* args, void* workspace, size_t workspace_bytes,
                                     struct ihipStream_t* stream);
@@ -224,9 +224,9 @@ mrr_status moe_rerouting_v2_offsets(const mrr_args* args, void* workspace, size_
  * permute_token_idx, from the row map or the table (mrr_plan_info.
  * gather_kernel) that a preceding moe_rerouting_v2_offsets() call with the
  * same arguments wrote into `workspace` on the same stream.
- * If that call found bad counts, or the workspace holds no table for this A,
- * N and E (for instance after a fused moe_rerouting_v2 call, which builds
- * none), nothing is written.
+ * If that call found bad counts, or the workspace holds no row map or table
+ * for this A, N, E and direction (for instance after a fused moe_rerouting_v2
+ * call, which builds neither), nothing is written.
  */
 mrr_status moe_rerouting_v2_gather(const mrr_args* args, void* workspace, size_t workspace_bytes,
                                    struct ihipStream_t* stream);

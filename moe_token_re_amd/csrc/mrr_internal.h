@@ -13,7 +13,8 @@ namespace mrr {
 // Workspace layout (all offsets from the workspace base):
 //   [0, 256)              WsHeader: validity of the counts the table was built from
 //   [256, 256 + T)        table[M + 1] of int32 pairs (output offset, input offset) in
-//                         output order, so that the first member is non-decreasing in m:
+//                         output order (written only when the gather searches it, i.e.
+//                         without a row map), so that the first member is non-decreasing in m:
 //                         forward: (DstOffset, SrcOffset) of cell m = j*N + i (column-major);
 //                         inverse: (SrcOffset, DstOffset) of cell m = i*E + j (row-major);
 //                         table[M] = (A, A)

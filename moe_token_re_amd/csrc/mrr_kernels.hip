@@ -13,21 +13,23 @@
 //                       permute_token_idx ("参数说明"; gather or scatter form).
 //
 // Kernels (the design is ours, not the Ascend tiling the article sketches).
-// Offsets phase: every kernel validates the counts, writes the status header,
-// expert_token_num and a table of int32 pairs in output order (forward: cell
-// j*N + i holds (dst_off, src_off); inverse: cell i*E + j holds (src_off,
-// dst_off)), and, where the plan asks for it, the row map: the input row of
-// every output row, one int32 per row.
+// Offsets phase: every kernel validates the counts, writes the status header
+// and expert_token_num, and then what the gather kernel of the plan reads:
+// the row map (the input row of every output row, one int32 per row) for the
+// stream gather, or else a table of int32 pairs in output order (forward:
+// cell j*N + i holds (dst_off, src_off); inverse: cell i*E + j holds
+// (src_off, dst_off)) for the row-workgroup gather.
 //   * offsets_small_kernel (at most 256 cells) and offsets_staged_kernel (at
 //     most 1024): each workgroup stages the counts in LDS and scans them
-//     row-major then column-major; workgroup 0 writes the table, header and
-//     expert_token_num, and every workgroup writes its slice of the row map,
-//     one row per thread, by a binary search over the cells in LDS.
+//     row-major then column-major; workgroup 0 writes the header,
+//     expert_token_num and any table, and every workgroup writes its slice of
+//     the row map, one row per thread: each cell marks where its rows start
+//     and a workgroup running maximum gives every row its cell.
 //   * offsets_banded_kernel (up to 2^17 cells, E <= 1024): the ranks are cut
 //     into bands; every workgroup sweeps the whole count matrix once for the
-//     validity flags and the column totals, then scans its own band, writes
-//     its rows of the table and, split over a few workgroups per band, walks
-//     contiguous runs of input rows to write the row map.
+//     validity flags and the column totals, then scans its own band and,
+//     split over a few workgroups per band, walks contiguous runs of input
+//     rows to write the row map (or writes its band's rows of the table).
 //   * offsets_global_kernel: one workgroup scans through global memory, for
 //     count matrices too large for the others (no row map).
 // Gather phase:
@@ -551,11 +553,12 @@ __global__ __launch_bounds__(kOffsetThreads) void offsets_staged_kernel(
   int64_t total = 0;
   uint32_t flags;
   // With a row map (one cell per thread only), workgroup b also writes the
-  // row map's rows [1024 b, 1024 b + 1024); workgroup 0 alone writes the
-  // table, expert_token_num and the status.
+  // row map's rows [1024 b, 1024 b + 1024); workgroup 0 alone writes
+  // expert_token_num, the status and, without a row map, the table.
   const bool lead = blockIdx.x == 0;
   if (kC == 1)
-    flags = offsets_cells<kOffsetThreads>(counts, N, E, A, inverse, s_dyn, col, lead ? table : nullptr, &sh, &total,
+    flags = offsets_cells<kOffsetThreads>(counts, N, E, A, inverse, s_dyn, col,
+                                          lead && rowmap == nullptr ? table : nullptr, &sh, &total,
                                           rowmap, static_cast<int>(blockIdx.x) * kOffsetThreads,
                                           col + E + 1);  // row marks after col (the launch sizes them)
   else
@@ -568,14 +571,14 @@ __global__ __launch_bounds__(kOffsetThreads) void offsets_staged_kernel(
 // Offsets and the row map for count matrices of at most kSmallCells cells:
 // the same work as offsets_staged_kernel<CountT, 1> in workgroups of
 // kSmallCells threads (short workgroup scans), one per kSmallCells rows of
-// the row map; workgroup 0 also writes the table, expert_token_num and the
-// status.
+// the row map; workgroup 0 also writes expert_token_num and the status. No
+// table: the gather that follows reads the row map only.
 constexpr int kSmallCells = kSmallOffsetCells;
 
 template <typename CountT>
 __global__ __launch_bounds__(kSmallCells) void offsets_small_kernel(
     const CountT* __restrict__ counts, int32_t N, int32_t E, int64_t A, int cumsum, int inverse,
-    CountT* __restrict__ etn, WsHeader* __restrict__ hdr, pair_t* __restrict__ table, int32_t* __restrict__ rowmap) {
+    CountT* __restrict__ etn, WsHeader* __restrict__ hdr, int32_t* __restrict__ rowmap) {
   __shared__ int32_t s_mats[2 * kSmallCells];
   __shared__ int32_t s_col[kSmallCells + 1];
   __shared__ ScanShared<kSmallCells> sh;
@@ -583,7 +586,7 @@ __global__ __launch_bounds__(kSmallCells) void offsets_small_kernel(
   const bool lead = blockIdx.x == 0;
   int64_t total = 0;
   const uint32_t flags =
-      offsets_cells<kSmallCells>(counts, N, E, A, inverse, s_mats, s_col, lead ? table : nullptr, &sh, &total, rowmap,
+      offsets_cells<kSmallCells>(counts, N, E, A, inverse, s_mats, s_col, nullptr, &sh, &total, rowmap,
                                  static_cast<int>(blockIdx.x) * kSmallCells, s_mark);
   if (!lead) return;
   if (flags == 0) write_etn<kSmallCells>(s_col, E, cumsum, etn);
@@ -775,8 +778,9 @@ __global__ __launch_bounds__(kOffsetThreads) void offsets_banded_kernel(
     int32_t* __restrict__ rowmap, int32_t split) {
   __shared__ BandShared s;
   const int tid = threadIdx.x;
-  // `split` workgroups share a band: each computes its offsets, slice 0
-  // writes its table entries, and each writes 1/split of its rows' row map.
+  // `split` workgroups share a band: each computes its offsets and writes
+  // 1/split of its rows' row map; without a row map, slice 0 writes the
+  // band's table entries.
   const int band = blockIdx.x / split;
   const int slice = blockIdx.x - band * split;
   const int i0 = band * band_rows;
@@ -909,7 +913,9 @@ __global__ __launch_bounds__(kOffsetThreads) void offsets_banded_kernel(
   if (in && ui == 0) s.cstart[uj] = ex3[1];
   __syncthreads();
   int32_t* words = reinterpret_cast<int32_t*>(table);
-  if (in && slice == 0) {  // output order: forward, cell j*N + i as (dst, src); inverse, cell i*E + j as (src, dst)
+  // The table only for a gather that searches it (no row map); output order:
+  // forward, cell j*N + i as (dst, src); inverse, cell i*E + j as (src, dst).
+  if (in && slice == 0 && rowmap == nullptr) {
     const int32_t src = static_cast<int32_t>(s.above_all + ex3[0]);
     const int32_t dst =
         static_cast<int32_t>(static_cast<uint32_t>(s.col[uj]) + s.above[uj] + (ex3[1] - s.cstart[uj]));
@@ -972,7 +978,7 @@ __global__ __launch_bounds__(kOffsetThreads) void offsets_banded_kernel(
       pair_t t;
       t.x = static_cast<int32_t>(A);
       t.y = static_cast<int32_t>(A);
-      table[N * E] = t;
+      if (rowmap == nullptr) table[N * E] = t;
       write_header(hdr, A, N, E, static_cast<int64_t>(s.grand), 0, kTablesValid, inverse);
     }
   }
@@ -1467,7 +1473,6 @@ mrr_status launch_offsets_t(const Plan& pl, const mrr_args* a, void* ws, hipStre
                        static_cast<const CountT*>(a->expert_token_num_per_rank), static_cast<int32_t>(pl.N),
                        static_cast<int32_t>(pl.E), pl.A, pl.cumsum ? 1 : 0, pl.inverse ? 1 : 0,
                        static_cast<CountT*>(a->expert_token_num), reinterpret_cast<WsHeader*>(base),
-                       reinterpret_cast<pair_t*>(base + pl.table_bytes),
                        reinterpret_cast<int32_t*>(base + pl.rowmap_bytes));
     return hipGetLastError() == hipSuccess ? MRR_SUCCESS : MRR_ERROR_HIP;
   }
