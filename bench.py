@@ -144,13 +144,16 @@ def time_oracle(w, budget_s=10.0, max_runs=7, inverse=False):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed calls (default 200; 1000 for the launch-bound tiny workload)")
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="pages_shape")
     ap.add_argument("--inverse", action="store_true", help="time the inverse re-route (expert-major -> rank-major)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the copy-ceiling measurement")
     opt = ap.parse_args()
+    if opt.steps is None:
+        opt.steps = 1000 if opt.workload == "tiny" else 200
 
     if opt.gpus != 1:
         print(f"bench.py measures one GPU only (the operator is per-device and has no collectives); "
