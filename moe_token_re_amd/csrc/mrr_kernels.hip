@@ -892,16 +892,11 @@ __global__ __launch_bounds__(kOffsetThreads) void offsets_banded_kernel(
       if (sum2[0] != static_cast<uint64_t>(A)) atomicOr(&s.flags, kFlagSumMismatch);
     }
   }
-  __syncthreads();
-  const uint32_t flags = s.flags;
-  if (flags != 0) {  // uniform: every workgroup saw every count
-    if (blockIdx.x == 0 && tid == 0)
-      write_header(hdr, A, N, E, static_cast<int64_t>(s.grand), flags, kTablesValid, inverse);
-    return;
-  }
 
   // Step 3: the band's cells in row-major (q = qi * E + qj) and column-major
-  // (u = uj * rows + ui) order.
+  // (u = uj * rows + ui) order. These scans need only the band's counts, so
+  // they start without waiting for step 2; their barrier also publishes step
+  // 2's results and flags.
   const int uj = div_small(tid, inv_rows);
   const int ui = tid - uj * rows;
   const bool in = tid < cells;
@@ -910,6 +905,12 @@ __global__ __launch_bounds__(kOffsetThreads) void offsets_banded_kernel(
   uint32_t ex3[2];
   uint64_t unused[2];
   block_scan_k<kOffsetThreads, 2, 0u>({cq, cu}, {0, 0}, ex3, unused, s.w + 2, s.t + 2);
+  const uint32_t flags = s.flags;
+  if (flags != 0) {  // uniform: every workgroup saw every count
+    if (blockIdx.x == 0 && tid == 0)
+      write_header(hdr, A, N, E, static_cast<int64_t>(s.grand), flags, kTablesValid, inverse);
+    return;
+  }
   if (in && ui == 0) s.cstart[uj] = ex3[1];
   __syncthreads();
   int32_t* words = reinterpret_cast<int32_t*>(table);
