@@ -47,7 +47,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 METRIC = "re-route GB/s (bytes read+written) and % of HBM peak; µs/call A=16384 H=7168"
-PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "pages_shape_counters.txt")
+PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "stream_gather_pages_shape_counters.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "moe_token_re_amd", "csrc", f)
                   for f in ("mrr_kernels.hip", "mrr_internal.h", "mrr_validate.cpp")]
 
