@@ -704,8 +704,9 @@ __global__ __launch_bounds__(kOffsetThreads) void offsets_global_kernel(
 }
 
 // Banded offsets for larger count matrices (kOffsetThreads < M, E <=
-// kOffsetThreads): workgroup b owns the band of ranks [i0, i0 + band_rows) and
-// writes the table entries of its cells; no workgroup waits for another.
+// kOffsetThreads): the workgroups of a band of ranks [i0, i0 + band_rows)
+// write that band's share of the row map (or its table entries); no
+// workgroup waits for another.
 //  1. Every workgroup reads the whole count matrix (from L2 after the first
 //     reader): thread t takes expert column j = t % E and every lanes-th rank
 //     from t / E (lanes * E <= kOffsetThreads, a power of two), with all its
@@ -721,8 +722,11 @@ __global__ __launch_bounds__(kOffsetThreads) void offsets_global_kernel(
 //     sum_j B_j) and in column-major order for DstOffset: a cell of column j
 //     gets DstOffset(0, j) + B_j plus the band's counts above it in its
 //     column (the column-major scan minus its value at the column's first
-//     band cell). Each order's threads write their half of the cell's
-//     (DstOffset, SrcOffset) pair.
+//     band cell). These scans start before step 2 ends (they need only the
+//     band's counts). Without a row map, each order's threads write their
+//     half of the cell's (DstOffset, SrcOffset) pair.
+//  4. With a row map, each workgroup of the band walks contiguous runs of
+//     its share of the band's source rows.
 // Every workgroup repeats step 1 over all M cells, which is why the per-cell
 // work is kept to a few instructions, and why the L2 reads grow as
 // M * (number of bands); the planner bounds M for this path.
