@@ -119,7 +119,7 @@ def traffic_from_profile(w, kernel_name, direction="forward"):
     return int(round((fetch + write) * 1024))
 
 
-def time_oracle(w, budget_s=10.0, max_runs=7, inverse=False):
+def time_oracle(w, budget_s=3.0, max_runs=400, inverse=False):
     """The CPU oracle on the full workload, single-threaded, outputs preallocated
     and pre-faulted; median over runs that fit the time budget."""
     from oracle import oracle
