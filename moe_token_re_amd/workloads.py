@@ -161,12 +161,26 @@ def tiny_segments(seed: int = 5) -> Workload:
                     weight, 1, 0)
 
 
+def odd_rows(seed: int = 6) -> Workload:
+    """Rows that are no multiple of 4 bytes: H = 79 f16 (158 bytes, the odd H
+    of the pages' graph-mode sample) over 262,144 tokens, balanced 16 x 16
+    counts, [A] fp32 scales."""
+    rng = np.random.default_rng(seed)
+    n = e = 16
+    a, h = 262144, 79
+    counts = (1 + rng.multinomial(a - n * e, [1.0 / (n * e)] * (n * e))).reshape(n, e).astype(np.int32)
+    tokens = rng.standard_normal((a, h), dtype=np.float32).astype(np.float16)
+    scales = rng.standard_normal(a, dtype=np.float32)
+    return Workload("odd_rows", counts, tokens, "float16", h, scales, "float32", None, 1, 0)
+
+
 CONFIGS = {
     "tiny": tiny,
     "pages_shape": pages_shape,
     "balanced_bf16": balanced_bf16,
     "mxfp8_skewed": mxfp8_skewed,
     "tiny_segments": tiny_segments,
+    "odd_rows": odd_rows,
 }
 
 
