@@ -168,7 +168,9 @@ typedef struct mrr_plan_info {
                                     recompute the offsets of the (small) count matrix in LDS
                                     (small calls); 0: it launches the offsets kernel, then the
                                     gather kernel */
-  int32_t token_vec_bytes;       /* bytes per load/store of the token copy: 16, 8, 4, 2 or 1 */
+  int32_t token_vec_bytes;       /* bytes per load/store of the token copy: 16, 8, 4, 2 or 1
+                                    (16 also for rows that are no multiple of 16 bytes when the
+                                    stream gather moves them as aligned 16-byte output blocks) */
   int32_t scale_vec_bytes;       /* the same for scale rows; 0 without scales */
   int32_t rows_per_workgroup;    /* adjacent output rows per workgroup of the fused kernel or
                                     the row-workgroup gather */

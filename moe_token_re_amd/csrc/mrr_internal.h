@@ -79,6 +79,9 @@ constexpr int64_t kMaxStreamGrid = int64_t(1) << 31;
 // path (offsets, then the stream gather) even when the single-kernel path
 // could run them.
 constexpr int64_t kFusedMaxTokenBytes = int64_t(64) << 20;
+// The same for rows the stream gather moves as aligned 16-byte blocks while
+// the single kernel would move them in narrow vectors.
+constexpr int64_t kFusedMaxByteRowBytes = int64_t(4) << 20;
 
 // Offsets computed in one workgroup's LDS (the single-workgroup offsets
 // kernel, and every workgroup of the fused kernel) use one of two layouts:
@@ -126,6 +129,9 @@ struct Plan {
   bool stream;              // the gather kernel is the stream kernel: 64-lane workgroups, one chunk of
                             // 64 vectors (token or scale rows) or 64 rows (items) each
   int64_t tok_chunks, sc_chunks, item_chunks;  // the stream kernel's chunks
+  bool byte_rows;           // token rows stream as bytes in 1 KiB chunks of aligned 16-byte blocks
+                            // (rows of 16 bytes or more that are no multiple of 16, both buffers
+                            // 16-byte aligned)
   int64_t stream_grid;      // its workgroups: the total number of chunks
   int64_t band_grid;        // banded offsets kernel: workgroups (bands); 0 = single-workgroup kernel
   int band_rows;            // ranks per band: min(N, kOffsetThreads / E)

@@ -40,6 +40,9 @@
 //     stores. A chunk that covers whole rows finds its first row with a
 //     multiply-high by a precomputed reciprocal, so all its lanes share one
 //     row-map word. The grid is the plain copy's, which measures fastest.
+//     Token rows that are no multiple of 16 bytes stream as bytes instead:
+//     each lane builds one aligned 16-byte block of the output from at most
+//     two input rows with aligned loads and byte funnel shifts.
 //   * gather_kernel (no row map): each workgroup owns a few adjacent output
 //     rows; every wave maps 64 of them to their input rows with a 64-way
 //     search over the table (a ballot over 64 pivots, then a shuffle search in
@@ -1253,6 +1256,8 @@ struct StreamGrid {
   uint32_t cpr_magic;    // ceil(2^32 / cpr): chunk / cpr by a multiply-high and one correction
   float inv_vpr;         // 1 / vpr and 1 / svpr, for rows shorter than a chunk
   float inv_svpr;
+  uint32_t byte_rows;    // token rows stream as bytes: aligned 16-byte blocks of the output
+  float inv_row;         // 1 / row bytes, for byte_rows with rows under 1 KiB
 };
 
 // The workspace header's verdict, read through the scalar cache: it was
@@ -1313,12 +1318,97 @@ __device__ __forceinline__ void stream_rows(const uint8_t* __restrict__ src, uin
   if (ok) __builtin_nontemporal_store(v, reinterpret_cast<T*>(dst + (g0 + lane) * V));
 }
 
+// Bytes [w, w + 16) of `base`, of which [n0, n1) are needed (w <= n0 < n1 <=
+// w + 16): two aligned 16-byte loads, each of a block that holds a needed
+// byte (a block with none takes the other's address, so no load leaves the
+// 16-byte blocks the needed bytes lie in), then a byte funnel shift.
+__device__ __forceinline__ VecT<16>::type window16(const uint8_t* __restrict__ base, int64_t w, int64_t n0,
+                                                   int64_t n1) {
+  using T = VecT<16>::type;
+  const int64_t a = w & ~int64_t(15);
+  const bool need_a = a + 16 > n0;
+  const bool need_b = a + 16 < n1;
+  const T lo = *reinterpret_cast<const T*>(base + (need_a ? a : a + 16));
+  const T hi = *reinterpret_cast<const T*>(base + (need_b ? a + 16 : a));
+  const uint32_t wd[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  const int sh = static_cast<int>(w - a);  // 0..15
+  const int q = sh >> 2;
+  const uint32_t r = static_cast<uint32_t>(sh & 3);
+  uint32_t x[5];  // wd[q .. q + 4]
+#pragma unroll
+  for (int i = 0; i < 5; ++i) x[i] = q == 0 ? wd[i] : q == 1 ? wd[i + 1] : q == 2 ? wd[i + 2] : wd[i + 3];
+  T out;
+  out.x = __builtin_amdgcn_alignbyte(x[1], x[0], r);
+  out.y = __builtin_amdgcn_alignbyte(x[2], x[1], r);
+  out.z = __builtin_amdgcn_alignbyte(x[3], x[2], r);
+  out.w = __builtin_amdgcn_alignbyte(x[4], x[3], r);
+  return out;
+}
+
+// Token rows that are no multiple of 16 bytes (but at least 16 bytes, with
+// both buffers 16-byte aligned), as one byte stream: lane l of chunk c builds
+// the aligned 16-byte block of the dense output at byte 1024 c + 16 l from at
+// most two output rows, i.e. two input rows (row map), with window16 each,
+// and stores it whole (the last, partial block byte by byte).
+__device__ __forceinline__ void stream_bytes_chunk(const GatherArgs& p, const StreamGrid& g, uint32_t chunk,
+                                                   bool valid) {
+  using T = VecT<16>::type;
+  const int lane = threadIdx.x & 63;
+  const int64_t R = p.row_bytes;
+  const int64_t total = int64_t(p.A) * R;
+  const int64_t o0 = int64_t(chunk) * 1024;
+  const int64_t d_base = o0 / R;  // the chunk's first row (uniform)
+  const int64_t o = o0 + 16 * lane;
+  if (o >= total) return;
+  // Row within the chunk: at most one boundary for rows of 1 KiB or more;
+  // below that, a small exact division (off < 2048).
+  const int off = static_cast<int>(o0 - d_base * R) + 16 * lane;  // < R + 1024
+  const int Ri = static_cast<int>(R);
+  const int dd = Ri >= 1024 ? (off >= Ri ? 1 : 0) : div_small(off, g.inv_row);
+  const int col1 = off - dd * Ri;
+  const int d1 = static_cast<int>(d_base) + dd;
+  const int len1 = min(16, Ri - col1);  // bytes from row d1; the rest from row d1 + 1
+  const bool has2 = len1 < 16;
+  const int d2 = has2 ? min(d1 + 1, p.A - 1) : d1;
+  int32_t s1 = p.rowmap[d1];
+  int32_t s2 = p.rowmap[d2];
+  const bool ok = valid & (static_cast<unsigned>(s1) < static_cast<unsigned>(p.A)) &
+                  (static_cast<unsigned>(s2) < static_cast<unsigned>(p.A));
+  s1 = ok ? s1 : 0;  // input row 0 when not moving: always valid here
+  s2 = ok ? s2 : 0;
+  const int64_t w1 = int64_t(s1) * R + col1;
+  const T x1 = window16(p.tokens, w1, w1, w1 + len1);
+  const int64_t r2 = int64_t(s2) * R;  // output byte b >= len1 is input byte r2 + b - len1
+  const T x2 = has2 ? window16(p.tokens, r2 - len1, r2, r2 + (16 - len1)) : x1;
+  uint32_t m[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int nb = min(max(len1 - 4 * k, 0), 4);  // bytes of dword k taken from x1
+    m[k] = nb >= 4 ? 0xffffffffu : (1u << (8 * nb)) - 1u;
+  }
+  T v;
+  v.x = (x1.x & m[0]) | (x2.x & ~m[0]);
+  v.y = (x1.y & m[1]) | (x2.y & ~m[1]);
+  v.z = (x1.z & m[2]) | (x2.z & ~m[2]);
+  v.w = (x1.w & m[3]) | (x2.w & ~m[3]);
+  if (!ok) return;
+  if (o + 16 <= total) {
+    __builtin_nontemporal_store(v, reinterpret_cast<T*>(p.out_tokens + o));
+  } else {
+    const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
+    for (int b = 0; b < static_cast<int>(total - o); ++b)
+      p.out_tokens[o + b] = static_cast<uint8_t>(wv[b >> 2] >> (8 * (b & 3)));
+  }
+}
+
 template <int V, bool kScatter, bool kWeight>
 __global__ __launch_bounds__(64) void stream_gather_kernel(GatherArgs p, StreamGrid g) {
   const bool valid = header_valid(p.hdr, p);
   const uint32_t b = blockIdx.x;  // one chunk per workgroup; uniform branches below
   if (b < g.tok_chunks) {
-    if (g.cpr != 0)
+    if (V < 16 && g.byte_rows != 0)
+      stream_bytes_chunk(p, g, b, valid);
+    else if (g.cpr != 0)
       stream_whole_row_chunk<V>(p, g, b, valid);
     else
       stream_rows<V>(p.tokens, p.out_tokens, p.row_bytes, p.vecs_per_row, g.inv_vpr, b, p.rowmap, p.A, valid);
@@ -1599,7 +1689,9 @@ StreamGrid stream_grid(const Plan& pl) {
   // cpr_magic = ceil(2^32 / cpr) puts umulhi(c, magic) at c / cpr or one above.
   sg.cpr = 0;
   sg.cpr_magic = 0;
-  if (pl.vecs_per_row % 64 == 0) {
+  sg.byte_rows = pl.byte_rows ? 1u : 0u;
+  sg.inv_row = 1.0f / static_cast<float>(pl.row_bytes);
+  if (!pl.byte_rows && pl.vecs_per_row % 64 == 0) {
     sg.cpr = static_cast<uint32_t>(pl.vecs_per_row / 64);
     sg.cpr_magic = sg.cpr == 1 ? 0u : static_cast<uint32_t>(((uint64_t(1) << 32) + sg.cpr - 1) / sg.cpr);
   }

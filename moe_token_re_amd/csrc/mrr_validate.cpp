@@ -62,12 +62,14 @@ struct Tuning {
   int offsets;      // 0 = automatic, 1 = single-workgroup offsets kernel, 2 = banded where it applies
   int stream;       // 1 (default): the stream gather kernel for the two-kernel path; 0: row workgroups
   bool fused;       // allow the single-kernel path (MRR_FUSED=0 turns it off)
+  bool byte_rows;   // rows that are no multiple of 16 bytes stream as aligned 16-byte blocks
   bool log;
   Tuning()
       : rows_per_wg(env_int("MRR_ROWS_PER_WG", 0)),
         offsets(env_int("MRR_OFFSETS", 0)),
         stream(env_int("MRR_STREAM", 1)),
         fused(env_int("MRR_FUSED", 1) != 0),
+        byte_rows(env_int("MRR_BYTE_ROWS", 1) != 0),
         log(env_int("MRR_LOG", 0) != 0) {}
 };
 
@@ -253,8 +255,11 @@ mrr_status make_plan(const mrr_args* a, const void* ws, size_t ws_bytes, Plan* p
     q.band_split = static_cast<int>(
         std::min<int64_t>(16, std::max<int64_t>(1, q.A / (q.band_grid * kOffsetThreads))));
   q.tok_chunks = q.sc_chunks = q.item_chunks = q.stream_grid = 0;
+  q.byte_rows = false;
   if (q.stream) {
-    q.tok_chunks = (q.A * q.vecs_per_row + 63) / 64;
+    q.byte_rows = tuning().byte_rows && q.token_vec < 16 && q.row_bytes >= 16 && aligned(a->tokens, 16) &&
+                  aligned(a->permute_tokens, 16);
+    q.tok_chunks = q.byte_rows ? (q.A * q.row_bytes + 1023) / 1024 : (q.A * q.vecs_per_row + 63) / 64;
     q.sc_chunks = Rs > 0 ? (q.A * (Rs / q.scale_vec) + 63) / 64 : 0;
     q.item_chunks = (q.A + 63) / 64;
     q.stream_grid = q.tok_chunks + q.sc_chunks + q.item_chunks;
@@ -264,6 +269,7 @@ mrr_status make_plan(const mrr_args* a, const void* ws, size_t ws_bytes, Plan* p
   // gather streams faster. The launch matters less than the rate from a few
   // tens of MiB of rows on.
   if (q.fused && q.stream && q.A * q.row_bytes >= kFusedMaxTokenBytes) q.fused = false;
+  if (q.fused && q.byte_rows && q.A * q.row_bytes >= kFusedMaxByteRowBytes) q.fused = false;
   q.table_bytes = kHeaderBytes;
   q.rowmap_bytes = kHeaderBytes + round_up(8 * (static_cast<size_t>(M) + 1), 256);
   *p = q;
@@ -292,7 +298,7 @@ extern "C" mrr_status mrr_describe_plan(const mrr_args* args, const void* worksp
   const mrr_status st = mrr::make_plan(args, workspace, workspace_bytes, &plan);
   if (st != MRR_SUCCESS) return st;
   info->fused = plan.fused ? 1 : 0;
-  info->token_vec_bytes = plan.token_vec;
+  info->token_vec_bytes = plan.byte_rows && !plan.fused ? 16 : plan.token_vec;
   info->scale_vec_bytes = plan.scale_row_bytes > 0 ? plan.scale_vec : 0;
   info->rows_per_workgroup = plan.rows_per_wg;
   info->threads_per_workgroup = plan.fused || !plan.stream ? mrr::kGatherThreads : 64;

@@ -217,10 +217,15 @@ def test_describe_plan():
     a.scales_ndim, a.scales_dims[1] = 2, 5
     st, info = describe(a)
     assert st == _lib.SUCCESS and info.rows_per_workgroup == 256 and info.scale_inline_bytes == 0
-    # odd rows fall back to narrower vectors
+    # odd rows fall back to narrower vectors in the single-kernel path
     a = valid_args(tok=_lib.F16, H=79)
     st, info = describe(a)
     assert st == _lib.SUCCESS and info.token_vec_bytes == 2 and info.token_row_bytes == 158
+    # ...and stream as aligned 16-byte blocks of the output in the stream gather: 1 KiB chunks of
+    # the 158-byte rows, the 4-byte scale rows and the items
+    st, info = describe(valid_args(tok=_lib.F16, H=79, A=262144, N=16, E=16))
+    assert st == _lib.SUCCESS and info.gather_kernel == 1 and info.token_vec_bytes == 16
+    assert info.gather_workgroups == (262144 * 158 + 1023) // 1024 + 262144 // 64 + 262144 // 64
     # empty input: nothing to gather, never the single-kernel path
     st, info = describe(valid_args(A=0, N=3, E=2))
     assert st == _lib.SUCCESS and info.fused == 0 and info.gather_workgroups == 0
