@@ -1377,20 +1377,21 @@ __device__ __forceinline__ void stream_bytes_chunk(const GatherArgs& p, const St
   s1 = ok ? s1 : 0;  // input row 0 when not moving: always valid here
   s2 = ok ? s2 : 0;
   const int64_t w1 = int64_t(s1) * R + col1;
-  const T x1 = window16(p.tokens, w1, w1, w1 + len1);
-  const int64_t r2 = int64_t(s2) * R;  // output byte b >= len1 is input byte r2 + b - len1
-  const T x2 = has2 ? window16(p.tokens, r2 - len1, r2, r2 + (16 - len1)) : x1;
-  uint32_t m[4];
+  T v = window16(p.tokens, w1, w1, w1 + len1);
+  if (has2) {  // the block crosses into the next row (a few lanes of a wave)
+    const int64_t r2 = int64_t(s2) * R;  // output byte b >= len1 is input byte r2 + b - len1
+    const T x2 = window16(p.tokens, r2 - len1, r2, r2 + (16 - len1));
+    uint32_t m[4];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int nb = min(max(len1 - 4 * k, 0), 4);  // bytes of dword k taken from x1
-    m[k] = nb >= 4 ? 0xffffffffu : (1u << (8 * nb)) - 1u;
+    for (int k = 0; k < 4; ++k) {
+      const int nb = min(max(len1 - 4 * k, 0), 4);  // bytes of dword k taken from the first row
+      m[k] = nb >= 4 ? 0xffffffffu : (1u << (8 * nb)) - 1u;
+    }
+    v.x = (v.x & m[0]) | (x2.x & ~m[0]);
+    v.y = (v.y & m[1]) | (x2.y & ~m[1]);
+    v.z = (v.z & m[2]) | (x2.z & ~m[2]);
+    v.w = (v.w & m[3]) | (x2.w & ~m[3]);
   }
-  T v;
-  v.x = (x1.x & m[0]) | (x2.x & ~m[0]);
-  v.y = (x1.y & m[1]) | (x2.y & ~m[1]);
-  v.z = (x1.z & m[2]) | (x2.z & ~m[2]);
-  v.w = (x1.w & m[3]) | (x2.w & ~m[3]);
   if (!ok) return;
   if (o + 16 <= total) {
     __builtin_nontemporal_store(v, reinterpret_cast<T*>(p.out_tokens + o));
