@@ -1251,6 +1251,7 @@ __global__ __launch_bounds__(kGatherThreads) void gather_kernel(GatherArgs p) {
 // workgroups with many loads per lane.
 struct StreamGrid {
   uint32_t tok_chunks;   // ceil(A * vpr / 64)
+  uint32_t small;        // scale and item chunks, which take the grid's first workgroups
   uint32_t sc_end;       // tok_chunks + ceil(A * svpr / 64) (no scale chunks without scales)
   uint32_t cpr;          // token chunks per row when whole (vpr % 64 == 0), else 0
   uint32_t cpr_magic;    // ceil(2^32 / cpr): chunk / cpr by a multiply-high and one correction
@@ -1273,19 +1274,25 @@ __device__ __forceinline__ bool header_valid(const WsHeader* hdr, const GatherAr
 }
 
 // A token chunk that lies in one row (the row is a whole number of chunks):
-// chunk c is part c % cpr of row c / cpr.
+// chunk c is part c % cpr of row c / cpr. The row's row-map word and the
+// workspace header are read through the scalar cache and waited for
+// together, so each wave's chain is one scalar round trip, the token load and
+// the store (the row map was written by an earlier kernel; this one does not
+// write it).
 template <int V>
-__device__ __forceinline__ void stream_whole_row_chunk(const GatherArgs& p, const StreamGrid& g, uint32_t c,
-                                                       bool valid) {
+__device__ __forceinline__ void stream_whole_row_chunk(const GatherArgs& p, const StreamGrid& g, uint32_t c) {
   using T = typename VecT<V>::type;
+  using CInt = const int32_t __attribute__((address_space(4)))*;
   uint32_t d = c;
   if (g.cpr != 1) {  // uniform
     d = __umulhi(c, g.cpr_magic);
     d -= d * g.cpr > c ? 1u : 0u;
   }
-  const int32_t s = p.rowmap[d];  // the same address in every lane
+  d = __builtin_amdgcn_readfirstlane(d);
+  const int32_t s = reinterpret_cast<CInt>(reinterpret_cast<uintptr_t>(p.rowmap))[d];
   const uint32_t col = (c - d * g.cpr) * 64u + (threadIdx.x & 63);  // vector within the row
-  const bool ok = valid && static_cast<unsigned>(s) < static_cast<unsigned>(p.A);
+  // `&`, not `&&`: the header loads issue beside the row-map load
+  const bool ok = header_valid(p.hdr, p) & (static_cast<unsigned>(s) < static_cast<unsigned>(p.A));
   const int64_t so = ok ? int64_t(s) * p.row_bytes + int64_t(col) * V : 0;
   const T v = __builtin_nontemporal_load(reinterpret_cast<const T*>(p.tokens + so));
   if (ok) __builtin_nontemporal_store(v, reinterpret_cast<T*>(p.out_tokens + int64_t(d) * p.row_bytes + int64_t(col) * V));
@@ -1402,15 +1409,22 @@ __device__ __forceinline__ void stream_bytes_chunk(const GatherArgs& p, const St
   }
 }
 
+// One chunk per workgroup. Chunk numbers: token chunks [0, tok_chunks), scale
+// chunks [tok_chunks, sc_end), then item chunks; the workgroups take the scale
+// and item chunks first, so that their scattered short loads run under the
+// token stream rather than in its tail. Branches are uniform.
 template <int V, bool kScatter, bool kWeight>
 __global__ __launch_bounds__(64) void stream_gather_kernel(GatherArgs p, StreamGrid g) {
+  const uint32_t bx = blockIdx.x;
+  const uint32_t b = bx >= g.small ? bx - g.small : bx + g.tok_chunks;
+  if (b < g.tok_chunks && g.cpr != 0) {  // cpr is 0 for byte rows
+    stream_whole_row_chunk<V>(p, g, b);
+    return;
+  }
   const bool valid = header_valid(p.hdr, p);
-  const uint32_t b = blockIdx.x;  // one chunk per workgroup; uniform branches below
   if (b < g.tok_chunks) {
     if (V < 16 && g.byte_rows != 0)
       stream_bytes_chunk(p, g, b, valid);
-    else if (g.cpr != 0)
-      stream_whole_row_chunk<V>(p, g, b, valid);
     else
       stream_rows<V>(p.tokens, p.out_tokens, p.row_bytes, p.vecs_per_row, g.inv_vpr, b, p.rowmap, p.A, valid);
   } else if (b < g.sc_end) {
@@ -1685,6 +1699,7 @@ StreamGrid stream_grid(const Plan& pl) {
   StreamGrid sg;
   sg.tok_chunks = static_cast<uint32_t>(pl.tok_chunks);
   sg.sc_end = static_cast<uint32_t>(pl.tok_chunks + pl.sc_chunks);
+  sg.small = static_cast<uint32_t>(pl.sc_chunks + pl.item_chunks);
   sg.inv_vpr = 1.0f / static_cast<float>(pl.vecs_per_row);
   sg.inv_svpr = pl.scale_row_bytes > 0 ? 1.0f / static_cast<float>(pl.scale_row_bytes / pl.scale_vec) : 0.0f;
   // cpr_magic = ceil(2^32 / cpr) puts umulhi(c, magic) at c / cpr or one above.
