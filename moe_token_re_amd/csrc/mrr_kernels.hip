@@ -1300,11 +1300,13 @@ __device__ __forceinline__ void stream_whole_row_chunk(const GatherArgs& p, cons
 
 // Chunk `chunk` of a row stream: vectors [64 chunk, 64 chunk + 64) of the
 // rows [0, A) of vpr vectors of V bytes each, output row d taken from
-// source row source_row(d).
+// source row rowmap[d]. The header check of p is computed after the row-map
+// load is issued (and without short-circuit), so its scalar loads overlap
+// that load instead of preceding it; the same holds in every chunk kind.
 template <int V>
 __device__ __forceinline__ void stream_rows(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
                                             int64_t row_bytes, int vpr, float inv_vpr, int64_t chunk,
-                                            const int32_t* __restrict__ rowmap, int A, bool valid) {
+                                            const int32_t* __restrict__ rowmap, int A, const GatherArgs& p) {
   using T = typename VecT<V>::type;
   const int lane = threadIdx.x & 63;
   const int64_t g0 = chunk * 64;
@@ -1318,7 +1320,7 @@ __device__ __forceinline__ void stream_rows(const uint8_t* __restrict__ src, uin
   const bool in = g0 + lane < total;
   const int d = static_cast<int>(d0) + (in ? dd : 0);  // in [d0, d0 + 63]
   const int32_t s = rowmap[d];
-  const bool ok = in && valid && static_cast<unsigned>(s) < static_cast<unsigned>(A);
+  const bool ok = in & header_valid(p.hdr, p) & (static_cast<unsigned>(s) < static_cast<unsigned>(A));
   // Branch-free load (row 0, column 0 when not moving: always valid here).
   const int64_t so = ok ? int64_t(s) * row_bytes + int64_t(col) * V : 0;
   const T v = __builtin_nontemporal_load(reinterpret_cast<const T*>(src + so));
@@ -1357,8 +1359,7 @@ __device__ __forceinline__ VecT<16>::type window16(const uint8_t* __restrict__ b
 // the aligned 16-byte block of the dense output at byte 1024 c + 16 l from at
 // most two output rows, i.e. two input rows (row map), with window16 each,
 // and stores it whole (the last, partial block byte by byte).
-__device__ __forceinline__ void stream_bytes_chunk(const GatherArgs& p, const StreamGrid& g, uint32_t chunk,
-                                                   bool valid) {
+__device__ __forceinline__ void stream_bytes_chunk(const GatherArgs& p, const StreamGrid& g, uint32_t chunk) {
   using T = VecT<16>::type;
   const int lane = threadIdx.x & 63;
   const int64_t R = p.row_bytes;
@@ -1379,7 +1380,7 @@ __device__ __forceinline__ void stream_bytes_chunk(const GatherArgs& p, const St
   const int d2 = has2 ? min(d1 + 1, p.A - 1) : d1;
   int32_t s1 = p.rowmap[d1];
   int32_t s2 = p.rowmap[d2];
-  const bool ok = valid & (static_cast<unsigned>(s1) < static_cast<unsigned>(p.A)) &
+  const bool ok = header_valid(p.hdr, p) & (static_cast<unsigned>(s1) < static_cast<unsigned>(p.A)) &
                   (static_cast<unsigned>(s2) < static_cast<unsigned>(p.A));
   s1 = ok ? s1 : 0;  // input row 0 when not moving: always valid here
   s2 = ok ? s2 : 0;
@@ -1421,30 +1422,29 @@ __global__ __launch_bounds__(64) void stream_gather_kernel(GatherArgs p, StreamG
     stream_whole_row_chunk<V>(p, g, b);
     return;
   }
-  const bool valid = header_valid(p.hdr, p);
   if (b < g.tok_chunks) {
     if (V < 16 && g.byte_rows != 0)
-      stream_bytes_chunk(p, g, b, valid);
+      stream_bytes_chunk(p, g, b);
     else
-      stream_rows<V>(p.tokens, p.out_tokens, p.row_bytes, p.vecs_per_row, g.inv_vpr, b, p.rowmap, p.A, valid);
+      stream_rows<V>(p.tokens, p.out_tokens, p.row_bytes, p.vecs_per_row, g.inv_vpr, b, p.rowmap, p.A, p);
   } else if (b < g.sc_end) {
     const int64_t c = b - g.tok_chunks;
     const int spr = p.scale_vecs_per_row;
     const int64_t Rs = p.scale_row_bytes;
     const float inv = g.inv_svpr;
     switch (p.scale_vec) {
-      case 16: stream_rows<16>(p.scales, p.out_scales, Rs, spr, inv, c, p.rowmap, p.A, valid); break;
-      case 8: stream_rows<8>(p.scales, p.out_scales, Rs, spr, inv, c, p.rowmap, p.A, valid); break;
-      case 4: stream_rows<4>(p.scales, p.out_scales, Rs, spr, inv, c, p.rowmap, p.A, valid); break;
-      case 2: stream_rows<2>(p.scales, p.out_scales, Rs, spr, inv, c, p.rowmap, p.A, valid); break;
-      default: stream_rows<1>(p.scales, p.out_scales, Rs, spr, inv, c, p.rowmap, p.A, valid); break;
+      case 16: stream_rows<16>(p.scales, p.out_scales, Rs, spr, inv, c, p.rowmap, p.A, p); break;
+      case 8: stream_rows<8>(p.scales, p.out_scales, Rs, spr, inv, c, p.rowmap, p.A, p); break;
+      case 4: stream_rows<4>(p.scales, p.out_scales, Rs, spr, inv, c, p.rowmap, p.A, p); break;
+      case 2: stream_rows<2>(p.scales, p.out_scales, Rs, spr, inv, c, p.rowmap, p.A, p); break;
+      default: stream_rows<1>(p.scales, p.out_scales, Rs, spr, inv, c, p.rowmap, p.A, p); break;
     }
   } else {
     const int r0 = static_cast<int>(b - g.sc_end) * 64;
     const int d = r0 + static_cast<int>(threadIdx.x & 63);
     const bool in = d < p.A;
     const int32_t s = p.rowmap[in ? d : r0];
-    const bool ok = in && valid && static_cast<unsigned>(s) < static_cast<unsigned>(p.A);
+    const bool ok = in & header_valid(p.hdr, p) & (static_cast<unsigned>(s) < static_cast<unsigned>(p.A));
     if (kWeight) {
       const uint32_t wv = p.weight[ok ? s : 0];
       if (ok) p.out_weight[d] = wv;
