@@ -185,7 +185,7 @@ def test_offsets_banded(n, e):
                               idx_type=(n * e) % 2, etn_type=(n + e) % 2)
     band_rows = min(n, 1024 // e)
     bands = -(-n // band_rows)
-    split = min(16, max(1, w.A // (bands * 1024)))  # workgroups sharing a band's row map writes
+    split = min(16, max(1, 2 * w.A // (bands * 1024)))  # workgroups sharing a band's row map writes
     assert _offsets_workgroups(w, _dev()) == bands * split
     check(w)
     check(w, phases=True)
