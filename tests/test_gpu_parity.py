@@ -88,6 +88,18 @@ def test_fuzz(case):
     check(w, phases=True)  # the two phases: the stream gather where the row map is written
 
 
+# The largest H the contract allows ("约束说明": 0 < H < 16384): 16383 for
+# 8- and 16-bit tokens (rows of 16383 and 32766 bytes, no multiple of 16: the
+# byte stream in the two-kernel path), 16382 for packed fp4 (H must be even).
+@pytest.mark.parametrize("tok", ["int8", "float16", "bfloat16", "float8_e4m3fn", "float4_e2m1fn_x2"])
+def test_largest_h(tok):
+    h = 16382 if tok.startswith("float4") else 16383
+    w = workloads.random_case(7000 + len(tok), 3, 5, h, tokens_dtype=tok, count_range=(0, 9), scales="e8m0",
+                              weight=True, idx_type=len(tok) % 2)
+    check(w)
+    check(w, phases=True)
+
+
 # Shapes named by the article's tests ("测试与验证"): (52, 21), (35, 15267),
 # (28, 6057), read both ways as (A, H); (N, E) in {(4,2), (23,2), (14,1)}.
 @pytest.mark.parametrize("a,h", [(52, 21), (21, 52), (35, 15267), (15267, 35), (28, 6057), (6057, 28)])
