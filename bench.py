@@ -19,7 +19,9 @@ calls. Prints ONE JSON line:
               committed counter summary matches the current kernel source
   cpu_baseline the CPU oracle on the same workload, one host thread
 plus the measured copy ceiling (hipMemcpyAsync device-to-device and a plain
-16-byte non-temporal copy kernel moving the same token bytes).
+16-byte non-temporal copy kernel moving the same token bytes), and the
+per-call time of the same calls captured in one HIP graph and replayed
+(us_per_call_graph: no host launch overhead; it matters for small calls).
 
 With --inverse the same workload runs the inverse re-route (its token rows
 taken as expert-major, returned to rank-major order), with the oracle's
@@ -180,8 +182,10 @@ def main():
     footprint = 2 * (w.A * (w.token_row_bytes + w.scale_row_bytes + 4 + (8 if w.weight is not None else 0)))
     n_sets = max(3, math.ceil((1 << 30) / max(footprint, 1)))
     calls = []
+    inputs = []
     for k in range(n_sets):
         t = base if k == 0 else {key: (v.clone() if isinstance(v, torch.Tensor) else v) for key, v in base.items()}
+        inputs.append(t)
         call, _ = api.make_call(t["tokens"], t["counts"], per_token_scales=t["scales"],
                                 expert_topk_weight=t["weight"], expert_token_num_type=w.etn_type,
                                 idx_type=w.idx_type, tokens_dtype=t["tokens_dtype"], stream=stream,
@@ -272,6 +276,39 @@ def main():
     torch.cuda.synchronize()
     hot_us = ev0.elapsed_time(ev1) * 1e3 / opt.steps
 
+    # the same calls captured in one HIP graph (the launch path allocates,
+    # sets and synchronizes nothing) and replayed: the per-call cost without
+    # the host's launch overhead, which dominates small calls
+    side = torch.cuda.Stream(dev)
+    n_cap = 20
+    gcalls = []
+    for t in inputs[:n_cap]:
+        gc, _ = api.make_call(t["tokens"], t["counts"], per_token_scales=t["scales"],
+                              expert_topk_weight=t["weight"], expert_token_num_type=w.etn_type,
+                              idx_type=w.idx_type, tokens_dtype=t["tokens_dtype"], stream=side,
+                              direction=_lib.INVERSE if opt.inverse else _lib.FORWARD)
+        gcalls.append(gc)
+    with torch.cuda.stream(side):
+        for gc in gcalls:
+            gc.run()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        for i in range(n_cap):
+            gcalls[i % len(gcalls)].run()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    reps = max(1, opt.steps // n_cap)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        graph.replay()
+    torch.cuda.synchronize()
+    graph_us = (time.perf_counter() - t0) * 1e6 / (reps * n_cap)
+    if any(gc.device_status() != _lib.SUCCESS for gc in gcalls[:1]):
+        raise SystemExit("device status after graph replays")
+    del graph, gcalls
+
     # copy ceiling over the same token bytes, same rotation
     ceiling = None
     if not opt.no_ceiling:
@@ -341,6 +378,7 @@ def main():
         "us_per_call_events": round(ev_ms * 1e3 / opt.steps, 2),
         "us_per_call_event_pair_median": round(per_call_median_us, 2),
         "us_per_call_hot_same_buffers": round(hot_us, 2),
+        "us_per_call_graph": round(graph_us, 2),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "algorithmic_bytes_per_call": alg_bytes,
         "launch_path": "fused single kernel" if plan["fused"] else "offsets kernel + gather kernel",
