@@ -49,10 +49,11 @@
 //     a 64-cell window), then the workgroup moves the items, one lane per
 //     row, and streams the row bytes with all loads of a thread issued before
 //     its stores (clamped, branch-free loads; predicated stores).
-//   * fused_kernel: for small count matrices, the whole call in one launch:
-//     every workgroup recomputes the offsets in its own LDS (a few KiB, read
-//     from L2) and maps its rows from there; workgroup 0 also writes
-//     expert_token_num and the status.
+//   * fused_kernel: for small count matrices, the whole call in one launch,
+//     in input order: every workgroup loads its own input rows first, then
+//     recomputes the offsets in its own LDS (a few KiB, read from L2) with
+//     the output row of each of its input rows, and stores the rows there;
+//     workgroup 0 also writes expert_token_num and the status.
 // No atomics on global memory; every output element is written exactly once,
 // so results are deterministic.
 #include <hip/hip_runtime.h>
@@ -295,21 +296,23 @@ __device__ __forceinline__ void finish_offsets(pair_t* tab, int32_t* col, int M,
 // SrcOffset) (coalesced); inverse, tab[i*E + j] = (SrcOffset, DstOffset);
 // then tab[M] = (A, A), and the expert starts col[j] = DstOffset(0, j),
 // col[E] = A. With a row map, also rowmap[d] for d = row0 + thread (one row
-// per thread, coalesced).
+// per thread, coalesced); with s_map instead, s_map[thread] = that value in
+// LDS (-1 past A).
 // Returns 0, or the rejection flags (the same in every thread; then tab and
 // col are not written).
 template <int kThreads, typename CountT>
 __device__ uint32_t offsets_cells(const CountT* __restrict__ counts, int N, int E, int64_t A, int inverse,
                                   int32_t* lds, int32_t* col, pair_t* tab, ScanShared<kThreads>* sh,
                                   int64_t* total_out, int32_t* __restrict__ rowmap = nullptr, int row0 = 0,
-                                  int32_t* s_mark = nullptr) {
+                                  int32_t* s_mark = nullptr, int32_t* s_map = nullptr) {
+  const bool mapping = rowmap != nullptr || s_map != nullptr;
   const int tid = threadIdx.x;
   const int M = N * E;
   int32_t* s_c = lds;      // counts, column-major
   int32_t* s_s = lds + M;  // SrcOffset, column-major
   if (tid == 0) sh->flags = 0;
   for (int j = tid; j <= E; j += kThreads) col[j] = 0;
-  if (rowmap != nullptr) s_mark[tid] = -1;
+  if (mapping) s_mark[tid] = -1;
   uint32_t flags = 0;
   // Thread t holds cell t in row-major (rank i, expert j) order.
   const bool in = tid < M;
@@ -346,7 +349,7 @@ __device__ uint32_t offsets_cells(const CountT* __restrict__ counts, int N, int 
     }
     if (i == 0) col[j] = static_cast<int32_t>(dst);
     s_c[tid] = static_cast<int32_t>(dst);  // this thread's own count was read before the scan
-    if (rowmap != nullptr && c2 > 0) {
+    if (mapping && c2 > 0) {
       // Mark where this cell's rows start among the workgroup's output rows
       // [row0, row0 + kThreads), by its output-order index (forward: this
       // column-major index; inverse: the row-major one), or at 0 if it covers
@@ -362,9 +365,10 @@ __device__ uint32_t offsets_cells(const CountT* __restrict__ counts, int N, int 
     }
   }
   finish_offsets(tab, col, M, E, A);
-  if (rowmap != nullptr) {
+  if (mapping) {
     const int o = block_max_scan<kThreads>(s_mark[tid], s_mark + kThreads);
     const int d = row0 + tid;
+    int32_t v = -1;
     if (d < A) {
       int u = o;  // the cell's column-major index
       if (inverse) {
@@ -372,8 +376,10 @@ __device__ uint32_t offsets_cells(const CountT* __restrict__ counts, int N, int 
         u = (o - i * E) * N + i;
       }
       // forward: s_s holds the input (source) offsets, s_c the output ones; inverse: the reverse
-      rowmap[d] = inverse ? s_c[u] + (d - s_s[u]) : s_s[u] + (d - s_c[u]);
+      v = inverse ? s_c[u] + (d - s_s[u]) : s_s[u] + (d - s_c[u]);
+      if (s_map == nullptr) rowmap[d] = v;
     }
+    if (s_map != nullptr) s_map[tid] = v;
   }
   return 0;
 }
@@ -1464,31 +1470,150 @@ struct FusedArgs {
   int32_t cumsum;
 };
 
+// Items [e0, e0 + kGatherThreads * kGatherUnroll) of `rows` input rows of
+// vpr vectors each, starting at input row row0, kGatherUnroll per thread
+// (item e is vector e % vpr of row e / vpr): the loads, and where each item
+// goes (c = -1: none). Items past the end load row row0, vector 0.
+template <int V>
+struct RowRound {
+  typename VecT<V>::type v[kGatherUnroll];
+  int r[kGatherUnroll];
+  int c[kGatherUnroll];
+};
+
+template <int V>
+__device__ __forceinline__ void load_round(RowRound<V>& q, const uint8_t* __restrict__ src, int64_t row_bytes,
+                                           int vpr, int rows, int row0, int e0) {
+  using T = typename VecT<V>::type;
+  const int total = rows * vpr;
+  const int e = e0 + static_cast<int>(threadIdx.x);
+  int r = e / vpr;
+  int c = e - r * vpr;
+  const int dr = kGatherThreads / vpr;
+  const int dc = kGatherThreads - dr * vpr;
+#pragma unroll
+  for (int k = 0; k < kGatherUnroll; ++k) {
+    const bool in = e + k * kGatherThreads < total;
+    q.r[k] = in ? r : 0;
+    q.c[k] = in ? c : -1;
+    const int64_t off = in ? int64_t(row0 + r) * row_bytes + int64_t(c) * V : int64_t(row0) * row_bytes;
+    q.v[k] = __builtin_nontemporal_load(reinterpret_cast<const T*>(src + off));
+    r += dr;
+    c += dc;
+    if (c >= vpr) {
+      c -= vpr;
+      ++r;
+    }
+  }
+}
+
+// Stores a round: item (r, c) to output row s_dst[r] (skipped when outside
+// [0, A)).
+template <int V>
+__device__ __forceinline__ void store_round(const RowRound<V>& q, uint8_t* __restrict__ dst, int64_t row_bytes,
+                                            int A, const int32_t* s_dst) {
+  using T = typename VecT<V>::type;
+#pragma unroll
+  for (int k = 0; k < kGatherUnroll; ++k) {
+    const int32_t d = s_dst[q.r[k]];
+    if (q.c[k] >= 0 && static_cast<unsigned>(d) < static_cast<unsigned>(A))
+      __builtin_nontemporal_store(q.v[k],
+                                  reinterpret_cast<T*>(dst + int64_t(d) * row_bytes + int64_t(q.c[k]) * V));
+  }
+}
+
+// All `rows` input rows from row0 on, vpr vectors each, to their output rows.
+template <int V>
+__device__ __forceinline__ void scatter_rows(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                             int64_t row_bytes, int vpr, int rows, int row0, int A,
+                                             const int32_t* s_dst, int e_start = 0) {
+  for (int e0 = e_start; e0 < rows * vpr; e0 += kGatherThreads * kGatherUnroll) {
+    RowRound<V> q;
+    load_round<V>(q, src, row_bytes, vpr, rows, row0, e0);
+    store_round<V>(q, dst, row_bytes, A, s_dst);
+  }
+}
+
+// The whole call for small count matrices, in input order: workgroup b owns
+// the input rows [b * rows_per_wg, ...). It issues the loads of its first
+// round of token vectors (and its scale pieces and weights) before anything
+// else, then computes the offsets of the whole matrix in its LDS, with the
+// output row of each of its input rows (the row map of the other direction),
+// and stores everything there. The row loads and the count loads are in
+// flight together, so a small call waits for one memory round trip before
+// its offsets rather than two.
 template <int V, int kSV, bool kScatter, bool kWeight, typename CountT>
 __global__ __launch_bounds__(kGatherThreads) void fused_kernel(GatherArgs p, FusedArgs f) {
   extern __shared__ int32_t s_dyn[];
-  __shared__ int32_t s_src[kMaxRowsPerWg];
+  __shared__ int32_t s_dst[kGatherThreads];                       // output row of input row row0 + t
+  __shared__ int32_t s_mark[kGatherThreads + kGatherThreads / 64];  // row marks, then wave maxima
   __shared__ ScanShared<kGatherThreads> sh;
+  const int tid = threadIdx.x;
   const int N = static_cast<int>(p.N);
   const int E = static_cast<int>(p.E);
-  auto* tab = reinterpret_cast<pair_t*>(s_dyn);  // [M + 1], first: 8-byte aligned
-  int32_t* mats = s_dyn + 2 * (p.M + 1);         // counts and source offsets, [M] each
-  int32_t* col = mats + 2 * p.M;                 // [E + 1]
+  const int row0 = blockIdx.x * p.rows_per_wg;
+  const int rows = min(p.rows_per_wg, p.A - row0);  // >= 1: the grid covers [0, A) exactly
+  const int64_t Rs = p.scale_row_bytes;
+
+  RowRound<V> q;
+  load_round<V>(q, p.tokens, p.row_bytes, p.vecs_per_row, rows, row0, 0);
+  using ST = typename VecT<(kSV > 0 ? kSV : 4)>::type;
+  ST piece{};
+  int sc_row = 0, sc_off = 0;
+  bool sc_in = false;
+  if (kSV > 0) {
+    const int spr = static_cast<int>(Rs / kSV);  // pieces per scale row
+    sc_row = tid / spr;
+    sc_off = (tid - sc_row * spr) * kSV;
+    sc_in = tid < rows * spr;
+    const int64_t off = sc_in ? int64_t(row0 + sc_row) * Rs + sc_off : 0;
+    piece = __builtin_nontemporal_load(reinterpret_cast<const ST*>(p.scales + off));
+  }
+  uint32_t wv = 0;
+  if (kWeight) wv = p.weight[tid < rows ? row0 + tid : row0];
+
+  int32_t* mats = s_dyn + 2 * (p.M + 1);  // counts and source offsets, [M] each
+  int32_t* col = mats + 2 * p.M;          // [E + 1]
   int64_t total = 0;
   const uint32_t flags =
-      offsets_cells<kGatherThreads>(static_cast<const CountT*>(f.counts), N, E, p.A, p.inverse, mats, col, tab,
-                                    &sh, &total);
+      offsets_cells<kGatherThreads>(static_cast<const CountT*>(f.counts), N, E, p.A, p.inverse ? 0 : 1, mats, col,
+                                    nullptr, &sh, &total, nullptr, row0, s_mark, s_dst);
   if (blockIdx.x == 0) {
     if (flags == 0) write_etn<kGatherThreads>(col, E, f.cumsum, static_cast<CountT*>(f.etn));
-    if (threadIdx.x == 0) write_header(p.hdr, p.A, p.N, p.E, total, flags, kCountsValid, p.inverse);
+    if (tid == 0) write_header(p.hdr, p.A, p.N, p.E, total, flags, kCountsValid, p.inverse);
   }
   if (flags != 0) return;  // uniform: nothing is written for rejected counts
+  __syncthreads();         // every thread's s_dst entry
 
-  const int row0 = blockIdx.x * p.rows_per_wg;
-  const int rows = min(p.rows_per_wg, p.A - row0);
-  map_rows(tab, p.M, p.A, row0, rows, s_src);
-  __syncthreads();
-  move_rows<V, kSV, kScatter, kWeight>(p, row0, rows, s_src);
+  store_round<V>(q, p.out_tokens, p.row_bytes, p.A, s_dst);
+  scatter_rows<V>(p.tokens, p.out_tokens, p.row_bytes, p.vecs_per_row, rows, row0, p.A, s_dst,
+                  kGatherThreads * kGatherUnroll);
+  if (kSV > 0 && sc_in) {
+    const int32_t d = s_dst[sc_row];
+    if (static_cast<unsigned>(d) < static_cast<unsigned>(p.A))
+      __builtin_nontemporal_store(piece, reinterpret_cast<ST*>(p.out_scales + int64_t(d) * Rs + sc_off));
+  }
+  if (tid < rows) {
+    const int32_t d = s_dst[tid];
+    const int s = row0 + tid;
+    if (static_cast<unsigned>(d) < static_cast<unsigned>(p.A)) {
+      if (kScatter)
+        p.idx[s] = d;
+      else
+        p.idx[d] = s;
+      if (kWeight) p.out_weight[d] = wv;
+    }
+  }
+  if (kSV == 0 && Rs > 0) {
+    const int spr = p.scale_vecs_per_row;
+    switch (p.scale_vec) {
+      case 16: scatter_rows<16>(p.scales, p.out_scales, Rs, spr, rows, row0, p.A, s_dst); break;
+      case 8: scatter_rows<8>(p.scales, p.out_scales, Rs, spr, rows, row0, p.A, s_dst); break;
+      case 4: scatter_rows<4>(p.scales, p.out_scales, Rs, spr, rows, row0, p.A, s_dst); break;
+      case 2: scatter_rows<2>(p.scales, p.out_scales, Rs, spr, rows, row0, p.A, s_dst); break;
+      default: scatter_rows<1>(p.scales, p.out_scales, Rs, spr, rows, row0, p.A, s_dst); break;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
