@@ -53,7 +53,9 @@
 //     in input order: every workgroup loads its own input rows first, then
 //     recomputes the offsets in its own LDS (a few KiB, read from L2) with
 //     the output row of each of its input rows, and stores the rows there;
-//     workgroup 0 also writes expert_token_num and the status.
+//     workgroup 0 also writes expert_token_num and the status. Up to 64
+//     cells, every wave computes the offsets in its registers (DPP scans,
+//     lane shuffles, a six-step search) with no barrier.
 // No atomics on global memory; every output element is written exactly once,
 // so results are deterministic.
 #include <hip/hip_runtime.h>
@@ -1470,6 +1472,69 @@ struct FusedArgs {
   int32_t cumsum;
 };
 
+// Offsets of a count matrix of at most 64 cells inside one wave, with no LDS
+// and no barrier (every wave of a workgroup computes them alike). Lane q
+// holds row-major cell q = i*E + j; lane u holds column-major cell u = j*N + i.
+struct WaveCells {
+  uint32_t src;     // lane q: SrcOffset of cell q
+  uint32_t dst;     // lane q: DstOffset of cell q
+  uint32_t dst_cm;  // lane u: DstOffset of cell u
+  uint32_t src_cm;  // lane u: SrcOffset of cell u
+  int first_row;    // lane u: 1 when cell u is in rank 0 (DstOffset(0, j) is an expert's start)
+  int expert;       // lane u: its expert j
+};
+
+// Returns the rejection flags (the same in every lane) and, in *total, the
+// exact sum of the clamped counts. All 64 lanes must be active.
+template <typename CountT>
+__device__ __forceinline__ uint32_t wave_offsets64(const CountT* __restrict__ counts, int N, int E, int64_t A,
+                                                   WaveCells* w, int64_t* total) {
+  const int lane = threadIdx.x & 63;
+  const int M = N * E;
+  uint32_t f = 0;
+  const uint32_t c = lane < M ? static_cast<uint32_t>(clamp_count(counts[lane], &f)) : 0u;
+  const uint64_t tot = wave_sum_u36(c);
+  uint32_t flags = tot != static_cast<uint64_t>(A) ? kFlagSumMismatch : 0u;
+  if (__builtin_amdgcn_ballot_w64((f & kFlagNegative) != 0) != 0) flags |= kFlagNegative;
+  if (__builtin_amdgcn_ballot_w64((f & kFlagTooLarge) != 0) != 0) flags |= kFlagTooLarge;
+  *total = static_cast<int64_t>(tot);
+  // Exact when flags == 0: the total is A <= INT32_MAX and no count is negative.
+  w->src = wave_scan_u32(c) - c;
+  const bool in = lane < M;
+  const int ju = div_small(lane, 1.0f / static_cast<float>(N));  // lane u = ju * N + iu
+  const int iu = lane - ju * N;
+  const int q_of_u = in ? iu * E + ju : lane;
+  const uint32_t c_u = static_cast<uint32_t>(__shfl(static_cast<int>(c), q_of_u));  // every lane takes part
+  const uint32_t cu = in ? c_u : 0u;
+  w->dst_cm = wave_scan_u32(cu) - cu;
+  w->src_cm = static_cast<uint32_t>(__shfl(static_cast<int>(w->src), q_of_u));
+  w->first_row = in && iu == 0;
+  w->expert = ju;
+  const int iq = div_small(lane, 1.0f / static_cast<float>(E));  // lane q = iq * E + jq
+  const int jq = lane - iq * E;
+  w->dst = static_cast<uint32_t>(__shfl(static_cast<int>(w->dst_cm), in ? jq * N + iq : lane));
+  return flags;
+}
+
+// Output row of input row s (< A) from the wave's cells: the last cell of the
+// input order that starts at or before s (empty cells share their start with
+// the next cell, so it is the one holding s). A branch-free six-step search
+// over the lanes; all 64 lanes must be active.
+__device__ __forceinline__ int32_t wave_map_row(const WaveCells& w, int M, int inverse, int32_t s) {
+  const uint32_t in_start = inverse ? w.dst_cm : w.src;   // input order: column-major when inverse
+  const uint32_t out_start = inverse ? w.src_cm : w.dst;
+  int k = 0;
+#pragma unroll
+  for (int b = 32; b >= 1; b >>= 1) {
+    const int cand = k + b;
+    const uint32_t v = static_cast<uint32_t>(__shfl(static_cast<int>(in_start), cand < M ? cand : 0));
+    if (cand < M && v <= static_cast<uint32_t>(s)) k = cand;
+  }
+  const uint32_t i0 = static_cast<uint32_t>(__shfl(static_cast<int>(in_start), k));
+  const uint32_t o0 = static_cast<uint32_t>(__shfl(static_cast<int>(out_start), k));
+  return static_cast<int32_t>(o0 + (static_cast<uint32_t>(s) - i0));
+}
+
 // Items [e0, e0 + kGatherThreads * kGatherUnroll) of `rows` input rows of
 // vpr vectors each, starting at input row row0, kGatherUnroll per thread
 // (item e is vector e % vpr of row e / vpr): the loads, and where each item
@@ -1575,15 +1640,32 @@ __global__ __launch_bounds__(kGatherThreads) void fused_kernel(GatherArgs p, Fus
   int32_t* mats = s_dyn + 2 * (p.M + 1);  // counts and source offsets, [M] each
   int32_t* col = mats + 2 * p.M;          // [E + 1]
   int64_t total = 0;
-  const uint32_t flags =
-      offsets_cells<kGatherThreads>(static_cast<const CountT*>(f.counts), N, E, p.A, p.inverse ? 0 : 1, mats, col,
-                                    nullptr, &sh, &total, nullptr, row0, s_mark, s_dst);
-  if (blockIdx.x == 0) {
-    if (flags == 0) write_etn<kGatherThreads>(col, E, f.cumsum, static_cast<CountT*>(f.etn));
-    if (tid == 0) write_header(p.hdr, p.A, p.N, p.E, total, flags, kCountsValid, p.inverse);
+  uint32_t flags;
+  if (p.M <= 64) {  // uniform: every wave computes the offsets by itself and maps its 64 rows
+    WaveCells w;
+    flags = wave_offsets64<CountT>(static_cast<const CountT*>(f.counts), N, E, p.A, &w, &total);
+    if (flags == 0) {
+      const int32_t s = row0 + tid;
+      const int32_t d = wave_map_row(w, p.M, p.inverse, s < p.A ? s : 0);
+      s_dst[tid] = s < p.A ? d : -1;
+      if (tid < 64) {
+        if (w.first_row) col[w.expert] = static_cast<int32_t>(w.dst_cm);
+        if (tid == 0) col[E] = static_cast<int32_t>(p.A);
+      }
+    }
+  } else {
+    flags = offsets_cells<kGatherThreads>(static_cast<const CountT*>(f.counts), N, E, p.A, p.inverse ? 0 : 1,
+                                          mats, col, nullptr, &sh, &total, nullptr, row0, s_mark, s_dst);
   }
-  if (flags != 0) return;  // uniform: nothing is written for rejected counts
-  __syncthreads();         // every thread's s_dst entry
+  if (flags != 0) {  // uniform: nothing is written for rejected counts
+    if (blockIdx.x == 0 && tid == 0) write_header(p.hdr, p.A, p.N, p.E, total, flags, kCountsValid, p.inverse);
+    return;
+  }
+  __syncthreads();  // every thread's s_dst entry, and the expert starts
+  if (blockIdx.x == 0) {
+    write_etn<kGatherThreads>(col, E, f.cumsum, static_cast<CountT*>(f.etn));
+    if (tid == 0) write_header(p.hdr, p.A, p.N, p.E, total, 0, kCountsValid, p.inverse);
+  }
 
   store_round<V>(q, p.out_tokens, p.row_bytes, p.A, s_dst);
   scatter_rows<V>(p.tokens, p.out_tokens, p.row_bytes, p.vecs_per_row, rows, row0, p.A, s_dst,
