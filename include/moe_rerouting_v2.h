@@ -165,15 +165,15 @@ mrr_status mrr_validate(const mrr_args* args, const void* workspace, size_t work
 /* How a call with these arguments is launched (filled by mrr_describe_plan). */
 typedef struct mrr_plan_info {
   int32_t fused;                 /* 1: moe_rerouting_v2 launches one kernel whose workgroups each
-                                    recompute the offsets of the (small) count matrix in LDS
-                                    (small calls); 0: it launches the offsets kernel, then the
-                                    gather kernel */
+                                    recompute the offsets of the (small) count matrix in LDS or
+                                    registers (small calls); 0: it launches the offsets kernel,
+                                    then the gather kernel */
   int32_t token_vec_bytes;       /* bytes per load/store of the token copy: 16, 8, 4, 2 or 1
                                     (16 also for rows that are no multiple of 16 bytes when the
                                     stream gather moves them as aligned 16-byte output blocks) */
   int32_t scale_vec_bytes;       /* the same for scale rows; 0 without scales */
-  int32_t rows_per_workgroup;    /* adjacent output rows per workgroup of the fused kernel or
-                                    the row-workgroup gather */
+  int32_t rows_per_workgroup;    /* adjacent rows per workgroup: input rows of the fused kernel,
+                                    output rows of the row-workgroup gather */
   int32_t threads_per_workgroup;
   int64_t gather_workgroups;
   int64_t token_row_bytes;
