@@ -19,6 +19,9 @@
 // stream gather, or else a table of int32 pairs in output order (forward:
 // cell j*N + i holds (dst_off, src_off); inverse: cell i*E + j holds
 // (src_off, dst_off)) for the row-workgroup gather.
+//   * offsets_regs_kernel (at most 64 cells): every wave computes the
+//     offsets in its registers and writes 64 rows of the row map, with no
+//     LDS and no barrier.
 //   * offsets_small_kernel (at most 256 cells) and offsets_staged_kernel (at
 //     most 1024): each workgroup stages the counts in LDS and scans them
 //     row-major then column-major; workgroup 0 writes the header,
@@ -1535,6 +1538,42 @@ __device__ __forceinline__ int32_t wave_map_row(const WaveCells& w, int M, int i
   return static_cast<int32_t>(o0 + (static_cast<uint32_t>(s) - i0));
 }
 
+// Offsets and the row map for count matrices of at most 64 cells, in
+// registers: every wave computes the offsets itself (wave_offsets64) and maps
+// its 64 output rows to their input rows with wave_map_row (the row map of a
+// direction is the input-to-output map of the other), with no LDS and no
+// barrier. Workgroups of 256 threads own 256 rows of the row map; wave 0 of
+// workgroup 0 also writes expert_token_num and the status.
+template <typename CountT>
+__global__ __launch_bounds__(256) void offsets_regs_kernel(
+    const CountT* __restrict__ counts, int32_t N, int32_t E, int64_t A, int cumsum, int inverse,
+    CountT* __restrict__ etn, WsHeader* __restrict__ hdr, int32_t* __restrict__ rowmap) {
+  const int lane = threadIdx.x & 63;
+  const bool lead = blockIdx.x == 0 && threadIdx.x < 64;
+  WaveCells w;
+  int64_t total = 0;
+  const uint32_t flags = wave_offsets64<CountT>(counts, N, E, A, &w, &total);
+  if (flags != 0) {  // the same in every wave: no row map
+    if (lead && lane == 0) write_header(hdr, A, N, E, total, flags, kTablesValid, inverse);
+    return;
+  }
+  const int M = N * E;
+  const int64_t d = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int32_t v = wave_map_row(w, M, inverse ? 0 : 1, d < A ? static_cast<int32_t>(d) : 0);
+  if (d < A) rowmap[d] = v;
+  if (lead) {
+    // expert j starts at the DstOffset of column-major cell j * N (rank 0)
+    for (int j0 = 0; j0 < E; j0 += 64) {
+      const int j = j0 + lane;
+      const int32_t cs = __shfl(static_cast<int>(w.dst_cm), j < E ? j * N : 0);
+      const int32_t cs1 = __shfl(static_cast<int>(w.dst_cm), j + 1 < E ? (j + 1) * N : 0);
+      const int32_t next = j + 1 < E ? cs1 : static_cast<int32_t>(A);
+      if (j < E) etn[j] = static_cast<CountT>(cumsum ? next : next - cs);
+    }
+    if (lane == 0) write_header(hdr, A, N, E, total, 0, kTablesValid, inverse);
+  }
+}
+
 // Items [e0, e0 + kGatherThreads * kGatherUnroll) of `rows` input rows of
 // vpr vectors each, starting at input row row0, kGatherUnroll per thread
 // (item e is vector e % vpr of row e / vpr): the loads, and where each item
@@ -1782,6 +1821,15 @@ mrr_status launch_offsets_t(const Plan& pl, const mrr_args* a, void* ws, hipStre
                        pl.cumsum ? 1 : 0, pl.inverse ? 1 : 0, static_cast<CountT*>(a->expert_token_num),
                        reinterpret_cast<WsHeader*>(base), reinterpret_cast<pair_t*>(base + pl.table_bytes),
                        pl.stream ? reinterpret_cast<int32_t*>(base + pl.rowmap_bytes) : nullptr, pl.band_split);
+    return hipGetLastError() == hipSuccess ? MRR_SUCCESS : MRR_ERROR_HIP;
+  }
+  if (pl.stream && pl.M <= 64) {
+    const unsigned grid = static_cast<unsigned>(std::max<int64_t>(1, (pl.A + kSmallCells - 1) / kSmallCells));
+    hipLaunchKernelGGL((offsets_regs_kernel<CountT>), dim3(grid), dim3(256), 0, stream,
+                       static_cast<const CountT*>(a->expert_token_num_per_rank), static_cast<int32_t>(pl.N),
+                       static_cast<int32_t>(pl.E), pl.A, pl.cumsum ? 1 : 0, pl.inverse ? 1 : 0,
+                       static_cast<CountT*>(a->expert_token_num), reinterpret_cast<WsHeader*>(base),
+                       reinterpret_cast<int32_t*>(base + pl.rowmap_bytes));
     return hipGetLastError() == hipSuccess ? MRR_SUCCESS : MRR_ERROR_HIP;
   }
   if (pl.stream && pl.M <= kSmallCells) {
