@@ -1270,6 +1270,8 @@ struct StreamGrid {
   float inv_svpr;
   uint32_t byte_rows;    // token rows stream as bytes: aligned 16-byte blocks of the output
   float inv_row;         // 1 / row bytes, for byte_rows with rows under 1 KiB
+  uint32_t rows8;        // byte_rows with R >= 147 and A >= 8: a 1 KiB chunk spans at most
+                         // floor(1023 / R) + 2 <= 8 rows
 };
 
 // The workspace header's verdict, read through the scalar cache: it was
@@ -1389,9 +1391,29 @@ __device__ __forceinline__ void stream_bytes_chunk(const GatherArgs& p, const St
   const int len1 = min(16, Ri - col1);  // bytes from row d1; the rest from row d1 + 1
   const bool has2 = len1 < 16;
   const int d2 = has2 ? min(d1 + 1, p.A - 1) : d1;
-  int32_t s1 = p.rowmap[d1];
-  int32_t s2 = p.rowmap[d2];
-  const bool ok = header_valid(p.hdr, p) & (static_cast<unsigned>(s1) < static_cast<unsigned>(p.A)) &
+  const bool hv = header_valid(p.hdr, p);  // its loads go out first, beside the row-map loads
+  int32_t s1, s2;
+  if (g.rows8) {  // uniform: the chunk's rows lie in 8 consecutive row-map words, read through the
+                  // scalar cache (beside the header loads) starting at min(d_base, A - 8)
+    using CInt = const int32_t __attribute__((address_space(4)))*;
+    const int base = min(static_cast<int>(d_base), p.A - 8);
+    const CInt m = reinterpret_cast<CInt>(reinterpret_cast<uintptr_t>(p.rowmap + base));
+    int32_t w[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w[k] = m[k];
+    const int k1 = d1 - base, k2 = d2 - base;  // in [0, 8)
+    s1 = w[0];
+    s2 = w[0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) {
+      s1 = k1 == k ? w[k] : s1;
+      s2 = k2 == k ? w[k] : s2;
+    }
+  } else {
+    s1 = p.rowmap[d1];
+    s2 = p.rowmap[d2];
+  }
+  const bool ok = hv & (static_cast<unsigned>(s1) < static_cast<unsigned>(p.A)) &
                   (static_cast<unsigned>(s2) < static_cast<unsigned>(p.A));
   s1 = ok ? s1 : 0;  // input row 0 when not moving: always valid here
   s2 = ok ? s2 : 0;
@@ -1962,6 +1984,7 @@ StreamGrid stream_grid(const Plan& pl) {
   sg.cpr_magic = 0;
   sg.byte_rows = pl.byte_rows ? 1u : 0u;
   sg.inv_row = 1.0f / static_cast<float>(pl.row_bytes);
+  sg.rows8 = pl.byte_rows && pl.row_bytes >= 147 && pl.A >= 8 ? 1u : 0u;
   if (!pl.byte_rows && pl.vecs_per_row % 64 == 0) {
     sg.cpr = static_cast<uint32_t>(pl.vecs_per_row / 64);
     sg.cpr_magic = sg.cpr == 1 ? 0u : static_cast<uint32_t>(((uint64_t(1) << 32) + sg.cpr - 1) / sg.cpr);
