@@ -31,8 +31,9 @@
 //   * offsets_banded_kernel (up to 2^17 cells, E <= 1024): the ranks are cut
 //     into bands; every workgroup sweeps the whole count matrix once for the
 //     validity flags and the column totals, then scans its own band and,
-//     split over a few workgroups per band, walks contiguous runs of input
-//     rows to write the row map (or writes its band's rows of the table).
+//     split over a few workgroups per band, writes the row map cell by cell
+//     (by a thread, a wave or the workgroups of the band, by cell size), or
+//     its band's rows of the table.
 //   * offsets_global_kernel: one workgroup scans through global memory, for
 //     count matrices too large for the others (no row map).
 // Gather phase:
@@ -739,11 +740,14 @@ __global__ __launch_bounds__(kOffsetThreads) void offsets_global_kernel(
 //     band cell). These scans start before step 2 ends (they need only the
 //     band's counts). Without a row map, each order's threads write their
 //     half of the cell's (DstOffset, SrcOffset) pair.
-//  4. With a row map, each workgroup of the band walks contiguous runs of
-//     its share of the band's source rows.
+//  4. With a row map, the workgroups of a band split its cells: a thread
+//     writes the rows of a cell of at most kBandCellRows rows, a wave those
+//     of a cell of at most kOffsetThreads rows, and every workgroup of the
+//     band its share of a larger cell's rows.
 // Every workgroup repeats step 1 over all M cells, which is why the per-cell
 // work is kept to a few instructions, and why the L2 reads grow as
 // M * (number of bands); the planner bounds M for this path.
+constexpr int kBandCellRows = 16;  // row-map rows a thread writes for one cell; larger cells take the workgroup
 constexpr int kBandUnroll = 16;  // count loads in flight per thread in step 1
 constexpr int kBandFanIn = 16;   // lanes' sums a column's thread adds up; more take a first LDS pass
 
@@ -761,6 +765,10 @@ struct BandShared {
   uint32_t flags;
   uint32_t above_all;
   uint64_t grand;
+  int32_t mid[kOffsetThreads];  // the workgroup's cells of (kBandCellRows, kOffsetThreads] rows
+  int32_t big[kOffsetThreads];  // and of more rows
+  int32_t nmid;
+  int32_t nbig;
 };
 
 
@@ -807,7 +815,11 @@ __global__ __launch_bounds__(kOffsetThreads) void offsets_banded_kernel(
   const int ES = E | 1;                     // LDS row stride of the band's counts
   const float inv_e = 1.0f / static_cast<float>(E);
   const float inv_rows = 1.0f / static_cast<float>(rows);
-  if (tid == 0) s.flags = 0;
+  if (tid == 0) {
+    s.flags = 0;
+    s.nmid = 0;
+    s.nbig = 0;
+  }
 
   // Step 1: per-lane column sums, and the band's counts.
   const int qi = div_small(tid, inv_e);  // row-major band cell q = tid: (qi, qj)
@@ -953,41 +965,56 @@ __global__ __launch_bounds__(kOffsetThreads) void offsets_banded_kernel(
     if (tid == cells - 1) s.src_q[cells] = static_cast<int32_t>(s.above_all + ex3[0] + cq);  // the band's end
   }
   if (rowmap != nullptr) {
-    // The row map for the band's rows: they are the source rows [S0, S1) in
-    // row-major cell order; each thread takes a contiguous slice, finds its
-    // first cell by a binary search over src_q and walks forward. Forward:
-    // output row DstOffset + k takes source row SrcOffset + k; inverse: the
-    // reverse (output rows are then the source rows, written contiguously).
+    // The row map for the band's cells: the workgroups of the band split its
+    // cells; a thread writes the rows of a cell with at most kBandCellRows
+    // rows itself, and the workgroup writes each larger cell's rows together,
+    // strided over all its threads. Forward: output row DstOffset + k takes
+    // source row SrcOffset + k; inverse: the reverse.
     __syncthreads();
-    const int rows_b = s.src_q[cells] - static_cast<int>(s.above_all);
-    const int per_slice = (rows_b + split - 1) / split;
-    const int S0 = static_cast<int>(s.above_all) + slice * per_slice;
-    const int S1 = static_cast<int>(s.above_all) + min(rows_b, (slice + 1) * per_slice);
-    const int Rt = (per_slice + kOffsetThreads - 1) / kOffsetThreads;
-    const int r0 = S0 + tid * Rt;
-    const int r1 = min(S1, r0 + Rt);
-    if (r0 < r1) {
-      int lo = 0, hi = cells;  // src_q[lo] <= r0 < src_q[hi]
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (s.src_q[mid] <= r0)
-          lo = mid;
-        else
-          hi = mid;
-      }
-      int q = lo;
-      int sq = s.src_q[q], dq = s.dst_q[q], next = s.src_q[q + 1];
-      for (int r = r0; r < r1; ++r) {
-        while (r >= next) {
-          ++q;
-          sq = next;
-          dq = s.dst_q[q];
-          next = s.src_q[q + 1];
+    {
+      const int per = (cells + split - 1) / split;
+      const int q = slice * per + tid;
+      if (tid < per && q < cells) {
+        const int sq = s.src_q[q], dq = s.dst_q[q], n = s.src_q[q + 1] - sq;
+        if (n <= kBandCellRows) {
+          for (int k = 0; k < n; ++k) {
+            if (inverse)
+              rowmap[sq + k] = dq + k;
+            else
+              rowmap[dq + k] = sq + k;
+          }
+        } else if (n <= kOffsetThreads) {
+          s.mid[atomicAdd(&s.nmid, 1)] = q;
         }
-        if (inverse)
-          rowmap[r] = dq + (r - sq);
-        else
-          rowmap[dq + (r - sq)] = r;
+      }
+      // cells of more than kOffsetThreads rows: every workgroup of the band
+      // takes its share of their rows
+      if (tid < cells && s.src_q[tid + 1] - s.src_q[tid] > kOffsetThreads) s.big[atomicAdd(&s.nbig, 1)] = tid;
+      __syncthreads();
+      const int nmid = s.nmid;
+      const int lane = tid & 63;
+      for (int b = tid >> 6; b < nmid; b += kOffsetThreads / 64) {  // one wave per cell
+        const int q2 = s.mid[b];
+        const int sq = s.src_q[q2], dq = s.dst_q[q2], n = s.src_q[q2 + 1] - sq;
+        for (int k = lane; k < n; k += 64) {
+          if (inverse)
+            rowmap[sq + k] = dq + k;
+          else
+            rowmap[dq + k] = sq + k;
+        }
+      }
+      const int nbig = s.nbig;
+      for (int b = 0; b < nbig; ++b) {  // uniform
+        const int q2 = s.big[b];
+        const int sq = s.src_q[q2], dq = s.dst_q[q2], n = s.src_q[q2 + 1] - sq;
+        const int share = (n + split - 1) / split;
+        const int k1 = min(n, (slice + 1) * share);
+        for (int k = slice * share + tid; k < k1; k += kOffsetThreads) {
+          if (inverse)
+            rowmap[sq + k] = dq + k;
+          else
+            rowmap[dq + k] = sq + k;
+        }
       }
     }
   }
