@@ -211,6 +211,29 @@ def test_offsets_banded_int64_cumsum():
     check(w, phases=True)
 
 
+# The banded kernel writes the row map cell by cell: a thread for cells of up
+# to 16 rows, a wave for cells of up to 1024 rows, every workgroup of the band
+# for larger ones. Mixed cell sizes put cells in all three classes, in several
+# bands and both directions.
+@pytest.mark.parametrize("direction", [_lib.FORWARD, _lib.INVERSE], ids=["forward", "inverse"])
+def test_offsets_banded_cell_sizes(direction):
+    rng = np.random.default_rng(77)
+    counts = rng.integers(0, 4, (64, 48)).astype(np.int32)
+    mid = rng.choice(counts.size, 60, replace=False)
+    counts.flat[mid] = rng.integers(17, 1025, 60)
+    counts[5, 7] = 5000        # larger than a workgroup
+    counts[40, 47] = 1025      # just above a wave's class
+    counts[33, 0] = 16         # the largest per-thread cell
+    counts[33, 1] = 17         # the smallest per-wave cell
+    a = int(counts.sum())
+    w = workloads.Workload("banded_cell_sizes", counts, rng.integers(-128, 128, (a, 48), dtype=np.int8), "int8", 48,
+                           rng.standard_normal(a, dtype=np.float32), "float32", rng.random((a, 1), dtype=np.float32),
+                           1, int(direction))
+    assert _offsets_workgroups(w, _dev()) > 1
+    check(w, direction=direction)
+    check(w, phases=True, direction=direction)
+
+
 # Rejected counts are seen by every workgroup of the banded kernel (each
 # reads the whole matrix); the bad cell sits in a band other than the first.
 @pytest.mark.parametrize("n,e,kind", [(64, 49, "negative"), (97, 96, "negative"), (256, 64, "too_large"),
