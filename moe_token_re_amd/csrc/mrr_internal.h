@@ -69,6 +69,7 @@ constexpr int kOffsetThreads = 1024;
 // Matrices of at most this many cells, when the row map is written, take
 // workgroups of this many threads (one per that many rows).
 constexpr int kSmallOffsetCells = 256;
+constexpr int kMidOffsetCells = 512;  // 256 < N*E <= 512: the same kernel with 512 threads
 constexpr int64_t kBandMaxCells = int64_t(1) << 17;
 
 // The stream gather kernel launches one workgroup per chunk; calls with more

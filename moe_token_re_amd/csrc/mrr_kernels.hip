@@ -22,7 +22,7 @@
 //   * offsets_regs_kernel (at most 64 cells): every wave computes the
 //     offsets in its registers and writes 64 rows of the row map, with no
 //     LDS and no barrier.
-//   * offsets_small_kernel (at most 256 cells) and offsets_staged_kernel (at
+//   * offsets_small_kernel (at most 256 or 512 cells) and offsets_staged_kernel (at
 //     most 1024): each workgroup stages the counts in LDS and scans them
 //     row-major then column-major; workgroup 0 writes the header,
 //     expert_token_num and any table, and every workgroup writes its slice of
@@ -583,28 +583,28 @@ __global__ __launch_bounds__(kOffsetThreads) void offsets_staged_kernel(
   if (threadIdx.x == 0) write_header(hdr, A, N, E, total, flags, kTablesValid, inverse);
 }
 
-// Offsets and the row map for count matrices of at most kSmallCells cells:
-// the same work as offsets_staged_kernel<CountT, 1> in workgroups of
-// kSmallCells threads (short workgroup scans), one per kSmallCells rows of
-// the row map; workgroup 0 also writes expert_token_num and the status. No
-// table: the gather that follows reads the row map only.
+// Offsets and the row map for count matrices of at most kT cells (kT = 256
+// or 512): the same work as offsets_staged_kernel<CountT, 1> in workgroups of
+// kT threads (shorter workgroup scans and barriers than its 1024), one per
+// kT rows of the row map; workgroup 0 also writes expert_token_num and the
+// status. No table: the gather that follows reads the row map only.
 constexpr int kSmallCells = kSmallOffsetCells;
 
-template <typename CountT>
-__global__ __launch_bounds__(kSmallCells) void offsets_small_kernel(
+template <typename CountT, int kT>
+__global__ __launch_bounds__(kT) void offsets_small_kernel(
     const CountT* __restrict__ counts, int32_t N, int32_t E, int64_t A, int cumsum, int inverse,
     CountT* __restrict__ etn, WsHeader* __restrict__ hdr, int32_t* __restrict__ rowmap) {
-  __shared__ int32_t s_mats[2 * kSmallCells];
-  __shared__ int32_t s_col[kSmallCells + 1];
-  __shared__ ScanShared<kSmallCells> sh;
-  __shared__ int32_t s_mark[kSmallCells + kSmallCells / 64];  // row marks, then wave maxima
+  __shared__ int32_t s_mats[2 * kT];
+  __shared__ int32_t s_col[kT + 1];
+  __shared__ ScanShared<kT> sh;
+  __shared__ int32_t s_mark[kT + kT / 64];  // row marks, then wave maxima
   const bool lead = blockIdx.x == 0;
   int64_t total = 0;
   const uint32_t flags =
-      offsets_cells<kSmallCells>(counts, N, E, A, inverse, s_mats, s_col, nullptr, &sh, &total, rowmap,
-                                 static_cast<int>(blockIdx.x) * kSmallCells, s_mark);
+      offsets_cells<kT>(counts, N, E, A, inverse, s_mats, s_col, nullptr, &sh, &total, rowmap,
+                        static_cast<int>(blockIdx.x) * kT, s_mark);
   if (!lead) return;
-  if (flags == 0) write_etn<kSmallCells>(s_col, E, cumsum, etn);
+  if (flags == 0) write_etn<kT>(s_col, E, cumsum, etn);
   if (threadIdx.x == 0) write_header(hdr, A, N, E, total, flags, kTablesValid, inverse);
 }
 
@@ -1883,7 +1883,17 @@ mrr_status launch_offsets_t(const Plan& pl, const mrr_args* a, void* ws, hipStre
   }
   if (pl.stream && pl.M <= kSmallCells) {
     const unsigned grid = static_cast<unsigned>(std::max<int64_t>(1, (pl.A + kSmallCells - 1) / kSmallCells));
-    hipLaunchKernelGGL((offsets_small_kernel<CountT>), dim3(grid), dim3(kSmallCells), 0, stream,
+    hipLaunchKernelGGL((offsets_small_kernel<CountT, kSmallCells>), dim3(grid), dim3(kSmallCells), 0, stream,
+                       static_cast<const CountT*>(a->expert_token_num_per_rank), static_cast<int32_t>(pl.N),
+                       static_cast<int32_t>(pl.E), pl.A, pl.cumsum ? 1 : 0, pl.inverse ? 1 : 0,
+                       static_cast<CountT*>(a->expert_token_num), reinterpret_cast<WsHeader*>(base),
+                       reinterpret_cast<int32_t*>(base + pl.rowmap_bytes));
+    return hipGetLastError() == hipSuccess ? MRR_SUCCESS : MRR_ERROR_HIP;
+  }
+  if (pl.stream && pl.M <= kMidOffsetCells) {
+    const unsigned grid =
+        static_cast<unsigned>(std::max<int64_t>(1, (pl.A + kMidOffsetCells - 1) / kMidOffsetCells));
+    hipLaunchKernelGGL((offsets_small_kernel<CountT, kMidOffsetCells>), dim3(grid), dim3(kMidOffsetCells), 0, stream,
                        static_cast<const CountT*>(a->expert_token_num_per_rank), static_cast<int32_t>(pl.N),
                        static_cast<int32_t>(pl.E), pl.A, pl.cumsum ? 1 : 0, pl.inverse ? 1 : 0,
                        static_cast<CountT*>(a->expert_token_num), reinterpret_cast<WsHeader*>(base),

@@ -316,6 +316,8 @@ extern "C" mrr_status mrr_describe_plan(const mrr_args* args, const void* worksp
                            : !plan.stream ? 1
                            : plan.M <= mrr::kSmallOffsetCells
                                ? std::max<int64_t>(1, (plan.A + mrr::kSmallOffsetCells - 1) / mrr::kSmallOffsetCells)
+                           : plan.M <= mrr::kMidOffsetCells
+                               ? std::max<int64_t>(1, (plan.A + mrr::kMidOffsetCells - 1) / mrr::kMidOffsetCells)
                                : std::max<int64_t>(1, (plan.A + mrr::kOffsetThreads - 1) / mrr::kOffsetThreads);
   info->gather_kernel = plan.stream ? 1 : 0;
   return MRR_SUCCESS;

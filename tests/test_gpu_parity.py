@@ -174,13 +174,15 @@ def _offsets_workgroups(w, dev):
 # 9 and 17 cells per thread (each class's lower and upper edge), and beyond
 # 17408 cells the path through global memory.
 @pytest.mark.parametrize("n,e", [(32, 32), (1, 1024), (2, 1025), (1, 3000), (4, 1280), (3, 1700), (5, 1100),
-                                 (8, 1152), (9, 1100), (16, 1088), (17, 1025), (130, 1040), (520, 256)])
+                                 (8, 1152), (9, 1100), (16, 1088), (17, 1025), (130, 1040), (520, 256),
+                                 (17, 16), (16, 32), (32, 16), (1, 512), (513, 1), (19, 27)])
 def test_offsets_single_workgroup(n, e):
     w = workloads.random_case(n * 7 + e, n, e, 40, tokens_dtype="int8", count_range=(0, 4), weight=True,
                               idx_type=(n + e) % 2, etn_type=(n * e) % 2)
-    # one workgroup; with the row map (one cell per thread), one per 256 rows up to 256 cells, else
-    # one per 1024 rows
-    want = 1 if n * e > 1024 else max(1, -(-w.A // (256 if n * e <= 256 else 1024)))
+    # one workgroup; with the row map (one cell per thread), one per 256 rows up to 256 cells, one
+    # per 512 rows up to 512 cells, else one per 1024 rows
+    rows = 256 if n * e <= 256 else 512 if n * e <= 512 else 1024
+    want = 1 if n * e > 1024 else max(1, -(-w.A // rows))
     assert _offsets_workgroups(w, _dev()) == want
     check(w)
     check(w, phases=True)
