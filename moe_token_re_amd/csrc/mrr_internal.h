@@ -81,6 +81,10 @@ constexpr int64_t kMaxStreamGrid = int64_t(1) << 31;
 // could run them (measured with 7168-byte rows: the single kernel is 1 us
 // faster at 17 MB, 0.2 us at 36 MB, 1.1 us slower at 54 MB).
 constexpr int64_t kFusedMaxTokenBytes = int64_t(48) << 20;
+// The same for count matrices of at most 64 cells, whose two-kernel path has
+// the cheaper register offsets kernel (8x8 counts, 7168-byte rows: the single
+// kernel is 0.7 us faster at 16 MB, 0.3 us at 23 MB, 0.75 us slower at 32 MB).
+constexpr int64_t kFusedMaxTokenBytesFewCells = int64_t(28) << 20;
 // The same for rows the stream gather moves as aligned 16-byte blocks while
 // the single kernel would move them in narrow vectors.
 constexpr int64_t kFusedMaxByteRowBytes = int64_t(4) << 20;

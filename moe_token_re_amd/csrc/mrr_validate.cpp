@@ -273,7 +273,8 @@ mrr_status make_plan(const mrr_args* a, const void* ws, size_t ws_bytes, Plan* p
   // The single-kernel path saves a launch; the two-kernel path's stream
   // gather streams faster. The launch matters less than the rate from a few
   // tens of MiB of rows on.
-  if (q.fused && q.stream && q.A * q.row_bytes >= kFusedMaxTokenBytes) q.fused = false;
+  if (q.fused && q.stream && q.A * q.row_bytes >= (M <= 64 ? kFusedMaxTokenBytesFewCells : kFusedMaxTokenBytes))
+    q.fused = false;
   if (q.fused && q.byte_rows && q.A * q.row_bytes >= kFusedMaxByteRowBytes) q.fused = false;
   q.table_bytes = kHeaderBytes;
   q.rowmap_bytes = kHeaderBytes + round_up(8 * (static_cast<size_t>(M) + 1), 256);
