@@ -240,6 +240,31 @@ def test_describe_plan():
         _lib.ERROR_INVALID_VALUE
 
 
+def test_plan_size_classes():
+    """The launch choices by count-matrix size and token bytes (launch shape
+    only; every choice computes the same bytes)."""
+    mib = 1 << 20
+    below28, above28, above48 = 28 * mib // 7168 - 1, 28 * mib // 7168 + 1, 48 * mib // 7168 + 1  # 7168-byte rows
+    # at most 64 cells: one kernel below 28 MiB of token rows, else offsets + gather
+    for n, e in [(8, 8), (4, 4), (1, 64)]:
+        st, info = describe(valid_args(A=below28, H=7168, N=n, E=e, tok=_lib.I8))
+        assert st == _lib.SUCCESS and info.fused == 1, (n, e)
+        st, info = describe(valid_args(A=above28, H=7168, N=n, E=e, tok=_lib.I8))
+        assert st == _lib.SUCCESS and info.fused == 0 and info.gather_kernel == 1, (n, e)
+        assert info.offsets_workgroups == -(-above28 // 256)
+    # 65..256 cells: the same below 48 MiB
+    st, info = describe(valid_args(A=above28, H=7168, N=16, E=16, tok=_lib.I8))
+    assert st == _lib.SUCCESS and info.fused == 1
+    st, info = describe(valid_args(A=above48, H=7168, N=16, E=16, tok=_lib.I8))
+    assert st == _lib.SUCCESS and info.fused == 0 and info.offsets_workgroups == -(-above48 // 256)
+    # 257..512 cells: offsets + gather, the offsets in 512-thread workgroups of 512 rows
+    st, info = describe(valid_args(A=3000, H=7168, N=16, E=32, tok=_lib.I8))
+    assert st == _lib.SUCCESS and info.fused == 0 and info.offsets_workgroups == -(-3000 // 512)
+    # 513..1024 cells: 1024-thread workgroups of 1024 rows
+    st, info = describe(valid_args(A=3000, H=7168, N=32, E=32, tok=_lib.I8))
+    assert st == _lib.SUCCESS and info.fused == 0 and info.offsets_workgroups == -(-3000 // 1024)
+
+
 def test_int64_counts_alignment():
     a = valid_args(cnt=_lib.I64)
     assert validate(a) == _lib.SUCCESS
