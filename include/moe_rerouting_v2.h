@@ -182,7 +182,7 @@ typedef struct mrr_plan_info {
                                     the token rows; 0: in a separate pass after them */
   int64_t offsets_workgroups;    /* workgroups of moe_rerouting_v2_offsets(): several for larger
                                     count matrices (bands of ranks) or when the row map is
-                                    written (one workgroup per 256 or 1024 rows); 1 otherwise;
+                                    written (one workgroup per 256, 512 or 1024 rows); 1 otherwise;
                                     0 when there are no cells */
   int32_t gather_kernel;         /* what moe_rerouting_v2_gather() launches: 1 = 64-lane
                                     workgroups, each moving 64 vectors of one output stream
