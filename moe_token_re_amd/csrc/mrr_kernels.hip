@@ -27,7 +27,7 @@
 //     row-major then column-major; workgroup 0 writes the header,
 //     expert_token_num and any table, and every workgroup writes its slice of
 //     the row map, one row per thread: each cell marks where its rows start
-//     and a workgroup running maximum gives every row its cell.
+//     and a wave running maximum gives every row its cell.
 //   * offsets_banded_kernel (up to 2^17 cells, E <= 1024): the ranks are cut
 //     into bands; every workgroup sweeps the whole count matrix once for the
 //     validity flags and the column totals, then scans its own band and,
@@ -256,30 +256,21 @@ __device__ __forceinline__ int div_small(int t, float inv) {
   return static_cast<int>((static_cast<float>(t) + 0.5f) * inv);
 }
 
-// Inclusive running maximum of v over the workgroup (thread order), for
-// values >= -1: DPP row shifts within each row of 16 lanes, the row maxima of
-// the wave by readlane, then the wave maxima through LDS (s_w holds
-// kThreads / 64 entries) behind one barrier. Every lane must be active.
-template <int kThreads>
-__device__ __forceinline__ int32_t block_max_scan(int32_t v, int32_t* s_w) {
+// Inclusive running maximum of v over the 64 lanes of a wave (values >= -1),
+// with no LDS. Every lane must be active.
+__device__ __forceinline__ int32_t wave_max_scan(int32_t v) {
   constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
   v = max(v, __builtin_amdgcn_update_dpp(-1, v, kRowShr1, 0xf, 0xf, false));
   v = max(v, __builtin_amdgcn_update_dpp(-1, v, kRowShr2, 0xf, 0xf, false));
   v = max(v, __builtin_amdgcn_update_dpp(-1, v, kRowShr4, 0xf, 0xf, false));
   v = max(v, __builtin_amdgcn_update_dpp(-1, v, kRowShr8, 0xf, 0xf, false));
-  const int lane = threadIdx.x & 63;
-  const int row = lane >> 4;
+  const int row = (threadIdx.x & 63) >> 4;
   const int32_t r0 = __builtin_amdgcn_readlane(v, 15);
   const int32_t r1 = __builtin_amdgcn_readlane(v, 31);
   const int32_t r2 = __builtin_amdgcn_readlane(v, 47);
   v = max(v, row >= 1 ? r0 : -1);
   v = max(v, row >= 2 ? r1 : -1);
-  v = max(v, row >= 3 ? r2 : -1);
-  const int wave = threadIdx.x >> 6;
-  if (lane == 63) s_w[wave] = v;
-  __syncthreads();
-  for (int k = 0; k < wave; ++k) v = max(v, s_w[k]);
-  return v;
+  return max(v, row >= 3 ? r2 : -1);
 }
 
 // Writes the end-of-table entries and finishes: tab[M] = (A, A), col[E] = A.
@@ -358,21 +349,26 @@ __device__ uint32_t offsets_cells(const CountT* __restrict__ counts, int N, int 
     if (mapping && c2 > 0) {
       // Mark where this cell's rows start among the workgroup's output rows
       // [row0, row0 + kThreads), by its output-order index (forward: this
-      // column-major index; inverse: the row-major one), or at 0 if it covers
-      // row0 from before. Output-order indices rise with the output offset,
-      // so a running maximum over the marks gives each row its cell.
+      // column-major index; inverse: the row-major one). Each wave's 64 rows
+      // are marked on their own: the cell that covers a wave's first row from
+      // before marks that row. Output-order indices rise with the output
+      // offset, so a running maximum over each wave's marks gives each row
+      // its cell, with no exchange between waves.
       const int32_t out_off = inverse ? s_s[tid] : static_cast<int32_t>(dst);
       const int lo = out_off - row0;
       const int o = inverse ? i * E + j : tid;
-      if (lo >= 0 && lo < kThreads)
-        s_mark[lo] = o;
-      else if (lo < 0 && out_off + static_cast<int32_t>(c2) > row0)
-        s_mark[0] = o;
+      if (lo >= 0 && lo < kThreads) s_mark[lo] = o;
+      const int32_t end = out_off + static_cast<int32_t>(c2);
+#pragma unroll
+      for (int w = 0; w < kThreads / 64; ++w) {
+        const int first = row0 + 64 * w;  // wave w's first row
+        if (out_off < first && end > first) s_mark[64 * w] = o;
+      }
     }
   }
   finish_offsets(tab, col, M, E, A);
   if (mapping) {
-    const int o = block_max_scan<kThreads>(s_mark[tid], s_mark + kThreads);
+    const int o = wave_max_scan(s_mark[tid]);
     const int d = row0 + tid;
     int32_t v = -1;
     if (d < A) {
@@ -597,7 +593,7 @@ __global__ __launch_bounds__(kT) void offsets_small_kernel(
   __shared__ int32_t s_mats[2 * kT];
   __shared__ int32_t s_col[kT + 1];
   __shared__ ScanShared<kT> sh;
-  __shared__ int32_t s_mark[kT + kT / 64];  // row marks, then wave maxima
+  __shared__ int32_t s_mark[kT];  // row marks
   const bool lead = blockIdx.x == 0;
   int64_t total = 0;
   const uint32_t flags =
@@ -1699,7 +1695,7 @@ template <int V, int kSV, bool kScatter, bool kWeight, typename CountT>
 __global__ __launch_bounds__(kGatherThreads) void fused_kernel(GatherArgs p, FusedArgs f) {
   extern __shared__ int32_t s_dyn[];
   __shared__ int32_t s_dst[kGatherThreads];                       // output row of input row row0 + t
-  __shared__ int32_t s_mark[kGatherThreads + kGatherThreads / 64];  // row marks, then wave maxima
+  __shared__ int32_t s_mark[kGatherThreads];  // row marks
   __shared__ ScanShared<kGatherThreads> sh;
   const int tid = threadIdx.x;
   const int N = static_cast<int>(p.N);
@@ -1850,8 +1846,8 @@ void launch_staged(const Plan& pl, const mrr_args* a, uint8_t* base, size_t lds,
   const unsigned grid =
       kC == 1 && pl.stream ? static_cast<unsigned>(std::max<int64_t>(1, (pl.A + kOffsetThreads - 1) / kOffsetThreads))
                            : 1u;
-  // one cell per thread with a row map: the row marks and wave maxima after col
-  const size_t dyn = lds + (kC == 1 && pl.stream ? 4 * static_cast<size_t>(kOffsetThreads + kOffsetThreads / 64) : 0);
+  // one cell per thread with a row map: the row marks after col
+  const size_t dyn = lds + (kC == 1 && pl.stream ? 4 * static_cast<size_t>(kOffsetThreads) : 0);
   hipLaunchKernelGGL((offsets_staged_kernel<CountT, kC>), dim3(grid), dim3(kOffsetThreads), dyn, stream,
                      static_cast<const CountT*>(a->expert_token_num_per_rank), static_cast<int32_t>(pl.N),
                      static_cast<int32_t>(pl.E), pl.A, pl.cumsum ? 1 : 0, pl.inverse ? 1 : 0,
