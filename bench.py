@@ -36,7 +36,6 @@ from __future__ import annotations
 
 import argparse
 import ctypes
-import hashlib
 import json
 import math
 import os
@@ -52,16 +51,14 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 METRIC = "re-route GB/s (bytes read+written) and % of HBM peak; µs/call A=16384 H=7168"
 PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "stream_gather_pages_shape_counters.txt")
-KERNEL_SOURCES = [os.path.join(ROOT, "moe_token_re_amd", "csrc", f)
-                  for f in ("mrr_kernels.hip", "mrr_internal.h", "mrr_validate.cpp")]
 
 
 def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+    """The hash of the library's current sources (the loaded library carries
+    the same one, or loading it fails)."""
+    from moe_token_re_amd import build
+
+    return build.source_hash()
 
 
 def bench_copy_lib():
@@ -391,7 +388,7 @@ def main():
                      "launch_us_mean": round(kern_mean_us, 2)},
         "copy_ceiling": ceiling,
         "cpu_baseline": cpu,
-        "kernel_source_hash": kernel_source_hash(),
+        "library_source_hash": _lib.library_source_hash(),
         "device": device,
     }
     print(json.dumps(line), flush=True)

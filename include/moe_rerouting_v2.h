@@ -189,6 +189,10 @@ typedef struct mrr_plan_info {
                                     (token rows, scale rows, per-row items) with the row map
                                     the offsets phase wrote; 0 = workgroups of whole rows that
                                     search the offsets table */
+  int64_t gather_launches;       /* kernel launches of the gather phase: 1, or more when its
+                                    workgroups hold 2^32 or more threads in all (a launch holds
+                                    at most 2^32 - 1), each piece taking the next workgroups;
+                                    0 when A == 0 */
 } mrr_plan_info;
 
 /*
@@ -242,8 +246,15 @@ mrr_status moe_rerouting_v2_gather(const mrr_args* args, void* workspace, size_t
  */
 mrr_status mrr_get_device_status(const void* workspace, struct ihipStream_t* stream);
 
-/* A static, human-readable name of a status code. */
+/* A static, human-readable name of a status code. (A convention of this
+ * library; the article defines no error codes.) */
 const char* mrr_status_string(mrr_status status);
+
+/* The identity of the sources this library was built from: 16 hex digits of
+ * a SHA-256 over the source files, fixed at build time, in static storage.
+ * (A convention of this library: loaders compare it with the sources they
+ * ship with and refuse a library built from others.) */
+const char* mrr_source_hash(void);
 
 #ifdef __cplusplus
 }

@@ -30,7 +30,8 @@ INVERSE = 1
 F16, BF16, I8, F8_E5M2, F8_E4M3FN, HIF8, F4_E2M1, F4_E1M2, I32, I64, F32, F8_E8M0 = range(12)
 
 EXPORTS = ("mrr_workspace_size", "mrr_validate", "mrr_describe_plan", "moe_rerouting_v2",
-           "moe_rerouting_v2_offsets", "moe_rerouting_v2_gather", "mrr_get_device_status", "mrr_status_string")
+           "moe_rerouting_v2_offsets", "moe_rerouting_v2_gather", "mrr_get_device_status", "mrr_status_string",
+           "mrr_source_hash")
 
 
 class MrrArgs(ctypes.Structure):
@@ -76,6 +77,7 @@ class MrrPlanInfo(ctypes.Structure):
         ("scale_inline_bytes", ctypes.c_int32),
         ("offsets_workgroups", ctypes.c_int64),
         ("gather_kernel", ctypes.c_int32),
+        ("gather_launches", ctypes.c_int64),
     ]
 
 
@@ -84,7 +86,8 @@ _lib = None
 
 
 def load() -> ctypes.CDLL:
-    """The loaded library; raises RuntimeError if it has not been built."""
+    """The loaded library; raises RuntimeError if it has not been built, or was
+    built from sources other than the ones beside it (mrr_source_hash)."""
     global _lib
     with _lock:
         if _lib is None:
@@ -92,7 +95,18 @@ def load() -> ctypes.CDLL:
                 raise RuntimeError(
                     f"{LIB_PATH} is missing: build it with `python -m moe_token_re_amd.build` "
                     "(there is no CPU fallback)")
+            from . import build
+
             lib = ctypes.CDLL(LIB_PATH)
+            if not hasattr(lib, "mrr_source_hash"):
+                raise RuntimeError(f"{LIB_PATH} carries no source hash: rebuild it "
+                                   "with `python -m moe_token_re_amd.build`")
+            lib.mrr_source_hash.argtypes = []
+            lib.mrr_source_hash.restype = ctypes.c_char_p
+            built, current = lib.mrr_source_hash().decode(), build.source_hash()
+            if built != current:
+                raise RuntimeError(f"{LIB_PATH} was built from other sources (hash {built}, sources {current}): "
+                                   "rebuild it with `python -m moe_token_re_amd.build`")
             P = ctypes.POINTER(MrrArgs)
             vp, sz = ctypes.c_void_p, ctypes.c_size_t
             lib.mrr_workspace_size.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int64]
@@ -111,6 +125,12 @@ def load() -> ctypes.CDLL:
             lib.mrr_status_string.restype = ctypes.c_char_p
             _lib = lib
         return _lib
+
+
+def library_source_hash() -> str:
+    """The source hash compiled into the loaded library (equal to the current
+    sources' hash, or load() would have refused it)."""
+    return load().mrr_source_hash().decode()
 
 
 def status_string(code: int) -> str:

@@ -152,6 +152,14 @@ def prepare(tokens, expert_token_num_per_rank, *, per_token_scales=None, expert_
             raise ValueError("expert_topk_weight must be 2-D [A, 1]")
         a.expert_topk_weight = _ptr(w)
 
+    # the outputs as InferShape gives them: (dtype, element count) each
+    sc, w = per_token_scales, expert_topk_weight
+    want = (("permute_tokens", tokens.dtype, tokens.numel()),
+            ("permute_per_token_scales", sc.dtype if sc is not None else torch.float32,
+             sc.numel() if sc is not None else A),
+            ("permute_token_idx", torch.int32, A),
+            ("expert_token_num", counts.dtype, E),
+            ("permute_topk_weight", torch.float32, w.numel() if w is not None else 0))
     if out is None:
         p_tok = torch.empty_like(tokens)
         p_sc = (torch.empty_like(per_token_scales) if per_token_scales is not None
@@ -161,6 +169,21 @@ def prepare(tokens, expert_token_num_per_rank, *, per_token_scales=None, expert_
         p_w = (torch.empty_like(expert_topk_weight) if expert_topk_weight is not None
                else torch.empty((0,), dtype=torch.float32, device=dev))
         out = (p_tok, p_sc, p_idx, p_etn, p_w)
+    else:
+        # The library sees only pointers: every output it writes must hold
+        # exactly the bytes InferShape gives it, densely, on this device.
+        if not isinstance(out, (tuple, list)) or len(out) != 5:
+            raise ValueError("out must be a 5-tuple like the result")
+        for t, (name, dtype, numel) in zip(out, want):
+            if name == "permute_per_token_scales" and per_token_scales is None:
+                continue  # never written when the scales are absent
+            if name == "permute_topk_weight" and expert_topk_weight is None:
+                continue  # never written when the weight is absent
+            _check_tensor(name, t, dev)
+            if t.dtype != dtype:
+                raise TypeError(f"out {name} has dtype {t.dtype}, expected {dtype}")
+            if t.numel() != numel:
+                raise ValueError(f"out {name} has {t.numel()} elements, expected {numel}")
     p_tok, p_sc, p_idx, p_etn, p_w = out
     a.permute_tokens = _ptr(p_tok)
     a.permute_per_token_scales = _ptr(p_sc) if per_token_scales is not None else None
@@ -185,7 +208,7 @@ class PreparedCall:
         self._lib = _lib.load()
         self._pargs = ctypes.byref(args)
         self._ws = workspace.data_ptr()
-        self._wsb = workspace.numel()
+        self._wsb = workspace.numel() * workspace.element_size()
         self._s = stream.cuda_stream
 
     def validate(self) -> int:
@@ -237,6 +260,8 @@ def make_call(tokens, expert_token_num_per_rank, *, per_token_scales=None, exper
     if need == 0:
         raise MrrValueError(_lib.ERROR_INVALID_SHAPE, "mrr_workspace_size")
     s = stream if stream is not None else torch.cuda.current_stream(dev)
+    if workspace is not None:
+        _check_tensor("workspace", workspace, dev)
     if workspace is None:
         workspace = torch.empty((need,), dtype=torch.uint8, device=dev)
         if s != torch.cuda.current_stream(dev):

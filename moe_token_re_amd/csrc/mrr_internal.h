@@ -1,6 +1,6 @@
 // mrr_internal.h -- shared between the host validation/planning code
 // (mrr_validate.cpp, which includes no HIP header) and the kernels and
-// launchers (mrr_kernels.hip). Not part of the public ABI.
+// launchers (the .hip files, through mrr_device.h). Not part of the public ABI.
 #pragma once
 
 #include <stddef.h>
@@ -72,9 +72,16 @@ constexpr int kSmallOffsetCells = 256;
 constexpr int kMidOffsetCells = 512;  // 256 < N*E <= 512: the same kernel with 512 threads
 constexpr int64_t kBandMaxCells = int64_t(1) << 17;
 
-// The stream gather kernel launches one workgroup per chunk; calls with more
-// chunks than this take the row-workgroup gather kernel instead.
+// The stream gather kernel has one workgroup per chunk and numbers chunks in
+// 32 bits; calls with more chunks than this take the row-workgroup gather
+// kernel instead.
 constexpr int64_t kMaxStreamGrid = int64_t(1) << 31;
+
+// A launch may hold at most 2^32 - 1 threads (grid x workgroup size), so a
+// gather with more workgroups than that is launched in pieces, each taking
+// the next workgroups in order.
+constexpr int64_t kMaxLaunchThreads = (int64_t(1) << 32) - 1;
+inline int64_t max_launch_grid(int64_t threads) { return kMaxLaunchThreads / threads; }
 
 // Calls whose token rows total at least this many bytes take the two-kernel
 // path (offsets, then the stream gather) even when the single-kernel path
@@ -139,6 +146,7 @@ struct Plan {
                             // (rows of 16 bytes or more that are no multiple of 16, both buffers
                             // 16-byte aligned)
   int64_t stream_grid;      // its workgroups: the total number of chunks
+  int64_t gather_launches;  // launches of the gather phase (pieces of at most max_launch_grid)
   int64_t band_grid;        // banded offsets kernel: workgroups (bands); 0 = single-workgroup kernel
   int band_rows;            // ranks per band: min(N, kOffsetThreads / E)
   int band_lanes;           // threads per column in the banded kernel's first step (a power of two)

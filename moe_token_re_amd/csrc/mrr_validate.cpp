@@ -95,6 +95,12 @@ extern "C" size_t mrr_workspace_size(int64_t A, int64_t N, int64_t E) {
   return mrr::kHeaderBytes + round_up(8 * (M + 1), 256) + round_up(4 * static_cast<size_t>(A), 256);
 }
 
+#ifndef MRR_SOURCE_HASH
+#define MRR_SOURCE_HASH "unknown"
+#endif
+
+extern "C" const char* mrr_source_hash(void) { return MRR_SOURCE_HASH; }
+
 extern "C" const char* mrr_status_string(mrr_status s) {
   switch (s) {
     case MRR_SUCCESS: return "MRR_SUCCESS";
@@ -276,6 +282,11 @@ mrr_status make_plan(const mrr_args* a, const void* ws, size_t ws_bytes, Plan* p
   if (q.fused && q.stream && q.A * q.row_bytes >= (M <= 64 ? kFusedMaxTokenBytesFewCells : kFusedMaxTokenBytes))
     q.fused = false;
   if (q.fused && q.byte_rows && q.A * q.row_bytes >= kFusedMaxByteRowBytes) q.fused = false;
+  // The single kernel is one launch: never more workgroups than a launch holds.
+  if (q.fused && q.grid > max_launch_grid(kGatherThreads)) q.fused = false;
+  q.gather_launches = q.A == 0 || q.fused ? (q.A == 0 ? 0 : 1)
+                    : q.stream ? (q.stream_grid + max_launch_grid(64) - 1) / max_launch_grid(64)
+                               : (q.grid + max_launch_grid(kGatherThreads) - 1) / max_launch_grid(kGatherThreads);
   q.table_bytes = kHeaderBytes;
   q.rowmap_bytes = kHeaderBytes + round_up(8 * (static_cast<size_t>(M) + 1), 256);
   *p = q;
@@ -321,5 +332,6 @@ extern "C" mrr_status mrr_describe_plan(const mrr_args* args, const void* worksp
                                ? std::max<int64_t>(1, (plan.A + mrr::kMidOffsetCells - 1) / mrr::kMidOffsetCells)
                                : std::max<int64_t>(1, (plan.A + mrr::kOffsetThreads - 1) / mrr::kOffsetThreads);
   info->gather_kernel = plan.stream ? 1 : 0;
+  info->gather_launches = plan.gather_launches;
   return MRR_SUCCESS;
 }

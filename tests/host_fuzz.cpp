@@ -89,6 +89,16 @@ void check(const mrr_args& a, const void* ws, size_t ws_bytes, bool must_pass) {
   if (info.threads_per_workgroup != 64 && info.threads_per_workgroup != 256) fail("threads per workgroup", a);
   if (info.gather_workgroups < 0 || info.gather_workgroups >= (1LL << 31)) fail("gather grid", a);
   if (info.offsets_workgroups < 0 || info.offsets_workgroups >= (1LL << 31)) fail("offsets grid", a);
+  // every launch holds at most 2^32 - 1 threads: the gather in gather_launches pieces, the
+  // fused kernel and the offsets kernels (workgroups of at most 1024 threads) in one
+  const long long max_threads = (1LL << 32) - 1;
+  const long long per_launch = info.gather_launches > 0
+                                   ? (info.gather_workgroups + info.gather_launches - 1) / info.gather_launches
+                                   : 0;
+  if (a.A > 0 && info.gather_launches < 1) fail("no gather launch", a);
+  if (per_launch * info.threads_per_workgroup > max_threads) fail("gather launch too large", a);
+  if (info.fused && info.gather_launches != 1) fail("fused kernel in several launches", a);
+  if (info.offsets_workgroups * 1024 > max_threads) fail("offsets launch too large", a);
   if (info.token_row_bytes != a.H * bits / 8) fail("token row bytes", a);
   const size_t need = mrr_workspace_size(a.A, a.N, a.E);
   if (need == 0 || need > ws_bytes) fail("workspace size", a);

@@ -306,3 +306,51 @@ def test_launch_entry_points_reject_before_launch():
     for fn in (L.moe_rerouting_v2, L.moe_rerouting_v2_offsets, L.moe_rerouting_v2_gather):
         assert fn(ctypes.byref(a), ws, nb, None) == _lib.ERROR_INVALID_VALUE
     assert L.mrr_get_device_status(None, None) == _lib.ERROR_INVALID_VALUE
+
+
+def test_gather_launches_stay_within_the_launch_limit():
+    """A launch holds at most 2^32 - 1 threads: gathers with more workgroups
+    than that are planned as several launches (the stream gather's 64-lane
+    workgroups: at most 2^26 - 1 per launch; the row workgroups of 256 threads:
+    at most 2^24 - 1)."""
+    max64, max256 = ((1 << 32) - 1) // 64, ((1 << 32) - 1) // 256
+    # 7168-byte int8 rows at odd addresses move one byte per lane: 112 token chunks per row,
+    # plus A / 64 chunks of 4-byte scale rows and A / 64 item chunks
+    for A, launches in [(599_000, 1), (600_000, 2)]:
+        a = valid_args(A=A, H=7168, N=16, E=16, tok=_lib.I8, weight=False)
+        a.tokens, a.permute_tokens = BASE["tokens"] + 1, BASE["p_tokens"] + 1
+        st, info = describe(a)
+        assert st == _lib.SUCCESS and info.gather_kernel == 1 and info.token_vec_bytes == 1
+        chunks = A * 7168 // 64 + 2 * (-(-A // 64))
+        assert info.gather_workgroups == chunks
+        assert info.gather_launches == launches == -(-chunks // max64)
+    # more than 2^31 stream chunks: the row-workgroup gather, one row per workgroup, in pieces
+    far = 1 << 44  # 16 TiB apart: each buffer below fits between its neighbours
+    A = (1 << 31) - 1
+    a = valid_args(A=A, H=7168, N=16, E=16, tok=_lib.I8, weight=False)
+    a.tokens, a.permute_tokens = far + 1, 2 * far + 1
+    a.per_token_scales, a.permute_per_token_scales = 3 * far, 4 * far
+    a.permute_token_idx, a.expert_token_num_per_rank, a.expert_token_num = 5 * far, 6 * far, 6 * far + 4096
+    ws = 7 * far
+    st, info = describe(a, ws=ws)
+    assert st == _lib.SUCCESS and info.fused == 0 and info.gather_kernel == 0 and info.rows_per_workgroup == 1
+    assert info.gather_workgroups == A and info.gather_launches == -(-A // max256)
+    # A = 0: nothing to launch
+    st, info = describe(valid_args(A=0, N=3, E=2))
+    assert st == _lib.SUCCESS and info.gather_launches == 0
+    st, info = describe(valid_args())
+    assert st == _lib.SUCCESS and info.gather_launches == 1
+
+
+def test_largest_count_matrix():
+    """N * E up to 2^30 cells is accepted (the table's end entry then sits at
+    int32 pair 2^30, word 2^31); one more is refused."""
+    L = _lib.load()
+    n = 1 << 15
+    assert L.mrr_workspace_size(0, n, n) == 256 + 8 * ((1 << 30) + 1) + 248
+    assert L.mrr_workspace_size(0, n + 1, n) == 0
+    a = valid_args(A=0, N=n, E=n, scales=None, weight=False)
+    st, info = describe(a)
+    assert st == _lib.SUCCESS and info.offsets_workgroups == 1 and info.gather_kernel == 0
+    a = valid_args(A=0, N=n + 1, E=n, scales=None, weight=False)
+    assert validate(a, ws_bytes=1 << 40) == _lib.ERROR_INVALID_SHAPE
