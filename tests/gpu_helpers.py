@@ -1,6 +1,10 @@
 """Shared by the GPU parity tests: run the HIP path through the C ABI on a
 workload (outputs pre-filled with a sentinel) and compare it with the CPU
-oracle byte for byte, in either direction."""
+oracle byte for byte, in either direction.
+
+Every output, and the workspace, lies between two guard bands of GUARD
+sentinel bytes inside a larger buffer; after each call the guards must be
+untouched, so a write before or past the end of any buffer fails the test."""
 import numpy as np
 import pytest
 import torch
@@ -9,6 +13,7 @@ from moe_token_re_amd import _lib, api, workloads
 from oracle import oracle
 
 SENTINEL = 0xA5
+GUARD = 4096  # sentinel bytes before and after each guarded buffer (keeps 256-byte alignment)
 
 
 def _dev():
@@ -25,19 +30,63 @@ def _np_bytes(a):
     return np.ascontiguousarray(a).view(np.uint8).reshape(-1)
 
 
+class Guarded:
+    """Tensors of given shapes and dtypes, each the middle of a sentinel-filled
+    uint8 buffer with GUARD bytes on either side."""
+
+    def __init__(self):
+        self._bufs = []  # (name, buffer, payload bytes)
+
+    def like(self, name, t):
+        if t.numel() == 0:
+            return t
+        nbytes = t.numel() * t.element_size()
+        buf = torch.full((nbytes + 2 * GUARD,), SENTINEL, dtype=torch.uint8, device=t.device)
+        self._bufs.append((name, buf, nbytes))
+        return buf[GUARD:GUARD + nbytes].view(t.dtype).view(t.shape)
+
+    def bytes(self, name, nbytes, device):
+        buf = torch.full((nbytes + 2 * GUARD,), SENTINEL, dtype=torch.uint8, device=device)
+        self._bufs.append((name, buf, nbytes))
+        return buf[GUARD:GUARD + nbytes]
+
+    def check(self, where=""):
+        """Asserts that no guard byte changed (call after synchronizing)."""
+        for name, buf, nbytes in self._bufs:
+            b = buf.cpu().numpy()
+            head, tail = b[:GUARD], b[GUARD + nbytes:]
+            assert (head == SENTINEL).all(), f"{where}: write before {name} (guard byte {np.flatnonzero(head != SENTINEL)[:4]})"
+            assert (tail == SENTINEL).all(), f"{where}: write past the end of {name} (+{np.flatnonzero(tail != SENTINEL)[:4]})"
+
+
+OUT_NAMES = ("permute_tokens", "permute_per_token_scales", "permute_token_idx", "expert_token_num",
+             "permute_topk_weight")
+
+
+def guarded_call(t, dev, guards, **kw):
+    """make_call with every output and the workspace inside guard bands, the
+    outputs pre-filled with the sentinel."""
+    _, outs = api.prepare(t["tokens"], t["counts"], **kw)
+    outs = tuple(guards.like(n, o) for n, o in zip(OUT_NAMES, outs))
+    for o in outs:
+        if o.numel():
+            o.view(-1).view(torch.uint8).fill_(SENTINEL)
+    A, N, E = t["tokens"].shape[0], t["counts"].shape[0], t["counts"].shape[1]
+    ws = guards.bytes("workspace", api.workspace_size(A, N, E), dev)
+    return api.make_call(t["tokens"], t["counts"], out=outs, workspace=ws, **kw)
+
+
 def run_hip(w: workloads.Workload, dev, phases=False, direction=_lib.FORWARD):
-    """Runs the HIP path on a workload with outputs pre-filled with a sentinel.
-    Returns (outputs on the host as raw bytes, the device status code)."""
+    """Runs the HIP path on a workload with outputs pre-filled with a sentinel,
+    inside guard bands. Returns (outputs on the host as raw bytes, the device
+    status code); fails if any guard byte changed."""
     print(f"[hip] {w.name} dir={direction} A={w.A} H={w.H} N={w.N} E={w.E} tok={w.tokens_dtype} "
           f"scales={w.scales_dtype} w={w.weight is not None} etn={w.etn_type} idx={w.idx_type}", flush=True)
     t = workloads.torch_inputs(w, dev)
     kw = dict(per_token_scales=t["scales"], expert_topk_weight=t["weight"], expert_token_num_type=w.etn_type,
               idx_type=w.idx_type, tokens_dtype=t["tokens_dtype"], direction=direction)
-    args, outs = api.prepare(t["tokens"], t["counts"], **kw)
-    for o in outs:
-        if o.numel():
-            o.view(-1).view(torch.uint8).fill_(SENTINEL)
-    call, outs = api.make_call(t["tokens"], t["counts"], out=outs, **kw)
+    guards = Guarded()
+    call, outs = guarded_call(t, dev, guards, **kw)
     if phases:
         call.run_offsets()
         call.run_gather()
@@ -45,6 +94,7 @@ def run_hip(w: workloads.Workload, dev, phases=False, direction=_lib.FORWARD):
         call.run()
     status = call.device_status()
     torch.cuda.synchronize()
+    guards.check(w.name)
     return [_bytes(o) for o in outs], status
 
 
