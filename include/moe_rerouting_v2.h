@@ -213,6 +213,31 @@ mrr_status moe_rerouting_v2(const mrr_args* args, void* workspace, size_t worksp
                             struct ihipStream_t* stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture that may not call hipMalloc, tight serving loops, harnesses that
+ * forbid allocation): moe_rerouting_v2 with no workspace argument. The library
+ * uses its own scratch instead, a static device array of
+ * MRR_NOALLOC_SCRATCH_BYTES on each GPU it runs on, held until the process
+ * ends. Nothing is allocated or freed, by the library or by anything it calls.
+ *   - A call fits when mrr_workspace_size(A, N, E) <= MRR_NOALLOC_SCRATCH_BYTES
+ *     (for instance A up to about 2 million rows with a 16 x 16 count matrix,
+ *     or 65536 rows with 256 x 64); larger calls return
+ *     MRR_ERROR_WORKSPACE_TOO_SMALL before any launch and touch no output.
+ *   - Every call on one GPU shares that GPU's scratch, which keeps the last
+ *     call's contents. Calls on one GPU must therefore be ordered (one stream,
+ *     or streams synchronized with each other): calls that overlap in time on
+ *     one GPU race, and their results are undefined.
+ *   - The results, the checks and their error codes are moe_rerouting_v2's.
+ *     Count errors found on the device leave the outputs unwritten as there;
+ *     this entry point offers no status readback (a caller that needs it uses
+ *     moe_rerouting_v2 with its own workspace and mrr_get_device_status).
+ *   - The first call on a device looks up the scratch's address there (a HIP
+ *     query, no allocation).
+ */
+#define MRR_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+mrr_status moe_rerouting_v2_noalloc(const mrr_args* args, struct ihipStream_t* stream);
+
+/*
  * First phase alone (article, "计算公式": the two double sums): scans the
  * count matrix (see mrr_plan_info.offsets_workgroups) and writes into the
  * workspace the validity status and what the second phase reads: for count

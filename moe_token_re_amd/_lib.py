@@ -31,7 +31,8 @@ F16, BF16, I8, F8_E5M2, F8_E4M3FN, HIF8, F4_E2M1, F4_E1M2, I32, I64, F32, F8_E8M
 
 EXPORTS = ("mrr_workspace_size", "mrr_validate", "mrr_describe_plan", "moe_rerouting_v2",
            "moe_rerouting_v2_offsets", "moe_rerouting_v2_gather", "mrr_get_device_status", "mrr_status_string",
-           "mrr_source_hash")
+           "mrr_source_hash", "moe_rerouting_v2_noalloc")
+NOALLOC_SCRATCH_BYTES = 8 << 20  # MRR_NOALLOC_SCRATCH_BYTES
 
 
 class MrrArgs(ctypes.Structure):
@@ -119,6 +120,8 @@ def load() -> ctypes.CDLL:
                 fn = getattr(lib, name)
                 fn.argtypes = [P, vp, sz, vp]
                 fn.restype = ctypes.c_int
+            lib.moe_rerouting_v2_noalloc.argtypes = [P, vp]
+            lib.moe_rerouting_v2_noalloc.restype = ctypes.c_int
             lib.mrr_get_device_status.argtypes = [vp, vp]
             lib.mrr_get_device_status.restype = ctypes.c_int
             lib.mrr_status_string.argtypes = [ctypes.c_int]

@@ -227,6 +227,13 @@ class PreparedCall:
         if st != _lib.SUCCESS:
             _raise(st, "moe_rerouting_v2")
 
+    def run_noalloc(self):
+        """The same call through moe_rerouting_v2_noalloc: the library's own
+        scratch instead of this call's workspace (no allocation)."""
+        st = self._lib.moe_rerouting_v2_noalloc(self._pargs, self._s)
+        if st != _lib.SUCCESS:
+            _raise(st, "moe_rerouting_v2_noalloc")
+
     def run_offsets(self):
         st = self._lib.moe_rerouting_v2_offsets(self._pargs, self._ws, self._wsb, self._s)
         if st != _lib.SUCCESS:

@@ -354,3 +354,17 @@ def test_largest_count_matrix():
     assert st == _lib.SUCCESS and info.offsets_workgroups == 1 and info.gather_kernel == 0
     a = valid_args(A=0, N=n + 1, E=n, scales=None, weight=False)
     assert validate(a, ws_bytes=1 << 40) == _lib.ERROR_INVALID_SHAPE
+
+
+def test_noalloc_rejects_before_any_hip_call():
+    """moe_rerouting_v2_noalloc refuses a call whose workspace would exceed the
+    static scratch, and NULL arguments, before it touches the GPU (none is
+    present here); its other checks are moe_rerouting_v2's."""
+    L = _lib.load()
+    assert L.moe_rerouting_v2_noalloc(None, None) == _lib.ERROR_INVALID_VALUE
+    # 16 x 16 counts: the row map of A rows takes 4 A bytes of the 8 MiB scratch
+    a_max = (_lib.NOALLOC_SCRATCH_BYTES - 256 - 2304) // 4
+    assert L.mrr_workspace_size(a_max, 16, 16) <= _lib.NOALLOC_SCRATCH_BYTES
+    assert L.mrr_workspace_size(a_max + 64, 16, 16) > _lib.NOALLOC_SCRATCH_BYTES
+    a = valid_args(A=a_max + 64, H=64, N=16, E=16)
+    assert L.moe_rerouting_v2_noalloc(ctypes.byref(a), None) == _lib.ERROR_WORKSPACE_TOO_SMALL
