@@ -262,6 +262,7 @@ struct ScanShared {
   uint32_t w[2][kThreads / 64];
   uint64_t t[2][kThreads / 64];
   uint32_t flags;
+  uint32_t wflags[kThreads / 64];  // each wave's rejection flags, published with its scan totals
 };
 
 // floor(t / d) for 0 <= t < 2^12 and 1 <= d <= 2^12, with inv = 1.0f / d:
@@ -322,7 +323,6 @@ __device__ uint32_t offsets_cells(const CountT* __restrict__ counts, int N, int 
   const int M = N * E;
   int32_t* s_c = lds;      // counts, column-major
   int32_t* s_s = lds + M;  // SrcOffset, column-major
-  if (tid == 0) sh->flags = 0;
   for (int j = tid; j <= E; j += kThreads) col[j] = 0;
   if (mapping) s_mark[tid] = -1;
   uint32_t flags = 0;
@@ -330,16 +330,24 @@ __device__ uint32_t offsets_cells(const CountT* __restrict__ counts, int N, int 
   const bool in = tid < M;
   uint32_t c = 0;
   if (in) c = static_cast<uint32_t>(clamp_count(counts[tid], &flags));
+  const int ci = in ? tid / E : 0;
+  const int cj = tid - ci * E;
+  if (in) s_c[cj * N + ci] = static_cast<int32_t>(c);  // column-major, ordered by the scan's barrier
+  // The wave's rejection flags go out with its scan totals: the scan's barrier
+  // publishes both.
+  {
+    uint32_t wf = 0;
+    if (__builtin_amdgcn_ballot_w64((flags & kFlagNegative) != 0) != 0) wf |= kFlagNegative;
+    if (__builtin_amdgcn_ballot_w64((flags & kFlagTooLarge) != 0) != 0) wf |= kFlagTooLarge;
+    if ((tid & 63) == 0) sh->wflags[tid >> 6] = wf;
+  }
   uint64_t total;
   const uint32_t src = block_scan_u32<kThreads, true>(c, c, sh->w[0], sh->t[0], &total);
-  if (in) {
-    const int i = tid / E;
-    const int j = tid - i * E;
-    s_c[j * N + i] = static_cast<int32_t>(c);
-    s_s[j * N + i] = static_cast<int32_t>(src);
-  }
+  flags = 0;
+#pragma unroll
+  for (int w = 0; w < kThreads / 64; ++w) flags |= sh->wflags[w];
+  if (in) s_s[cj * N + ci] = static_cast<int32_t>(src);
   *total_out = static_cast<int64_t>(total);
-  flags = block_or(flags, &sh->flags);  // also orders the writes above before the reads below
   if (total != static_cast<uint64_t>(A)) flags |= kFlagSumMismatch;
   if (flags != 0) return flags;
   // Thread u now holds cell u in column-major (expert j, rank i) order.

@@ -242,8 +242,13 @@ struct StreamGrid {
   float inv_svpr;
   uint32_t byte_rows;    // token rows stream as bytes: aligned 16-byte blocks of the output
   float inv_row;         // 1 / row bytes, for byte_rows with rows under 1 KiB
+  double inv_row_d;      // 1 / row bytes, for a chunk's first row (a quotient below 2^45)
   uint32_t rows8;        // byte_rows with R >= 147 and A >= 8: a 1 KiB chunk spans at most
                          // floor(1023 / R) + 2 <= 8 rows
+  uint32_t fold_scales;  // scale rows of one 4-byte word move in the item chunks
+  uint32_t idx16;        // permute_token_idx is 16-byte aligned (a lane's four indices in one store)
+  uint32_t w16;          // permute_topk_weight is 16-byte aligned (the same for its weights)
+  uint32_t sc16;         // permute_per_token_scales is 16-byte aligned (the same for folded scales)
   uint32_t base;         // workgroups of earlier launches of the same call
 };
 
@@ -313,6 +318,23 @@ __device__ __forceinline__ void stream_rows(const uint8_t* __restrict__ src, uin
   if (ok) __builtin_nontemporal_store(v, reinterpret_cast<T*>(dst + (g0 + lane) * V));
 }
 
+// The 16 bytes at byte sh (0..15) of the 32-byte concatenation lo:hi, by
+// byte funnel shifts (cheapest when sh is the same in every lane).
+__device__ __forceinline__ VecT<16>::type funnel16(const VecT<16>::type& lo, const VecT<16>::type& hi, int sh) {
+  const uint32_t wd[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  const int q = sh >> 2;
+  const uint32_t r = static_cast<uint32_t>(sh & 3);
+  uint32_t x[5];  // wd[q .. q + 4]
+#pragma unroll
+  for (int i = 0; i < 5; ++i) x[i] = q == 0 ? wd[i] : q == 1 ? wd[i + 1] : q == 2 ? wd[i + 2] : wd[i + 3];
+  VecT<16>::type out;
+  out.x = __builtin_amdgcn_alignbyte(x[1], x[0], r);
+  out.y = __builtin_amdgcn_alignbyte(x[2], x[1], r);
+  out.z = __builtin_amdgcn_alignbyte(x[3], x[2], r);
+  out.w = __builtin_amdgcn_alignbyte(x[4], x[3], r);
+  return out;
+}
+
 // Bytes [w, w + 16) of `base`, of which [n0, n1) are needed (w <= n0 < n1 <=
 // w + 16): two aligned 16-byte loads, each of a block that holds a needed
 // byte (a block with none takes the other's address, so no load leaves the
@@ -325,35 +347,55 @@ __device__ __forceinline__ VecT<16>::type window16(const uint8_t* __restrict__ b
   const bool need_b = a + 16 < n1;
   const T lo = *reinterpret_cast<const T*>(base + (need_a ? a : a + 16));
   const T hi = *reinterpret_cast<const T*>(base + (need_b ? a + 16 : a));
-  const uint32_t wd[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-  const int sh = static_cast<int>(w - a);  // 0..15
-  const int q = sh >> 2;
-  const uint32_t r = static_cast<uint32_t>(sh & 3);
-  uint32_t x[5];  // wd[q .. q + 4]
-#pragma unroll
-  for (int i = 0; i < 5; ++i) x[i] = q == 0 ? wd[i] : q == 1 ? wd[i + 1] : q == 2 ? wd[i + 2] : wd[i + 3];
-  T out;
-  out.x = __builtin_amdgcn_alignbyte(x[1], x[0], r);
-  out.y = __builtin_amdgcn_alignbyte(x[2], x[1], r);
-  out.z = __builtin_amdgcn_alignbyte(x[3], x[2], r);
-  out.w = __builtin_amdgcn_alignbyte(x[4], x[3], r);
-  return out;
+  return funnel16(lo, hi, static_cast<int>(w - a));
 }
 
-// Token rows that are no multiple of 16 bytes (but at least 16 bytes, with
-// both buffers 16-byte aligned), as one byte stream: lane l of chunk c builds
-// the aligned 16-byte block of the dense output at byte 1024 c + 16 l from at
-// most two output rows, i.e. two input rows (row map), with window16 each,
-// and stores it whole (the last, partial block byte by byte).
+// One aligned 16-byte block of a run copy: output byte o takes input byte
+// o + delta for the whole chunk (sh = delta & 15, the same in every lane).
+// Loads the aligned input block holding byte o + delta, and the next one when
+// sh != 0 (both then hold some of the 16 bytes), and funnel-shifts them.
+__device__ __forceinline__ VecT<16>::type run_block(const uint8_t* __restrict__ tokens, int64_t o, int64_t delta,
+                                                    int sh) {
+  using T = VecT<16>::type;
+  const int64_t a = o + (delta - sh);
+  const T lo = __builtin_nontemporal_load(reinterpret_cast<const T*>(tokens + a));
+  if (sh == 0) return lo;  // uniform
+  const T hi = __builtin_nontemporal_load(reinterpret_cast<const T*>(tokens + a + 16));
+  return funnel16(lo, hi, sh);
+}
+
+// Token rows that are no multiple of 16 bytes (at least 17 bytes, both
+// buffers 16-byte aligned), as one byte stream: lane l of chunk c builds the
+// aligned 16-byte block of the dense output at byte 1024 c + 16 l, from the
+// chunk's output rows (at most 1024 / 17 + 2 < 64 of them).
+//  * Run copy: when those rows come from consecutive input rows (one segment,
+//    or segments that continue each other) and the chunk is whole, its 1 KiB
+//    is one byte range of the input at a fixed distance (the pages' moves copy
+//    a segment's rows in order, so a segment is contiguous on both sides):
+//    run_block per lane.
+//  * Otherwise each block takes its bytes from at most two output rows, i.e.
+//    two input rows, with window16 each; the last, partial block of the output
+//    is stored byte by byte.
+// With rows of 147 bytes or more (rows8) a chunk spans at most 8 rows, whose
+// row-map words the wave reads through the scalar cache beside the header, and
+// the run check is scalar; with shorter rows lane k loads the k-th row's word
+// and a ballot checks the run.
 __device__ __forceinline__ void stream_bytes_chunk(const GatherArgs& p, const StreamGrid& g, uint32_t chunk) {
   using T = VecT<16>::type;
   const int lane = threadIdx.x & 63;
   const int64_t R = p.row_bytes;
   const int64_t total = int64_t(p.A) * R;
   const int64_t o0 = int64_t(chunk) * 1024;
-  const int64_t d_base = o0 / R;  // the chunk's first row (uniform)
+  // the chunk's first row, floor(o0 / R): a double estimate within 2^-10 of
+  // the quotient, then an exact integer correction
+  int64_t d_base = static_cast<int64_t>(static_cast<double>(o0) * g.inv_row_d);
+  d_base -= d_base * R > o0 ? 1 : 0;
+  d_base += (d_base + 1) * R <= o0 ? 1 : 0;
+  const int64_t o_last = min(o0 + 1023, total - 1);
+  const int span = static_cast<int>(o_last / R - d_base) + 1;  // rows the chunk touches (uniform)
+  const bool whole = o0 + 1024 <= total;
+  const bool hv = header_valid(p.hdr, p);  // its loads go out first, beside the row-map loads
   const int64_t o = o0 + 16 * lane;
-  if (o >= total) return;
   // Row within the chunk: at most one boundary for rows of 1 KiB or more;
   // below that, a small exact division (off < 2048).
   const int off = static_cast<int>(o0 - d_base * R) + 16 * lane;  // < R + 1024
@@ -364,16 +406,25 @@ __device__ __forceinline__ void stream_bytes_chunk(const GatherArgs& p, const St
   const int len1 = min(16, Ri - col1);  // bytes from row d1; the rest from row d1 + 1
   const bool has2 = len1 < 16;
   const int d2 = has2 ? min(d1 + 1, p.A - 1) : d1;
-  const bool hv = header_valid(p.hdr, p);  // its loads go out first, beside the row-map loads
   int32_t s1, s2;
-  if (g.rows8) {  // uniform: the chunk's rows lie in 8 consecutive row-map words, read through the
-                  // scalar cache (beside the header loads) starting at min(d_base, A - 8)
+  if (g.rows8) {  // uniform: the chunk's rows lie in 8 consecutive row-map words from
+                  // min(d_base, A - 8) on
     using CInt = const int32_t __attribute__((address_space(4)))*;
     const int base = min(static_cast<int>(d_base), p.A - 8);
     const CInt m = reinterpret_cast<CInt>(reinterpret_cast<uintptr_t>(p.rowmap + base));
     int32_t w[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) w[k] = m[k];
+    bool run = whole & (base == d_base);
+#pragma unroll
+    for (int k = 1; k < 8; ++k) run &= (k >= span) | (w[k] == w[0] + k);
+    if (run) {  // uniform
+      const bool ok = hv & (w[0] >= 0) & (int64_t(w[0]) + span <= p.A);
+      const int64_t delta = ok ? (int64_t(w[0]) - d_base) * R : -o0;  // not moving: input bytes [0, 1024)
+      const T v = run_block(p.tokens, o, delta, static_cast<int>(delta & 15));
+      if (ok) __builtin_nontemporal_store(v, reinterpret_cast<T*>(p.out_tokens + o));
+      return;
+    }
     const int k1 = d1 - base, k2 = d2 - base;  // in [0, 8)
     s1 = w[0];
     s2 = w[0];
@@ -383,9 +434,22 @@ __device__ __forceinline__ void stream_bytes_chunk(const GatherArgs& p, const St
       s2 = k2 == k ? w[k] : s2;
     }
   } else {
-    s1 = p.rowmap[d1];
-    s2 = p.rowmap[d2];
+    const int32_t word = p.rowmap[min(static_cast<int>(d_base) + lane, p.A - 1)];
+    const int32_t s0 = __builtin_amdgcn_readfirstlane(word);
+    const bool brk = lane < span && word != s0 + lane;
+    if (__builtin_amdgcn_ballot_w64(brk) == 0 && whole) {  // uniform: run copy
+      const bool ok = hv & (s0 >= 0) & (int64_t(s0) + span <= p.A);
+      const int64_t delta = ok ? (int64_t(s0) - d_base) * R : -o0;  // not moving: input bytes [0, 1024)
+      const int sh = __builtin_amdgcn_readfirstlane(static_cast<int>(delta & 15));
+      const T v = run_block(p.tokens, o, delta, sh);
+      if (ok) __builtin_nontemporal_store(v, reinterpret_cast<T*>(p.out_tokens + o));
+      return;
+    }
+    // the rows' words from the lanes that loaded them (every lane takes part)
+    s1 = __shfl(word, min(dd, 63), 64);
+    s2 = __shfl(word, min(d2 - static_cast<int>(d_base), 63), 64);
   }
+  if (o >= total) return;
   const bool ok = hv & (static_cast<unsigned>(s1) < static_cast<unsigned>(p.A)) &
                   (static_cast<unsigned>(s2) < static_cast<unsigned>(p.A));
   s1 = ok ? s1 : 0;  // input row 0 when not moving: always valid here
@@ -414,6 +478,85 @@ __device__ __forceinline__ void stream_bytes_chunk(const GatherArgs& p, const St
     for (int b = 0; b < static_cast<int>(total - o); ++b)
       p.out_tokens[o + b] = static_cast<uint8_t>(wv[b >> 2] >> (8 * (b & 3)));
   }
+}
+
+// Four words to dst[0..3]: one 16-byte store when `whole` (all four move and
+// dst is 16-byte aligned), else the words of the rows that move.
+__device__ __forceinline__ void store_words4(uint32_t* dst, const uint32_t (&v)[kItemRowsPerLane],
+                                             const bool (&ok)[kItemRowsPerLane], bool whole) {
+  using U4 = uint32_t __attribute__((ext_vector_type(4)));
+  if (whole) {
+    U4 x;
+    x.x = v[0];
+    x.y = v[1];
+    x.z = v[2];
+    x.w = v[3];
+    *reinterpret_cast<U4*>(dst) = x;
+  } else {
+#pragma unroll
+    for (int k = 0; k < kItemRowsPerLane; ++k)
+      if (ok[k]) dst[k] = v[k];
+  }
+}
+
+// Item chunk c: output rows [c * kItemRows, (c + 1) * kItemRows), four per
+// lane (lane l: rows d0 = c * kItemRows + 4 l to d0 + 3): their index and
+// weight and, with fold_scales, their one-word scale rows. The four row-map
+// words come in one 16-byte load; the four rows' indices (gather form),
+// weights and scale words are adjacent in the output and go out in one
+// 16-byte store each when aligned.
+template <bool kScatter, bool kWeight>
+__device__ __forceinline__ void stream_items_chunk(const GatherArgs& p, const StreamGrid& g, uint32_t c) {
+  using I4 = int32_t __attribute__((ext_vector_type(4)));
+  const int lane = threadIdx.x & 63;
+  const int d0 = static_cast<int>(c) * kItemRows + kItemRowsPerLane * lane;
+  int32_t s[kItemRowsPerLane];
+  if (d0 + kItemRowsPerLane <= p.A) {  // the row map sits 16-byte aligned in the workspace, d0 % 4 == 0
+    const I4 w = *reinterpret_cast<const I4*>(p.rowmap + d0);
+    s[0] = w.x;
+    s[1] = w.y;
+    s[2] = w.z;
+    s[3] = w.w;
+  } else {
+#pragma unroll
+    for (int k = 0; k < kItemRowsPerLane; ++k) s[k] = p.rowmap[min(d0 + k, p.A - 1)];
+  }
+  const bool hv = header_valid(p.hdr, p);
+  bool ok[kItemRowsPerLane];
+  bool all = true;
+#pragma unroll
+  for (int k = 0; k < kItemRowsPerLane; ++k) {
+    ok[k] = hv & (d0 + k < p.A) & (static_cast<unsigned>(s[k]) < static_cast<unsigned>(p.A));
+    all &= ok[k];
+  }
+  uint32_t wv[kItemRowsPerLane], sv[kItemRowsPerLane];
+  if (kWeight) {
+#pragma unroll
+    for (int k = 0; k < kItemRowsPerLane; ++k) wv[k] = p.weight[ok[k] ? s[k] : 0];  // branch-free
+  }
+  const uint32_t* sc = reinterpret_cast<const uint32_t*>(p.scales);
+  if (g.fold_scales) {  // uniform
+#pragma unroll
+    for (int k = 0; k < kItemRowsPerLane; ++k) sv[k] = sc[ok[k] ? s[k] : 0];
+  }
+  if (kScatter) {
+#pragma unroll
+    for (int k = 0; k < kItemRowsPerLane; ++k)
+      if (ok[k]) p.idx[s[k]] = d0 + k;
+  } else if (all && g.idx16) {
+    I4 v;
+    v.x = s[0];
+    v.y = s[1];
+    v.z = s[2];
+    v.w = s[3];
+    *reinterpret_cast<I4*>(p.idx + d0) = v;
+  } else {
+#pragma unroll
+    for (int k = 0; k < kItemRowsPerLane; ++k)
+      if (ok[k]) p.idx[d0 + k] = s[k];
+  }
+  if (kWeight) store_words4(p.out_weight + d0, wv, ok, all && g.w16);
+  if (g.fold_scales) store_words4(reinterpret_cast<uint32_t*>(p.out_scales) + d0, sv, ok, all && g.sc16);
 }
 
 // One chunk per workgroup. Chunk numbers: token chunks [0, tok_chunks), scale
@@ -446,21 +589,7 @@ __global__ __launch_bounds__(64) void stream_gather_kernel(GatherArgs p, StreamG
       default: stream_rows<1>(p.scales, p.out_scales, Rs, spr, inv, c, p.rowmap, p.A, p); break;
     }
   } else {
-    const int r0 = static_cast<int>(b - g.sc_end) * 64;
-    const int d = r0 + static_cast<int>(threadIdx.x & 63);
-    const bool in = d < p.A;
-    const int32_t s = p.rowmap[in ? d : r0];
-    const bool ok = in & header_valid(p.hdr, p) & (static_cast<unsigned>(s) < static_cast<unsigned>(p.A));
-    if (kWeight) {
-      const uint32_t wv = p.weight[ok ? s : 0];
-      if (ok) p.out_weight[d] = wv;
-    }
-    if (ok) {
-      if (kScatter)
-        p.idx[s] = d;
-      else
-        p.idx[d] = s;
-    }
+    stream_items_chunk<kScatter, kWeight>(p, g, b - g.sc_end);
   }
 }
 
@@ -482,7 +611,12 @@ StreamGrid stream_grid(const Plan& pl) {
   sg.cpr_magic = 0;
   sg.byte_rows = pl.byte_rows ? 1u : 0u;
   sg.inv_row = 1.0f / static_cast<float>(pl.row_bytes);
+  sg.inv_row_d = 1.0 / static_cast<double>(pl.row_bytes);
   sg.rows8 = pl.byte_rows && pl.row_bytes >= 147 && pl.A >= 8 ? 1u : 0u;
+  sg.fold_scales = pl.fold_scales ? 1u : 0u;
+  sg.idx16 = 0;
+  sg.w16 = 0;
+  sg.sc16 = 0;
   if (!pl.byte_rows && pl.vecs_per_row % 64 == 0) {
     sg.cpr = static_cast<uint32_t>(pl.vecs_per_row / 64);
     sg.cpr_magic = sg.cpr == 1 ? 0u : static_cast<uint32_t>(((uint64_t(1) << 32) + sg.cpr - 1) / sg.cpr);
@@ -495,6 +629,9 @@ StreamGrid stream_grid(const Plan& pl) {
 template <bool S, bool W>
 void launch_stream_sw(const Plan& pl, const GatherArgs& g, hipStream_t stream) {
   StreamGrid sg = stream_grid(pl);
+  sg.idx16 = reinterpret_cast<uintptr_t>(g.idx) % 16 == 0 ? 1u : 0u;
+  sg.w16 = reinterpret_cast<uintptr_t>(g.out_weight) % 16 == 0 ? 1u : 0u;
+  sg.sc16 = reinterpret_cast<uintptr_t>(g.out_scales) % 16 == 0 ? 1u : 0u;
   const int64_t piece = max_launch_grid(64);
   for (int64_t base = 0; base < pl.stream_grid; base += piece) {
     sg.base = static_cast<uint32_t>(base);  // < kMaxStreamGrid

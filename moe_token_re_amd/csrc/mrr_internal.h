@@ -77,6 +77,11 @@ constexpr int64_t kBandMaxCells = int64_t(1) << 17;
 // kernel instead.
 constexpr int64_t kMaxStreamGrid = int64_t(1) << 31;
 
+// The stream gather's per-row items (index, weight, and scale rows of one
+// 4-byte word) move in chunks of kItemRows rows, four per lane.
+constexpr int kItemRowsPerLane = 4;
+constexpr int kItemRows = 64 * kItemRowsPerLane;
+
 // A launch may hold at most 2^32 - 1 threads (grid x workgroup size), so a
 // gather with more workgroups than that is launched in pieces, each taking
 // the next workgroups in order.
@@ -142,6 +147,7 @@ struct Plan {
   bool stream;              // the gather kernel is the stream kernel: 64-lane workgroups, one chunk of
                             // 64 vectors (token or scale rows) or 64 rows (items) each
   int64_t tok_chunks, sc_chunks, item_chunks;  // the stream kernel's chunks
+  bool fold_scales;         // scale rows of one 4-byte word move with the items (no scale chunks)
   bool byte_rows;           // token rows stream as bytes in 1 KiB chunks of aligned 16-byte blocks
                             // (rows of 16 bytes or more that are no multiple of 16, both buffers
                             // 16-byte aligned)

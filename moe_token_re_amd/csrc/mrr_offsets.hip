@@ -380,14 +380,16 @@ __global__ __launch_bounds__(kOffsetThreads) void offsets_global_kernel(
 //     band cell). These scans start before step 2 ends (they need only the
 //     band's counts). Without a row map, each order's threads write their
 //     half of the cell's (DstOffset, SrcOffset) pair.
-//  4. With a row map, the workgroups of a band split its cells: a thread
-//     writes the rows of a cell of at most kBandCellRows rows, a wave those
-//     of a cell of at most kOffsetThreads rows, and every workgroup of the
-//     band its share of a larger cell's rows.
+//  4. With a row map, the workgroups of a band split its cells, taken in
+//     output order: a group of threads (the workgroup's threads over its
+//     cells, up to kBandCellRows) writes the rows of a cell of at most
+//     kBandCellRows rows, a wave those of a cell of at most kOffsetThreads
+//     rows, and every workgroup of the band its share of a larger cell's
+//     rows.
 // Every workgroup repeats step 1 over all M cells, which is why the per-cell
 // work is kept to a few instructions, and why the L2 reads grow as
 // M * (number of bands); the planner bounds M for this path.
-constexpr int kBandCellRows = 16;  // row-map rows a thread writes for one cell; larger cells take the workgroup
+constexpr int kBandCellRows = 16;  // row-map rows of a cell written by a group of threads; larger cells take a wave
 constexpr int kBandUnroll = 16;  // count loads in flight per thread in step 1
 constexpr int kBandFanIn = 16;   // lanes' sums a column's thread adds up; more take a first LDS pass
 
@@ -520,10 +522,21 @@ __global__ __launch_bounds__(kOffsetThreads) void offsets_banded_kernel(
   uint64_t tot_j = 0;
   uint32_t bef_j = 0;
   if (is_col) {
+    // all kBandFanIn reads issued before the sums (k < fan <= lanes keeps k * E + tid
+    // below lanes * E <= kOffsetThreads; unused slots read lane 0's and add nothing)
     const int fan = lanes < kBandFanIn ? lanes : kBandFanIn;
-    for (int k = 0; k < fan; ++k) {
-      tot_j += s.tot[k * E + tid];
-      bef_j += s.bef[k * E + tid];
+    uint64_t t[kBandFanIn];
+    uint32_t f[kBandFanIn];
+#pragma unroll
+    for (int k = 0; k < kBandFanIn; ++k) {
+      const int kk = k < fan ? k : 0;
+      t[k] = s.tot[kk * E + tid];
+      f[k] = s.bef[kk * E + tid];
+    }
+#pragma unroll
+    for (int k = 0; k < kBandFanIn; ++k) {
+      tot_j += k < fan ? t[k] : 0;
+      bef_j += k < fan ? f[k] : 0u;
     }
   }
   const uint32_t t32 = static_cast<uint32_t>(tot_j);
@@ -606,24 +619,33 @@ __global__ __launch_bounds__(kOffsetThreads) void offsets_banded_kernel(
   }
   if (rowmap != nullptr) {
     // The row map for the band's cells: the workgroups of the band split its
-    // cells; a thread writes the rows of a cell with at most kBandCellRows
-    // rows itself, and the workgroup writes each larger cell's rows together,
-    // strided over all its threads. Forward: output row DstOffset + k takes
-    // source row SrcOffset + k; inverse: the reverse.
+    // cells; a group of threads writes the rows of a cell with at most
+    // kBandCellRows rows, and the workgroup writes each larger cell's rows
+    // together, strided over all its threads. Forward: output row DstOffset +
+    // k takes source row SrcOffset + k; inverse: the reverse.
     __syncthreads();
     {
+      // The slice's cells in output order (forward: column-major, so that
+      // neighbouring cells' rows are neighbours in the row map), tpc threads
+      // per cell (a power of two, the workgroup's threads over its cells):
+      // thread sub of a cell writes its rows sub, sub + tpc, ...
       const int per = (cells + split - 1) / split;
-      const int q = slice * per + tid;
-      if (tid < per && q < cells) {
+      int tpc = 1;
+      while (tpc < kBandCellRows && tpc * 2 * per <= kOffsetThreads) tpc *= 2;
+      const int o = slice * per + tid / tpc;  // output-order index of the cell
+      const int sub = tid & (tpc - 1);
+      if (tid / tpc < per && o < cells) {
+        const int oj = div_small(o, inv_rows);  // forward: o = oj * rows + oi
+        const int q = inverse ? o : (o - oj * rows) * E + oj;
         const int sq = s.src_q[q], dq = s.dst_q[q], n = s.src_q[q + 1] - sq;
         if (n <= kBandCellRows) {
-          for (int k = 0; k < n; ++k) {
+          for (int k = sub; k < n; k += tpc) {
             if (inverse)
               rowmap[sq + k] = dq + k;
             else
               rowmap[dq + k] = sq + k;
           }
-        } else if (n <= kOffsetThreads) {
+        } else if (n <= kOffsetThreads && sub == 0) {
           s.mid[atomicAdd(&s.nmid, 1)] = q;
         }
       }

@@ -267,12 +267,14 @@ mrr_status make_plan(const mrr_args* a, const void* ws, size_t ws_bytes, Plan* p
     q.band_split = std::min(16, tuning().band_split);
   q.tok_chunks = q.sc_chunks = q.item_chunks = q.stream_grid = 0;
   q.byte_rows = false;
+  q.fold_scales = false;
   if (q.stream) {
     q.byte_rows = tuning().byte_rows && q.token_vec < 16 && q.row_bytes >= 16 && aligned(a->tokens, 16) &&
                   aligned(a->permute_tokens, 16);
     q.tok_chunks = q.byte_rows ? (q.A * q.row_bytes + 1023) / 1024 : (q.A * q.vecs_per_row + 63) / 64;
-    q.sc_chunks = Rs > 0 ? (q.A * (Rs / q.scale_vec) + 63) / 64 : 0;
-    q.item_chunks = (q.A + 63) / 64;
+    q.fold_scales = Rs == 4 && q.scale_vec == 4;
+    q.sc_chunks = Rs > 0 && !q.fold_scales ? (q.A * (Rs / q.scale_vec) + 63) / 64 : 0;
+    q.item_chunks = (q.A + kItemRows - 1) / kItemRows;
     q.stream_grid = q.tok_chunks + q.sc_chunks + q.item_chunks;
     if (q.stream_grid >= kMaxStreamGrid) q.stream = false;  // 32-bit chunk numbers and grid
   }

@@ -186,12 +186,12 @@ def describe(a, ws=BASE["ws"]):
 def test_describe_plan():
     # pages' shape: 7168-byte rows in 16-byte vectors; 112 MiB of token rows take the two-kernel
     # path with the stream gather: 64-lane workgroups over 64-vector chunks of the token rows
-    # (16384 * 448 / 64), the scale rows (16384 4-byte vectors / 64) and the items (16384 / 64)
+    # (16384 * 448 / 64) and chunks of 256 rows' items (index, and the 4-byte scale rows with them)
     st, info = describe(valid_args(A=16384, H=7168, N=16, E=16, tok=_lib.I8))
     assert st == _lib.SUCCESS
     assert info.fused == 0 and info.gather_kernel == 1 and info.token_vec_bytes == 16
     assert info.token_row_bytes == 7168 and info.scale_row_bytes == 4 and info.scale_vec_bytes == 4
-    assert info.threads_per_workgroup == 64 and info.gather_workgroups == 114688 + 256 + 256
+    assert info.threads_per_workgroup == 64 and info.gather_workgroups == 114688 + 16384 // 256
     assert info.offsets_workgroups == 64           # the row map: one workgroup per 256 rows (<= 256 cells)
     # a smaller call with the same counts: one kernel whose workgroups each recompute the offsets
     st, info = describe(valid_args(A=2048, H=7168, N=16, E=16, tok=_lib.I8))
@@ -222,10 +222,14 @@ def test_describe_plan():
     st, info = describe(a)
     assert st == _lib.SUCCESS and info.token_vec_bytes == 2 and info.token_row_bytes == 158
     # ...and stream as aligned 16-byte blocks of the output in the stream gather: 1 KiB chunks of
-    # the 158-byte rows, the 4-byte scale rows and the items
+    # the 158-byte rows, and 256-row chunks of the items with their 4-byte scale rows
     st, info = describe(valid_args(tok=_lib.F16, H=79, A=262144, N=16, E=16))
     assert st == _lib.SUCCESS and info.gather_kernel == 1 and info.token_vec_bytes == 16
-    assert info.gather_workgroups == (262144 * 158 + 1023) // 1024 + 262144 // 64 + 262144 // 64
+    assert info.gather_workgroups == (262144 * 158 + 1023) // 1024 + 262144 // 256
+    # scale rows of more than 16 bytes keep chunks of their own (e8m0 [A, 112, 2]: 224 bytes a row)
+    st, info = describe(valid_args(A=32768, H=7168, N=32, E=8, tok=_lib.F8_E4M3FN, scales="e8m0"))
+    assert st == _lib.SUCCESS and info.gather_kernel == 1
+    assert info.gather_workgroups == 32768 * 448 // 64 + 32768 * 14 // 64 + 32768 // 256
     # empty input: nothing to gather, never the single-kernel path
     st, info = describe(valid_args(A=0, N=3, E=2))
     assert st == _lib.SUCCESS and info.fused == 0 and info.gather_workgroups == 0
@@ -315,13 +319,13 @@ def test_gather_launches_stay_within_the_launch_limit():
     at most 2^24 - 1)."""
     max64, max256 = ((1 << 32) - 1) // 64, ((1 << 32) - 1) // 256
     # 7168-byte int8 rows at odd addresses move one byte per lane: 112 token chunks per row,
-    # plus A / 64 chunks of 4-byte scale rows and A / 64 item chunks
+    # plus A / 256 item chunks (which also move the 4-byte scale rows)
     for A, launches in [(599_000, 1), (600_000, 2)]:
         a = valid_args(A=A, H=7168, N=16, E=16, tok=_lib.I8, weight=False)
         a.tokens, a.permute_tokens = BASE["tokens"] + 1, BASE["p_tokens"] + 1
         st, info = describe(a)
         assert st == _lib.SUCCESS and info.gather_kernel == 1 and info.token_vec_bytes == 1
-        chunks = A * 7168 // 64 + 2 * (-(-A // 64))
+        chunks = A * 7168 // 64 + (-(-A // 256))
         assert info.gather_workgroups == chunks
         assert info.gather_launches == launches == -(-chunks // max64)
     # more than 2^31 stream chunks: the row-workgroup gather, one row per workgroup, in pieces
