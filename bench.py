@@ -1,36 +1,44 @@
 """Throughput of the MoE re-routing operator (MoeReRoutingV2) on one MI355X.
 
-A step is one whole call of the operator (offsets kernel + gather kernel) on
-one batch of synthetic input already resident in HBM. The default workload is
-the shape of the pages' single-operator example: A=16384 tokens of H=7168 int8
-values, N=E=16, one huge segment, [A] fp32 scales (see
-moe_token_re_amd/workloads.py for the recipe).
+A step is one whole call of the operator (offsets kernel + gather kernel, or
+the single fused kernel for small calls) on one batch of synthetic input
+already resident in HBM. The headline workload is the shape of the pages'
+single-operator example: A=16384 tokens of H=7168 int8 values, N=E=16, one
+huge segment, [A] fp32 scales (moe_token_re_amd/workloads.py has the recipe).
 
 Calls rotate over several identical buffer sets whose total footprint is at
 least 1 GiB, so the 256 MB Infinity Cache cannot hold the working set between
 calls. Prints ONE JSON line:
-  value       re-route GB/s = algorithmic bytes per call / wall time per call
-  roofline    the dominant kernel alone (the fused kernel, or the gather
-              kernel of the two-kernel path; the row map it reads is
-              implementation traffic, not counted): algorithmic bytes per launch /
-              its mean duration over back-to-back launches (HIP events on
-              the launch stream) against 8 TB/s HBM;
-              traffic from rocprofv3 FETCH_SIZE/WRITE_SIZE counters when the
-              committed counter summary matches the current kernel source
+  value        re-route GB/s = algorithmic bytes per call / wall time per call,
+               the wall clock around exactly K calls, synchronized on both
+               sides (nothing else inside the timed region)
+  roofline     the dominant kernel alone (the gather kernel of the two-kernel
+               path, or the fused kernel): algorithmic bytes per launch / its
+               mean duration, measured live as the mean period of K launches
+               back to back between two HIP events on the launch stream (an
+               event pair around each single launch adds ~2.5 us of its own).
+               launch_us_rocprof is the average duration the committed
+               rocprofv3 kernel-trace summary of this command holds for the
+               same kernel (the profiler adds ~0.5 us per launch), given only
+               when that summary was taken from the loaded library's sources.
+               traffic: rocprofv3 FETCH_SIZE/WRITE_SIZE counters, under the
+               same condition
   cpu_baseline the CPU oracle on the same workload, one host thread
+  workloads    the other named workloads (and the inverse re-route at the
+               pages' shape), each with its µs per call, GB/s, the gather's
+               fraction of 8 TB/s and the call's and the gather's fractions of
+               the measured copy ceiling (no oracle timing, no graph)
 plus the measured copy ceiling (hipMemcpyAsync device-to-device and a plain
 16-byte non-temporal copy kernel moving the same token bytes), and the
 per-call time of the same calls captured in one HIP graph and replayed
-(us_per_call_graph: no host launch overhead, which matters for small calls;
-the graph rotates over at most 1000 buffer sets, which for small calls fit
-in the Infinity Cache).
+(us_per_call_graph: no host launch overhead, which matters for small calls).
 
-With --inverse the same workload runs the inverse re-route (its token rows
+With --inverse the headline workload runs the inverse re-route (its token rows
 taken as expert-major, returned to rank-major order), with the oracle's
 inverse as the CPU baseline.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--inverse] [--no-cpu] [--no-ceiling]
+                       [--inverse] [--no-cpu] [--no-ceiling] [--no-workloads]
 """
 from __future__ import annotations
 
@@ -51,6 +59,10 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 METRIC = "re-route GB/s (bytes read+written) and % of HBM peak; µs/call A=16384 H=7168"
 PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "stream_gather_pages_shape_counters.txt")
+STATS_SUMMARY = os.path.join(ROOT, "profiles", "pages_shape_kernel_stats.md")
+# the other workloads the default run reports (name, direction)
+OTHER_WORKLOADS = (("tiny", "forward"), ("balanced_bf16", "forward"), ("mxfp8_skewed", "forward"),
+                   ("tiny_segments", "forward"), ("pages_shape", "inverse"), ("odd_rows", "forward"))
 
 
 def kernel_source_hash() -> str:
@@ -120,6 +132,22 @@ def traffic_from_profile(w, kernel_name, direction="forward"):
     return int(round((fetch + write) * 1024))
 
 
+def rocprof_average_us(w, kernel_name, direction="forward"):
+    """The committed rocprofv3 kernel-trace average duration (µs) of the kernel
+    for this workload and direction; None unless the summary names them and
+    was taken from the current sources."""
+    if not os.path.exists(STATS_SUMMARY):
+        return None
+    fields = dict(re.findall(r"^(\w+):\s*(\S+)\s*$", open(STATS_SUMMARY).read(), flags=re.M))
+    if (fields.get("source_hash") != kernel_source_hash() or fields.get("workload") != w.name
+            or fields.get("direction", "forward") != direction):
+        return None
+    try:
+        return float(fields[f"average_ns_{kernel_name}"]) / 1e3
+    except (KeyError, ValueError):
+        return None
+
+
 def time_oracle(w, budget_s=3.0, max_runs=400, inverse=False):
     """The CPU oracle on the full workload, single-threaded, outputs preallocated
     and pre-faulted; median over runs that fit the time budget."""
@@ -142,6 +170,200 @@ def time_oracle(w, budget_s=3.0, max_runs=400, inverse=False):
     return statistics.median(times), len(times)
 
 
+class Bench:
+    """One workload's calls on rotating buffer sets, and the timings of them."""
+
+    def __init__(self, torch, dev, w, inverse, label):
+        from moe_token_re_amd import _lib, api, workloads
+
+        self.torch, self.dev, self.w, self.inverse, self.label = torch, dev, w, inverse, label
+        self._lib = _lib
+        self.stream = torch.cuda.current_stream(dev)
+        base = workloads.torch_inputs(w, dev)
+        footprint = 2 * (w.A * (w.token_row_bytes + w.scale_row_bytes + 4 + (8 if w.weight is not None else 0)))
+        self.n_sets = max(3, math.ceil((1 << 30) / max(footprint, 1)))
+        self.inputs, self.calls = [], []
+        self.direction = _lib.INVERSE if inverse else _lib.FORWARD
+        for k in range(self.n_sets):
+            t = base if k == 0 else {key: (v.clone() if isinstance(v, torch.Tensor) else v) for key, v in base.items()}
+            self.inputs.append(t)
+            call, _ = api.make_call(t["tokens"], t["counts"], per_token_scales=t["scales"],
+                                    expert_topk_weight=t["weight"], expert_token_num_type=w.etn_type,
+                                    idx_type=w.idx_type, tokens_dtype=t["tokens_dtype"], stream=self.stream,
+                                    direction=self.direction)
+            self.calls.append(call)
+        torch.cuda.synchronize()
+        self.plan = self.calls[0].plan()
+        self.alg_bytes = w.algorithmic_bytes()
+
+    def warm(self, n):
+        for i in range(n):
+            self.calls[i % self.n_sets].run()
+        for c in self.calls:
+            c.run()
+        self.torch.cuda.synchronize()
+        st = self.calls[0].device_status()
+        if st != self._lib.SUCCESS:
+            raise SystemExit(f"{self.label}: device status {self._lib.status_string(st)}")
+
+    def wall_us(self, k):
+        """Wall time per call around exactly k whole calls, synchronized on
+        both sides, with nothing else in the timed region."""
+        torch, calls, n = self.torch, self.calls, self.n_sets
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(k):
+            calls[i % n].run()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e6 / k
+
+    def _events(self, k):
+        ev = self.torch.cuda.Event
+        return [(ev(enable_timing=True), ev(enable_timing=True)) for _ in range(k)]
+
+    def back_to_back_us(self, fn, k):
+        """Mean period of k launches of fn between two events on the launch stream."""
+        torch, calls, n, s = self.torch, self.calls, self.n_sets, self.stream
+        for i in range(min(10, k)):
+            fn(calls[i % n])
+        torch.cuda.synchronize()
+        e0, e1 = self._events(1)[0]
+        e0.record(s)
+        for i in range(k):
+            fn(calls[i % n])
+        e1.record(s)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / k
+
+    def pair_us(self, fn, k):
+        """Mean and median over k launches of fn of the span between an event
+        recorded just before and one just after each launch."""
+        torch, calls, n, s = self.torch, self.calls, self.n_sets, self.stream
+        pairs = self._events(k)
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(pairs):
+            a.record(s)
+            fn(calls[i % n])
+            b.record(s)
+        torch.cuda.synchronize()
+        spans = [a.elapsed_time(b) * 1e3 for a, b in pairs]
+        return statistics.mean(spans), statistics.median(spans)
+
+    def kernel(self, k):
+        """The dominant kernel: (name, algorithmic bytes per launch, back-to-back
+        µs, event-pair mean µs), and the offsets kernel's back-to-back µs."""
+        if self.plan["fused"]:
+            run = lambda c: c.run()  # noqa: E731
+            name, kbytes, off = "fused_kernel", self.alg_bytes, None
+        else:
+            name = "stream_gather_kernel" if self.plan["gather_kernel"] == 1 else "gather_kernel"
+            kbytes = gather_bytes_per_launch(self.w)
+            off = self.back_to_back_us(lambda c: c.run_offsets(), k)
+            for c in self.calls:
+                c.run_offsets()  # every set holds its row map for the gather-only launches
+            run = lambda c: c.run_gather()  # noqa: E731
+        b2b_us = self.back_to_back_us(run, k)
+        pair_us, _ = self.pair_us(run, k)
+        return name, kbytes, b2b_us, pair_us, off
+
+    def copy_ceiling(self, lib, k):
+        """The plain 16-byte non-temporal copy kernel and hipMemcpyAsync moving
+        the workload's token bytes over the same rotation; the faster rate."""
+        torch, w, n, s = self.torch, self.w, self.n_sets, self.stream
+        nbytes16 = (w.A * w.token_row_bytes) // 16 * 16
+        srcs = [c.args.tokens for c in self.calls]
+        dsts = [torch.empty(nbytes16, dtype=torch.uint8, device=self.dev) for _ in range(n)]
+        hip = ctypes.CDLL("libamdhip64.so")
+        hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
+                                       ctypes.c_void_p]
+        hip.hipMemcpyAsync.restype = ctypes.c_int
+        hip_d2d = 3  # hipMemcpyDeviceToDevice
+        sp = s.cuda_stream
+        for i in range(10):
+            assert lib.mrr_bench_copy(dsts[i % n].data_ptr(), srcs[i % n], nbytes16, sp) == 0
+            assert hip.hipMemcpyAsync(dsts[i % n].data_ptr(), srcs[i % n], nbytes16, hip_d2d, sp) == 0
+        ev = torch.cuda.Event
+        e0, e1 = ev(enable_timing=True), ev(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(s)
+        for i in range(k):
+            lib.mrr_bench_copy(dsts[i % n].data_ptr(), srcs[i % n], nbytes16, sp)
+        e1.record(s)
+        torch.cuda.synchronize()
+        kern_us = e0.elapsed_time(e1) * 1e3 / k
+        e0.record(s)
+        for i in range(k):
+            hip.hipMemcpyAsync(dsts[i % n].data_ptr(), srcs[i % n], nbytes16, hip_d2d, sp)
+        e1.record(s)
+        torch.cuda.synchronize()
+        memcpy_us = e0.elapsed_time(e1) * 1e3 / k
+        del dsts
+        gbps = max(2 * nbytes16 / (kern_us * 1e-6) / 1e9, 2 * nbytes16 / (memcpy_us * 1e-6) / 1e9)
+        return {"copy_kernel_us": round(kern_us, 2), "memcpy_d2d_us": round(memcpy_us, 2),
+                "bytes_read_plus_written": 2 * nbytes16, "ceiling_GBps": round(gbps, 1)}
+
+    def graph_us(self, k):
+        """Per-call time of the same calls captured in one HIP graph (on a side
+        stream, each call on its own buffer set, at most 1000) and replayed."""
+        from moe_token_re_amd import api
+
+        torch, w = self.torch, self.w
+        side = torch.cuda.Stream(self.dev)
+        n_cap = min(self.n_sets, 1000)
+        gcalls = []
+        for t in self.inputs[:n_cap]:
+            gc, _ = api.make_call(t["tokens"], t["counts"], per_token_scales=t["scales"],
+                                  expert_topk_weight=t["weight"], expert_token_num_type=w.etn_type,
+                                  idx_type=w.idx_type, tokens_dtype=t["tokens_dtype"], stream=side,
+                                  direction=self.direction)
+            gcalls.append(gc)
+        with torch.cuda.stream(side):
+            for gc in gcalls:
+                gc.run()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=side):
+            for gc in gcalls:
+                gc.run()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        reps = max(1, k // n_cap)
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            graph.replay()
+        torch.cuda.synchronize()
+        us = (time.perf_counter() - t0) * 1e6 / (reps * n_cap)
+        if gcalls[0].device_status() != self._lib.SUCCESS:
+            raise SystemExit("device status after graph replays")
+        return us
+
+
+def workload_summary(torch, dev, name, direction, copy_lib, steps):
+    """µs per call, GB/s and roofline fractions of one more workload."""
+    from moe_token_re_amd import workloads
+
+    w = workloads.make(name)
+    b = Bench(torch, dev, w, direction == "inverse", f"{name}/{direction}")
+    k = 1000 if name == "tiny" else steps
+    b.warm(10)
+    us = b.wall_us(k)
+    kname, kbytes, k_us, _, _ = b.kernel(k)
+    ceil = b.copy_ceiling(copy_lib, k)
+    gbps = b.alg_bytes / (us * 1e-6) / 1e9
+    k_gbps = kbytes / (k_us * 1e-6) / 1e9
+    out = {"direction": direction, "us_per_call": round(us, 2), "GBps": round(gbps, 1),
+           "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2), "algorithmic_bytes_per_call": b.alg_bytes,
+           "path": "fused single kernel" if b.plan["fused"] else "offsets kernel + gather kernel",
+           "kernel": kname, "kernel_us_back_to_back": round(k_us, 2),
+           "kernel_frac_of_8TBps": round(k_gbps / HBM_PEAK_GBPS, 4),
+           "copy_ceiling_GBps": ceil["ceiling_GBps"],
+           "kernel_frac_of_ceiling": round(k_gbps / ceil["ceiling_GBps"], 4),
+           "call_frac_of_ceiling": round(gbps / ceil["ceiling_GBps"], 4), "calls_timed": k}
+    print(f"[bench] {name}/{direction}: {out}", file=sys.stderr, flush=True)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -152,6 +374,7 @@ def main():
     ap.add_argument("--inverse", action="store_true", help="time the inverse re-route (expert-major -> rank-major)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-oracle baseline")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the copy-ceiling measurement")
+    ap.add_argument("--no-workloads", action="store_true", help="skip the other workloads")
     opt = ap.parse_args()
     if opt.steps is None:
         opt.steps = 1000 if opt.workload == "tiny" else 200
@@ -161,199 +384,65 @@ def main():
               f"--gpus {opt.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np  # noqa: F401
     import torch
 
-    from moe_token_re_amd import _lib, api, workloads
+    from moe_token_re_amd import _lib, workloads
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = workloads.make(opt.workload)
-    alg_bytes = w.algorithmic_bytes()
-    bench_lib = bench_copy_lib()
-    device = device_facts(torch, dev, bench_lib)
+    copy_lib = bench_copy_lib()
+    device = device_facts(torch, dev, copy_lib)
     print(f"[bench] device {device}", file=sys.stderr, flush=True)
     print(f"[bench] workload {w.name}: A={w.A} H={w.H} N={w.N} E={w.E} tokens={w.tokens_dtype} "
-          f"algorithmic bytes/call={alg_bytes}", file=sys.stderr, flush=True)
-
-    base = workloads.torch_inputs(w, dev)
-    stream = torch.cuda.current_stream(dev)
-    footprint = 2 * (w.A * (w.token_row_bytes + w.scale_row_bytes + 4 + (8 if w.weight is not None else 0)))
-    n_sets = max(3, math.ceil((1 << 30) / max(footprint, 1)))
-    calls = []
-    inputs = []
-    for k in range(n_sets):
-        t = base if k == 0 else {key: (v.clone() if isinstance(v, torch.Tensor) else v) for key, v in base.items()}
-        inputs.append(t)
-        call, _ = api.make_call(t["tokens"], t["counts"], per_token_scales=t["scales"],
-                                expert_topk_weight=t["weight"], expert_token_num_type=w.etn_type,
-                                idx_type=w.idx_type, tokens_dtype=t["tokens_dtype"], stream=stream,
-                                direction=_lib.INVERSE if opt.inverse else _lib.FORWARD)
-        calls.append(call)
-    torch.cuda.synchronize()
-
-    # warmup
-    for i in range(opt.warmup):
-        calls[i % n_sets].run()
-    torch.cuda.synchronize()
-    for c in calls:
-        c.run()
-    torch.cuda.synchronize()
-    st = calls[0].device_status()
-    if st != _lib.SUCCESS:
-        raise SystemExit(f"device status {_lib.status_string(st)}")
+          f"algorithmic bytes/call={w.algorithmic_bytes()}", file=sys.stderr, flush=True)
+    b = Bench(torch, dev, w, opt.inverse, w.name)
+    b.warm(opt.warmup)
 
     # timed: exactly K whole calls, synchronized on both sides
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(opt.steps):
-        calls[i % n_sets].run()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall_s = time.perf_counter() - t0
-    ev_ms = ev0.elapsed_time(ev1)
-    ms_per_step = wall_s * 1e3 / opt.steps
-    value = alg_bytes / (ms_per_step * 1e-3) / 1e9
-    print(f"[bench] {opt.steps} calls: wall {ms_per_step * 1e3:.2f} us/call, events "
-          f"{ev_ms * 1e3 / opt.steps:.2f} us/call, {value:.1f} GB/s", file=sys.stderr, flush=True)
+    us = b.wall_us(opt.steps)
+    value = b.alg_bytes / (us * 1e-6) / 1e9
+    print(f"[bench] {opt.steps} calls: wall {us:.2f} us/call, {value:.1f} GB/s", file=sys.stderr, flush=True)
 
-    # the median of per-call event pairs (a separate pass: the events between
-    # calls cost a little)
-    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(opt.steps)]
-    torch.cuda.synchronize()
-    for i, (a, b) in enumerate(pairs):
-        a.record(stream)
-        calls[i % n_sets].run()
-        b.record(stream)
-    torch.cuda.synchronize()
-    per_call_median_us = statistics.median(a.elapsed_time(b) for a, b in pairs) * 1e3
-    del pairs
-
-    # per-kernel: K back-to-back launches of one kernel between two events on
-    # the launch stream, rotating over the buffer sets. When the call is one
-    # fused kernel that kernel is the dominant one; otherwise the gather
-    # kernel is, timed on tables its sets' offsets kernels built beforehand.
-    plan = calls[0].plan()
+    # the same calls between two events (GPU time without the host's start and end)
+    ev_us = b.back_to_back_us(lambda c: c.run(), opt.steps)
+    _, pair_median_us = b.pair_us(lambda c: c.run(), opt.steps)
     n_k = max(opt.steps, 50)
-
-    def back_to_back_us(fn):
-        for i in range(min(10, n_k)):
-            fn(calls[i % n_sets])
-        torch.cuda.synchronize()
-        ev0.record(stream)
-        for i in range(n_k):
-            fn(calls[i % n_sets])
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        return ev0.elapsed_time(ev1) * 1e3 / n_k
-
-    off_mean_us = None
-    if plan["fused"]:
-        kernel_name = "fused_kernel"
-        kern_mean_us = back_to_back_us(lambda c: c.run())
-        kbytes = alg_bytes
-    else:
-        kernel_name = "stream_gather_kernel" if plan["gather_kernel"] == 1 else "gather_kernel"
-        off_mean_us = back_to_back_us(lambda c: c.run_offsets())
-        for c in calls:
-            c.run_offsets()
-        kern_mean_us = back_to_back_us(lambda c: c.run_gather())
-        kbytes = gather_bytes_per_launch(w)
-    achieved = kbytes / (kern_mean_us * 1e-6) / 1e9
-    print(f"[bench] plan {plan}", file=sys.stderr, flush=True)
-    print(f"[bench] per kernel ({n_k} back-to-back launches): {kernel_name} {kern_mean_us:.2f} us, "
-          f"{achieved:.1f} GB/s; offsets kernel {off_mean_us} us", file=sys.stderr, flush=True)
+    kname, kbytes, k_us, k_pair, off_us = b.kernel(n_k)
+    achieved = kbytes / (k_us * 1e-6) / 1e9
+    print(f"[bench] plan {b.plan}", file=sys.stderr, flush=True)
+    print(f"[bench] {kname}: {k_us:.2f} us back to back, {achieved:.1f} GB/s ({k_pair:.2f} us per event pair); "
+          f"offsets kernel {off_us} us back to back", file=sys.stderr, flush=True)
 
     # hot (same buffers every call), labelled as such
-    torch.cuda.synchronize()
-    ev0.record(stream)
+    b.torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(b.stream)
     for _ in range(opt.steps):
-        calls[0].run()
-    ev1.record(stream)
+        b.calls[0].run()
+    e1.record(b.stream)
     torch.cuda.synchronize()
-    hot_us = ev0.elapsed_time(ev1) * 1e3 / opt.steps
+    hot_us = e0.elapsed_time(e1) * 1e3 / opt.steps
+    graph_us = b.graph_us(opt.steps)
 
-    # the same calls captured in one HIP graph (the launch path allocates,
-    # sets and synchronizes nothing) and replayed: the per-call cost without
-    # the host's launch overhead, which dominates small calls
-    side = torch.cuda.Stream(dev)
-    n_cap = min(n_sets, 1000)  # calls per graph, each on its own buffer set
-    gcalls = []
-    for t in inputs[:n_cap]:
-        gc, _ = api.make_call(t["tokens"], t["counts"], per_token_scales=t["scales"],
-                              expert_topk_weight=t["weight"], expert_token_num_type=w.etn_type,
-                              idx_type=w.idx_type, tokens_dtype=t["tokens_dtype"], stream=side,
-                              direction=_lib.INVERSE if opt.inverse else _lib.FORWARD)
-        gcalls.append(gc)
-    with torch.cuda.stream(side):
-        for gc in gcalls:
-            gc.run()
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=side):
-        for i in range(n_cap):
-            gcalls[i % len(gcalls)].run()
-    torch.cuda.synchronize()
-    graph.replay()
-    torch.cuda.synchronize()
-    reps = max(1, opt.steps // n_cap)
-    t0 = time.perf_counter()
-    for _ in range(reps):
-        graph.replay()
-    torch.cuda.synchronize()
-    graph_us = (time.perf_counter() - t0) * 1e6 / (reps * n_cap)
-    if any(gc.device_status() != _lib.SUCCESS for gc in gcalls[:1]):
-        raise SystemExit("device status after graph replays")
-    del graph, gcalls
-
-    # copy ceiling over the same token bytes, same rotation
     ceiling = None
     if not opt.no_ceiling:
-        nbytes16 = (w.A * w.token_row_bytes) // 16 * 16
-        srcs = [c.args.tokens for c in calls]
-        dsts = [torch.empty(nbytes16, dtype=torch.uint8, device=dev) for _ in range(n_sets)]
-        hip = ctypes.CDLL("libamdhip64.so")
-        hip.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
-                                       ctypes.c_void_p]
-        hip.hipMemcpyAsync.restype = ctypes.c_int
-        hip_d2d = 3  # hipMemcpyDeviceToDevice
-        s_ptr = stream.cuda_stream
-        for i in range(10):
-            assert bench_lib.mrr_bench_copy(dsts[i % n_sets].data_ptr(), srcs[i % n_sets], nbytes16, s_ptr) == 0
-            assert hip.hipMemcpyAsync(dsts[i % n_sets].data_ptr(), srcs[i % n_sets], nbytes16, hip_d2d, s_ptr) == 0
-        torch.cuda.synchronize()
-        ev0.record(stream)
-        for i in range(opt.steps):
-            bench_lib.mrr_bench_copy(dsts[i % n_sets].data_ptr(), srcs[i % n_sets], nbytes16, s_ptr)
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        kern_us = ev0.elapsed_time(ev1) * 1e3 / opt.steps
-        ev0.record(stream)
-        for i in range(opt.steps):
-            hip.hipMemcpyAsync(dsts[i % n_sets].data_ptr(), srcs[i % n_sets], nbytes16, hip_d2d, s_ptr)
-        ev1.record(stream)
-        torch.cuda.synchronize()
-        memcpy_us = ev0.elapsed_time(ev1) * 1e3 / opt.steps
-        ceil_gbps = max(2 * nbytes16 / (kern_us * 1e-6) / 1e9, 2 * nbytes16 / (memcpy_us * 1e-6) / 1e9)
-        ceiling = {"copy_kernel_us": round(kern_us, 2), "memcpy_d2d_us": round(memcpy_us, 2),
-                   "bytes_read_plus_written": 2 * nbytes16, "ceiling_GBps": round(ceil_gbps, 1),
-                   "gather_frac_of_ceiling": round(achieved / ceil_gbps, 4),
-                   "call_frac_of_ceiling": round(value / ceil_gbps, 4)}
-        print(f"[bench] copy ceiling: kernel {kern_us:.2f} us, hipMemcpyAsync {memcpy_us:.2f} us, "
-              f"{ceil_gbps:.1f} GB/s", file=sys.stderr, flush=True)
-        del dsts
+        ceiling = b.copy_ceiling(copy_lib, opt.steps)
+        ceiling["gather_frac_of_ceiling"] = round(achieved / ceiling["ceiling_GBps"], 4)
+        ceiling["call_frac_of_ceiling"] = round(value / ceiling["ceiling_GBps"], 4)
+        print(f"[bench] copy ceiling: {ceiling}", file=sys.stderr, flush=True)
 
     cpu = None
     if not opt.no_cpu:
         med_s, runs = time_oracle(w, inverse=opt.inverse)
-        cpu = {"value": round(alg_bytes / med_s / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+        cpu = {"value": round(b.alg_bytes / med_s / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
                "sample": f"the full {w.name} workload (one whole call), median of {runs} runs, "
                          f"{med_s * 1e3:.1f} ms/call; host has {os.cpu_count()} logical CPUs",
                "cpu_model": cpu_model()}
         print(f"[bench] oracle: {med_s * 1e3:.1f} ms/call on 1 thread", file=sys.stderr, flush=True)
 
+    direction = "inverse" if opt.inverse else "forward"
+    k_rp = rocprof_average_us(w, kname, direction)
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -361,7 +450,7 @@ def main():
         "n_gpus": 1,
         "steps": opt.steps,
         "warmup": opt.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(us * 1e-3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -371,26 +460,40 @@ def main():
                    "tokens_dtype": w.tokens_dtype, "counts_dtype": str(w.counts.dtype),
                    "scales": None if w.scales is None else f"{w.scales_dtype}{list(w.scales.shape)}",
                    "topk_weight": w.weight is not None, "expert_token_num_type": w.etn_type,
-                   "idx_type": w.idx_type, "direction": "inverse" if opt.inverse else "forward",
-                   "buffer_sets": n_sets, "parallelism": "single GPU"},
-        "us_per_call": round(ms_per_step * 1e3, 2),
-        "us_per_call_events": round(ev_ms * 1e3 / opt.steps, 2),
-        "us_per_call_event_pair_median": round(per_call_median_us, 2),
+                   "idx_type": w.idx_type, "direction": direction,
+                   "buffer_sets": b.n_sets, "parallelism": "single GPU"},
+        "us_per_call": round(us, 2),
+        "us_per_call_events": round(ev_us, 2),
+        "us_per_call_event_pair_median": round(pair_median_us, 2),
         "us_per_call_hot_same_buffers": round(hot_us, 2),
         "us_per_call_graph": round(graph_us, 2),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
-        "algorithmic_bytes_per_call": alg_bytes,
-        "launch_path": "fused single kernel" if plan["fused"] else "offsets kernel + gather kernel",
-        "offsets_kernel_us_mean": None if off_mean_us is None else round(off_mean_us, 2),
+        "algorithmic_bytes_per_call": b.alg_bytes,
+        "launch_path": "fused single kernel" if b.plan["fused"] else "offsets kernel + gather kernel",
+        "offsets_kernel_us_back_to_back": None if off_us is None else round(off_us, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic_from_profile(w, kernel_name, "inverse" if opt.inverse else "forward"),
-                     "kernel": kernel_name, "bytes_per_launch": kbytes,
-                     "launch_us_mean": round(kern_mean_us, 2)},
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic_from_profile(w, kname, direction),
+                     "kernel": kname, "bytes_per_launch": kbytes,
+                     "launch_us_mean": round(k_us, 2),
+                     "launch_us_source": f"{n_k} launches back to back between two HIP events on the launch stream",
+                     "launch_us_rocprof": None if k_rp is None else round(k_rp, 2),
+                     "frac_rocprof": None if k_rp is None else round(kbytes / (k_rp * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "launch_us_source_rocprof": None if k_rp is None else
+                     "profiles/pages_shape_kernel_stats.md (rocprofv3 --kernel-trace --stats of this bench)"},
         "copy_ceiling": ceiling,
         "cpu_baseline": cpu,
         "library_source_hash": _lib.library_source_hash(),
         "device": device,
     }
+    del b
+    if not opt.no_workloads and not opt.inverse and w.name == "pages_shape":
+        others = {}
+        for name, d in OTHER_WORKLOADS:
+            others[name if d == "forward" else f"{name}_{d}"] = workload_summary(
+                torch, dev, name, d, copy_lib, max(50, min(opt.steps, 200)))
+            torch.cuda.empty_cache()
+        line["workloads"] = others
     print(json.dumps(line), flush=True)
 
 

@@ -242,7 +242,7 @@ struct StreamGrid {
   float inv_svpr;
   uint32_t byte_rows;    // token rows stream as bytes: aligned 16-byte blocks of the output
   float inv_row;         // 1 / row bytes, for byte_rows with rows under 1 KiB
-  double inv_row_d;      // 1 / row bytes, for a chunk's first row (a quotient below 2^45)
+  uint32_t row_magic;    // ceil(2^32 / row bytes): quotients by the row length (byte_rows)
   uint32_t rows8;        // byte_rows with R >= 147 and A >= 8: a 1 KiB chunk spans at most
                          // floor(1023 / R) + 2 <= 8 rows
   uint32_t fold_scales;  // scale rows of one 4-byte word move in the item chunks
@@ -335,6 +335,48 @@ __device__ __forceinline__ VecT<16>::type funnel16(const VecT<16>::type& lo, con
   return out;
 }
 
+// funnel16 for a shift that is the same in every lane: a branch on q = sh / 4
+// picks the four byte-aligned word pairs.
+__device__ __forceinline__ VecT<16>::type funnel16_uniform(const VecT<16>::type& lo, const VecT<16>::type& hi,
+                                                           int sh) {
+  const uint32_t r = static_cast<uint32_t>(sh & 3);
+  VecT<16>::type o;
+  switch (sh >> 2) {
+    case 0:
+      o.x = __builtin_amdgcn_alignbyte(lo.y, lo.x, r);
+      o.y = __builtin_amdgcn_alignbyte(lo.z, lo.y, r);
+      o.z = __builtin_amdgcn_alignbyte(lo.w, lo.z, r);
+      o.w = __builtin_amdgcn_alignbyte(hi.x, lo.w, r);
+      break;
+    case 1:
+      o.x = __builtin_amdgcn_alignbyte(lo.z, lo.y, r);
+      o.y = __builtin_amdgcn_alignbyte(lo.w, lo.z, r);
+      o.z = __builtin_amdgcn_alignbyte(hi.x, lo.w, r);
+      o.w = __builtin_amdgcn_alignbyte(hi.y, hi.x, r);
+      break;
+    case 2:
+      o.x = __builtin_amdgcn_alignbyte(lo.w, lo.z, r);
+      o.y = __builtin_amdgcn_alignbyte(hi.x, lo.w, r);
+      o.z = __builtin_amdgcn_alignbyte(hi.y, hi.x, r);
+      o.w = __builtin_amdgcn_alignbyte(hi.z, hi.y, r);
+      break;
+    default:
+      o.x = __builtin_amdgcn_alignbyte(hi.x, lo.w, r);
+      o.y = __builtin_amdgcn_alignbyte(hi.y, hi.x, r);
+      o.z = __builtin_amdgcn_alignbyte(hi.z, hi.y, r);
+      o.w = __builtin_amdgcn_alignbyte(hi.w, hi.z, r);
+      break;
+  }
+  return o;
+}
+
+// floor(n / d) for n < 2^31 and 2 <= d < 2^16, with magic = ceil(2^32 / d):
+// the multiply-high is the quotient or one more.
+__device__ __forceinline__ uint32_t div_magic(uint32_t n, uint32_t d, uint32_t magic) {
+  const uint32_t q = __umulhi(n, magic);
+  return q - (q * d > n ? 1u : 0u);
+}
+
 // Bytes [w, w + 16) of `base`, of which [n0, n1) are needed (w <= n0 < n1 <=
 // w + 16): two aligned 16-byte loads, each of a block that holds a needed
 // byte (a block with none takes the other's address, so no load leaves the
@@ -353,103 +395,32 @@ __device__ __forceinline__ VecT<16>::type window16(const uint8_t* __restrict__ b
 // One aligned 16-byte block of a run copy: output byte o takes input byte
 // o + delta for the whole chunk (sh = delta & 15, the same in every lane).
 // Loads the aligned input block holding byte o + delta, and the next one when
-// sh != 0 (both then hold some of the 16 bytes), and funnel-shifts them.
+// sh != 0 (both then hold some of the 16 bytes), and funnel-shifts them. The
+// two loads of neighbouring lanes overlap, so they are plain loads: the second
+// one then finds the block in the cache (with non-temporal loads a shifted
+// 41 MB copy measured 15.95 us against 14.40 us with plain loads and 13.88
+// us for an aligned copy).
 __device__ __forceinline__ VecT<16>::type run_block(const uint8_t* __restrict__ tokens, int64_t o, int64_t delta,
                                                     int sh) {
   using T = VecT<16>::type;
   const int64_t a = o + (delta - sh);
-  const T lo = __builtin_nontemporal_load(reinterpret_cast<const T*>(tokens + a));
-  if (sh == 0) return lo;  // uniform
-  const T hi = __builtin_nontemporal_load(reinterpret_cast<const T*>(tokens + a + 16));
-  return funnel16(lo, hi, sh);
+  if (sh == 0)  // uniform
+    return __builtin_nontemporal_load(reinterpret_cast<const T*>(tokens + a));
+  const T lo = *reinterpret_cast<const T*>(tokens + a);
+  const T hi = *reinterpret_cast<const T*>(tokens + a + 16);
+  return funnel16_uniform(lo, hi, sh);
 }
 
-// Token rows that are no multiple of 16 bytes (at least 17 bytes, both
-// buffers 16-byte aligned), as one byte stream: lane l of chunk c builds the
-// aligned 16-byte block of the dense output at byte 1024 c + 16 l, from the
-// chunk's output rows (at most 1024 / 17 + 2 < 64 of them).
-//  * Run copy: when those rows come from consecutive input rows (one segment,
-//    or segments that continue each other) and the chunk is whole, its 1 KiB
-//    is one byte range of the input at a fixed distance (the pages' moves copy
-//    a segment's rows in order, so a segment is contiguous on both sides):
-//    run_block per lane.
-//  * Otherwise each block takes its bytes from at most two output rows, i.e.
-//    two input rows, with window16 each; the last, partial block of the output
-//    is stored byte by byte.
-// With rows of 147 bytes or more (rows8) a chunk spans at most 8 rows, whose
-// row-map words the wave reads through the scalar cache beside the header, and
-// the run check is scalar; with shorter rows lane k loads the k-th row's word
-// and a ballot checks the run.
-__device__ __forceinline__ void stream_bytes_chunk(const GatherArgs& p, const StreamGrid& g, uint32_t chunk) {
+// One aligned 16-byte block o of the dense output of byte rows, in general:
+// its bytes come from output rows d1 (from byte col1, len1 bytes) and, when
+// has2, the next one, i.e. from input rows s1 and s2, each with window16; a
+// byte mask merges the two parts. The last, partial block of the output is
+// stored byte by byte. Nothing is stored unless hv and both input rows lie in
+// [0, A).
+__device__ __forceinline__ void byte_block(const GatherArgs& p, int64_t o, int64_t total, int col1, int len1,
+                                           bool has2, int32_t s1, int32_t s2, bool hv) {
   using T = VecT<16>::type;
-  const int lane = threadIdx.x & 63;
   const int64_t R = p.row_bytes;
-  const int64_t total = int64_t(p.A) * R;
-  const int64_t o0 = int64_t(chunk) * 1024;
-  // the chunk's first row, floor(o0 / R): a double estimate within 2^-10 of
-  // the quotient, then an exact integer correction
-  int64_t d_base = static_cast<int64_t>(static_cast<double>(o0) * g.inv_row_d);
-  d_base -= d_base * R > o0 ? 1 : 0;
-  d_base += (d_base + 1) * R <= o0 ? 1 : 0;
-  const int64_t o_last = min(o0 + 1023, total - 1);
-  const int span = static_cast<int>(o_last / R - d_base) + 1;  // rows the chunk touches (uniform)
-  const bool whole = o0 + 1024 <= total;
-  const bool hv = header_valid(p.hdr, p);  // its loads go out first, beside the row-map loads
-  const int64_t o = o0 + 16 * lane;
-  // Row within the chunk: at most one boundary for rows of 1 KiB or more;
-  // below that, a small exact division (off < 2048).
-  const int off = static_cast<int>(o0 - d_base * R) + 16 * lane;  // < R + 1024
-  const int Ri = static_cast<int>(R);
-  const int dd = Ri >= 1024 ? (off >= Ri ? 1 : 0) : div_small(off, g.inv_row);
-  const int col1 = off - dd * Ri;
-  const int d1 = static_cast<int>(d_base) + dd;
-  const int len1 = min(16, Ri - col1);  // bytes from row d1; the rest from row d1 + 1
-  const bool has2 = len1 < 16;
-  const int d2 = has2 ? min(d1 + 1, p.A - 1) : d1;
-  int32_t s1, s2;
-  if (g.rows8) {  // uniform: the chunk's rows lie in 8 consecutive row-map words from
-                  // min(d_base, A - 8) on
-    using CInt = const int32_t __attribute__((address_space(4)))*;
-    const int base = min(static_cast<int>(d_base), p.A - 8);
-    const CInt m = reinterpret_cast<CInt>(reinterpret_cast<uintptr_t>(p.rowmap + base));
-    int32_t w[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) w[k] = m[k];
-    bool run = whole & (base == d_base);
-#pragma unroll
-    for (int k = 1; k < 8; ++k) run &= (k >= span) | (w[k] == w[0] + k);
-    if (run) {  // uniform
-      const bool ok = hv & (w[0] >= 0) & (int64_t(w[0]) + span <= p.A);
-      const int64_t delta = ok ? (int64_t(w[0]) - d_base) * R : -o0;  // not moving: input bytes [0, 1024)
-      const T v = run_block(p.tokens, o, delta, static_cast<int>(delta & 15));
-      if (ok) __builtin_nontemporal_store(v, reinterpret_cast<T*>(p.out_tokens + o));
-      return;
-    }
-    const int k1 = d1 - base, k2 = d2 - base;  // in [0, 8)
-    s1 = w[0];
-    s2 = w[0];
-#pragma unroll
-    for (int k = 1; k < 8; ++k) {
-      s1 = k1 == k ? w[k] : s1;
-      s2 = k2 == k ? w[k] : s2;
-    }
-  } else {
-    const int32_t word = p.rowmap[min(static_cast<int>(d_base) + lane, p.A - 1)];
-    const int32_t s0 = __builtin_amdgcn_readfirstlane(word);
-    const bool brk = lane < span && word != s0 + lane;
-    if (__builtin_amdgcn_ballot_w64(brk) == 0 && whole) {  // uniform: run copy
-      const bool ok = hv & (s0 >= 0) & (int64_t(s0) + span <= p.A);
-      const int64_t delta = ok ? (int64_t(s0) - d_base) * R : -o0;  // not moving: input bytes [0, 1024)
-      const int sh = __builtin_amdgcn_readfirstlane(static_cast<int>(delta & 15));
-      const T v = run_block(p.tokens, o, delta, sh);
-      if (ok) __builtin_nontemporal_store(v, reinterpret_cast<T*>(p.out_tokens + o));
-      return;
-    }
-    // the rows' words from the lanes that loaded them (every lane takes part)
-    s1 = __shfl(word, min(dd, 63), 64);
-    s2 = __shfl(word, min(d2 - static_cast<int>(d_base), 63), 64);
-  }
-  if (o >= total) return;
   const bool ok = hv & (static_cast<unsigned>(s1) < static_cast<unsigned>(p.A)) &
                   (static_cast<unsigned>(s2) < static_cast<unsigned>(p.A));
   s1 = ok ? s1 : 0;  // input row 0 when not moving: always valid here
@@ -457,8 +428,8 @@ __device__ __forceinline__ void stream_bytes_chunk(const GatherArgs& p, const St
   const int64_t w1 = int64_t(s1) * R + col1;
   T v = window16(p.tokens, w1, w1, w1 + len1);
   if (has2) {  // the block crosses into the next row (a few lanes of a wave)
-    const int64_t r2 = int64_t(s2) * R;  // output byte b >= len1 is input byte r2 + b - len1
-    const T x2 = window16(p.tokens, r2 - len1, r2, r2 + (16 - len1));
+    const int64_t r2b = int64_t(s2) * R;  // output byte b >= len1 is input byte r2b + b - len1
+    const T x2 = window16(p.tokens, r2b - len1, r2b, r2b + (16 - len1));
     uint32_t m[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -478,6 +449,104 @@ __device__ __forceinline__ void stream_bytes_chunk(const GatherArgs& p, const St
     for (int b = 0; b < static_cast<int>(total - o); ++b)
       p.out_tokens[o + b] = static_cast<uint8_t>(wv[b >> 2] >> (8 * (b & 3)));
   }
+}
+
+// Token rows that are no multiple of 16 bytes (at least 17 bytes, both
+// buffers 16-byte aligned), as one byte stream: lane l of chunk c builds the
+// aligned 16-byte block of the dense output at byte 1024 c + 16 l, from the
+// chunk's output rows.
+//  * Run copy: when those rows come from consecutive input rows (one segment,
+//    or segments that continue each other) and the chunk is whole, its 1 KiB
+//    is one byte range of the input at a fixed distance (the pages' moves copy
+//    a segment's rows in order, so a segment is contiguous on both sides):
+//    run_block.
+//  * Otherwise byte_block.
+// With rows of 147 bytes or more (rows8) a chunk spans at most 8 rows, whose
+// row-map words the wave reads through the scalar cache beside the header, and
+// the run check is scalar; with shorter rows (at most 1024 / 17 + 2 < 64 of
+// them) lane k loads the k-th row's word and a ballot checks the run. The
+// chunk's first row and its offset there come from 32-bit scalar quotients by
+// R. (2 KiB chunks of 16 scalar words, amortizing this prologue, measured no
+// faster at odd_rows.)
+__device__ __forceinline__ void stream_bytes_chunk(const GatherArgs& p, const StreamGrid& g, uint32_t chunk) {
+  using T = VecT<16>::type;
+  const int lane = threadIdx.x & 63;
+  const int64_t R = p.row_bytes;
+  const uint32_t R32 = static_cast<uint32_t>(R);
+  const int Ri = static_cast<int>(R32);
+  const int64_t total = int64_t(p.A) * R;
+  const int64_t o0 = int64_t(chunk) * 1024;
+  // d_base = floor(1024 c / R) and off0 = 1024 c - d_base R: with c = qc R +
+  // rc, 1024 c / R = 1024 qc + 1024 rc / R, and 1024 rc < 2^25.
+  const uint32_t qc = div_magic(chunk, R32, g.row_magic);
+  const uint32_t rc = chunk - qc * R32;
+  const uint32_t r2 = div_magic(1024u * rc, R32, g.row_magic);
+  const int d_base = static_cast<int>(1024u * qc + r2);  // < A
+  const uint32_t off0 = 1024u * rc - r2 * R32;           // < R
+  const bool whole = o0 + 1024 <= total;
+  // rows the chunk touches: up to the one holding its last byte
+  const uint32_t last = whole ? 1023u : static_cast<uint32_t>(total - 1 - o0);
+  const int span = static_cast<int>(div_magic(off0 + last, R32, g.row_magic)) + 1;
+  const int64_t o = o0 + 16 * lane;
+  // this lane's block: from output row d_base + dd, byte col1, len1 bytes, the rest from the next row
+  const int off = static_cast<int>(off0) + 16 * lane;  // < R + 1024
+  int32_t s1, s2;
+  bool hv;
+  int dd;
+  if (g.rows8) {  // uniform: the chunk's rows lie in 8 consecutive row-map words from
+                  // min(d_base, A - 8) on, read through the scalar cache
+    using CInt = const int32_t __attribute__((address_space(4)))*;
+    const int base = min(d_base, p.A - 8);
+    const CInt m = reinterpret_cast<CInt>(reinterpret_cast<uintptr_t>(p.rowmap + base));
+    int32_t w[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) w[k] = m[k];
+    hv = header_valid(p.hdr, p);  // its loads go out after the row-map loads, both waited for once
+    // a run: w[k] == w[0] + k for the chunk's rows k < span
+    uint32_t diff = 0;
+#pragma unroll
+    for (int k = 1; k < 8; ++k) diff |= k < span ? static_cast<uint32_t>(w[k] - w[0] - k) : 0u;
+    if (whole & (base == d_base) & (diff == 0)) {  // uniform: run copy
+      const bool ok = hv & (w[0] >= 0) & (int64_t(w[0]) + span <= p.A);
+      const int64_t delta = ok ? (int64_t(w[0]) - d_base) * R : -o0;  // not moving: input bytes [0, 1024)
+      const T v = run_block(p.tokens, o, delta, static_cast<int>(delta & 15));
+      if (ok) __builtin_nontemporal_store(v, reinterpret_cast<T*>(p.out_tokens + o));
+      return;
+    }
+    // row within the chunk: at most one boundary for rows of 1 KiB or more; below that,
+    // a small exact division (off < 2048)
+    dd = Ri >= 1024 ? (off >= Ri ? 1 : 0) : div_small(off, g.inv_row);
+    const int k1 = d_base + dd - base;
+    const int k2 = min(d_base + dd + 1, p.A - 1) - base;  // in [0, 8) for lanes inside the output
+    s1 = w[0];
+    s2 = w[0];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) {
+      s1 = k1 == k ? w[k] : s1;
+      s2 = k2 == k ? w[k] : s2;
+    }
+  } else {
+    const int32_t word = p.rowmap[min(d_base + lane, p.A - 1)];
+    hv = header_valid(p.hdr, p);  // its loads go out beside the row-map load
+    const int32_t s0 = __builtin_amdgcn_readfirstlane(word);
+    const bool brk = lane < span && word != s0 + lane;
+    if (__builtin_amdgcn_ballot_w64(brk) == 0 && whole) {  // uniform: run copy
+      const bool ok = hv & (s0 >= 0) & (int64_t(s0) + span <= p.A);
+      const int64_t delta = ok ? (int64_t(s0) - d_base) * R : -o0;  // not moving: input bytes [0, 1024)
+      const int sh = __builtin_amdgcn_readfirstlane(static_cast<int>(delta & 15));
+      const T v = run_block(p.tokens, o, delta, sh);
+      if (ok) __builtin_nontemporal_store(v, reinterpret_cast<T*>(p.out_tokens + o));
+      return;
+    }
+    dd = Ri >= 1024 ? (off >= Ri ? 1 : 0) : div_small(off, g.inv_row);
+    // the rows' words from the lanes that loaded them (every lane takes part)
+    s1 = __shfl(word, min(dd, 63), 64);
+    s2 = __shfl(word, min(min(d_base + dd + 1, p.A - 1) - d_base, 63), 64);
+  }
+  const int col1 = off - dd * Ri;
+  const int len1 = min(16, Ri - col1);
+  const bool has2 = len1 < 16;
+  if (o < total) byte_block(p, o, total, col1, len1, has2, s1, has2 ? s2 : s1, hv);
 }
 
 // Four words to dst[0..3]: one 16-byte store when `whole` (all four move and
@@ -611,7 +680,7 @@ StreamGrid stream_grid(const Plan& pl) {
   sg.cpr_magic = 0;
   sg.byte_rows = pl.byte_rows ? 1u : 0u;
   sg.inv_row = 1.0f / static_cast<float>(pl.row_bytes);
-  sg.inv_row_d = 1.0 / static_cast<double>(pl.row_bytes);
+  sg.row_magic = pl.byte_rows ? static_cast<uint32_t>(((uint64_t(1) << 32) + pl.row_bytes - 1) / pl.row_bytes) : 0u;
   sg.rows8 = pl.byte_rows && pl.row_bytes >= 147 && pl.A >= 8 ? 1u : 0u;
   sg.fold_scales = pl.fold_scales ? 1u : 0u;
   sg.idx16 = 0;

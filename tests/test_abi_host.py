@@ -226,6 +226,10 @@ def test_describe_plan():
     st, info = describe(valid_args(tok=_lib.F16, H=79, A=262144, N=16, E=16))
     assert st == _lib.SUCCESS and info.gather_kernel == 1 and info.token_vec_bytes == 16
     assert info.gather_workgroups == (262144 * 158 + 1023) // 1024 + 262144 // 256
+    # rows under 147 bytes: the same 1 KiB chunks (their row-map words loaded one per lane)
+    st, info = describe(valid_args(tok=_lib.F16, H=63, A=65536, N=16, E=16))
+    assert st == _lib.SUCCESS and info.gather_kernel == 1 and info.fused == 0
+    assert info.gather_workgroups == (65536 * 126 + 1023) // 1024 + 65536 // 256
     # scale rows of more than 16 bytes keep chunks of their own (e8m0 [A, 112, 2]: 224 bytes a row)
     st, info = describe(valid_args(A=32768, H=7168, N=32, E=8, tok=_lib.F8_E4M3FN, scales="e8m0"))
     assert st == _lib.SUCCESS and info.gather_kernel == 1

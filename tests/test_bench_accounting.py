@@ -58,3 +58,19 @@ def test_traffic_needs_matching_source(tmp_path, monkeypatch):
     assert bench.traffic_from_profile(w, "k", "inverse") is None
     summary.write_text(summary.read_text().replace(bench.kernel_source_hash(), "0" * 16))
     assert bench.traffic_from_profile(w, "k") is None
+
+
+def test_rocprof_average_needs_matching_source(tmp_path, monkeypatch):
+    """The committed kernel-trace average is reported only for its workload and
+    direction, and only while its source hash matches the library's sources."""
+    w = workloads.make("tiny")
+    summary = tmp_path / "stats.md"
+    fields = {"workload": "tiny", "direction": "forward", "source_hash": bench.kernel_source_hash(),
+              "average_ns_fused_kernel": "3740.5"}
+    summary.write_text("# a summary\n\n" + "".join(f"{k}: {v}\n" for k, v in fields.items()))
+    monkeypatch.setattr(bench, "STATS_SUMMARY", str(summary))
+    assert bench.rocprof_average_us(w, "fused_kernel") == pytest.approx(3.7405)
+    assert bench.rocprof_average_us(w, "stream_gather_kernel") is None
+    assert bench.rocprof_average_us(w, "fused_kernel", "inverse") is None
+    summary.write_text(summary.read_text().replace(bench.kernel_source_hash(), "0" * 16))
+    assert bench.rocprof_average_us(w, "fused_kernel") is None
