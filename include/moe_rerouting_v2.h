@@ -151,6 +151,10 @@ enum { MRR_FORWARD = 0, MRR_INVERSE = 1 };
  * E is negative, A > INT32_MAX, or N*E is too large for 32-bit cell indices.
  * The caller allocates it (no zeroing needed); it may be reused by calls
  * ordered on one stream.
+ * (A convention of this library: the article's operator keeps its offsets in
+ * per-core tiling data instead. The size depends on A, not only on N and E,
+ * because the gather reads the source row of every output row from the
+ * workspace.)
  */
 size_t mrr_workspace_size(int64_t A, int64_t N, int64_t E);
 
@@ -159,6 +163,12 @@ size_t mrr_workspace_size(int64_t A, int64_t N, int64_t E);
  * on the host only: no HIP call is made, so this runs without a GPU. The
  * pointers are compared and tested for alignment, never dereferenced.
  * Returns MRR_SUCCESS or the first error found.
+ * The checks are the article's contract (parameter table "参数说明", the
+ * constraints "约束说明" and the InferShape rules: dtypes, 0 < H < 16384,
+ * shapes of the optional inputs, the pairing of the top-k weight input and
+ * output) plus this library's own: pointer alignment, no overlap between any
+ * output and any other buffer, and the workspace's size. The workspace
+ * pointer is an argument because the alignment and overlap checks need it.
  */
 mrr_status mrr_validate(const mrr_args* args, const void* workspace, size_t workspace_bytes);
 
@@ -197,16 +207,20 @@ typedef struct mrr_plan_info {
 
 /*
  * Runs the same host checks as mrr_validate() and, on success, describes the
- * launch in *info. Host only, no HIP call.
+ * launch in *info. Host only, no HIP call. (A convention of this library.)
  */
 mrr_status mrr_describe_plan(const mrr_args* args, const void* workspace, size_t workspace_bytes,
                              mrr_plan_info* info);
 
 /*
- * The whole operator on `stream`, asynchronous. Depending on the size of the
- * count matrix (see mrr_plan_info.fused) this launches either one fused
- * kernel, or moe_rerouting_v2_offsets() then moe_rerouting_v2_gather(); the
- * results are identical. Host-detectable errors are returned before any
+ * The whole operator on `stream`, asynchronous (article "CANN ops-transformer
+ * MoeReRoutingV2", section "计算公式": the two double sums and the moves of
+ * tokens, per_token_scales and expert_topk_weight; section "参数说明": the
+ * inputs, outputs and attributes of mrr_args, permute_token_idx in gather or
+ * scatter form, expert_token_num as counts or their running sum). Depending on
+ * the size of the call (see mrr_plan_info.fused) this launches either one
+ * fused kernel, or moe_rerouting_v2_offsets() then moe_rerouting_v2_gather();
+ * the results are identical. Host-detectable errors are returned before any
  * launch; count errors are found on the device (see mrr_get_device_status).
  */
 mrr_status moe_rerouting_v2(const mrr_args* args, void* workspace, size_t workspace_bytes,
@@ -267,7 +281,10 @@ mrr_status moe_rerouting_v2_gather(const mrr_args* args, void* workspace, size_t
  * phase) left in `workspace`: MRR_SUCCESS (the counts were valid),
  * MRR_ERROR_BAD_COUNTS, MRR_ERROR_INVALID_VALUE if the workspace holds no
  * status (no call ran on it), or MRR_ERROR_HIP if the copy or the wait fails.
- * Synchronizing: not for use inside a hot loop.
+ * Synchronizing: not for use inside a hot loop. (The verdict on the article's
+ * constraints of "约束说明" — counts summing to A, no negative count — which
+ * only the device can check; how it is reported is this library's
+ * convention.)
  */
 mrr_status mrr_get_device_status(const void* workspace, struct ihipStream_t* stream);
 

@@ -311,10 +311,12 @@ __device__ __forceinline__ void finish_offsets(pair_t* tab, int32_t* col, int M,
 // col[E] = A. With a row map, also rowmap[d] for d = row0 + thread (one row
 // per thread, coalesced); with s_map instead, s_map[thread] = that value in
 // LDS (-1 past A).
-// Returns 0, or the rejection flags (the same in every thread; then tab and
-// col are not written).
+// raw is the thread's count (row-major cell tid; anything past the matrix),
+// loaded by the caller ahead of its other loads so that the offsets wait for
+// it alone. Returns 0, or the rejection flags (the same in every thread; then
+// tab and col are not written).
 template <int kThreads, typename CountT>
-__device__ uint32_t offsets_cells(const CountT* __restrict__ counts, int N, int E, int64_t A, int inverse,
+__device__ uint32_t offsets_cells(CountT raw, int N, int E, int64_t A, int inverse,
                                   int32_t* lds, int32_t* col, pair_t* tab, ScanShared<kThreads>* sh,
                                   int64_t* total_out, int32_t* __restrict__ rowmap = nullptr, int row0 = 0,
                                   int32_t* s_mark = nullptr, int32_t* s_map = nullptr) {
@@ -329,7 +331,7 @@ __device__ uint32_t offsets_cells(const CountT* __restrict__ counts, int N, int 
   // Thread t holds cell t in row-major (rank i, expert j) order.
   const bool in = tid < M;
   uint32_t c = 0;
-  if (in) c = static_cast<uint32_t>(clamp_count(counts[tid], &flags));
+  if (in) c = static_cast<uint32_t>(clamp_count(raw, &flags));
   const int ci = in ? tid / E : 0;
   const int cj = tid - ci * E;
   if (in) s_c[cj * N + ci] = static_cast<int32_t>(c);  // column-major, ordered by the scan's barrier
@@ -433,15 +435,32 @@ struct WaveCells {
   int expert;       // lane u: its expert j
 };
 
-// Returns the rejection flags (the same in every lane) and, in *total, the
-// exact sum of the clamped counts. All 64 lanes must be active.
+// The raw count of row-major cell threadIdx.x, 0 past the matrix (no load:
+// the count pointer may be null when the matrix has no cells).
 template <typename CountT>
-__device__ __forceinline__ uint32_t wave_offsets64(const CountT* __restrict__ counts, int N, int E, int64_t A,
-                                                   WaveCells* w, int64_t* total) {
+__device__ __forceinline__ CountT load_count(const CountT* __restrict__ counts, int M) {
+  return static_cast<int>(threadIdx.x) < M ? counts[threadIdx.x] : CountT(0);
+}
+
+// The raw count of the cell a lane of a wave holds in wave_offsets64 (lane q:
+// row-major cell q), 0 past the matrix. Loaded by the caller ahead of other
+// loads, so that the offsets wait for it alone.
+template <typename CountT>
+__device__ __forceinline__ CountT load_count64(const CountT* __restrict__ counts, int M) {
+  const int lane = threadIdx.x & 63;
+  return lane < M ? counts[lane] : CountT(0);
+}
+
+// Returns the rejection flags (the same in every lane) and, in *total, the
+// exact sum of the clamped counts; raw is load_count64's value. All 64 lanes
+// must be active.
+template <typename CountT>
+__device__ __forceinline__ uint32_t wave_offsets64(CountT raw, int N, int E, int64_t A, WaveCells* w,
+                                                   int64_t* total) {
   const int lane = threadIdx.x & 63;
   const int M = N * E;
   uint32_t f = 0;
-  const uint32_t c = lane < M ? static_cast<uint32_t>(clamp_count(counts[lane], &f)) : 0u;
+  const uint32_t c = lane < M ? static_cast<uint32_t>(clamp_count(raw, &f)) : 0u;
   const uint64_t tot = wave_sum_u42(c);
   uint32_t flags = tot != static_cast<uint64_t>(A) ? kFlagSumMismatch : 0u;
   if (__builtin_amdgcn_ballot_w64((f & kFlagNegative) != 0) != 0) flags |= kFlagNegative;

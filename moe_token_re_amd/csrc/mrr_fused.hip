@@ -97,6 +97,10 @@ __global__ __launch_bounds__(kGatherThreads) void fused_kernel(GatherArgs p, Fus
   const int rows = min(p.rows_per_wg, p.A - row0);  // >= 1: the grid covers [0, A) exactly
   const int64_t Rs = p.scale_row_bytes;
 
+  // The count first: its load is the oldest in flight, so the offsets below
+  // wait for it alone while the row loads issued next are still under way.
+  const CountT* counts = static_cast<const CountT*>(f.counts);
+  const CountT craw = p.M <= 64 ? load_count64(counts, p.M) : load_count(counts, p.M);
   RowRound<V> q;
   load_round<V>(q, p.tokens, p.row_bytes, p.vecs_per_row, rows, row0, 0);
   using ST = typename VecT<(kSV > 0 ? kSV : 4)>::type;
@@ -120,7 +124,7 @@ __global__ __launch_bounds__(kGatherThreads) void fused_kernel(GatherArgs p, Fus
   uint32_t flags;
   if (p.M <= 64) {  // uniform: every wave computes the offsets by itself and maps its 64 rows
     WaveCells w;
-    flags = wave_offsets64<CountT>(static_cast<const CountT*>(f.counts), N, E, p.A, &w, &total);
+    flags = wave_offsets64<CountT>(craw, N, E, p.A, &w, &total);
     if (flags == 0) {
       const int32_t s = row0 + tid;
       const int32_t d = wave_map_row(w, p.M, p.inverse, s < p.A ? s : 0);
@@ -131,7 +135,7 @@ __global__ __launch_bounds__(kGatherThreads) void fused_kernel(GatherArgs p, Fus
       }
     }
   } else {
-    flags = offsets_cells<kGatherThreads>(static_cast<const CountT*>(f.counts), N, E, p.A, p.inverse ? 0 : 1,
+    flags = offsets_cells<kGatherThreads>(craw, N, E, p.A, p.inverse ? 0 : 1,
                                           mats, col, nullptr, &sh, &total, nullptr, row0, s_mark, s_dst);
   }
   if (flags != 0) {  // uniform: nothing is written for rejected counts

@@ -212,7 +212,7 @@ __global__ __launch_bounds__(kOffsetThreads) void offsets_staged_kernel(
   // expert_token_num, the status and, without a row map, the table.
   const bool lead = blockIdx.x == 0;
   if (kC == 1)
-    flags = offsets_cells<kOffsetThreads>(counts, N, E, A, inverse, s_dyn, col,
+    flags = offsets_cells<kOffsetThreads>(load_count(counts, N * E), N, E, A, inverse, s_dyn, col,
                                           lead && rowmap == nullptr ? table : nullptr, &sh, &total,
                                           rowmap, static_cast<int>(blockIdx.x) * kOffsetThreads,
                                           col + E + 1);  // row marks after col (the launch sizes them)
@@ -241,7 +241,7 @@ __global__ __launch_bounds__(kT) void offsets_small_kernel(
   const bool lead = blockIdx.x == 0;
   int64_t total = 0;
   const uint32_t flags =
-      offsets_cells<kT>(counts, N, E, A, inverse, s_mats, s_col, nullptr, &sh, &total, rowmap,
+      offsets_cells<kT>(load_count(counts, N * E), N, E, A, inverse, s_mats, s_col, nullptr, &sh, &total, rowmap,
                         static_cast<int>(blockIdx.x) * kT, s_mark);
   if (!lead) return;
   if (flags == 0) write_etn<kT>(s_col, E, cumsum, etn);
@@ -472,12 +472,18 @@ __global__ __launch_bounds__(kOffsetThreads) void offsets_banded_kernel(
     const int r = qi;  // lane r of column j = qj
     const int j = qj;
     if (r < lanes) {
-      const CountT* p = counts + j;
+      // Bounds and strides are uniform scalars and each thread walks one pointer: per-load
+      // addresses of the form (ib + k * lanes) * E made the compiler use 64-bit multiply-adds
+      // whose unused high half shares a register with band_raw's load, so the sweep waited for
+      // that load before issuing its own.
+      const int lim = N - (kBandUnroll - 1) * lanes;  // uniform
+      const int stride = lanes * E;                    // uniform: elements between a thread's loads
       int ib = r;
-      for (; ib + (kBandUnroll - 1) * lanes < N; ib += kBandUnroll * lanes) {
+      const CountT* p = counts + (j + r * E);          // M <= kBandMaxCells: 32-bit element offsets
+      for (; ib < lim; ib += kBandUnroll * lanes, p += kBandUnroll * stride) {
         CountT raw[kBandUnroll];
 #pragma unroll
-        for (int k = 0; k < kBandUnroll; ++k) raw[k] = p[(ib + k * lanes) * E];
+        for (int k = 0; k < kBandUnroll; ++k) raw[k] = p[k * stride];
 #pragma unroll
         for (int k = 0; k < kBandUnroll; ++k) acc.add(raw[k], ib + k * lanes < i0);
       }
@@ -486,7 +492,7 @@ __global__ __launch_bounds__(kOffsetThreads) void offsets_banded_kernel(
 #pragma unroll
         for (int k = 0; k < kBandUnroll; ++k) {
           const int i = ib + k * lanes;
-          raw[k] = p[(i < N ? i : N - 1) * E];
+          raw[k] = counts[j + (i < N ? i : N - 1) * E];
         }
 #pragma unroll
         for (int k = 0; k < kBandUnroll; ++k)
@@ -706,7 +712,7 @@ __global__ __launch_bounds__(256) void offsets_regs_kernel(
   const bool lead = blockIdx.x == 0 && threadIdx.x < 64;
   WaveCells w;
   int64_t total = 0;
-  const uint32_t flags = wave_offsets64<CountT>(counts, N, E, A, &w, &total);
+  const uint32_t flags = wave_offsets64<CountT>(load_count64(counts, N * E), N, E, A, &w, &total);
   if (flags != 0) {  // the same in every wave: no row map
     if (lead && lane == 0) write_header(hdr, A, N, E, total, flags, kTablesValid, inverse);
     return;
