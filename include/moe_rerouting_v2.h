@@ -174,10 +174,14 @@ mrr_status mrr_validate(const mrr_args* args, const void* workspace, size_t work
 
 /* How a call with these arguments is launched (filled by mrr_describe_plan). */
 typedef struct mrr_plan_info {
-  int32_t fused;                 /* 1: moe_rerouting_v2 launches one kernel whose workgroups each
-                                    recompute the offsets of the (small) count matrix in LDS or
-                                    registers (small calls); 0: it launches the offsets kernel,
-                                    then the gather kernel */
+  int32_t fused;                 /* what moe_rerouting_v2 launches: 1 = one kernel whose workgroups
+                                    each recompute the offsets of the (small) count matrix in LDS
+                                    or registers (small calls); 2 = one kernel of 64-lane
+                                    workgroups (count matrices of at most 256 cells, token rows of
+                                    whole KiB): item waves of 64 output rows, then one wave per
+                                    1 KiB of an input row, each computing the offsets it needs
+                                    from the counts; 0 = the offsets kernel, then the gather
+                                    kernel (the two-phase entry points always do that) */
   int32_t token_vec_bytes;       /* bytes per load/store of the token copy: 16, 8, 4, 2 or 1
                                     (16 also for rows that are no multiple of 16 bytes when the
                                     stream gather moves them as aligned 16-byte output blocks) */
@@ -203,6 +207,8 @@ typedef struct mrr_plan_info {
                                     workgroups hold 2^32 or more threads in all (a launch holds
                                     at most 2^32 - 1), each piece taking the next workgroups;
                                     0 when A == 0 */
+  int64_t one_launch_workgroups; /* workgroups of moe_rerouting_v2's single launch when fused is
+                                    1 or 2; 0 otherwise */
 } mrr_plan_info;
 
 /*

@@ -79,6 +79,7 @@ class MrrPlanInfo(ctypes.Structure):
         ("offsets_workgroups", ctypes.c_int64),
         ("gather_kernel", ctypes.c_int32),
         ("gather_launches", ctypes.c_int64),
+        ("one_launch_workgroups", ctypes.c_int64),
     ]
 
 

@@ -102,6 +102,25 @@ struct FusedArgs {
   int32_t cumsum;
 };
 
+// The one-launch stream kernel's own arguments (count matrices of at most 256
+// cells, token rows of whole 1 KiB chunks).
+struct StreamFusedArgs {
+  const void* counts;
+  void* etn;
+  int32_t cumsum;
+  int32_t item_waves;  // workgroups [0, item_waves) move the per-row items, 64 output rows each
+  uint32_t cpr;        // 1 KiB chunks per token row
+  uint32_t cpr_magic;  // ceil(2^32 / cpr): chunk / cpr by a multiply-high and one correction
+  int32_t minor;       // cells per major index in input order: E forward, N inverse
+  int32_t major;       // N forward, E inverse
+  float inv_minor;     // 1 / minor
+  float inv_spr;       // 1 / (scale vectors per row), when there are scales
+  // The output-order position of input-order cell m = 4 l + k (m < 256) in
+  // byte k of outpos[l]: it depends on N, E and the direction alone, so the
+  // host computes it once instead of every wave.
+  uint32_t outpos[64];
+};
+
 namespace {
 
 // ---------------------------------------------------------------------------
@@ -163,6 +182,18 @@ __device__ __forceinline__ uint32_t wave_scan_u32(uint32_t v) {
   const uint32_t r2 = __builtin_amdgcn_readlane(v, 47);
   const int row = (threadIdx.x & 63) >> 4;
   return v + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+}
+
+// Sum over the 64 lanes of a wave (wrapping 32-bit adds), in every lane: DPP
+// row shifts sum each row of 16 lanes, then the four row totals are added.
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+  constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kRowShr1, 0xf, 0xf, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kRowShr2, 0xf, 0xf, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kRowShr4, 0xf, 0xf, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kRowShr8, 0xf, 0xf, false));
+  return __builtin_amdgcn_readlane(v, 15) + __builtin_amdgcn_readlane(v, 31) + __builtin_amdgcn_readlane(v, 47) +
+         __builtin_amdgcn_readlane(v, 63);
 }
 
 // Exact sum over the 64 lanes of a wave of values below 2^42, without LDS:
@@ -512,6 +543,7 @@ __device__ __forceinline__ int32_t wave_map_row(const WaveCells& w, int M, int i
 mrr_status launch_offsets(const Plan& pl, const mrr_args* a, void* ws, hipStream_t stream);
 mrr_status launch_gather(const Plan& pl, const mrr_args* a, void* ws, hipStream_t stream);
 mrr_status launch_fused(const Plan& pl, const mrr_args* a, void* ws, hipStream_t stream);
+mrr_status launch_stream_fused(const Plan& pl, const mrr_args* a, void* ws, hipStream_t stream);
 GatherArgs gather_args(const Plan& pl, const mrr_args* a, void* ws);
 
 // Launches kernel K<V, SV, scatter, weight> (gather or fused) for the plan's

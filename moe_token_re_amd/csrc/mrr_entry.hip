@@ -63,6 +63,7 @@ extern "C" mrr_status moe_rerouting_v2(const mrr_args* args, void* workspace, si
   mrr_status st = mrr::make_plan(args, workspace, workspace_bytes, &plan);
   if (st != MRR_SUCCESS) return st;
   if (plan.fused) return mrr::launch_fused(plan, args, workspace, stream);
+  if (plan.stream_fused) return mrr::launch_stream_fused(plan, args, workspace, stream);
   st = mrr::launch_offsets(plan, args, workspace, stream);
   if (st != MRR_SUCCESS) return st;
   return mrr::launch_gather(plan, args, workspace, stream);

@@ -179,6 +179,363 @@ __global__ __launch_bounds__(kGatherThreads) void fused_kernel(GatherArgs p, Fus
   }
 }
 
+// ---------------------------------------------------------------------------
+// The whole call in one launch of 64-lane workgroups, for count matrices of at
+// most 256 cells and token rows of whole 1 KiB chunks. Workgroups
+// [0, item_waves) move the per-row items and scale rows of 64 output rows
+// each; every later workgroup moves one 1 KiB chunk of one input row, in input
+// order, so that its token load goes out at once (beside the count load); it
+// then works out where the row goes from the counts while the load is in
+// flight. Every wave checks the counts itself and writes nothing when they
+// are rejected; workgroup 0 writes expert_token_num and the status.
+// ---------------------------------------------------------------------------
+
+constexpr int kCellsPerLane = 4;  // 64 lanes x 4 = 256 cells
+constexpr int kScaleRound = 4;    // scale vectors per lane loaded before they are stored
+
+// The raw counts of this lane's cells m = 4 lane + k in input order (forward:
+// row-major (rank, expert), the order of SrcOffset; inverse: column-major), 0
+// past the matrix. Every wave reads the whole matrix, so the number of load
+// instructions matters: with kVec (the counts 16-byte aligned, M a multiple of
+// 4) a lane's four counts come in one 16-byte load (two for int64) in matrix
+// order, and the inverse puts them in column-major order afterwards through
+// LDS (order_cells); else in four loads. kVec is a template choice, not a
+// branch: at a join of two load paths the compiler would wait for the counts
+// before the token load goes out.
+template <typename CountT>
+struct RawCells {
+  CountT r[kCellsPerLane];
+  uint32_t pos;  // this lane's word of the host's output-position table (loaded with the counts)
+};
+
+template <typename CountT, bool kVec>
+__device__ __forceinline__ void load_cells(const CountT* __restrict__ counts, int M, int inverse,
+                                           const StreamFusedArgs& f, RawCells<CountT>& rc) {
+  const int lane = threadIdx.x & 63;
+  rc.pos = f.outpos[lane];
+  if (kVec) {
+    const bool in = kCellsPerLane * lane < M;  // then all four cells are (M % 4 == 0)
+    const CountT* q = counts + (in ? kCellsPerLane * lane : 0);
+    CountT r[kCellsPerLane];
+    if (sizeof(CountT) == 4) {
+      using I4 = int32_t __attribute__((ext_vector_type(4)));
+      const I4 v = *reinterpret_cast<const I4*>(q);
+      r[0] = static_cast<CountT>(v.x);
+      r[1] = static_cast<CountT>(v.y);
+      r[2] = static_cast<CountT>(v.z);
+      r[3] = static_cast<CountT>(v.w);
+    } else {
+      using L2 = int64_t __attribute__((ext_vector_type(2)));
+      const L2 v0 = reinterpret_cast<const L2*>(q)[0];
+      const L2 v1 = reinterpret_cast<const L2*>(q)[1];
+      r[0] = static_cast<CountT>(v0.x);
+      r[1] = static_cast<CountT>(v0.y);
+      r[2] = static_cast<CountT>(v1.x);
+      r[3] = static_cast<CountT>(v1.y);
+    }
+#pragma unroll
+    for (int k = 0; k < kCellsPerLane; ++k) rc.r[k] = in ? r[k] : CountT(0);
+    return;
+  }
+  // Addresses first, branch-free (a branch on `inverse` between the loads
+  // would make the compiler wait for the earlier ones at its join). Inverse,
+  // cell (rank b, expert a) of the column-major order sits at b * E + a.
+  const int inv_mask = -inverse;  // 0 or all ones
+  int at[kCellsPerLane];
+#pragma unroll
+  for (int k = 0; k < kCellsPerLane; ++k) {
+    const int m = kCellsPerLane * lane + k;
+    const int a = div_small(m, f.inv_minor);
+    const int cm = (m - a * f.minor) * f.major + a;
+    at[k] = m < M ? m + ((cm - m) & inv_mask) : 0;  // M >= 1 here
+  }
+#pragma unroll
+  for (int k = 0; k < kCellsPerLane; ++k) {
+    const CountT raw = counts[at[k]];
+    rc.r[k] = kCellsPerLane * lane + k < M ? raw : CountT(0);
+  }
+}
+
+// With kVec and the inverse direction: the counts loaded in matrix order
+// (row-major) rearranged into column-major order through s_c (M counts), one
+// LDS write and four reads per lane. Called after the token load is issued.
+// The LDS operations of one wave complete in order, so the reads see the
+// writes.
+template <typename CountT, bool kVec>
+__device__ __forceinline__ void order_cells(RawCells<CountT>& rc, CountT* s_c, int M, int inverse) {
+  if (!kVec || !inverse) return;
+  const int lane = threadIdx.x & 63;
+  if (kCellsPerLane * lane < M) {
+#pragma unroll
+    for (int k = 0; k < kCellsPerLane; ++k) s_c[kCellsPerLane * lane + k] = rc.r[k];
+  }
+  __builtin_amdgcn_wave_barrier();
+  // Inverse, the output order is the matrix order: the output position of
+  // input-order cell m is its matrix index (rank * E + expert).
+#pragma unroll
+  for (int k = 0; k < kCellsPerLane; ++k) {
+    const CountT v = s_c[(rc.pos >> (8 * k)) & 0xffu];  // 0 past the matrix
+    rc.r[k] = kCellsPerLane * lane + k < M ? v : CountT(0);
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+// The position of each of this lane's cells in output order, from the
+// host's table (cell (major a, minor b) of the input order is cell
+// b * major + a of the output order). Past the matrix the value means nothing
+// (those cells count 0 and are never looked up or written).
+__device__ __forceinline__ void cell_positions(uint32_t word, uint32_t (&out)[kCellsPerLane]) {
+#pragma unroll
+  for (int k = 0; k < kCellsPerLane; ++k) out[k] = (word >> (8 * k)) & 0xffu;
+}
+
+// The position of cell m in output order, in every lane (word: this lane's
+// cell_positions word).
+__device__ __forceinline__ uint32_t cell_position(uint32_t word, int m) {
+  return (__builtin_amdgcn_readlane(word, m >> 2) >> (8 * (m & 3))) & 0xffu;
+}
+
+// What every wave derives from its cells: the counts, each cell's input
+// offset (the exclusive prefix in input order: SrcOffset forward, DstOffset
+// inverse), and the verdict on the whole matrix. Exactness: each count is
+// below 2^31 (larger ones are flagged). While every count is below 2^22 the
+// 256 of them sum below 2^30, so the wrapping 32-bit sum is exact. Otherwise
+// (rare: a cell of 4M rows or more), with H the sum of the counts' bits from
+// 2^20 up, the true sum lies below H 2^20 + 2^28; while H < 1024 it is below
+// 2^32 and the wrapping sum is exact, and a valid matrix sums to A < 2^30
+// (the plan sends only A < 2^30 here), so its H is below 1024.
+struct InCells {
+  int32_t c[kCellsPerLane];
+  uint32_t start[kCellsPerLane];
+  uint32_t total;  // uniform: the wrapping 32-bit sum
+  uint32_t flags;  // uniform: kFlag* of the whole matrix (0: valid)
+};
+
+template <typename CountT>
+__device__ __forceinline__ void finish_cells(const RawCells<CountT>& rc, int A, InCells& w) {
+  uint32_t fl = 0;
+  uint32_t own = 0;
+#pragma unroll
+  for (int k = 0; k < kCellsPerLane; ++k) {
+    w.c[k] = clamp_count(rc.r[k], &fl);
+    own += static_cast<uint32_t>(w.c[k]);
+  }
+  const uint32_t incl = wave_scan_u32(own);
+  w.total = __builtin_amdgcn_readlane(incl, 63);
+  w.start[0] = incl - own;
+#pragma unroll
+  for (int k = 1; k < kCellsPerLane; ++k) w.start[k] = w.start[k - 1] + static_cast<uint32_t>(w.c[k - 1]);
+  uint32_t flags = (__ballot(fl & kFlagNegative) != 0 ? kFlagNegative : 0u) |
+                   (__ballot(fl & kFlagTooLarge) != 0 ? kFlagTooLarge : 0u);
+  const uint32_t any = static_cast<uint32_t>(w.c[0] | w.c[1] | w.c[2] | w.c[3]);  // counts are >= 0 here
+  if (__ballot(any >= (1u << 22)) != 0) {  // uniform and rare
+    uint32_t hi = 0;
+#pragma unroll
+    for (int k = 0; k < kCellsPerLane; ++k) hi += static_cast<uint32_t>(w.c[k]) >> 20;
+    if (wave_sum_u32(hi) >= 1024u) flags |= kFlagSumMismatch;
+  }
+  if (w.total != static_cast<uint32_t>(A)) flags |= kFlagSumMismatch;
+  w.flags = flags;
+}
+
+// v[k] of the lane holding cell m (k = m % 4), in every lane: every lane
+// selects its own v[k] by the bits of k (named values, not an index into the
+// array, which would put it in scratch memory), then that lane is read.
+__device__ __forceinline__ uint32_t cell_value(const uint32_t (&v)[kCellsPerLane], int m) {
+  const uint32_t v0 = v[0], v1 = v[1], v2 = v[2], v3 = v[3];
+  const uint32_t lo = (m & 1) ? v1 : v0, hi = (m & 1) ? v3 : v2;
+  return __builtin_amdgcn_readlane((m & 2) ? hi : lo, m >> 2);
+}
+
+// Token wave c: 1 KiB chunk c % cpr of input row c / cpr (one 16-byte load
+// and store per lane: this chip streams fastest with one-wave workgroups of
+// one load each; two chunks a wave measured slower).
+template <typename CountT, bool kVec>
+__device__ __forceinline__ void stream_fused_tokens(const GatherArgs& p, const StreamFusedArgs& f, uint32_t c,
+                                                    uint32_t* s_lds) {
+  using T = VecT<16>::type;
+  const int lane = threadIdx.x & 63;
+  uint32_t s = c;
+  if (f.cpr != 1) {  // uniform
+    const uint32_t q = __umulhi(c, f.cpr_magic);
+    s = q - (q * f.cpr > c ? 1u : 0u);
+  }
+  s = __builtin_amdgcn_readfirstlane(s);
+  const int64_t col = int64_t(c - s * f.cpr) * 1024 + lane * 16;
+  RawCells<CountT> rc;
+  load_cells<CountT, kVec>(static_cast<const CountT*>(f.counts), p.M, p.inverse, f, rc);
+  const T v = __builtin_nontemporal_load(reinterpret_cast<const T*>(p.tokens + int64_t(s) * p.row_bytes + col));
+  // The offsets below wait for the counts alone (loads return in issue
+  // order). The compiler would otherwise sink the token load below them, next
+  // to its store: this barrier names the token buffer, so the load stays here.
+  asm volatile("" ::"s"(p.tokens) : "memory");
+  order_cells<CountT, kVec>(rc, reinterpret_cast<CountT*>(s_lds), p.M, p.inverse);
+  InCells w;
+  finish_cells<CountT>(rc, p.A, w);
+  uint32_t outp[kCellsPerLane];
+  cell_positions(rc.pos, outp);
+  // The cell of input row s is the last one that starts at or before it.
+  int m = -1;
+#pragma unroll
+  for (int k = 0; k < kCellsPerLane; ++k) m += __popcll(__ballot(w.start[k] <= s));
+  m = max(m, 0);  // -1 only for rejected counts
+  const uint32_t src_m = cell_value(w.start, m);
+  const uint32_t out_m = cell_position(rc.pos, m);
+  // Its output offset: the counts of the cells before it in output order.
+  uint32_t before = 0;
+#pragma unroll
+  for (int k = 0; k < kCellsPerLane; ++k) before += outp[k] < out_m ? static_cast<uint32_t>(w.c[k]) : 0u;
+  const uint32_t d = wave_sum_u32(before) + (s - src_m);
+  if (w.flags == 0 && d < static_cast<uint32_t>(p.A))
+    __builtin_nontemporal_store(v, reinterpret_cast<T*>(p.out_tokens + int64_t(d) * p.row_bytes + col));
+}
+
+// The scale rows of output rows [d0, d0 + rows), taken from input row
+// `src` of lane r for output row d0 + r; kScaleRound vectors per lane are
+// loaded before they are stored.
+template <int SV>
+__device__ __forceinline__ void stream_fused_scales(const GatherArgs& p, const StreamFusedArgs& f, int d0, int rows,
+                                                    int32_t src) {
+  using T = typename VecT<SV>::type;
+  const int lane = threadIdx.x & 63;
+  const int spr = p.scale_vecs_per_row;
+  const int64_t Rs = p.scale_row_bytes;
+  const int total = rows * spr;  // < 2^22 (Rs is at most 4 KiB here): div_small is exact
+  for (int e0 = 0; e0 < total; e0 += 64 * kScaleRound) {
+    T v[kScaleRound];
+    int64_t to[kScaleRound];
+    bool in[kScaleRound];
+#pragma unroll
+    for (int k = 0; k < kScaleRound; ++k) {
+      const int e = e0 + 64 * k + lane;
+      in[k] = e < total;
+      const int r = in[k] ? div_small(e, f.inv_spr) : 0;
+      const int cv = e - r * spr;
+      const int32_t sr = __shfl(src, r);  // every lane takes part
+      v[k] = __builtin_nontemporal_load(
+          reinterpret_cast<const T*>(p.scales + (in[k] ? int64_t(sr) * Rs + int64_t(cv) * SV : 0)));
+      to[k] = int64_t(d0 + r) * Rs + int64_t(cv) * SV;
+    }
+#pragma unroll
+    for (int k = 0; k < kScaleRound; ++k)
+      if (in[k]) __builtin_nontemporal_store(v[k], reinterpret_cast<T*>(p.out_scales + to[k]));
+  }
+}
+
+// Item wave iw: output rows [64 iw, 64 iw + 64). The offsets in output order
+// come from one exchange of the counts through LDS; each row finds its cell by
+// a mark at every cell start within the 64 rows and a running maximum.
+template <bool kScatter, bool kWeight, typename CountT, bool kVec>
+__device__ __forceinline__ void stream_fused_items(const GatherArgs& p, const StreamFusedArgs& f, int iw,
+                                                   uint32_t* s_lds) {
+  uint32_t* s_cnt = s_lds;                                 // by output position: the count,
+  uint32_t* s_in = s_lds + kCellsPerLane * 64;             // the input offset,
+  uint32_t* s_out = s_lds + 2 * kCellsPerLane * 64;        // the output offset
+  int32_t* s_mark = reinterpret_cast<int32_t*>(s_lds + 3 * kCellsPerLane * 64);  // [64]
+  const int lane = threadIdx.x & 63;
+  const int M = p.M, A = p.A;
+  RawCells<CountT> rc;
+  load_cells<CountT, kVec>(static_cast<const CountT*>(f.counts), M, p.inverse, f, rc);
+  order_cells<CountT, kVec>(rc, reinterpret_cast<CountT*>(s_lds), M, p.inverse);
+  InCells w;
+  finish_cells<CountT>(rc, A, w);
+  uint32_t outp[kCellsPerLane];
+  cell_positions(rc.pos, outp);
+  const int d0 = iw * 64;
+  s_mark[lane] = -1;
+#pragma unroll
+  for (int k = 0; k < kCellsPerLane; ++k)
+    if (kCellsPerLane * lane + k < M) {
+      s_cnt[outp[k]] = static_cast<uint32_t>(w.c[k]);
+      s_in[outp[k]] = w.start[k];
+    }
+  __syncthreads();
+  uint32_t co[kCellsPerLane], ostart[kCellsPerLane];
+  uint32_t own = 0;
+#pragma unroll
+  for (int k = 0; k < kCellsPerLane; ++k) {
+    co[k] = kCellsPerLane * lane + k < M ? s_cnt[kCellsPerLane * lane + k] : 0u;
+    own += co[k];
+  }
+  ostart[0] = wave_scan_u32(own) - own;
+#pragma unroll
+  for (int k = 1; k < kCellsPerLane; ++k) ostart[k] = ostart[k - 1] + co[k - 1];
+  // the cell holding row d0 (the last one starting at or before it) marks the
+  // first row; every later cell starting within the 64 rows marks its start
+  int u0 = -1;
+#pragma unroll
+  for (int k = 0; k < kCellsPerLane; ++k) {
+    const int u = kCellsPerLane * lane + k;
+    if (u < M) {
+      s_out[u] = ostart[k];
+      if (co[k] > 0 && ostart[k] > static_cast<uint32_t>(d0) && ostart[k] < static_cast<uint32_t>(d0 + 64))
+        s_mark[ostart[k] - d0] = u;
+    }
+    u0 += __popcll(__ballot(u < M && ostart[k] <= static_cast<uint32_t>(d0)));
+  }
+  if (lane == 0) s_mark[0] = u0;
+  __syncthreads();
+  const int u = max(wave_max_scan(s_mark[lane]), 0);  // -1 only for rejected counts
+  const int d = d0 + lane;
+  const bool valid = w.flags == 0;
+  const bool live = valid && d < A;
+  const int32_t src = live ? static_cast<int32_t>(s_in[u] + (static_cast<uint32_t>(d) - s_out[u])) : 0;
+  if (live) {
+    if (kScatter)
+      p.idx[src] = d;
+    else
+      p.idx[d] = src;
+    if (kWeight) p.out_weight[d] = p.weight[src];
+  }
+  if (valid && p.scale_row_bytes > 0) {  // uniform
+    const int rows = min(64, A - d0);
+    switch (p.scale_vec) {
+      case 16: stream_fused_scales<16>(p, f, d0, rows, src); break;
+      case 8: stream_fused_scales<8>(p, f, d0, rows, src); break;
+      case 4: stream_fused_scales<4>(p, f, d0, rows, src); break;
+      case 2: stream_fused_scales<2>(p, f, d0, rows, src); break;
+      default: stream_fused_scales<1>(p, f, d0, rows, src); break;
+    }
+  }
+  if (iw == 0) {
+    // expert j's rows start at the output offset of output position j * N
+    // forward (expert-major output), at the input offset of output position j
+    // inverse (expert-major input; output position j is cell (0, j))
+    const int E = static_cast<int>(p.E), N = static_cast<int>(p.N);
+    if (valid)
+      for (int j = lane; j < E; j += 64) {
+        const uint32_t a0 = p.inverse ? s_in[j] : s_out[j * N];
+        const uint32_t a1 = j + 1 < E ? (p.inverse ? s_in[j + 1] : s_out[(j + 1) * N]) : static_cast<uint32_t>(A);
+        static_cast<CountT*>(f.etn)[j] = static_cast<CountT>(f.cumsum ? a1 : a1 - a0);
+      }
+    // the exact sum for the header: the bits from 2^20 up and the low 20
+    // bits summed apart (each sum exact in 32 bits)
+    uint32_t hi = 0, lo = 0;
+#pragma unroll
+    for (int k = 0; k < kCellsPerLane; ++k) {
+      hi += static_cast<uint32_t>(w.c[k]) >> 20;
+      lo += static_cast<uint32_t>(w.c[k]) & 0xfffffu;
+    }
+    const int64_t total = (int64_t(wave_sum_u32(hi)) << 20) + wave_sum_u32(lo);
+    if (lane == 0) write_header(p.hdr, p.A, p.N, p.E, total, w.flags, kCountsValid, p.inverse);
+  }
+}
+
+// LDS of a workgroup: the item waves' three tables of 256 cells and 64 row
+// marks; the token waves use its first 256 counts (inverse, kVec).
+constexpr int kStreamFusedLdsWords = 3 * kCellsPerLane * 64 + 64;
+
+template <bool kScatter, bool kWeight, typename CountT, bool kVec>
+__global__ __launch_bounds__(64) void stream_fused_kernel(GatherArgs p, StreamFusedArgs f) {
+  __shared__ uint32_t s_lds[kStreamFusedLdsWords];
+  const int b = static_cast<int>(blockIdx.x);
+  if (b < f.item_waves) {  // uniform
+    stream_fused_items<kScatter, kWeight, CountT, kVec>(p, f, b, s_lds);
+    return;
+  }
+  stream_fused_tokens<CountT, kVec>(p, f, static_cast<uint32_t>(b - f.item_waves), s_lds);
+}
+
 template <int V, int SV, bool S, bool W>
 struct FusedK32 {
   static auto fn() { return &fused_kernel<V, SV, S, W, int32_t>; }
@@ -188,7 +545,57 @@ struct FusedK64 {
   static auto fn() { return &fused_kernel<V, SV, S, W, int64_t>; }
 };
 
+template <typename CountT, bool kVec>
+void launch_stream_fused_c(const Plan& pl, const GatherArgs& g, const StreamFusedArgs& f, unsigned grid,
+                           hipStream_t stream) {
+  const dim3 block(64);
+  if (pl.scatter) {
+    if (pl.has_weight)
+      hipLaunchKernelGGL((stream_fused_kernel<true, true, CountT, kVec>), dim3(grid), block, 0, stream, g, f);
+    else
+      hipLaunchKernelGGL((stream_fused_kernel<true, false, CountT, kVec>), dim3(grid), block, 0, stream, g, f);
+  } else {
+    if (pl.has_weight)
+      hipLaunchKernelGGL((stream_fused_kernel<false, true, CountT, kVec>), dim3(grid), block, 0, stream, g, f);
+    else
+      hipLaunchKernelGGL((stream_fused_kernel<false, false, CountT, kVec>), dim3(grid), block, 0, stream, g, f);
+  }
+}
+
 }  // namespace
+
+mrr_status launch_stream_fused(const Plan& pl, const mrr_args* a, void* ws, hipStream_t stream) {
+  const GatherArgs g = gather_args(pl, a, ws);
+  StreamFusedArgs f{};
+  f.counts = a->expert_token_num_per_rank;
+  f.etn = a->expert_token_num;
+  f.cumsum = pl.cumsum ? 1 : 0;
+  f.item_waves = static_cast<int32_t>(pl.sf_item_waves);
+  f.cpr = static_cast<uint32_t>(pl.row_bytes / 1024);
+  f.cpr_magic = f.cpr == 1 ? 0u : static_cast<uint32_t>(((uint64_t(1) << 32) + f.cpr - 1) / f.cpr);
+  f.minor = static_cast<int32_t>(pl.inverse ? pl.N : pl.E);
+  f.major = static_cast<int32_t>(pl.inverse ? pl.E : pl.N);
+  f.inv_minor = 1.0f / static_cast<float>(f.minor);
+  f.inv_spr = g.scale_vecs_per_row > 0 ? 1.0f / static_cast<float>(g.scale_vecs_per_row) : 0.0f;
+  for (int l = 0; l < 64; ++l) {
+    uint32_t word = 0;
+    for (int k = 0; k < kCellsPerLane; ++k) {
+      const int m = kCellsPerLane * l + k;  // input-order cell (major m / minor, minor m % minor)
+      if (m < pl.M) word |= static_cast<uint32_t>((m % f.minor) * f.major + m / f.minor) << (8 * k);
+    }
+    f.outpos[l] = word;
+  }
+  const unsigned grid = static_cast<unsigned>(pl.sf_grid);
+  // a lane's four counts in one or two 16-byte loads: aligned, whole groups of four cells
+  const bool vec = reinterpret_cast<uintptr_t>(a->expert_token_num_per_rank) % 16 == 0 && pl.M % kCellsPerLane == 0;
+  if (pl.count_bytes == 8)
+    vec ? launch_stream_fused_c<int64_t, true>(pl, g, f, grid, stream)
+        : launch_stream_fused_c<int64_t, false>(pl, g, f, grid, stream);
+  else
+    vec ? launch_stream_fused_c<int32_t, true>(pl, g, f, grid, stream)
+        : launch_stream_fused_c<int32_t, false>(pl, g, f, grid, stream);
+  return hipGetLastError() == hipSuccess ? MRR_SUCCESS : MRR_ERROR_HIP;
+}
 
 mrr_status launch_fused(const Plan& pl, const mrr_args* a, void* ws, hipStream_t stream) {
   const GatherArgs g = gather_args(pl, a, ws);

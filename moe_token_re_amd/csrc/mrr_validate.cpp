@@ -64,6 +64,7 @@ struct Tuning {
   int band_split;   // 0 = automatic; else workgroups per band of the banded offsets kernel (1..16)
   bool fused;       // allow the single-kernel path (MRR_FUSED=0 turns it off)
   bool byte_rows;   // rows that are no multiple of 16 bytes stream as aligned 16-byte blocks
+  bool stream_fused;  // allow the one-launch stream kernel (MRR_STREAM_FUSED=0 turns it off)
   bool log;
   Tuning()
       : rows_per_wg(env_int("MRR_ROWS_PER_WG", 0)),
@@ -72,6 +73,7 @@ struct Tuning {
         band_split(env_int("MRR_BAND_SPLIT", 0)),
         fused(env_int("MRR_FUSED", 1) != 0),
         byte_rows(env_int("MRR_BYTE_ROWS", 1) != 0),
+        stream_fused(env_int("MRR_STREAM_FUSED", 1) != 0),
         log(env_int("MRR_LOG", 0) != 0) {}
 };
 
@@ -286,6 +288,22 @@ mrr_status make_plan(const mrr_args* a, const void* ws, size_t ws_bytes, Plan* p
   if (q.fused && q.byte_rows && q.A * q.row_bytes >= kFusedMaxByteRowBytes) q.fused = false;
   // The single kernel is one launch: never more workgroups than a launch holds.
   if (q.fused && q.grid > max_launch_grid(kGatherThreads)) q.fused = false;
+  // Where the two kernels would run, the one-launch stream kernel runs instead
+  // when its shape fits: at most 256 cells, token rows of whole 1 KiB chunks
+  // (16-byte vectors), scale rows of at most 4 KiB, A < 2^30 (its exact-sum
+  // check), and one launch of at most 2^31 workgroups.
+  q.stream_fused = false;
+  q.sf_item_waves = q.sf_grid = 0;
+  if (tuning().stream_fused && !q.fused && q.A > 0 && M <= kStreamFusedMaxCells && q.token_vec == 16 &&
+      q.row_bytes % 1024 == 0 && q.scale_row_bytes <= kStreamFusedMaxScaleRow && q.A < (int64_t(1) << 30)) {
+    const int64_t waves = (q.A + 63) / 64;
+    const int64_t grid = waves + q.A * (q.row_bytes / 1024);
+    if (grid < kMaxStreamGrid && grid <= max_launch_grid(64)) {
+      q.stream_fused = true;
+      q.sf_item_waves = waves;
+      q.sf_grid = grid;
+    }
+  }
   q.gather_launches = q.A == 0 || q.fused ? (q.A == 0 ? 0 : 1)
                     : q.stream ? (q.stream_grid + max_launch_grid(64) - 1) / max_launch_grid(64)
                                : (q.grid + max_launch_grid(kGatherThreads) - 1) / max_launch_grid(kGatherThreads);
@@ -316,12 +334,13 @@ extern "C" mrr_status mrr_describe_plan(const mrr_args* args, const void* worksp
   mrr::Plan plan;
   const mrr_status st = mrr::make_plan(args, workspace, workspace_bytes, &plan);
   if (st != MRR_SUCCESS) return st;
-  info->fused = plan.fused ? 1 : 0;
+  info->fused = plan.fused ? 1 : plan.stream_fused ? 2 : 0;
   info->token_vec_bytes = plan.byte_rows && !plan.fused ? 16 : plan.token_vec;
   info->scale_vec_bytes = plan.scale_row_bytes > 0 ? plan.scale_vec : 0;
   info->rows_per_workgroup = plan.rows_per_wg;
   info->threads_per_workgroup = plan.fused || !plan.stream ? mrr::kGatherThreads : 64;
   info->gather_workgroups = plan.fused || !plan.stream ? plan.grid : plan.stream_grid;
+  info->one_launch_workgroups = plan.fused ? plan.grid : plan.stream_fused ? plan.sf_grid : 0;
   info->token_row_bytes = plan.row_bytes;
   info->scale_row_bytes = plan.scale_row_bytes;
   info->scale_inline_bytes = plan.scale_inline;

@@ -66,7 +66,7 @@ int token_bits(int32_t dt) {
 
 int g_fail = 0;
 long g_random_ok = 0;
-long g_paths[2][2] = {{0, 0}, {0, 0}};  // [fused][stream gather] among accepted consistent sets
+long g_paths[3][2] = {{0, 0}, {0, 0}, {0, 0}};  // [fused: 0, 1, 2][stream gather] among accepted sets
 
 void fail(const char* what, const mrr_args& a) {
   if (g_fail++ < 20)
@@ -84,7 +84,8 @@ void check(const mrr_args& a, const void* ws, size_t ws_bytes, bool must_pass) {
   if (must_pass && v != MRR_SUCCESS) fail("a consistent argument set was rejected", a);
   if (v != MRR_SUCCESS) return;
   if (!must_pass) ++g_random_ok;
-  if (must_pass) ++g_paths[info.fused ? 1 : 0][info.gather_kernel ? 1 : 0];
+  if (info.fused < 0 || info.fused > 2) fail("fused", a);
+  if (must_pass) ++g_paths[info.fused][info.gather_kernel ? 1 : 0];
   const int bits = token_bits(a.tokens_dtype);
   if (info.threads_per_workgroup != 64 && info.threads_per_workgroup != 256) fail("threads per workgroup", a);
   if (info.gather_workgroups < 0 || info.gather_workgroups >= (1LL << 31)) fail("gather grid", a);
@@ -97,7 +98,10 @@ void check(const mrr_args& a, const void* ws, size_t ws_bytes, bool must_pass) {
                                    : 0;
   if (a.A > 0 && info.gather_launches < 1) fail("no gather launch", a);
   if (per_launch * info.threads_per_workgroup > max_threads) fail("gather launch too large", a);
-  if (info.fused && info.gather_launches != 1) fail("fused kernel in several launches", a);
+  if (info.fused == 1 && info.gather_launches != 1) fail("fused kernel in several launches", a);
+  // moe_rerouting_v2's single launch: 256-thread workgroups (fused 1) or 64-lane ones (fused 2)
+  if ((info.fused != 0) != (info.one_launch_workgroups > 0)) fail("one-launch workgroups", a);
+  if (info.one_launch_workgroups * (info.fused == 1 ? 256 : 64) > max_threads) fail("one launch too large", a);
   if (info.offsets_workgroups * 1024 > max_threads) fail("offsets launch too large", a);
   if (info.token_row_bytes != a.H * bits / 8) fail("token row bytes", a);
   const size_t need = mrr_workspace_size(a.A, a.N, a.E);
@@ -195,8 +199,9 @@ int main(int argc, char** argv) {
     ++accepted;
     (void)mrr_workspace_size(pick_int(), pick_int(), pick_int());
   }
-  printf("host_fuzz: %ld iterations, %ld random sets accepted, %ld consistent sets (fused %ld, row workgroups %ld, "
-         "stream %ld), %d failures\n",
-         iters, g_random_ok, accepted, g_paths[1][0] + g_paths[1][1], g_paths[0][0], g_paths[0][1], g_fail);
+  printf("host_fuzz: %ld iterations, %ld random sets accepted, %ld consistent sets (fused %ld, one-launch stream "
+         "%ld, row workgroups %ld, stream %ld), %d failures\n",
+         iters, g_random_ok, accepted, g_paths[1][0] + g_paths[1][1], g_paths[2][0] + g_paths[2][1], g_paths[0][0],
+         g_paths[0][1], g_fail);
   return g_fail == 0 ? 0 : 1;
 }

@@ -184,18 +184,22 @@ def describe(a, ws=BASE["ws"]):
 
 
 def test_describe_plan():
-    # pages' shape: 7168-byte rows in 16-byte vectors; 112 MiB of token rows take the two-kernel
-    # path with the stream gather: 64-lane workgroups over 64-vector chunks of the token rows
-    # (16384 * 448 / 64) and chunks of 256 rows' items (index, and the 4-byte scale rows with them)
+    # pages' shape: 7168-byte rows in 16-byte vectors; 112 MiB of token rows take the one-launch
+    # stream kernel: 64-lane workgroups, 16384 / 64 item waves, then one per KiB of an input row
     st, info = describe(valid_args(A=16384, H=7168, N=16, E=16, tok=_lib.I8))
     assert st == _lib.SUCCESS
-    assert info.fused == 0 and info.gather_kernel == 1 and info.token_vec_bytes == 16
+    assert info.fused == 2 and info.one_launch_workgroups == 16384 // 64 + 16384 * 7
+    # the two phases: the offsets kernel, then the stream gather over 64-vector chunks of the
+    # token rows (16384 * 448 / 64) and chunks of 256 rows' items (index, and the 4-byte scale
+    # rows with them)
+    assert info.gather_kernel == 1 and info.token_vec_bytes == 16
     assert info.token_row_bytes == 7168 and info.scale_row_bytes == 4 and info.scale_vec_bytes == 4
     assert info.threads_per_workgroup == 64 and info.gather_workgroups == 114688 + 16384 // 256
     assert info.offsets_workgroups == 64           # the row map: one workgroup per 256 rows (<= 256 cells)
     # a smaller call with the same counts: one kernel whose workgroups each recompute the offsets
     st, info = describe(valid_args(A=2048, H=7168, N=16, E=16, tok=_lib.I8))
     assert st == _lib.SUCCESS and info.fused == 1 and info.threads_per_workgroup == 256
+    assert info.one_launch_workgroups == info.gather_workgroups
     assert info.scale_inline_bytes == 4            # one 4-byte piece per row, loaded with the tokens
     rows = max(1, info.threads_per_workgroup * 8 // 448)
     assert info.rows_per_workgroup == min(rows, 256)
@@ -237,6 +241,7 @@ def test_describe_plan():
     # empty input: nothing to gather, never the single-kernel path
     st, info = describe(valid_args(A=0, N=3, E=2))
     assert st == _lib.SUCCESS and info.fused == 0 and info.gather_workgroups == 0
+    assert info.one_launch_workgroups == 0
     assert info.offsets_workgroups == 1
     st, info = describe(valid_args(A=0, N=0, E=2))
     assert st == _lib.SUCCESS and info.offsets_workgroups == 0
@@ -253,18 +258,32 @@ def test_plan_size_classes():
     only; every choice computes the same bytes)."""
     mib = 1 << 20
     below28, above28, above48 = 28 * mib // 7168 - 1, 28 * mib // 7168 + 1, 48 * mib // 7168 + 1  # 7168-byte rows
-    # at most 64 cells: one kernel below 28 MiB of token rows, else offsets + gather
+    # at most 64 cells: the fused kernel below 28 MiB of token rows, else the one-launch stream
+    # kernel (rows of whole KiB); the two phases: offsets + stream gather
     for n, e in [(8, 8), (4, 4), (1, 64)]:
         st, info = describe(valid_args(A=below28, H=7168, N=n, E=e, tok=_lib.I8))
         assert st == _lib.SUCCESS and info.fused == 1, (n, e)
         st, info = describe(valid_args(A=above28, H=7168, N=n, E=e, tok=_lib.I8))
-        assert st == _lib.SUCCESS and info.fused == 0 and info.gather_kernel == 1, (n, e)
+        assert st == _lib.SUCCESS and info.fused == 2 and info.gather_kernel == 1, (n, e)
+        assert info.one_launch_workgroups == -(-above28 // 64) + above28 * 7
         assert info.offsets_workgroups == -(-above28 // 256)
     # 65..256 cells: the same below 48 MiB
     st, info = describe(valid_args(A=above28, H=7168, N=16, E=16, tok=_lib.I8))
     assert st == _lib.SUCCESS and info.fused == 1
     st, info = describe(valid_args(A=above48, H=7168, N=16, E=16, tok=_lib.I8))
-    assert st == _lib.SUCCESS and info.fused == 0 and info.offsets_workgroups == -(-above48 // 256)
+    assert st == _lib.SUCCESS and info.fused == 2 and info.offsets_workgroups == -(-above48 // 256)
+    # above the fused kernel's sizes but not the one-launch kernel's shape: offsets + gather
+    st, info = describe(valid_args(A=above48, H=7000, N=16, E=16, tok=_lib.I8))   # rows of 7000 bytes
+    assert st == _lib.SUCCESS and info.fused == 0 and info.one_launch_workgroups == 0
+    a = valid_args(A=above48, H=7168, N=16, E=16, tok=_lib.I8)
+    a.scales_ndim, a.scales_dims[1] = 2, 1025                                      # 4100-byte scale rows
+    st, info = describe(a)
+    assert st == _lib.SUCCESS and info.fused == 0
+    a.scales_dims[1] = 1024                                                        # 4096 bytes: still one launch
+    st, info = describe(a)
+    assert st == _lib.SUCCESS and info.fused == 2
+    st, info = describe(valid_args(A=above48, H=7168, N=1, E=257, tok=_lib.I8))   # 257 cells
+    assert st == _lib.SUCCESS and info.fused == 0
     # 257..512 cells: offsets + gather, the offsets in 512-thread workgroups of 512 rows
     st, info = describe(valid_args(A=3000, H=7168, N=16, E=32, tok=_lib.I8))
     assert st == _lib.SUCCESS and info.fused == 0 and info.offsets_workgroups == -(-3000 // 512)

@@ -1,0 +1,115 @@
+"""Parity of the one-launch stream kernel with the CPU oracle, byte for byte.
+
+moe_rerouting_v2 takes that kernel for count matrices of at most 256 cells,
+token rows of whole KiB and scale rows of at most 4 KiB, once the call is
+large enough (every case below first checks, through the plan, that it does):
+item waves of 64 output rows, then one wave per KiB of an input row, each
+wave computing the offsets it needs from the counts. Cases cover both
+directions, int32 and int64 counts, empty cells, one rank or one expert,
+count matrices of 35 and 64 cells, both index forms and expert_token_num
+modes, weights, and scale rows of 4 bytes, 12 bytes, e8m0 and 4000 bytes.
+Rejected counts (negative, a wrong sum, a count above INT32_MAX, int32
+counts whose sum wraps to A modulo 2^32) leave every output untouched."""
+import numpy as np
+import pytest
+
+from gpu_helpers import SENTINEL, _dev, assert_parity, run_hip, run_oracle
+from moe_token_re_amd import _lib, api, workloads
+
+pytestmark = pytest.mark.gpu
+
+MIB = 1 << 20
+DIRS = [_lib.FORWARD, _lib.INVERSE]
+DIR_IDS = ["forward", "inverse"]
+
+
+def sized_case(seed, n, e, h, tokens_dtype, target_mib=56, zero_cells=False, **kw):
+    """A random case whose token rows total about target_mib MiB."""
+    bits = workloads.TOKEN_DTYPES[tokens_dtype][0]
+    rows = target_mib * MIB // (h * bits // 8)
+    mean = max(1, rows // (n * e))
+    lo = 0 if zero_cells else mean // 2
+    return workloads.random_case(seed, n, e, h, tokens_dtype=tokens_dtype, count_range=(lo, 2 * mean - lo + 1),
+                                 **kw)
+
+
+def takes_one_launch(w, direction):
+    dev = _dev()
+    t = workloads.torch_inputs(w, dev)
+    call, _ = api.make_call(t["tokens"], t["counts"], per_token_scales=t["scales"], expert_topk_weight=t["weight"],
+                            expert_token_num_type=w.etn_type, idx_type=w.idx_type, tokens_dtype=t["tokens_dtype"],
+                            direction=direction)
+    return call.plan()["fused"] == 2
+
+
+CASES = {
+    "16x16_int8_a": dict(seed=501, n=16, e=16, h=1024, tokens_dtype="int8", scales="a"),
+    "16x16_bf16_i64_w_scatter_cumsum": dict(seed=502, n=16, e=16, h=2048, tokens_dtype="bfloat16",
+                                            counts_dtype=np.int64, weight=True, idx_type=1, etn_type=0),
+    "32x8_fp8_e8m0_w_scatter": dict(seed=503, n=32, e=8, h=7168, tokens_dtype="float8_e4m3fn", scales="e8m0",
+                                    weight=True, idx_type=1),
+    "5x7_f16_as3_zeros": dict(seed=504, n=5, e=7, h=512, tokens_dtype="float16", scales="as", S=3, zero_cells=True),
+    "1x256_int8": dict(seed=505, n=1, e=256, h=1024, tokens_dtype="int8", weight=True),
+    "256x1_fp4_a": dict(seed=506, n=256, e=1, h=4096, tokens_dtype="float4_e2m1fn_x2", scales="a", etn_type=0),
+    "8x8_f16_as37_w": dict(seed=507, n=8, e=8, h=512, tokens_dtype="float16", scales="as", S=37, weight=True),
+    "16x16_int8_wide_rows_zeros": dict(seed=508, n=16, e=16, h=15360, tokens_dtype="int8", zero_cells=True,
+                                       weight=True),
+    "4x4_int8_as1000": dict(seed=509, n=4, e=4, h=3072, tokens_dtype="int8", scales="as", S=1000, idx_type=1),
+    "16x13_bf16_e8m0_i64": dict(seed=510, n=16, e=13, h=1536, tokens_dtype="bfloat16", scales="e8m0",
+                                counts_dtype=np.int64, etn_type=0),
+}
+
+
+@pytest.mark.parametrize("direction", DIRS, ids=DIR_IDS)
+@pytest.mark.parametrize("name", list(CASES))
+def test_one_launch_parity(name, direction):
+    w = sized_case(**CASES[name])
+    assert takes_one_launch(w, direction), name
+    out, status = run_hip(w, _dev(), direction=direction)
+    assert status == _lib.SUCCESS, _lib.status_string(status)
+    assert_parity(w, out, run_oracle(w, direction))
+
+
+@pytest.mark.parametrize("direction", DIRS, ids=DIR_IDS)
+def test_one_launch_equals_two_phases(direction):
+    """The same call through the two phases (offsets kernel, stream gather)."""
+    w = sized_case(511, 16, 16, 1024, "int8", scales="e8m0", weight=True, idx_type=1)
+    assert takes_one_launch(w, direction)
+    whole, st1 = run_hip(w, _dev(), direction=direction)
+    parts, st2 = run_hip(w, _dev(), phases=True, direction=direction)
+    assert st1 == st2 == _lib.SUCCESS
+    for x, y in zip(whole, parts):
+        assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("direction", DIRS, ids=DIR_IDS)
+@pytest.mark.parametrize("kind", ["negative", "sum_low", "sum_high", "too_large", "wraps"])
+def test_one_launch_bad_counts_write_nothing(kind, direction):
+    rng = np.random.default_rng(77)
+    n, e, row = 16, 16, 1024
+    counts = rng.integers(180, 220, (n, e)).astype(np.int64 if kind == "too_large" else np.int32)
+    a = int(counts.sum())
+    if kind == "negative":
+        counts[1, 1] = -counts[1, 1]
+        counts[2, 2] += 2 * abs(int(counts[1, 1]))   # keep the sum at a
+    elif kind == "sum_low":
+        counts[0, 0] -= 1
+    elif kind == "sum_high":
+        counts[0, 0] += 1
+    elif kind == "too_large":
+        counts[3, 2] = (1 << 32) + counts[3, 2]     # above INT32_MAX
+    else:
+        # two counts at INT32_MAX: the true sum is a + 2^32, its low 32 bits a
+        o = int(counts[0, 0]) + int(counts[0, 1])
+        counts[0, 0] = counts[0, 1] = (1 << 31) - 1
+        counts[0, 2] += o + 2
+        assert int(counts.astype(np.int64).sum()) == a + (1 << 32)
+    tok = rng.integers(0, 256, (a, row), dtype=np.uint8)
+    w = workloads.Workload(f"bad_{kind}", counts, tok, "int8", row,
+                           rng.standard_normal(a, dtype=np.float32), "float32",
+                           rng.random((a, 1), dtype=np.float32), 1, 0)
+    assert takes_one_launch(w, direction)
+    out, status = run_hip(w, _dev(), direction=direction)
+    assert status == _lib.ERROR_BAD_COUNTS, kind
+    for o in out:
+        assert (o == SENTINEL).all(), kind
