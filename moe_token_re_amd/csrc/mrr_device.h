@@ -167,33 +167,26 @@ __device__ __forceinline__ uint32_t block_or(uint32_t flags, uint32_t* s_flags) 
   return *s_flags;
 }
 
-// Inclusive scan over the 64 lanes of a wave (wrapping 32-bit adds), with no
-// LDS traffic: DPP row shifts by 1, 2, 4 and 8 scan each row of 16 lanes, then
-// the row totals (read with readlane) are added to the later rows. Every lane
-// of the wave must be active.
+// Inclusive scan over the 64 lanes of a wave (wrapping 32-bit adds) in DPP
+// alone, with no LDS: row shifts by 1, 2, 4 and 8 scan each row of 16 lanes,
+// then row_bcast:15 adds lane 15's total to row 1 and lane 47's to row 3, and
+// row_bcast:31 adds lane 31's (rows 0-1) to rows 2 and 3; rows outside a
+// step's row mask keep their value. Every lane of the wave must be active.
 __device__ __forceinline__ uint32_t wave_scan_u32(uint32_t v) {
   constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+  constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
   v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kRowShr1, 0xf, 0xf, false));
   v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kRowShr2, 0xf, 0xf, false));
   v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kRowShr4, 0xf, 0xf, false));
   v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kRowShr8, 0xf, 0xf, false));
-  const uint32_t r0 = __builtin_amdgcn_readlane(v, 15);
-  const uint32_t r1 = __builtin_amdgcn_readlane(v, 31);
-  const uint32_t r2 = __builtin_amdgcn_readlane(v, 47);
-  const int row = (threadIdx.x & 63) >> 4;
-  return v + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kRowBcast15, 0xa, 0xf, false));
+  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kRowBcast31, 0xc, 0xf, false));
+  return v;
 }
 
-// Sum over the 64 lanes of a wave (wrapping 32-bit adds), in every lane: DPP
-// row shifts sum each row of 16 lanes, then the four row totals are added.
+// Sum over the 64 lanes of a wave (wrapping 32-bit adds), in every lane.
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-  constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
-  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kRowShr1, 0xf, 0xf, false));
-  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kRowShr2, 0xf, 0xf, false));
-  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kRowShr4, 0xf, 0xf, false));
-  v += static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), kRowShr8, 0xf, 0xf, false));
-  return __builtin_amdgcn_readlane(v, 15) + __builtin_amdgcn_readlane(v, 31) + __builtin_amdgcn_readlane(v, 47) +
-         __builtin_amdgcn_readlane(v, 63);
+  return __builtin_amdgcn_readlane(wave_scan_u32(v), 63);
 }
 
 // Exact sum over the 64 lanes of a wave of values below 2^42, without LDS:

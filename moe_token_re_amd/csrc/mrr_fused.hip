@@ -208,9 +208,9 @@ struct RawCells {
   uint32_t pos;  // this lane's word of the host's output-position table (loaded with the counts)
 };
 
-template <typename CountT, bool kVec>
-__device__ __forceinline__ void load_cells(const CountT* __restrict__ counts, int M, int inverse,
-                                           const StreamFusedArgs& f, RawCells<CountT>& rc) {
+template <typename CountT, bool kVec, bool kInv>
+__device__ __forceinline__ void load_cells(const CountT* __restrict__ counts, int M, const StreamFusedArgs& f,
+                                           RawCells<CountT>& rc) {
   const int lane = threadIdx.x & 63;
   rc.pos = f.outpos[lane];
   if (kVec) {
@@ -237,17 +237,19 @@ __device__ __forceinline__ void load_cells(const CountT* __restrict__ counts, in
     for (int k = 0; k < kCellsPerLane; ++k) rc.r[k] = in ? r[k] : CountT(0);
     return;
   }
-  // Addresses first, branch-free (a branch on `inverse` between the loads
-  // would make the compiler wait for the earlier ones at its join). Inverse,
-  // cell (rank b, expert a) of the column-major order sits at b * E + a.
-  const int inv_mask = -inverse;  // 0 or all ones
+  // Addresses first (no branch between the loads: at its join the compiler
+  // would wait for the earlier ones). Inverse, cell (rank b, expert a) of the
+  // column-major order sits at b * E + a.
   int at[kCellsPerLane];
 #pragma unroll
   for (int k = 0; k < kCellsPerLane; ++k) {
     const int m = kCellsPerLane * lane + k;
-    const int a = div_small(m, f.inv_minor);
-    const int cm = (m - a * f.minor) * f.major + a;
-    at[k] = m < M ? m + ((cm - m) & inv_mask) : 0;  // M >= 1 here
+    int cm = m;
+    if (kInv) {
+      const int a = div_small(m, f.inv_minor);
+      cm = (m - a * f.minor) * f.major + a;
+    }
+    at[k] = m < M ? cm : 0;  // M >= 1 here
   }
 #pragma unroll
   for (int k = 0; k < kCellsPerLane; ++k) {
@@ -261,9 +263,9 @@ __device__ __forceinline__ void load_cells(const CountT* __restrict__ counts, in
 // LDS write and four reads per lane. Called after the token load is issued.
 // The LDS operations of one wave complete in order, so the reads see the
 // writes.
-template <typename CountT, bool kVec>
-__device__ __forceinline__ void order_cells(RawCells<CountT>& rc, CountT* s_c, int M, int inverse) {
-  if (!kVec || !inverse) return;
+template <typename CountT, bool kVec, bool kInv>
+__device__ __forceinline__ void order_cells(RawCells<CountT>& rc, CountT* s_c, int M) {
+  if (!kVec || !kInv) return;
   const int lane = threadIdx.x & 63;
   if (kCellsPerLane * lane < M) {
 #pragma unroll
@@ -311,13 +313,23 @@ struct InCells {
   uint32_t flags;  // uniform: kFlag* of the whole matrix (0: valid)
 };
 
-template <typename CountT>
+// kFlags: the flags say why the counts are rejected (item waves: workgroup 0
+// writes them to the header); without it (token waves) any rejection shows
+// as kFlagNegative, which is enough to write nothing and costs fewer
+// instructions (a count is in [0, 2^31) when its bits from 31 up are 0).
+template <typename CountT, bool kFlags>
 __device__ __forceinline__ void finish_cells(const RawCells<CountT>& rc, int A, InCells& w) {
   uint32_t fl = 0;
   uint32_t own = 0;
 #pragma unroll
   for (int k = 0; k < kCellsPerLane; ++k) {
-    w.c[k] = clamp_count(rc.r[k], &fl);
+    if (kFlags) {
+      w.c[k] = clamp_count(rc.r[k], &fl);
+    } else {
+      const uint64_t u = static_cast<uint64_t>(static_cast<int64_t>(rc.r[k]));
+      w.c[k] = static_cast<int32_t>(u & 0x7fffffffu);
+      fl |= static_cast<uint32_t>(u >> 31);  // 0 for counts in [0, 2^31)
+    }
     own += static_cast<uint32_t>(w.c[k]);
   }
   const uint32_t incl = wave_scan_u32(own);
@@ -325,8 +337,9 @@ __device__ __forceinline__ void finish_cells(const RawCells<CountT>& rc, int A, 
   w.start[0] = incl - own;
 #pragma unroll
   for (int k = 1; k < kCellsPerLane; ++k) w.start[k] = w.start[k - 1] + static_cast<uint32_t>(w.c[k - 1]);
-  uint32_t flags = (__ballot(fl & kFlagNegative) != 0 ? kFlagNegative : 0u) |
-                   (__ballot(fl & kFlagTooLarge) != 0 ? kFlagTooLarge : 0u);
+  uint32_t flags = kFlags ? (__ballot(fl & kFlagNegative) != 0 ? kFlagNegative : 0u) |
+                               (__ballot(fl & kFlagTooLarge) != 0 ? kFlagTooLarge : 0u)
+                         : (__ballot(fl != 0) != 0 ? kFlagNegative : 0u);
   const uint32_t any = static_cast<uint32_t>(w.c[0] | w.c[1] | w.c[2] | w.c[3]);  // counts are >= 0 here
   if (__ballot(any >= (1u << 22)) != 0) {  // uniform and rare
     uint32_t hi = 0;
@@ -350,28 +363,28 @@ __device__ __forceinline__ uint32_t cell_value(const uint32_t (&v)[kCellsPerLane
 // Token wave c: 1 KiB chunk c % cpr of input row c / cpr (one 16-byte load
 // and store per lane: this chip streams fastest with one-wave workgroups of
 // one load each; two chunks a wave measured slower).
-template <typename CountT, bool kVec>
+template <typename CountT, bool kVec, bool kInv>
 __device__ __forceinline__ void stream_fused_tokens(const GatherArgs& p, const StreamFusedArgs& f, uint32_t c,
                                                     uint32_t* s_lds) {
   using T = VecT<16>::type;
   const int lane = threadIdx.x & 63;
-  uint32_t s = c;
-  if (f.cpr != 1) {  // uniform
-    const uint32_t q = __umulhi(c, f.cpr_magic);
-    s = q - (q * f.cpr > c ? 1u : 0u);
-  }
-  s = __builtin_amdgcn_readfirstlane(s);
+  // s = c / cpr, branch-free (a branch here would make the compiler fetch the
+  // kernel arguments one after the other): the multiply-high is c / cpr or one
+  // above; cpr == 1 (magic 0) takes c itself.
+  const uint32_t q = __umulhi(c, f.cpr_magic);
+  uint32_t s = q - (q * f.cpr > c ? 1u : 0u);
+  s = __builtin_amdgcn_readfirstlane(f.cpr == 1 ? c : s);
   const int64_t col = int64_t(c - s * f.cpr) * 1024 + lane * 16;
   RawCells<CountT> rc;
-  load_cells<CountT, kVec>(static_cast<const CountT*>(f.counts), p.M, p.inverse, f, rc);
+  load_cells<CountT, kVec, kInv>(static_cast<const CountT*>(f.counts), p.M, f, rc);
   const T v = __builtin_nontemporal_load(reinterpret_cast<const T*>(p.tokens + int64_t(s) * p.row_bytes + col));
   // The offsets below wait for the counts alone (loads return in issue
   // order). The compiler would otherwise sink the token load below them, next
   // to its store: this barrier names the token buffer, so the load stays here.
   asm volatile("" ::"s"(p.tokens) : "memory");
-  order_cells<CountT, kVec>(rc, reinterpret_cast<CountT*>(s_lds), p.M, p.inverse);
+  order_cells<CountT, kVec, kInv>(rc, reinterpret_cast<CountT*>(s_lds), p.M);
   InCells w;
-  finish_cells<CountT>(rc, p.A, w);
+  finish_cells<CountT, false>(rc, p.A, w);
   uint32_t outp[kCellsPerLane];
   cell_positions(rc.pos, outp);
   // The cell of input row s is the last one that starts at or before it.
@@ -425,7 +438,7 @@ __device__ __forceinline__ void stream_fused_scales(const GatherArgs& p, const S
 // Item wave iw: output rows [64 iw, 64 iw + 64). The offsets in output order
 // come from one exchange of the counts through LDS; each row finds its cell by
 // a mark at every cell start within the 64 rows and a running maximum.
-template <bool kScatter, bool kWeight, typename CountT, bool kVec>
+template <bool kScatter, bool kWeight, typename CountT, bool kVec, bool kInv>
 __device__ __forceinline__ void stream_fused_items(const GatherArgs& p, const StreamFusedArgs& f, int iw,
                                                    uint32_t* s_lds) {
   uint32_t* s_cnt = s_lds;                                 // by output position: the count,
@@ -435,10 +448,10 @@ __device__ __forceinline__ void stream_fused_items(const GatherArgs& p, const St
   const int lane = threadIdx.x & 63;
   const int M = p.M, A = p.A;
   RawCells<CountT> rc;
-  load_cells<CountT, kVec>(static_cast<const CountT*>(f.counts), M, p.inverse, f, rc);
-  order_cells<CountT, kVec>(rc, reinterpret_cast<CountT*>(s_lds), M, p.inverse);
+  load_cells<CountT, kVec, kInv>(static_cast<const CountT*>(f.counts), M, f, rc);
+  order_cells<CountT, kVec, kInv>(rc, reinterpret_cast<CountT*>(s_lds), M);
   InCells w;
-  finish_cells<CountT>(rc, A, w);
+  finish_cells<CountT, true>(rc, A, w);
   uint32_t outp[kCellsPerLane];
   cell_positions(rc.pos, outp);
   const int d0 = iw * 64;
@@ -504,8 +517,8 @@ __device__ __forceinline__ void stream_fused_items(const GatherArgs& p, const St
     const int E = static_cast<int>(p.E), N = static_cast<int>(p.N);
     if (valid)
       for (int j = lane; j < E; j += 64) {
-        const uint32_t a0 = p.inverse ? s_in[j] : s_out[j * N];
-        const uint32_t a1 = j + 1 < E ? (p.inverse ? s_in[j + 1] : s_out[(j + 1) * N]) : static_cast<uint32_t>(A);
+        const uint32_t a0 = kInv ? s_in[j] : s_out[j * N];
+        const uint32_t a1 = j + 1 < E ? (kInv ? s_in[j + 1] : s_out[(j + 1) * N]) : static_cast<uint32_t>(A);
         static_cast<CountT*>(f.etn)[j] = static_cast<CountT>(f.cumsum ? a1 : a1 - a0);
       }
     // the exact sum for the header: the bits from 2^20 up and the low 20
@@ -525,15 +538,19 @@ __device__ __forceinline__ void stream_fused_items(const GatherArgs& p, const St
 // marks; the token waves use its first 256 counts (inverse, kVec).
 constexpr int kStreamFusedLdsWords = 3 * kCellsPerLane * 64 + 64;
 
-template <bool kScatter, bool kWeight, typename CountT, bool kVec>
+template <bool kScatter, bool kWeight, typename CountT, bool kVec, bool kInv>
 __global__ __launch_bounds__(64) void stream_fused_kernel(GatherArgs p, StreamFusedArgs f) {
   __shared__ uint32_t s_lds[kStreamFusedLdsWords];
   const int b = static_cast<int>(blockIdx.x);
+  // The scalars a token wave needs before its loads, fetched together with the
+  // first kernel arguments (the compiler would fetch them one after the
+  // other inside the branch, each a scalar-cache round trip).
+  asm volatile("" ::"s"(p.tokens), "s"(f.counts), "s"(f.cpr), "s"(f.cpr_magic), "s"(p.row_bytes), "s"(p.M));
   if (b < f.item_waves) {  // uniform
-    stream_fused_items<kScatter, kWeight, CountT, kVec>(p, f, b, s_lds);
+    stream_fused_items<kScatter, kWeight, CountT, kVec, kInv>(p, f, b, s_lds);
     return;
   }
-  stream_fused_tokens<CountT, kVec>(p, f, static_cast<uint32_t>(b - f.item_waves), s_lds);
+  stream_fused_tokens<CountT, kVec, kInv>(p, f, static_cast<uint32_t>(b - f.item_waves), s_lds);
 }
 
 template <int V, int SV, bool S, bool W>
@@ -545,21 +562,32 @@ struct FusedK64 {
   static auto fn() { return &fused_kernel<V, SV, S, W, int64_t>; }
 };
 
-template <typename CountT, bool kVec>
+template <typename CountT, bool kVec, bool kInv>
 void launch_stream_fused_c(const Plan& pl, const GatherArgs& g, const StreamFusedArgs& f, unsigned grid,
                            hipStream_t stream) {
   const dim3 block(64);
   if (pl.scatter) {
     if (pl.has_weight)
-      hipLaunchKernelGGL((stream_fused_kernel<true, true, CountT, kVec>), dim3(grid), block, 0, stream, g, f);
+      hipLaunchKernelGGL((stream_fused_kernel<true, true, CountT, kVec, kInv>), dim3(grid), block, 0, stream, g, f);
     else
-      hipLaunchKernelGGL((stream_fused_kernel<true, false, CountT, kVec>), dim3(grid), block, 0, stream, g, f);
+      hipLaunchKernelGGL((stream_fused_kernel<true, false, CountT, kVec, kInv>), dim3(grid), block, 0, stream, g, f);
   } else {
     if (pl.has_weight)
-      hipLaunchKernelGGL((stream_fused_kernel<false, true, CountT, kVec>), dim3(grid), block, 0, stream, g, f);
+      hipLaunchKernelGGL((stream_fused_kernel<false, true, CountT, kVec, kInv>), dim3(grid), block, 0, stream, g, f);
     else
-      hipLaunchKernelGGL((stream_fused_kernel<false, false, CountT, kVec>), dim3(grid), block, 0, stream, g, f);
+      hipLaunchKernelGGL((stream_fused_kernel<false, false, CountT, kVec, kInv>), dim3(grid), block, 0, stream, g, f);
   }
+}
+
+template <typename CountT>
+void launch_stream_fused_v(const Plan& pl, const GatherArgs& g, const StreamFusedArgs& f, unsigned grid, bool vec,
+                           hipStream_t stream) {
+  if (vec)
+    pl.inverse ? launch_stream_fused_c<CountT, true, true>(pl, g, f, grid, stream)
+               : launch_stream_fused_c<CountT, true, false>(pl, g, f, grid, stream);
+  else
+    pl.inverse ? launch_stream_fused_c<CountT, false, true>(pl, g, f, grid, stream)
+               : launch_stream_fused_c<CountT, false, false>(pl, g, f, grid, stream);
 }
 
 }  // namespace
@@ -589,11 +617,9 @@ mrr_status launch_stream_fused(const Plan& pl, const mrr_args* a, void* ws, hipS
   // a lane's four counts in one or two 16-byte loads: aligned, whole groups of four cells
   const bool vec = reinterpret_cast<uintptr_t>(a->expert_token_num_per_rank) % 16 == 0 && pl.M % kCellsPerLane == 0;
   if (pl.count_bytes == 8)
-    vec ? launch_stream_fused_c<int64_t, true>(pl, g, f, grid, stream)
-        : launch_stream_fused_c<int64_t, false>(pl, g, f, grid, stream);
+    launch_stream_fused_v<int64_t>(pl, g, f, grid, vec, stream);
   else
-    vec ? launch_stream_fused_c<int32_t, true>(pl, g, f, grid, stream)
-        : launch_stream_fused_c<int32_t, false>(pl, g, f, grid, stream);
+    launch_stream_fused_v<int32_t>(pl, g, f, grid, vec, stream);
   return hipGetLastError() == hipSuccess ? MRR_SUCCESS : MRR_ERROR_HIP;
 }
 
