@@ -1,7 +1,9 @@
 """Throughput of the MoE re-routing operator (MoeReRoutingV2) on one MI355X.
 
-A step is one whole call of the operator (offsets kernel + gather kernel, or
-the single fused kernel for small calls) on one batch of synthetic input
+A step is one whole call of the operator (the one-launch stream kernel for
+count matrices of at most 256 cells and token rows of whole KiB, the fused
+kernel for small calls, else offsets kernel + gather kernel) on one batch of
+synthetic input
 already resident in HBM. The headline workload is the shape of the pages'
 single-operator example: A=16384 tokens of H=7168 int8 values, N=E=16, one
 huge segment, [A] fp32 scales (moe_token_re_amd/workloads.py has the recipe).
@@ -12,8 +14,9 @@ calls. Prints ONE JSON line:
   value        re-route GB/s = algorithmic bytes per call / wall time per call,
                the wall clock around exactly K calls, synchronized on both
                sides (nothing else inside the timed region)
-  roofline     the dominant kernel alone (the gather kernel of the two-kernel
-               path, or the fused kernel): algorithmic bytes per launch / its
+  roofline     the dominant kernel alone (the one-launch kernel, the fused
+               kernel, or the gather kernel of the two-kernel path):
+               algorithmic bytes per launch / its
                mean duration, measured live as the mean period of K launches
                back to back between two HIP events on the launch stream (an
                event pair around each single launch adds ~2.5 us of its own).
@@ -254,7 +257,8 @@ class Bench:
         µs, event-pair mean µs), and the offsets kernel's back-to-back µs."""
         if self.plan["fused"]:
             run = lambda c: c.run()  # noqa: E731
-            name, kbytes, off = "fused_kernel", self.alg_bytes, None
+            name = "stream_fused_kernel" if self.plan["fused"] == 2 else "fused_kernel"
+            kbytes, off = self.alg_bytes, None
         else:
             name = "stream_gather_kernel" if self.plan["gather_kernel"] == 1 else "gather_kernel"
             kbytes = gather_bytes_per_launch(self.w)
@@ -339,6 +343,11 @@ class Bench:
         return us
 
 
+def launch_path(plan):
+    return {2: "one-launch stream kernel", 1: "fused single kernel"}.get(plan["fused"],
+                                                                         "offsets kernel + gather kernel")
+
+
 def workload_summary(torch, dev, name, direction, copy_lib, steps):
     """µs per call, GB/s and roofline fractions of one more workload."""
     from moe_token_re_amd import workloads
@@ -354,7 +363,7 @@ def workload_summary(torch, dev, name, direction, copy_lib, steps):
     k_gbps = kbytes / (k_us * 1e-6) / 1e9
     out = {"direction": direction, "us_per_call": round(us, 2), "GBps": round(gbps, 1),
            "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2), "algorithmic_bytes_per_call": b.alg_bytes,
-           "path": "fused single kernel" if b.plan["fused"] else "offsets kernel + gather kernel",
+           "path": launch_path(b.plan),
            "kernel": kname, "kernel_us_back_to_back": round(k_us, 2),
            "kernel_frac_of_8TBps": round(k_gbps / HBM_PEAK_GBPS, 4),
            "copy_ceiling_GBps": ceil["ceiling_GBps"],
@@ -469,7 +478,7 @@ def main():
         "us_per_call_graph": round(graph_us, 2),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "algorithmic_bytes_per_call": b.alg_bytes,
-        "launch_path": "fused single kernel" if b.plan["fused"] else "offsets kernel + gather kernel",
+        "launch_path": launch_path(b.plan),
         "offsets_kernel_us_back_to_back": None if off_us is None else round(off_us, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4),

@@ -196,12 +196,16 @@ def test_describe_plan():
     assert info.token_row_bytes == 7168 and info.scale_row_bytes == 4 and info.scale_vec_bytes == 4
     assert info.threads_per_workgroup == 64 and info.gather_workgroups == 114688 + 16384 // 256
     assert info.offsets_workgroups == 64           # the row map: one workgroup per 256 rows (<= 256 cells)
-    # a smaller call with the same counts: one kernel whose workgroups each recompute the offsets
+    # a smaller call with the same counts: the same one-launch kernel, whatever the size
     st, info = describe(valid_args(A=2048, H=7168, N=16, E=16, tok=_lib.I8))
+    assert st == _lib.SUCCESS and info.fused == 2 and info.one_launch_workgroups == 2048 // 64 + 2048 * 7
+    # rows that are no whole number of KiB (7184 bytes): one kernel of 256-thread workgroups that each
+    # recompute the offsets of the (small) count matrix
+    st, info = describe(valid_args(A=2048, H=7184, N=16, E=16, tok=_lib.I8))
     assert st == _lib.SUCCESS and info.fused == 1 and info.threads_per_workgroup == 256
     assert info.one_launch_workgroups == info.gather_workgroups
     assert info.scale_inline_bytes == 4            # one 4-byte piece per row, loaded with the tokens
-    rows = max(1, info.threads_per_workgroup * 8 // 448)
+    rows = max(1, info.threads_per_workgroup * 8 // 449)
     assert info.rows_per_workgroup == min(rows, 256)
     assert info.gather_workgroups == -(-2048 // info.rows_per_workgroup)
     # 256x64 counts are too many to recompute per workgroup: two kernels
@@ -257,29 +261,32 @@ def test_plan_size_classes():
     """The launch choices by count-matrix size and token bytes (launch shape
     only; every choice computes the same bytes)."""
     mib = 1 << 20
-    below28, above28, above48 = 28 * mib // 7168 - 1, 28 * mib // 7168 + 1, 48 * mib // 7168 + 1  # 7168-byte rows
-    # at most 64 cells: the fused kernel below 28 MiB of token rows, else the one-launch stream
-    # kernel (rows of whole KiB); the two phases: offsets + stream gather
+    # token rows of whole KiB (7168 bytes), at most 256 cells: the one-launch stream kernel at any size
+    for n, e in [(8, 8), (4, 4), (1, 64), (16, 16)]:
+        for a_rows in (1, 100, 48 * mib // 7168 + 1):
+            st, info = describe(valid_args(A=a_rows, H=7168, N=n, E=e, tok=_lib.I8))
+            assert st == _lib.SUCCESS and info.fused == 2, (n, e, a_rows)
+            assert info.one_launch_workgroups == -(-a_rows // 64) + a_rows * 7
+    # rows of 7184 bytes (16-byte vectors, no whole KiB): the fused kernel up to 28 MiB of token
+    # rows with at most 64 cells, 48 MiB with at most 256, else offsets + gather
+    below28, above28, above48 = 28 * mib // 7184 - 1, 28 * mib // 7184 + 1, 48 * mib // 7184 + 1
     for n, e in [(8, 8), (4, 4), (1, 64)]:
-        st, info = describe(valid_args(A=below28, H=7168, N=n, E=e, tok=_lib.I8))
+        st, info = describe(valid_args(A=below28, H=7184, N=n, E=e, tok=_lib.I8))
         assert st == _lib.SUCCESS and info.fused == 1, (n, e)
-        st, info = describe(valid_args(A=above28, H=7168, N=n, E=e, tok=_lib.I8))
-        assert st == _lib.SUCCESS and info.fused == 2 and info.gather_kernel == 1, (n, e)
-        assert info.one_launch_workgroups == -(-above28 // 64) + above28 * 7
-        assert info.offsets_workgroups == -(-above28 // 256)
-    # 65..256 cells: the same below 48 MiB
-    st, info = describe(valid_args(A=above28, H=7168, N=16, E=16, tok=_lib.I8))
+        st, info = describe(valid_args(A=above28, H=7184, N=n, E=e, tok=_lib.I8))
+        assert st == _lib.SUCCESS and info.fused == 0 and info.gather_kernel == 1, (n, e)
+        assert info.one_launch_workgroups == 0 and info.offsets_workgroups == -(-above28 // 256)
+    st, info = describe(valid_args(A=above28, H=7184, N=16, E=16, tok=_lib.I8))
     assert st == _lib.SUCCESS and info.fused == 1
-    st, info = describe(valid_args(A=above48, H=7168, N=16, E=16, tok=_lib.I8))
-    assert st == _lib.SUCCESS and info.fused == 2 and info.offsets_workgroups == -(-above48 // 256)
-    # above the fused kernel's sizes but not the one-launch kernel's shape: offsets + gather
-    st, info = describe(valid_args(A=above48, H=7000, N=16, E=16, tok=_lib.I8))   # rows of 7000 bytes
-    assert st == _lib.SUCCESS and info.fused == 0 and info.one_launch_workgroups == 0
+    st, info = describe(valid_args(A=above48, H=7184, N=16, E=16, tok=_lib.I8))
+    assert st == _lib.SUCCESS and info.fused == 0 and info.offsets_workgroups == -(-above48 // 256)
+    # whole-KiB rows but not the one-launch kernel's other limits (above 48 MiB: offsets + gather)
+    above48 = 48 * mib // 7168 + 1
     a = valid_args(A=above48, H=7168, N=16, E=16, tok=_lib.I8)
     a.scales_ndim, a.scales_dims[1] = 2, 1025                                      # 4100-byte scale rows
     st, info = describe(a)
     assert st == _lib.SUCCESS and info.fused == 0
-    a.scales_dims[1] = 1024                                                        # 4096 bytes: still one launch
+    a.scales_dims[1] = 1024                                                        # 4096 bytes: one launch
     st, info = describe(a)
     assert st == _lib.SUCCESS and info.fused == 2
     st, info = describe(valid_args(A=above48, H=7168, N=1, E=257, tok=_lib.I8))   # 257 cells

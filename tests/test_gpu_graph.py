@@ -19,17 +19,21 @@ def _host_bytes(outs):
 
 
 @pytest.mark.parametrize("direction", [_lib.FORWARD, _lib.INVERSE], ids=["forward", "inverse"])
-@pytest.mark.parametrize("n,e,fused", [(4, 3, True), (40, 30, False)], ids=["fused", "two_kernel"])
-def test_graph_replays_match_oracle(n, e, fused, direction):
+# (N, E, H, counts, the plan's launch): the fused kernel, the two kernels, and
+# the one-launch stream kernel (50 MiB of 1 KiB bf16 rows)
+@pytest.mark.parametrize("n,e,h,count_range,fused", [(4, 3, 256, (0, 6), 1), (40, 30, 256, (0, 6), 0),
+                                                     (16, 16, 512, (180, 221), 2)],
+                         ids=["fused", "two_kernel", "one_launch"])
+def test_graph_replays_match_oracle(n, e, h, count_range, fused, direction):
     dev = _dev()
-    base = workloads.random_case(71, n, e, 256, tokens_dtype="bfloat16", count_range=(0, 6), scales="as", S=3,
+    base = workloads.random_case(71, n, e, h, tokens_dtype="bfloat16", count_range=count_range, scales="as", S=3,
                                  weight=True, idx_type=1, etn_type=0)
     t = workloads.torch_inputs(base, dev)
     side = torch.cuda.Stream(dev)
     call, outs = api.make_call(t["tokens"], t["counts"], per_token_scales=t["scales"],
                                expert_topk_weight=t["weight"], expert_token_num_type=base.etn_type,
                                idx_type=base.idx_type, stream=side, direction=direction)
-    assert call.plan()["fused"] == int(fused)
+    assert call.plan()["fused"] == fused
     with torch.cuda.stream(side):
         call.run()  # eager first call: one-time per-device set-up happens outside the capture
     torch.cuda.synchronize()

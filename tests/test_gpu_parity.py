@@ -355,21 +355,22 @@ def test_bad_counts_raise_with_check():
         api.moe_re_routing(tokens, counts, check=True)
 
 
-@pytest.mark.parametrize("first", ["offsets", "fused_call"])
+@pytest.mark.parametrize("first", ["offsets", "fused_call", "one_launch_call"])
 def test_gather_needs_matching_tables(first):
     """A gather phase on a workspace whose table was built for another
-    (A, N, E), or that holds no table (a fused whole call builds none),
-    writes nothing."""
+    (A, N, E), or that holds no table (a whole call in one launch, fused or
+    one-launch stream kernel, builds none), writes nothing."""
     dev = _dev()
-    w1 = workloads.random_case(1, 3, 3, 64, tokens_dtype="int8", count_range=(1, 5))
+    h = 1024 if first == "one_launch_call" else 64
+    w1 = workloads.random_case(1, 3, 3, h, tokens_dtype="int8", count_range=(1, 5))
     t1 = workloads.torch_inputs(w1, dev)
     call1, _ = api.make_call(t1["tokens"], t1["counts"])
     if first == "offsets":
         call1.run_offsets()
     else:
-        assert call1.plan()["fused"] == 1
+        assert call1.plan()["fused"] == (2 if first == "one_launch_call" else 1)
         call1.run()
-    w2 = (workloads.random_case(2, 3, 4, 64, tokens_dtype="int8", count_range=(1, 5)) if first == "offsets"
+    w2 = (workloads.random_case(2, 3, 4, h, tokens_dtype="int8", count_range=(1, 5)) if first == "offsets"
           else w1)
     t2 = workloads.torch_inputs(w2, dev)
     args, outs = api.prepare(t2["tokens"], t2["counts"])
