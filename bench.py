@@ -61,7 +61,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 METRIC = "re-route GB/s (bytes read+written) and % of HBM peak; µs/call A=16384 H=7168"
-PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "stream_gather_pages_shape_counters.txt")
+PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "stream_fused_pages_shape_counters.txt")
 STATS_SUMMARY = os.path.join(ROOT, "profiles", "pages_shape_kernel_stats.md")
 # the other workloads the default run reports (name, direction)
 OTHER_WORKLOADS = (("tiny", "forward"), ("balanced_bf16", "forward"), ("mxfp8_skewed", "forward"),
