@@ -103,14 +103,15 @@ struct FusedArgs {
 };
 
 // The one-launch stream kernel's own arguments (count matrices of at most 256
-// cells, token rows of whole 1 KiB chunks).
+// cells, token rows of whole 16-byte vectors, at least 1 KiB).
 struct StreamFusedArgs {
   const void* counts;
   void* etn;
   int32_t cumsum;
   int32_t item_waves;  // workgroups [0, item_waves) move the per-row items, 64 output rows each
-  uint32_t cpr;        // 1 KiB chunks per token row
-  uint32_t cpr_magic;  // ceil(2^32 / cpr): chunk / cpr by a multiply-high and one correction
+  uint32_t vpr;        // 16-byte vectors per token row (at least 64)
+  uint32_t vpr_magic;  // ceil(2^32 / vpr): n / vpr by a multiply-high and one correction (n < 2^32)
+  uint32_t vectors;    // A * vpr: the token vectors of the call
   int32_t minor;       // cells per major index in input order: E forward, N inverse
   int32_t major;       // N forward, E inverse
   float inv_minor;     // 1 / minor

@@ -181,12 +181,12 @@ __global__ __launch_bounds__(kGatherThreads) void fused_kernel(GatherArgs p, Fus
 
 // ---------------------------------------------------------------------------
 // The whole call in one launch of 64-lane workgroups, for count matrices of at
-// most 256 cells and token rows of whole 1 KiB chunks. Workgroups
-// [0, item_waves) move the per-row items and scale rows of 64 output rows
-// each; every later workgroup moves one 1 KiB chunk of one input row, in input
-// order, so that its token load goes out at once (beside the count load); it
-// then works out where the row goes from the counts while the load is in
-// flight. Every wave checks the counts itself and writes nothing when they
+// most 256 cells and token rows of 16-byte vectors and at least 1 KiB.
+// Workgroups [0, item_waves) move the per-row items and scale rows of 64
+// output rows each; every later workgroup moves one 1 KiB chunk of the input
+// token rows, in input order, so that its token load goes out at once (beside
+// the count load); it then works out where its row (or two rows) go from the
+// counts while the load is in flight. Every wave checks the counts itself and writes nothing when they
 // are rejected; workgroup 0 writes expert_token_num and the status.
 // ---------------------------------------------------------------------------
 
@@ -360,24 +360,47 @@ __device__ __forceinline__ uint32_t cell_value(const uint32_t (&v)[kCellsPerLane
   return __builtin_amdgcn_readlane((m & 2) ? hi : lo, m >> 2);
 }
 
-// Token wave c: 1 KiB chunk c % cpr of input row c / cpr (one 16-byte load
-// and store per lane: this chip streams fastest with one-wave workgroups of
-// one load each; two chunks a wave measured slower).
+// The cell holding input row s (the last one that starts at or before it),
+// in every lane; 0 when the counts are rejected and no cell qualifies.
+__device__ __forceinline__ int cell_of(uint32_t s, const InCells& w) {
+  int m = -1;
+#pragma unroll
+  for (int k = 0; k < kCellsPerLane; ++k) m += __popcll(__ballot(w.start[k] <= s));
+  return max(m, 0);
+}
+
+// The output row of input row s in cell m: the cell's output offset (the
+// counts of the cells before it in output order) plus s's place in the cell.
+__device__ __forceinline__ uint32_t dest_row(uint32_t s, int m, const InCells& w, uint32_t pos,
+                                             const uint32_t (&outp)[kCellsPerLane]) {
+  const uint32_t out_m = cell_position(pos, m);
+  uint32_t before = 0;
+#pragma unroll
+  for (int k = 0; k < kCellsPerLane; ++k) before += outp[k] < out_m ? static_cast<uint32_t>(w.c[k]) : 0u;
+  return wave_sum_u32(before) + (s - cell_value(w.start, m));
+}
+
+// Token wave c: the 16-byte vectors [64 c, 64 c + 64) of the input token rows
+// taken as one stream (input order, vpr >= 64 vectors a row), one load and
+// store per lane: this chip streams fastest with one-wave workgroups of one
+// load each (two chunks a wave measured slower). The load needs no offsets.
+// The chunk lies in row s0, or reaches into row s0 + 1 when the rows are no
+// whole number of KiB; then the wave also works out where row s0 + 1 goes
+// (the next output row when it is in the same cell).
 template <typename CountT, bool kVec, bool kInv>
 __device__ __forceinline__ void stream_fused_tokens(const GatherArgs& p, const StreamFusedArgs& f, uint32_t c,
                                                     uint32_t* s_lds) {
   using T = VecT<16>::type;
   const int lane = threadIdx.x & 63;
-  // s = c / cpr, branch-free (a branch here would make the compiler fetch the
-  // kernel arguments one after the other): the multiply-high is c / cpr or one
-  // above; cpr == 1 (magic 0) takes c itself.
-  const uint32_t q = __umulhi(c, f.cpr_magic);
-  uint32_t s = q - (q * f.cpr > c ? 1u : 0u);
-  s = __builtin_amdgcn_readfirstlane(f.cpr == 1 ? c : s);
-  const int64_t col = int64_t(c - s * f.cpr) * 1024 + lane * 16;
+  const uint32_t n0 = c * 64u;  // the chunk's first vector; A * vpr < 2^32 (the plan checks)
+  // s0 = n0 / vpr: the multiply-high is the quotient or one above
+  const uint32_t q = __umulhi(n0, f.vpr_magic);
+  const uint32_t s0 = __builtin_amdgcn_readfirstlane(q - (q * f.vpr > n0 ? 1u : 0u));
+  const uint32_t v = n0 + static_cast<uint32_t>(lane);
+  const bool in = v < f.vectors;  // the last chunk may be partial
   RawCells<CountT> rc;
   load_cells<CountT, kVec, kInv>(static_cast<const CountT*>(f.counts), p.M, f, rc);
-  const T v = __builtin_nontemporal_load(reinterpret_cast<const T*>(p.tokens + int64_t(s) * p.row_bytes + col));
+  const T x = __builtin_nontemporal_load(reinterpret_cast<const T*>(p.tokens + (in ? int64_t(v) * 16 : 0)));
   // The offsets below wait for the counts alone (loads return in issue
   // order). The compiler would otherwise sink the token load below them, next
   // to its store: this barrier names the token buffer, so the load stays here.
@@ -387,20 +410,19 @@ __device__ __forceinline__ void stream_fused_tokens(const GatherArgs& p, const S
   finish_cells<CountT, false>(rc, p.A, w);
   uint32_t outp[kCellsPerLane];
   cell_positions(rc.pos, outp);
-  // The cell of input row s is the last one that starts at or before it.
-  int m = -1;
-#pragma unroll
-  for (int k = 0; k < kCellsPerLane; ++k) m += __popcll(__ballot(w.start[k] <= s));
-  m = max(m, 0);  // -1 only for rejected counts
-  const uint32_t src_m = cell_value(w.start, m);
-  const uint32_t out_m = cell_position(rc.pos, m);
-  // Its output offset: the counts of the cells before it in output order.
-  uint32_t before = 0;
-#pragma unroll
-  for (int k = 0; k < kCellsPerLane; ++k) before += outp[k] < out_m ? static_cast<uint32_t>(w.c[k]) : 0u;
-  const uint32_t d = wave_sum_u32(before) + (s - src_m);
-  if (w.flags == 0 && d < static_cast<uint32_t>(p.A))
-    __builtin_nontemporal_store(v, reinterpret_cast<T*>(p.out_tokens + int64_t(d) * p.row_bytes + col));
+  const int m0 = cell_of(s0, w);
+  const uint32_t d0 = dest_row(s0, m0, w, rc.pos, outp);
+  const uint32_t b = (s0 + 1) * f.vpr;  // the first vector of row s0 + 1 (<= A * vpr)
+  uint32_t d1 = d0 + 1;
+  if (b < n0 + 64u && s0 + 1 < static_cast<uint32_t>(p.A)) {  // uniform: the chunk reaches row s0 + 1
+    const int m1 = cell_of(s0 + 1, w);
+    if (m1 != m0) d1 = dest_row(s0 + 1, m1, w, rc.pos, outp);  // uniform
+  }
+  const bool second = v >= b;
+  const uint32_t d = second ? d1 : d0;
+  const uint32_t col = v - (second ? s0 + 1 : s0) * f.vpr;  // the vector within its row
+  if (w.flags == 0 && in && d < static_cast<uint32_t>(p.A))
+    __builtin_nontemporal_store(x, reinterpret_cast<T*>(p.out_tokens + int64_t(d) * p.row_bytes + int64_t(col) * 16));
 }
 
 // The scale rows of output rows [d0, d0 + rows), taken from input row
@@ -545,7 +567,7 @@ __global__ __launch_bounds__(64) void stream_fused_kernel(GatherArgs p, StreamFu
   // The scalars a token wave needs before its loads, fetched together with the
   // first kernel arguments (the compiler would fetch them one after the
   // other inside the branch, each a scalar-cache round trip).
-  asm volatile("" ::"s"(p.tokens), "s"(f.counts), "s"(f.cpr), "s"(f.cpr_magic), "s"(p.row_bytes), "s"(p.M));
+  asm volatile("" ::"s"(p.tokens), "s"(f.counts), "s"(f.vpr), "s"(f.vpr_magic), "s"(f.vectors), "s"(p.M));
   if (b < f.item_waves) {  // uniform
     stream_fused_items<kScatter, kWeight, CountT, kVec, kInv>(p, f, b, s_lds);
     return;
@@ -599,8 +621,9 @@ mrr_status launch_stream_fused(const Plan& pl, const mrr_args* a, void* ws, hipS
   f.etn = a->expert_token_num;
   f.cumsum = pl.cumsum ? 1 : 0;
   f.item_waves = static_cast<int32_t>(pl.sf_item_waves);
-  f.cpr = static_cast<uint32_t>(pl.row_bytes / 1024);
-  f.cpr_magic = f.cpr == 1 ? 0u : static_cast<uint32_t>(((uint64_t(1) << 32) + f.cpr - 1) / f.cpr);
+  f.vpr = static_cast<uint32_t>(pl.row_bytes / 16);  // >= 64
+  f.vpr_magic = static_cast<uint32_t>(((uint64_t(1) << 32) + f.vpr - 1) / f.vpr);
+  f.vectors = static_cast<uint32_t>(pl.A * f.vpr);   // < 2^32 (the plan checks)
   f.minor = static_cast<int32_t>(pl.inverse ? pl.N : pl.E);
   f.major = static_cast<int32_t>(pl.inverse ? pl.E : pl.N);
   f.inv_minor = 1.0f / static_cast<float>(f.minor);

@@ -102,8 +102,9 @@ constexpr int64_t kFusedMaxTokenBytesFewCells = int64_t(28) << 20;
 constexpr int64_t kFusedMaxByteRowBytes = int64_t(4) << 20;
 
 // The one-launch stream kernel (count matrices of at most 256 cells, token
-// rows of whole 1 KiB chunks): its item waves move 64 scale rows each, so
-// scale rows are limited to this many bytes (larger ones take two kernels).
+// rows of 16-byte vectors and at least 1 KiB): its item waves move 64 scale
+// rows each, so scale rows are limited to this many bytes (larger ones take
+// two kernels).
 constexpr int kStreamFusedMaxCells = 256;
 constexpr int64_t kStreamFusedMaxScaleRow = 4096;
 
@@ -149,10 +150,10 @@ struct Plan {
   bool inverse;             // direction == MRR_INVERSE: the table in row-major cell order
   bool fused;               // moe_rerouting_v2 runs the single fused kernel
   bool stream_fused;        // moe_rerouting_v2 runs the one-launch stream kernel instead (64-lane
-                            // workgroups: item waves of 64 output rows, then one 1 KiB token
-                            // chunk of one input row each)
+                            // workgroups: item waves of 64 output rows, then one 1 KiB chunk of
+                            // the input token rows each)
   int64_t sf_item_waves;    // its item waves: ceil(A / 64)
-  int64_t sf_grid;          // its workgroups: item waves + A * R / 1024
+  int64_t sf_grid;          // its workgroups: item waves + ceil(A * R / 1024)
   int rows_per_wg;
   int64_t grid;             // gather workgroups
   bool stream;              // the gather kernel is the stream kernel: 64-lane workgroups, one chunk of

@@ -290,17 +290,18 @@ mrr_status make_plan(const mrr_args* a, const void* ws, size_t ws_bytes, Plan* p
   if (q.fused && q.grid > max_launch_grid(kGatherThreads)) q.fused = false;
   // The one-launch stream kernel runs in place of both the fused kernel and
   // the two kernels whenever its shape fits: at most 256 cells, token rows of
-  // whole 1 KiB chunks (16-byte vectors), scale rows of at most 4 KiB,
-  // A < 2^30 (its exact-sum check), and one launch of at most 2^31
-  // workgroups. (16x16 counts with 7168-byte rows, whole call: 1.8 MiB 4.7
+  // 16-byte vectors (both buffers aligned) and at least 1 KiB, scale rows of
+  // at most 4 KiB, A < 2^30 (its exact-sum check), fewer than 2^32 token
+  // vectors in all, and one launch of at most 2^31 workgroups. (16x16 counts with 7168-byte rows, whole call: 1.8 MiB 4.7
   // against 5.7 us for the fused kernel, 27 MiB 11.2 against 14.1, 46 MiB
   // 17.6 against 21.4; at 112 MiB 37 against 41 us for the two kernels.)
   q.stream_fused = false;
   q.sf_item_waves = q.sf_grid = 0;
-  if (tuning().stream_fused && q.A > 0 && M <= kStreamFusedMaxCells && q.token_vec == 16 &&
-      q.row_bytes % 1024 == 0 && q.scale_row_bytes <= kStreamFusedMaxScaleRow && q.A < (int64_t(1) << 30)) {
+  if (tuning().stream_fused && q.A > 0 && M <= kStreamFusedMaxCells && q.token_vec == 16 && q.row_bytes >= 1024 &&
+      q.scale_row_bytes <= kStreamFusedMaxScaleRow && q.A < (int64_t(1) << 30) &&
+      q.A * (q.row_bytes / 16) < (int64_t(1) << 32)) {
     const int64_t waves = (q.A + 63) / 64;
-    const int64_t grid = waves + q.A * (q.row_bytes / 1024);
+    const int64_t grid = waves + (q.A * (q.row_bytes / 16) + 63) / 64;
     if (grid < kMaxStreamGrid && grid <= max_launch_grid(64)) {
       q.stream_fused = true;
       q.fused = false;

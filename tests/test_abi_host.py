@@ -199,13 +199,17 @@ def test_describe_plan():
     # a smaller call with the same counts: the same one-launch kernel, whatever the size
     st, info = describe(valid_args(A=2048, H=7168, N=16, E=16, tok=_lib.I8))
     assert st == _lib.SUCCESS and info.fused == 2 and info.one_launch_workgroups == 2048 // 64 + 2048 * 7
-    # rows that are no whole number of KiB (7184 bytes): one kernel of 256-thread workgroups that each
-    # recompute the offsets of the (small) count matrix
+    # rows of 16-byte vectors that are no whole number of KiB (7184 bytes): the same kernel, its 1 KiB
+    # chunks of the input rows taken as one stream (a chunk may reach into the next row)
     st, info = describe(valid_args(A=2048, H=7184, N=16, E=16, tok=_lib.I8))
+    assert st == _lib.SUCCESS and info.fused == 2 and info.one_launch_workgroups == 2048 // 64 + 2048 * 449 // 64
+    # rows under 1 KiB (1008 bytes): one kernel of 256-thread workgroups that each recompute the offsets of
+    # the (small) count matrix
+    st, info = describe(valid_args(A=2048, H=1008, N=16, E=16, tok=_lib.I8))
     assert st == _lib.SUCCESS and info.fused == 1 and info.threads_per_workgroup == 256
     assert info.one_launch_workgroups == info.gather_workgroups
     assert info.scale_inline_bytes == 4            # one 4-byte piece per row, loaded with the tokens
-    rows = max(1, info.threads_per_workgroup * 8 // 449)
+    rows = max(1, info.threads_per_workgroup * 8 // 63)
     assert info.rows_per_workgroup == min(rows, 256)
     assert info.gather_workgroups == -(-2048 // info.rows_per_workgroup)
     # 256x64 counts are too many to recompute per workgroup: two kernels
@@ -267,18 +271,23 @@ def test_plan_size_classes():
             st, info = describe(valid_args(A=a_rows, H=7168, N=n, E=e, tok=_lib.I8))
             assert st == _lib.SUCCESS and info.fused == 2, (n, e, a_rows)
             assert info.one_launch_workgroups == -(-a_rows // 64) + a_rows * 7
-    # rows of 7184 bytes (16-byte vectors, no whole KiB): the fused kernel up to 28 MiB of token
-    # rows with at most 64 cells, 48 MiB with at most 256, else offsets + gather
-    below28, above28, above48 = 28 * mib // 7184 - 1, 28 * mib // 7184 + 1, 48 * mib // 7184 + 1
+    # the same for rows of 16-byte vectors that are no whole number of KiB (7184 bytes: 449 vectors)
+    for a_rows in (1, 100, 48 * mib // 7184 + 1):
+        st, info = describe(valid_args(A=a_rows, H=7184, N=16, E=16, tok=_lib.I8))
+        assert st == _lib.SUCCESS and info.fused == 2, a_rows
+        assert info.one_launch_workgroups == -(-a_rows // 64) + -(-a_rows * 449 // 64)
+    # rows under 1 KiB (1008 bytes): the fused kernel up to 28 MiB of token rows with at most 64 cells,
+    # 48 MiB with at most 256, else offsets + gather
+    below28, above28, above48 = 28 * mib // 1008 - 1, 28 * mib // 1008 + 1, 48 * mib // 1008 + 1
     for n, e in [(8, 8), (4, 4), (1, 64)]:
-        st, info = describe(valid_args(A=below28, H=7184, N=n, E=e, tok=_lib.I8))
+        st, info = describe(valid_args(A=below28, H=1008, N=n, E=e, tok=_lib.I8))
         assert st == _lib.SUCCESS and info.fused == 1, (n, e)
-        st, info = describe(valid_args(A=above28, H=7184, N=n, E=e, tok=_lib.I8))
+        st, info = describe(valid_args(A=above28, H=1008, N=n, E=e, tok=_lib.I8))
         assert st == _lib.SUCCESS and info.fused == 0 and info.gather_kernel == 1, (n, e)
         assert info.one_launch_workgroups == 0 and info.offsets_workgroups == -(-above28 // 256)
-    st, info = describe(valid_args(A=above28, H=7184, N=16, E=16, tok=_lib.I8))
+    st, info = describe(valid_args(A=above28, H=1008, N=16, E=16, tok=_lib.I8))
     assert st == _lib.SUCCESS and info.fused == 1
-    st, info = describe(valid_args(A=above48, H=7184, N=16, E=16, tok=_lib.I8))
+    st, info = describe(valid_args(A=above48, H=1008, N=16, E=16, tok=_lib.I8))
     assert st == _lib.SUCCESS and info.fused == 0 and info.offsets_workgroups == -(-above48 // 256)
     # whole-KiB rows but not the one-launch kernel's other limits (above 48 MiB: offsets + gather)
     above48 = 48 * mib // 7168 + 1

@@ -1,13 +1,15 @@
 """Parity of the one-launch stream kernel with the CPU oracle, byte for byte.
 
 moe_rerouting_v2 takes that kernel for count matrices of at most 256 cells,
-token rows of whole KiB and scale rows of at most 4 KiB, once the call is
-large enough (every case below first checks, through the plan, that it does):
-item waves of 64 output rows, then one wave per KiB of an input row, each
-wave computing the offsets it needs from the counts. Cases cover both
-directions, int32 and int64 counts, empty cells, one rank or one expert,
-count matrices of 35 and 64 cells, both index forms and expert_token_num
-modes, weights, and scale rows of 4 bytes, 12 bytes, e8m0 and 4000 bytes.
+token rows of 16-byte vectors and at least 1 KiB, and scale rows of at most
+4 KiB, at any size (every case below first checks, through the plan, that it
+does): item waves of 64 output rows, then one wave per KiB of the input token
+rows, each wave computing the offsets it needs from the counts. Cases cover
+both directions, int32 and int64 counts, empty cells, one rank or one expert,
+count matrices of 8, 35, 64 and 256 cells, both index forms and
+expert_token_num modes, weights, scale rows of 4 bytes, 12 bytes, e8m0 and
+4000 bytes, and rows that are no whole number of KiB (a wave's KiB then
+reaches into the next row, often of another cell).
 Rejected counts (negative, a wrong sum, a count above INT32_MAX, int32
 counts whose sum wraps to A modulo 2^32) leave every output untouched."""
 import numpy as np
@@ -26,7 +28,7 @@ DIR_IDS = ["forward", "inverse"]
 def sized_case(seed, n, e, h, tokens_dtype, target_mib=56, zero_cells=False, **kw):
     """A random case whose token rows total about target_mib MiB."""
     bits = workloads.TOKEN_DTYPES[tokens_dtype][0]
-    rows = target_mib * MIB // (h * bits // 8)
+    rows = int(target_mib * MIB) // (h * bits // 8)
     mean = max(1, rows // (n * e))
     lo = 0 if zero_cells else mean // 2
     return workloads.random_case(seed, n, e, h, tokens_dtype=tokens_dtype, count_range=(lo, 2 * mean - lo + 1),
@@ -57,6 +59,17 @@ CASES = {
     "4x4_int8_as1000": dict(seed=509, n=4, e=4, h=3072, tokens_dtype="int8", scales="as", S=1000, idx_type=1),
     "16x13_bf16_e8m0_i64": dict(seed=510, n=16, e=13, h=1536, tokens_dtype="bfloat16", scales="e8m0",
                                 counts_dtype=np.int64, etn_type=0),
+    # rows that are no whole number of KiB
+    "16x16_fp8_3584_a": dict(seed=520, n=16, e=16, h=3584, tokens_dtype="float8_e4m3fn", scales="a", target_mib=16),
+    "16x16_int8_1040_small_cells": dict(seed=521, n=16, e=16, h=1040, tokens_dtype="int8", zero_cells=True,
+                                        weight=True, target_mib=1),
+    "8x32_fp8_2880_i64_w_scatter": dict(seed=522, n=8, e=32, h=2880, tokens_dtype="float8_e5m2",
+                                        counts_dtype=np.int64, weight=True, idx_type=1, scales="e8m0",
+                                        target_mib=24),
+    "4x60_bf16_1440_as5_cumsum": dict(seed=523, n=4, e=60, h=720, tokens_dtype="bfloat16", scales="as", S=5,
+                                      etn_type=0, target_mib=12),
+    "2x4_int8_1040_tiny": dict(seed=524, n=2, e=4, h=1040, tokens_dtype="int8", scales="a", target_mib=0.04),
+    "1x1_f16_1040": dict(seed=525, n=1, e=1, h=520, tokens_dtype="float16", weight=True, target_mib=2),
 }
 
 
