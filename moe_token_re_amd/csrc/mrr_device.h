@@ -108,7 +108,10 @@ struct StreamFusedArgs {
   const void* counts;
   void* etn;
   int32_t cumsum;
-  int32_t item_waves;  // workgroups [0, item_waves) move the per-row items, 64 output rows each
+  int32_t item_waves;  // workgroups [0, item_waves) move the per-row items, 64 rpl output rows each
+  int32_t rpl;         // output rows per lane of an item wave: 4, or 1 for scale rows over 16 bytes
+  int32_t idx16;       // permute_token_idx is 16-byte aligned (four rows' indices in one store)
+  int32_t w16;         // permute_topk_weight is 16-byte aligned (the same for the weights)
   uint32_t vpr;        // 16-byte vectors per token row (at least 64)
   uint32_t vpr_magic;  // ceil(2^32 / vpr): n / vpr by a multiply-high and one correction (n < 2^32)
   uint32_t vectors;    // A * vpr: the token vectors of the call

@@ -191,6 +191,7 @@ __global__ __launch_bounds__(kGatherThreads) void fused_kernel(GatherArgs p, Fus
 // ---------------------------------------------------------------------------
 
 constexpr int kCellsPerLane = 4;  // 64 lanes x 4 = 256 cells
+constexpr int kItemWaveRows = 4 * 64;  // the most output rows of an item wave (four per lane)
 constexpr int kScaleRound = 4;    // scale vectors per lane loaded before they are stored
 
 // The raw counts of this lane's cells m = 4 lane + k in input order (forward:
@@ -425,12 +426,12 @@ __device__ __forceinline__ void stream_fused_tokens(const GatherArgs& p, const S
     __builtin_nontemporal_store(x, reinterpret_cast<T*>(p.out_tokens + int64_t(d) * p.row_bytes + int64_t(col) * 16));
 }
 
-// The scale rows of output rows [d0, d0 + rows), taken from input row
-// `src` of lane r for output row d0 + r; kScaleRound vectors per lane are
-// loaded before they are stored.
+// The scale rows of output rows [d0, d0 + rows), output row d0 + r taken
+// from input row s_src[r] (LDS); kScaleRound vectors per lane are loaded
+// before they are stored.
 template <int SV>
 __device__ __forceinline__ void stream_fused_scales(const GatherArgs& p, const StreamFusedArgs& f, int d0, int rows,
-                                                    int32_t src) {
+                                                    const uint32_t* s_src) {
   using T = typename VecT<SV>::type;
   const int lane = threadIdx.x & 63;
   const int spr = p.scale_vecs_per_row;
@@ -446,9 +447,8 @@ __device__ __forceinline__ void stream_fused_scales(const GatherArgs& p, const S
       in[k] = e < total;
       const int r = in[k] ? div_small(e, f.inv_spr) : 0;
       const int cv = e - r * spr;
-      const int32_t sr = __shfl(src, r);  // every lane takes part
       v[k] = __builtin_nontemporal_load(
-          reinterpret_cast<const T*>(p.scales + (in[k] ? int64_t(sr) * Rs + int64_t(cv) * SV : 0)));
+          reinterpret_cast<const T*>(p.scales + (in[k] ? int64_t(s_src[r]) * Rs + int64_t(cv) * SV : 0)));
       to[k] = int64_t(d0 + r) * Rs + int64_t(cv) * SV;
     }
 #pragma unroll
@@ -457,16 +457,41 @@ __device__ __forceinline__ void stream_fused_scales(const GatherArgs& p, const S
   }
 }
 
-// Item wave iw: output rows [64 iw, 64 iw + 64). The offsets in output order
-// come from one exchange of the counts through LDS; each row finds its cell by
-// a mark at every cell start within the 64 rows and a running maximum.
+// Four 4-byte words of four adjacent rows: one 16-byte store when all four are
+// live and the address is 16-byte aligned, else a store per live word.
+__device__ __forceinline__ void store_word_quad(uint32_t* dst, const uint32_t (&v)[4], const bool (&live)[4],
+                                               bool aligned16) {
+  using U4 = uint32_t __attribute__((ext_vector_type(4)));
+  if (aligned16 && live[0] && live[1] && live[2] && live[3]) {
+    U4 q;
+    q.x = v[0];
+    q.y = v[1];
+    q.z = v[2];
+    q.w = v[3];
+    *reinterpret_cast<U4*>(dst) = q;
+  } else {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (live[r]) dst[r] = v[r];
+  }
+}
+
+// Item wave iw: output rows [64 rpl iw, 64 rpl (iw + 1)), rpl = f.rpl rows a
+// lane (lane l: rows 64 rpl iw + rpl l + r, r < rpl). The offsets in output
+// order come from one exchange of the counts through LDS; each row finds its
+// cell by a mark at every cell start within the wave's rows and a running
+// maximum (within the lane's rows, then over the lanes). Four rows a lane
+// where the scale rows are small: a quarter of the item waves (at pages_shape,
+// 256 item waves at the head of the grid cost ~1 us per call, 128 ~0.1); one
+// where they are larger, so that more waves carry the scale traffic.
 template <bool kScatter, bool kWeight, typename CountT, bool kVec, bool kInv>
 __device__ __forceinline__ void stream_fused_items(const GatherArgs& p, const StreamFusedArgs& f, int iw,
                                                    uint32_t* s_lds) {
-  uint32_t* s_cnt = s_lds;                                 // by output position: the count,
+  uint32_t* s_cnt = s_lds;                                 // by output position: the count (later the
+                                                           // rows' source rows),
   uint32_t* s_in = s_lds + kCellsPerLane * 64;             // the input offset,
-  uint32_t* s_out = s_lds + 2 * kCellsPerLane * 64;        // the output offset
-  int32_t* s_mark = reinterpret_cast<int32_t*>(s_lds + 3 * kCellsPerLane * 64);  // [64]
+  uint32_t* s_out = s_lds + 2 * kCellsPerLane * 64;        // the output offset;
+  int32_t* s_mark = reinterpret_cast<int32_t*>(s_lds + 3 * kCellsPerLane * 64);  // row marks [256]
   const int lane = threadIdx.x & 63;
   const int M = p.M, A = p.A;
   RawCells<CountT> rc;
@@ -476,8 +501,11 @@ __device__ __forceinline__ void stream_fused_items(const GatherArgs& p, const St
   finish_cells<CountT, true>(rc, A, w);
   uint32_t outp[kCellsPerLane];
   cell_positions(rc.pos, outp);
-  const int d0 = iw * 64;
-  s_mark[lane] = -1;
+  const int rpl = f.rpl;  // 1 or 4
+  const int rows_w = 64 * rpl;
+  const int d0 = iw * rows_w;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) s_mark[4 * lane + r] = -1;
 #pragma unroll
   for (int k = 0; k < kCellsPerLane; ++k)
     if (kCellsPerLane * lane + k < M) {
@@ -496,40 +524,65 @@ __device__ __forceinline__ void stream_fused_items(const GatherArgs& p, const St
 #pragma unroll
   for (int k = 1; k < kCellsPerLane; ++k) ostart[k] = ostart[k - 1] + co[k - 1];
   // the cell holding row d0 (the last one starting at or before it) marks the
-  // first row; every later cell starting within the 64 rows marks its start
+  // first row; every later cell starting within the 256 rows marks its start
   int u0 = -1;
 #pragma unroll
   for (int k = 0; k < kCellsPerLane; ++k) {
     const int u = kCellsPerLane * lane + k;
     if (u < M) {
       s_out[u] = ostart[k];
-      if (co[k] > 0 && ostart[k] > static_cast<uint32_t>(d0) && ostart[k] < static_cast<uint32_t>(d0 + 64))
+      if (co[k] > 0 && ostart[k] > static_cast<uint32_t>(d0) && ostart[k] < static_cast<uint32_t>(d0 + rows_w))
         s_mark[ostart[k] - d0] = u;
     }
     u0 += __popcll(__ballot(u < M && ostart[k] <= static_cast<uint32_t>(d0)));
   }
   if (lane == 0) s_mark[0] = u0;
   __syncthreads();
-  const int u = max(wave_max_scan(s_mark[lane]), 0);  // -1 only for rejected counts
-  const int d = d0 + lane;
+  // running maximum: within the lane's four rows, then the lanes before it
+  int cell[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) cell[r] = r < rpl ? s_mark[rpl * lane + r] : -1;
+#pragma unroll
+  for (int r = 1; r < 4; ++r) cell[r] = max(cell[r], cell[r - 1]);
+  const int before = __shfl_up(wave_max_scan(cell[3]), 1);  // the lanes before this one
   const bool valid = w.flags == 0;
-  const bool live = valid && d < A;
-  const int32_t src = live ? static_cast<int32_t>(s_in[u] + (static_cast<uint32_t>(d) - s_out[u])) : 0;
-  if (live) {
-    if (kScatter)
-      p.idx[src] = d;
-    else
-      p.idx[d] = src;
-    if (kWeight) p.out_weight[d] = p.weight[src];
+  uint32_t src[4], dv[4];
+  bool live[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int u = max(lane == 0 ? cell[r] : max(cell[r], before), 0);  // -1 only for rejected counts
+    const int d = d0 + rpl * lane + r;
+    live[r] = valid && r < rpl && d < A;
+    dv[r] = static_cast<uint32_t>(d);
+    src[r] = live[r] ? s_in[u] + (static_cast<uint32_t>(d) - s_out[u]) : 0u;
+  }
+  if (kScatter) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (live[r]) p.idx[src[r]] = static_cast<int32_t>(dv[r]);
+  } else {
+    store_word_quad(reinterpret_cast<uint32_t*>(p.idx) + d0 + rpl * lane, src, live, rpl == 4 && f.idx16 != 0);
+  }
+  if (kWeight) {
+    uint32_t wv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) wv[r] = p.weight[src[r]];  // src is 0 when not live
+    store_word_quad(p.out_weight + d0 + rpl * lane, wv, live, rpl == 4 && f.w16 != 0);
   }
   if (valid && p.scale_row_bytes > 0) {  // uniform
-    const int rows = min(64, A - d0);
+    // the rows' source rows to LDS (over the counts, no longer read), for the
+    // scale vectors' lanes
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      if (r < rpl) s_cnt[rpl * lane + r] = src[r];
+    __builtin_amdgcn_wave_barrier();
+    const int rows = min(rows_w, A - d0);
     switch (p.scale_vec) {
-      case 16: stream_fused_scales<16>(p, f, d0, rows, src); break;
-      case 8: stream_fused_scales<8>(p, f, d0, rows, src); break;
-      case 4: stream_fused_scales<4>(p, f, d0, rows, src); break;
-      case 2: stream_fused_scales<2>(p, f, d0, rows, src); break;
-      default: stream_fused_scales<1>(p, f, d0, rows, src); break;
+      case 16: stream_fused_scales<16>(p, f, d0, rows, s_cnt); break;
+      case 8: stream_fused_scales<8>(p, f, d0, rows, s_cnt); break;
+      case 4: stream_fused_scales<4>(p, f, d0, rows, s_cnt); break;
+      case 2: stream_fused_scales<2>(p, f, d0, rows, s_cnt); break;
+      default: stream_fused_scales<1>(p, f, d0, rows, s_cnt); break;
     }
   }
   if (iw == 0) {
@@ -556,9 +609,9 @@ __device__ __forceinline__ void stream_fused_items(const GatherArgs& p, const St
   }
 }
 
-// LDS of a workgroup: the item waves' three tables of 256 cells and 64 row
+// LDS of a workgroup: the item waves' three tables of 256 cells and 256 row
 // marks; the token waves use its first 256 counts (inverse, kVec).
-constexpr int kStreamFusedLdsWords = 3 * kCellsPerLane * 64 + 64;
+constexpr int kStreamFusedLdsWords = 3 * kCellsPerLane * 64 + kItemWaveRows;
 
 template <bool kScatter, bool kWeight, typename CountT, bool kVec, bool kInv>
 __global__ __launch_bounds__(64) void stream_fused_kernel(GatherArgs p, StreamFusedArgs f) {
@@ -621,6 +674,9 @@ mrr_status launch_stream_fused(const Plan& pl, const mrr_args* a, void* ws, hipS
   f.etn = a->expert_token_num;
   f.cumsum = pl.cumsum ? 1 : 0;
   f.item_waves = static_cast<int32_t>(pl.sf_item_waves);
+  f.rpl = pl.sf_rows_per_lane;
+  f.idx16 = reinterpret_cast<uintptr_t>(g.idx) % 16 == 0 ? 1 : 0;
+  f.w16 = reinterpret_cast<uintptr_t>(g.out_weight) % 16 == 0 ? 1 : 0;
   f.vpr = static_cast<uint32_t>(pl.row_bytes / 16);  // >= 64
   f.vpr_magic = static_cast<uint32_t>(((uint64_t(1) << 32) + f.vpr - 1) / f.vpr);
   f.vectors = static_cast<uint32_t>(pl.A * f.vpr);   // < 2^32 (the plan checks)

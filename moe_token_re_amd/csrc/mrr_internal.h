@@ -150,9 +150,10 @@ struct Plan {
   bool inverse;             // direction == MRR_INVERSE: the table in row-major cell order
   bool fused;               // moe_rerouting_v2 runs the single fused kernel
   bool stream_fused;        // moe_rerouting_v2 runs the one-launch stream kernel instead (64-lane
-                            // workgroups: item waves of 64 output rows, then one 1 KiB chunk of
+                            // workgroups: item waves of 256 (or 64) output rows, then one 1 KiB chunk of
                             // the input token rows each)
-  int64_t sf_item_waves;    // its item waves: ceil(A / 64)
+  int64_t sf_item_waves;    // its item waves: ceil(A / (64 sf_rows_per_lane))
+  int sf_rows_per_lane;     // output rows per lane of an item wave: 4, or 1 for scale rows over 16 bytes
   int64_t sf_grid;          // its workgroups: item waves + ceil(A * R / 1024)
   int rows_per_wg;
   int64_t grid;             // gather workgroups

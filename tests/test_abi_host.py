@@ -185,10 +185,10 @@ def describe(a, ws=BASE["ws"]):
 
 def test_describe_plan():
     # pages' shape: 7168-byte rows in 16-byte vectors; 112 MiB of token rows take the one-launch
-    # stream kernel: 64-lane workgroups, 16384 / 64 item waves, then one per KiB of an input row
+    # stream kernel: 64-lane workgroups, 16384 / 256 item waves, then one per KiB of the input rows
     st, info = describe(valid_args(A=16384, H=7168, N=16, E=16, tok=_lib.I8))
     assert st == _lib.SUCCESS
-    assert info.fused == 2 and info.one_launch_workgroups == 16384 // 64 + 16384 * 7
+    assert info.fused == 2 and info.one_launch_workgroups == 16384 // 256 + 16384 * 7
     # the two phases: the offsets kernel, then the stream gather over 64-vector chunks of the
     # token rows (16384 * 448 / 64) and chunks of 256 rows' items (index, and the 4-byte scale
     # rows with them)
@@ -198,11 +198,11 @@ def test_describe_plan():
     assert info.offsets_workgroups == 64           # the row map: one workgroup per 256 rows (<= 256 cells)
     # a smaller call with the same counts: the same one-launch kernel, whatever the size
     st, info = describe(valid_args(A=2048, H=7168, N=16, E=16, tok=_lib.I8))
-    assert st == _lib.SUCCESS and info.fused == 2 and info.one_launch_workgroups == 2048 // 64 + 2048 * 7
+    assert st == _lib.SUCCESS and info.fused == 2 and info.one_launch_workgroups == 2048 // 256 + 2048 * 7
     # rows of 16-byte vectors that are no whole number of KiB (7184 bytes): the same kernel, its 1 KiB
     # chunks of the input rows taken as one stream (a chunk may reach into the next row)
     st, info = describe(valid_args(A=2048, H=7184, N=16, E=16, tok=_lib.I8))
-    assert st == _lib.SUCCESS and info.fused == 2 and info.one_launch_workgroups == 2048 // 64 + 2048 * 449 // 64
+    assert st == _lib.SUCCESS and info.fused == 2 and info.one_launch_workgroups == 2048 // 256 + 2048 * 449 // 64
     # rows under 1 KiB (1008 bytes): one kernel of 256-thread workgroups that each recompute the offsets of
     # the (small) count matrix
     st, info = describe(valid_args(A=2048, H=1008, N=16, E=16, tok=_lib.I8))
@@ -270,12 +270,12 @@ def test_plan_size_classes():
         for a_rows in (1, 100, 48 * mib // 7168 + 1):
             st, info = describe(valid_args(A=a_rows, H=7168, N=n, E=e, tok=_lib.I8))
             assert st == _lib.SUCCESS and info.fused == 2, (n, e, a_rows)
-            assert info.one_launch_workgroups == -(-a_rows // 64) + a_rows * 7
+            assert info.one_launch_workgroups == -(-a_rows // 256) + a_rows * 7
     # the same for rows of 16-byte vectors that are no whole number of KiB (7184 bytes: 449 vectors)
     for a_rows in (1, 100, 48 * mib // 7184 + 1):
         st, info = describe(valid_args(A=a_rows, H=7184, N=16, E=16, tok=_lib.I8))
         assert st == _lib.SUCCESS and info.fused == 2, a_rows
-        assert info.one_launch_workgroups == -(-a_rows // 64) + -(-a_rows * 449 // 64)
+        assert info.one_launch_workgroups == -(-a_rows // 256) + -(-a_rows * 449 // 64)
     # rows under 1 KiB (1008 bytes): the fused kernel up to 28 MiB of token rows with at most 64 cells,
     # 48 MiB with at most 256, else offsets + gather
     below28, above28, above48 = 28 * mib // 1008 - 1, 28 * mib // 1008 + 1, 48 * mib // 1008 + 1
@@ -298,6 +298,8 @@ def test_plan_size_classes():
     a.scales_dims[1] = 1024                                                        # 4096 bytes: one launch
     st, info = describe(a)
     assert st == _lib.SUCCESS and info.fused == 2
+    # scale rows over 16 bytes: item waves of 64 output rows instead of 256
+    assert info.one_launch_workgroups == -(-above48 // 64) + above48 * 7
     st, info = describe(valid_args(A=above48, H=7168, N=1, E=257, tok=_lib.I8))   # 257 cells
     assert st == _lib.SUCCESS and info.fused == 0
     # 257..512 cells: offsets + gather, the offsets in 512-thread workgroups of 512 rows
