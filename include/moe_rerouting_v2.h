@@ -177,7 +177,7 @@ typedef struct mrr_plan_info {
   int32_t fused;                 /* what moe_rerouting_v2 launches: 1 = one kernel whose workgroups
                                     each recompute the offsets of the (small) count matrix in LDS
                                     or registers (small calls); 2 = one kernel of 64-lane
-                                    workgroups (count matrices of at most 256 cells, token rows of
+                                    workgroups (count matrices of at most 512 cells, token rows of
                                     16-byte vectors and at least 1 KiB): item waves of 256 output
                                     rows (64 with scale rows over 16 bytes), then one wave per
                                     1 KiB of the input token rows, each

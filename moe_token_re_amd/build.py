@@ -1,8 +1,9 @@
 """Builds the HIP library libmoe_rerouting_v2.so in-tree, for gfx950.
 
 The host checks (mrr_validate.cpp) are compiled by g++ with no HIP header; the
-kernel files (mrr_offsets.hip, mrr_gather.hip, mrr_fused.hip) and the entry
-points (mrr_entry.hip) by hipcc, in parallel. Packed-fp32 instructions are
+kernel files (mrr_offsets.hip, mrr_gather.hip, mrr_fused.hip,
+mrr_one_launch.hip) and the entry points (mrr_entry.hip) by hipcc, in
+parallel. Packed-fp32 instructions are
 disabled for all device code.
 """
 from __future__ import annotations
@@ -54,7 +55,7 @@ def _run(cmd, verbose):
     subprocess.run(cmd, check=True)
 
 
-HIP_SOURCES = ("mrr_offsets.hip", "mrr_gather.hip", "mrr_fused.hip", "mrr_entry.hip")
+HIP_SOURCES = ("mrr_offsets.hip", "mrr_gather.hip", "mrr_fused.hip", "mrr_one_launch.hip", "mrr_entry.hip")
 
 
 def build_library(verbose: bool = False) -> str:

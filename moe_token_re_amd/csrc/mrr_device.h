@@ -22,6 +22,9 @@
 //                    chunk of 64 vectors of one output stream, row map) and the
 //                    row-workgroup gather (table search);
 //   mrr_fused.hip    the whole call in one launch for small count matrices;
+//   mrr_one_launch.hip  the whole call in one launch of one-wave workgroups
+//                    for count matrices of at most 512 cells and token rows
+//                    of 16-byte vectors from 1 KiB, at any size;
 //   mrr_entry.hip    the C entry points.
 // This header holds the workgroup and wave scans, the count checks and the
 // workspace header, the offsets of a count matrix in a workgroup's LDS (one
@@ -119,10 +122,12 @@ struct StreamFusedArgs {
   int32_t major;       // N forward, E inverse
   float inv_minor;     // 1 / minor
   float inv_spr;       // 1 / (scale vectors per row), when there are scales
-  // The output-order position of input-order cell m = 4 l + k (m < 256) in
-  // byte k of outpos[l]: it depends on N, E and the direction alone, so the
-  // host computes it once instead of every wave.
-  uint32_t outpos[64];
+  // The output-order position of each input-order cell: it depends on N, E
+  // and the direction alone, so the host computes it once instead of every
+  // wave. With 4 cells a lane (at most 256 cells), cell m = 4 l + k in byte k
+  // of outpos[l]; with 8 (at most 512), cell m = 8 l + k in bits
+  // [16 (k % 2), 16 (k % 2) + 16) of outpos[4 l + k / 2]. 0 past the matrix.
+  alignas(16) uint32_t outpos[256];
 };
 
 namespace {

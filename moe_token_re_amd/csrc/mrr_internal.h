@@ -101,11 +101,11 @@ constexpr int64_t kFusedMaxTokenBytesFewCells = int64_t(28) << 20;
 // the single kernel would move them in narrow vectors.
 constexpr int64_t kFusedMaxByteRowBytes = int64_t(4) << 20;
 
-// The one-launch stream kernel (count matrices of at most 256 cells, token
-// rows of 16-byte vectors and at least 1 KiB): its item waves move 64 scale
-// rows each, so scale rows are limited to this many bytes (larger ones take
-// two kernels).
-constexpr int kStreamFusedMaxCells = 256;
+// The one-launch stream kernel (count matrices of at most 512 cells, 4 or 8
+// a lane, token rows of 16-byte vectors and at least 1 KiB): its item waves
+// move 64 scale rows each, so scale rows are limited to this many bytes
+// (larger ones take two kernels).
+constexpr int kStreamFusedMaxCells = 512;
 constexpr int64_t kStreamFusedMaxScaleRow = 4096;
 
 // Offsets computed in one workgroup's LDS (the single-workgroup offsets
@@ -154,6 +154,7 @@ struct Plan {
                             // the input token rows each)
   int64_t sf_item_waves;    // its item waves: ceil(A / (64 sf_rows_per_lane))
   int sf_rows_per_lane;     // output rows per lane of an item wave: 4, or 1 for scale rows over 16 bytes
+  int sf_cells_per_lane;    // cells of the count matrix per lane: 4 (at most 256 cells) or 8 (at most 512)
   int64_t sf_grid;          // its workgroups: item waves + ceil(A * R / 1024)
   int rows_per_wg;
   int64_t grid;             // gather workgroups

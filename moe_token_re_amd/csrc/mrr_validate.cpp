@@ -289,7 +289,7 @@ mrr_status make_plan(const mrr_args* a, const void* ws, size_t ws_bytes, Plan* p
   // The single kernel is one launch: never more workgroups than a launch holds.
   if (q.fused && q.grid > max_launch_grid(kGatherThreads)) q.fused = false;
   // The one-launch stream kernel runs in place of both the fused kernel and
-  // the two kernels whenever its shape fits: at most 256 cells, token rows of
+  // the two kernels whenever its shape fits: at most 512 cells, token rows of
   // 16-byte vectors (both buffers aligned) and at least 1 KiB, scale rows of
   // at most 4 KiB, A < 2^30 (its exact-sum check), fewer than 2^32 token
   // vectors in all, and one launch of at most 2^31 workgroups. (16x16 counts with 7168-byte rows, whole call: 1.8 MiB 4.7
@@ -298,6 +298,7 @@ mrr_status make_plan(const mrr_args* a, const void* ws, size_t ws_bytes, Plan* p
   q.stream_fused = false;
   q.sf_item_waves = q.sf_grid = 0;
   q.sf_rows_per_lane = 1;
+  q.sf_cells_per_lane = M > 256 ? 8 : 4;
   if (tuning().stream_fused && q.A > 0 && M <= kStreamFusedMaxCells && q.token_vec == 16 && q.row_bytes >= 1024 &&
       q.scale_row_bytes <= kStreamFusedMaxScaleRow && q.A < (int64_t(1) << 30) &&
       q.A * (q.row_bytes / 16) < (int64_t(1) << 32)) {

@@ -300,10 +300,19 @@ def test_plan_size_classes():
     assert st == _lib.SUCCESS and info.fused == 2
     # scale rows over 16 bytes: item waves of 64 output rows instead of 256
     assert info.one_launch_workgroups == -(-above48 // 64) + above48 * 7
-    st, info = describe(valid_args(A=above48, H=7168, N=1, E=257, tok=_lib.I8))   # 257 cells
+    # 257..512 cells: the one-launch kernel too (eight cells a lane)
+    for n, e in [(1, 257), (16, 32), (24, 16), (512, 1), (16, 24)]:
+        for a_rows in (1, 3000, above48):
+            st, info = describe(valid_args(A=a_rows, H=7168, N=n, E=e, tok=_lib.I8))
+            assert st == _lib.SUCCESS and info.fused == 2, (n, e, a_rows)
+            assert info.one_launch_workgroups == -(-a_rows // 256) + a_rows * 7
+    st, info = describe(valid_args(A=above48, H=7168, N=1, E=513, tok=_lib.I8))   # 513 cells
     assert st == _lib.SUCCESS and info.fused == 0
-    # 257..512 cells: offsets + gather, the offsets in 512-thread workgroups of 512 rows
-    st, info = describe(valid_args(A=3000, H=7168, N=16, E=32, tok=_lib.I8))
+    # 257..512 cells outside the one-launch kernel's limits (4100-byte scale rows): offsets + gather,
+    # the offsets in 512-thread workgroups of 512 rows
+    a = valid_args(A=3000, H=7168, N=16, E=32, tok=_lib.I8)
+    a.scales_ndim, a.scales_dims[1] = 2, 1025
+    st, info = describe(a)
     assert st == _lib.SUCCESS and info.fused == 0 and info.offsets_workgroups == -(-3000 // 512)
     # 513..1024 cells: 1024-thread workgroups of 1024 rows
     st, info = describe(valid_args(A=3000, H=7168, N=32, E=32, tok=_lib.I8))

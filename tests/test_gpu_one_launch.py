@@ -1,15 +1,18 @@
 """Parity of the one-launch stream kernel with the CPU oracle, byte for byte.
 
-moe_rerouting_v2 takes that kernel for count matrices of at most 256 cells,
+moe_rerouting_v2 takes that kernel for count matrices of at most 512 cells,
 token rows of 16-byte vectors and at least 1 KiB, and scale rows of at most
 4 KiB, at any size (every case below first checks, through the plan, that it
-does): item waves of 64 output rows, then one wave per KiB of the input token
-rows, each wave computing the offsets it needs from the counts. Cases cover
-both directions, int32 and int64 counts, empty cells, one rank or one expert,
-count matrices of 8, 35, 64 and 256 cells, both index forms and
-expert_token_num modes, weights, scale rows of 4 bytes, 12 bytes, e8m0 and
-4000 bytes, and rows that are no whole number of KiB (a wave's KiB then
-reaches into the next row, often of another cell).
+does): item waves of 64 or 256 output rows, then one wave per KiB of the
+input token rows, each wave computing the offsets it needs from the counts.
+Cases cover both directions, int32 and int64 counts, empty cells, one rank or
+one expert, count matrices of 8, 35, 64 and 256 cells (four a lane) and of
+300, 323, 384 and 512 cells (eight a lane, among them counts in 16-byte
+groups that end half-way through a lane and matrices of no whole number of
+such groups), both index forms and expert_token_num modes, weights, scale
+rows of 4 bytes, 12 bytes, e8m0 and 4000 bytes, and rows that are no whole
+number of KiB (a wave's KiB then reaches into the next row, often of another
+cell).
 Rejected counts (negative, a wrong sum, a count above INT32_MAX, int32
 counts whose sum wraps to A modulo 2^32) leave every output untouched."""
 import numpy as np
@@ -70,6 +73,19 @@ CASES = {
                                       etn_type=0, target_mib=12),
     "2x4_int8_1040_tiny": dict(seed=524, n=2, e=4, h=1040, tokens_dtype="int8", scales="a", target_mib=0.04),
     "1x1_f16_1040": dict(seed=525, n=1, e=1, h=520, tokens_dtype="float16", weight=True, target_mib=2),
+    # 257..512 cells: eight a lane
+    "16x32_int8_a": dict(seed=530, n=16, e=32, h=7168, tokens_dtype="int8", scales="a"),
+    "24x16_bf16_i64_w_scatter_cumsum": dict(seed=531, n=24, e=16, h=2048, tokens_dtype="bfloat16",
+                                            counts_dtype=np.int64, weight=True, idx_type=1, etn_type=0),
+    "1x512_int8_w": dict(seed=532, n=1, e=512, h=1024, tokens_dtype="int8", weight=True, zero_cells=True),
+    "512x1_fp8_e8m0": dict(seed=533, n=512, e=1, h=4096, tokens_dtype="float8_e4m3fn", scales="e8m0"),
+    "17x19_f16_as3_zeros": dict(seed=534, n=17, e=19, h=512, tokens_dtype="float16", scales="as", S=3,
+                                zero_cells=True),
+    "20x15_int8_1040_w": dict(seed=535, n=20, e=15, h=1040, tokens_dtype="int8", weight=True, target_mib=8),
+    "16x32_fp4_as1000_i64_scatter": dict(seed=536, n=16, e=32, h=4096, tokens_dtype="float4_e2m1fn_x2",
+                                         scales="as", S=1000, counts_dtype=np.int64, idx_type=1),
+    "32x16_fp8_3584_w_cumsum": dict(seed=537, n=32, e=16, h=3584, tokens_dtype="float8_e5m2", weight=True,
+                                    etn_type=0, target_mib=20),
 }
 
 
@@ -84,9 +100,10 @@ def test_one_launch_parity(name, direction):
 
 
 @pytest.mark.parametrize("direction", DIRS, ids=DIR_IDS)
-def test_one_launch_equals_two_phases(direction):
+@pytest.mark.parametrize("ne", [(16, 16), (16, 32)], ids=["256_cells", "512_cells"])
+def test_one_launch_equals_two_phases(ne, direction):
     """The same call through the two phases (offsets kernel, stream gather)."""
-    w = sized_case(511, 16, 16, 1024, "int8", scales="e8m0", weight=True, idx_type=1)
+    w = sized_case(511, ne[0], ne[1], 1024, "int8", scales="e8m0", weight=True, idx_type=1)
     assert takes_one_launch(w, direction)
     whole, st1 = run_hip(w, _dev(), direction=direction)
     parts, st2 = run_hip(w, _dev(), phases=True, direction=direction)
@@ -96,10 +113,11 @@ def test_one_launch_equals_two_phases(direction):
 
 
 @pytest.mark.parametrize("direction", DIRS, ids=DIR_IDS)
+@pytest.mark.parametrize("ne", [(16, 16), (24, 16)], ids=["256_cells", "384_cells"])
 @pytest.mark.parametrize("kind", ["negative", "sum_low", "sum_high", "too_large", "wraps"])
-def test_one_launch_bad_counts_write_nothing(kind, direction):
+def test_one_launch_bad_counts_write_nothing(kind, ne, direction):
     rng = np.random.default_rng(77)
-    n, e, row = 16, 16, 1024
+    (n, e), row = ne, 1024
     counts = rng.integers(180, 220, (n, e)).astype(np.int64 if kind == "too_large" else np.int32)
     a = int(counts.sum())
     if kind == "negative":
