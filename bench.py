@@ -64,7 +64,8 @@ PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "stream_fused_pages_shape_count
 STATS_SUMMARY = os.path.join(ROOT, "profiles", "pages_shape_kernel_stats.md")
 # the other workloads the default run reports (name, direction)
 OTHER_WORKLOADS = (("tiny", "forward"), ("balanced_bf16", "forward"), ("mxfp8_skewed", "forward"),
-                   ("tiny_segments", "forward"), ("pages_shape", "inverse"), ("odd_rows", "forward"))
+                   ("tiny_segments", "forward"), ("pages_shape", "inverse"), ("odd_rows", "forward"),
+                   ("experts_384", "forward"))
 
 
 def kernel_source_hash() -> str:

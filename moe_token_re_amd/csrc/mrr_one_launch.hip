@@ -284,9 +284,10 @@ __device__ __forceinline__ void stream_fused_tokens(const GatherArgs& p, const S
   cell_positions<kC>(rc.pos, outp);
   const int m0 = cell_of<kC>(s0, w);
   const uint32_t d0 = dest_row<kC>(s0, m0, w, rc.pos, outp);
-  const uint32_t b = (s0 + 1) * f.vpr;  // the first vector of row s0 + 1 (<= A * vpr)
+  const uint32_t b = (s0 + 1) * f.vpr;  // the first vector of row s0 + 1 (<= A * vpr, > n0)
   uint32_t d1 = d0 + 1;
-  if (b < n0 + 64u && s0 + 1 < static_cast<uint32_t>(p.A)) {  // uniform: the chunk reaches row s0 + 1
+  // uniform: the chunk reaches row s0 + 1 (b - n0 does not wrap, n0 + 64 can at the last chunk)
+  if (b - n0 < 64u && s0 + 1 < static_cast<uint32_t>(p.A)) {
     const int m1 = cell_of<kC>(s0 + 1, w);
     if (m1 != m0) d1 = dest_row<kC>(s0 + 1, m1, w, rc.pos, outp);  // uniform
   }

@@ -17,8 +17,11 @@ The five named workloads follow the shapes of the pages' examples:
     weights, e8m0 scales [A, H/64, 2], top-k weights, scatter index;
   * "tiny_segments": N=256, E=64, A=65536, fp4 tokens packed two per byte
     (H=2048, 1024 bytes a row), [A, 32] fp32 scales, top-k weights.
-No public dataset is named by the pages; these synthetic draws stand in for
-the all-to-all output the operator would receive.
+Two more stand for shapes the examples leave out: "odd_rows" (H=79 f16
+rows, 158 bytes) and "experts_384" (a 384-cell count matrix, N=16 x E=24,
+A=16384 fp8 rows of 7168 bytes). No public dataset is named by the pages;
+these synthetic draws stand in for the all-to-all output the operator would
+receive.
 
 Token arrays hold raw bits: bf16 as uint16, fp8/hif8/fp4 as uint8, fp16 as
 float16, int8 as int8. Casts from float32 go through torch on the CPU
@@ -161,6 +164,21 @@ def tiny_segments(seed: int = 5) -> Workload:
                     weight, 1, 0)
 
 
+def experts_384(seed: int = 7) -> Workload:
+    """A count matrix of 384 cells, the size of a 384-expert model's expert
+    set spread over 16 ranks (N=16, E=24 local experts): A=16384 fp8-e4m3
+    tokens of H=7168, counts 1 + a uniform multinomial, [A] fp32 per-token
+    scales, top-k weights."""
+    rng = np.random.default_rng(seed)
+    n, e = 16, 24
+    a, h = 16384, 7168
+    counts = (1 + rng.multinomial(a - n * e, [1.0 / (n * e)] * (n * e))).reshape(n, e).astype(np.int32)
+    tokens = rng.integers(0, 256, (a, h), dtype=np.uint8)
+    scales = rng.standard_normal(a, dtype=np.float32)
+    weight = rng.random((a, 1), dtype=np.float32)
+    return Workload("experts_384", counts, tokens, "float8_e4m3fn", h, scales, "float32", weight, 1, 0)
+
+
 def odd_rows(seed: int = 6) -> Workload:
     """Rows that are no multiple of 4 bytes: H = 79 f16 (158 bytes, the odd H
     of the pages' graph-mode sample) over 262,144 tokens, balanced 16 x 16
@@ -181,6 +199,7 @@ CONFIGS = {
     "mxfp8_skewed": mxfp8_skewed,
     "tiny_segments": tiny_segments,
     "odd_rows": odd_rows,
+    "experts_384": experts_384,
 }
 
 

@@ -4,7 +4,7 @@ Algorithmic bytes are what the operator must read or write: token and scale
 rows read and written, the top-k weights read and written, permute_token_idx
 written, the count matrix read and expert_token_num written. The totals below
 are worked out by hand from the workload shapes (the pages' example shape and
-the four other named workloads), not from the code under test."""
+four other named workloads), not from the code under test."""
 import os
 import sys
 
@@ -23,10 +23,11 @@ SHAPES = {
     "balanced_bf16": (16384, 14336, 0, True, 8, 256, 16),   # bf16 rows, int64 counts, weights
     "mxfp8_skewed": (32768, 7168, 224, True, 4, 256, 8),     # fp8 rows, e8m0 [A,112,2] scales
     "tiny_segments": (65536, 1024, 128, True, 4, 16384, 64),  # packed fp4 rows, [A,32] f32 scales
+    "experts_384": (16384, 7168, 4, True, 4, 384, 24),       # fp8 rows, [A] f32 scales, weights
 }
 # the same totals written out as numbers
 TOTALS = {"pages_shape": 235_078_720, "balanced_bf16": 469_960_832, "mxfp8_skewed": 484_836_384,
-          "tiny_segments": 151_847_168}
+          "tiny_segments": 151_847_168, "experts_384": 235_210_336}
 
 
 def by_hand(name):
