@@ -2,11 +2,11 @@
 (no workspace argument: the library's static device scratch), against
 moe_rerouting_v2 with a workspace of its own, through the C ABI on the GPU.
 
-Four calls go out back to back on one stream, each with a smaller input than
+Six calls go out back to back on one stream, each with a smaller input than
 the one before, so each finds the scratch holding the previous call's header
 and row map: a 2-million-row call that fills the scratch nearly to its limit,
-the 256 x 64 banded shape, a 32 x 32 call with 158-byte rows, and the
-single-kernel tiny call. Every output byte must equal the existing entry
+the 256 x 64 banded shape, two calls of the one-launch kernel (384 and 256
+cells), a 32 x 32 call with 158-byte rows, and the single-kernel tiny call. Every output byte must equal the existing entry
 point's on the same inputs (and the oracle's)."""
 import numpy as np
 import pytest
@@ -24,6 +24,11 @@ def _cases():
         workloads.random_case(71, 16, 16, 16, tokens_dtype="float16", count_range=(7000, 8600), scales="a",
                               weight=True),
         workloads.make("tiny_segments"),
+        # one-launch kernel: 16 x 24 counts (eight cells a lane), then 16 x 16 (four a lane)
+        workloads.random_case(73, 16, 24, 1024, tokens_dtype="int8", count_range=(60, 100), scales="a",
+                              weight=True),
+        workloads.random_case(74, 16, 16, 1024, tokens_dtype="bfloat16", count_range=(40, 60), scales="e8m0",
+                              idx_type=1, counts_dtype=np.int64),
         workloads.random_case(72, 32, 32, 79, tokens_dtype="float16", count_range=(0, 20), scales="e8m0",
                               idx_type=1, etn_type=0),
         workloads.make("tiny"),
