@@ -7,7 +7,7 @@ does): item waves of 64 or 256 output rows, then one wave per KiB of the
 input token rows, each wave computing the offsets it needs from the counts.
 Cases cover both directions, int32 and int64 counts, empty cells, one rank or
 one expert, count matrices of 8, 35, 64 and 256 cells (four a lane) and of
-300, 323, 384 and 512 cells (eight a lane, among them counts in 16-byte
+299, 300, 323, 384 and 512 cells (eight a lane, among them counts in 16-byte
 groups that end half-way through a lane and matrices of no whole number of
 such groups), both index forms and expert_token_num modes, weights, scale
 rows of 4 bytes, 12 bytes, e8m0 and 4000 bytes, and rows that are no whole
@@ -86,6 +86,8 @@ CASES = {
                                          scales="as", S=1000, counts_dtype=np.int64, idx_type=1),
     "32x16_fp8_3584_w_cumsum": dict(seed=537, n=32, e=16, h=3584, tokens_dtype="float8_e5m2", weight=True,
                                     etn_type=0, target_mib=20),
+    "13x23_bf16_i64_as2_zeros": dict(seed=538, n=13, e=23, h=1024, tokens_dtype="bfloat16", scales="as", S=2,
+                                     counts_dtype=np.int64, zero_cells=True, idx_type=1, target_mib=24),
 }
 
 
