@@ -32,7 +32,8 @@ struct PosFmt {
 
 // The raw counts of this lane's cells m = kC lane + k in input order
 // (forward: row-major (rank, expert), the order of SrcOffset; inverse:
-// column-major), 0 past the matrix. Every wave reads the whole matrix, so the
+// column-major); past the matrix, the matrix's first counts, until mask_cells
+// or order_cells sets them to 0. Every wave reads the whole matrix, so the
 // number of load instructions matters: with kVec (the counts 16-byte aligned,
 // M a multiple of 4) each group of four counts comes in one 16-byte load (two
 // for int64) in matrix order, and the inverse puts them in column-major order
@@ -76,7 +77,7 @@ __device__ __forceinline__ void load_cells(const CountT* __restrict__ counts, in
         r[3] = static_cast<CountT>(v1.y);
       }
 #pragma unroll
-      for (int k = 0; k < 4; ++k) rc.r[4 * g + k] = in ? r[k] : CountT(0);
+      for (int k = 0; k < 4; ++k) rc.r[4 * g + k] = r[k];
     }
     return;
   }
@@ -95,10 +96,17 @@ __device__ __forceinline__ void load_cells(const CountT* __restrict__ counts, in
     at[k] = m < M ? cm : 0;  // M >= 1 here
   }
 #pragma unroll
-  for (int k = 0; k < kC; ++k) {
-    const CountT raw = counts[at[k]];
-    rc.r[k] = kC * lane + k < M ? raw : CountT(0);
-  }
+  for (int k = 0; k < kC; ++k) rc.r[k] = counts[at[k]];
+}
+
+// The loaded counts past the matrix (read from its start) set to 0; not
+// needed after order_cells, which does the same.
+template <typename CountT, int kC, bool kVec, bool kInv>
+__device__ __forceinline__ void mask_cells(RawCells<CountT, kC>& rc, int M) {
+  if (kVec && kInv) return;
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int k = 0; k < kC; ++k) rc.r[k] = kC * lane + k < M ? rc.r[k] : CountT(0);
 }
 
 // The position of each of this lane's cells in output order, from the host's
@@ -175,7 +183,8 @@ struct InCells {
 // kFlags: the flags say why the counts are rejected (item waves: workgroup 0
 // writes them to the header); without it (token waves) any rejection shows
 // as kFlagNegative, which is enough to write nothing and costs fewer
-// instructions (a count is in [0, 2^31) when its bits from 31 up are 0).
+// instructions (a count is in [0, 2^31) when its bits from 31 up are 0; the
+// sums and scans over a rejected matrix are never used).
 template <typename CountT, int kC, bool kFlags>
 __device__ __forceinline__ void finish_cells(const RawCells<CountT, kC>& rc, int A, InCells<kC>& w) {
   uint32_t fl = 0;
@@ -186,13 +195,17 @@ __device__ __forceinline__ void finish_cells(const RawCells<CountT, kC>& rc, int
     if (kFlags) {
       w.c[k] = clamp_count(rc.r[k], &fl);
     } else {
+      // the low word as the count; an int64 count's high word must be 0
       const uint64_t u = static_cast<uint64_t>(static_cast<int64_t>(rc.r[k]));
-      w.c[k] = static_cast<int32_t>(u & 0x7fffffffu);
-      fl |= static_cast<uint32_t>(u >> 31);  // 0 for counts in [0, 2^31)
+      w.c[k] = static_cast<int32_t>(static_cast<uint32_t>(u));
+      if (sizeof(CountT) == 8) fl |= static_cast<uint32_t>(u >> 32);
     }
     own += static_cast<uint32_t>(w.c[k]);
     any |= static_cast<uint32_t>(w.c[k]);
   }
+  // Without kFlags, a count outside [0, 2^31) sets bit 31 of the OR of the
+  // low words or a bit of an int64 high word.
+  if (!kFlags) fl |= any >> 31;
   const uint32_t incl = wave_scan_u32(own);
   w.total = __builtin_amdgcn_readlane(incl, 63);
   w.start[0] = incl - own;
@@ -270,13 +283,24 @@ __device__ __forceinline__ void stream_fused_tokens(const GatherArgs& p, const S
   const uint32_t s0 = __builtin_amdgcn_readfirstlane(q - (q * f.vpr > n0 ? 1u : 0u));
   const uint32_t v = n0 + static_cast<uint32_t>(lane);
   const bool in = v < f.vectors;  // the last chunk may be partial
+  const uint32_t lane16 = static_cast<uint32_t>(lane) * 16u;
   RawCells<CountT, kC> rc;
   load_cells<CountT, kC, kVec, kInv>(static_cast<const CountT*>(f.counts), p.M, f, rc);
-  const T x = __builtin_nontemporal_load(reinterpret_cast<const T*>(p.tokens + (in ? int64_t(v) * 16 : 0)));
+  // a uniform base and a 32-bit lane offset (a lane past the end reads the chunk's first vector)
+  const uint8_t* tok = p.tokens + static_cast<uint64_t>(n0) * 16u;
+  const T x = __builtin_nontemporal_load(reinterpret_cast<const T*>(tok + (in ? lane16 : 0u)));
   // The offsets below wait for the counts alone (loads return in issue
   // order). The compiler would otherwise sink the token load below them, next
   // to its store: this barrier names the token buffer, so the load stays here.
+  // The count and position registers then pass through empty statements after
+  // it, so no arithmetic on them (and no wait for them) is scheduled ahead of
+  // the token load either.
   asm volatile("" ::"s"(p.tokens) : "memory");
+#pragma unroll
+  for (int k = 0; k < kC; ++k) asm volatile("" : "+v"(rc.r[k]));
+#pragma unroll
+  for (int j = 0; j < PosFmt<kC>::kWords; ++j) asm volatile("" : "+v"(rc.pos[j]));
+  mask_cells<CountT, kC, kVec, kInv>(rc, p.M);
   order_cells<CountT, kC, kVec, kInv>(rc, reinterpret_cast<CountT*>(s_lds), p.M);
   InCells<kC> w;
   finish_cells<CountT, kC, false>(rc, p.A, w);
@@ -285,9 +309,15 @@ __device__ __forceinline__ void stream_fused_tokens(const GatherArgs& p, const S
   const int m0 = cell_of<kC>(s0, w);
   const uint32_t d0 = dest_row<kC>(s0, m0, w, rc.pos, outp);
   const uint32_t b = (s0 + 1) * f.vpr;  // the first vector of row s0 + 1 (<= A * vpr, > n0)
+  if (b - n0 >= 64u) {  // uniform (every chunk when the rows are whole KiB): the chunk lies in row s0
+    uint8_t* out = p.out_tokens + static_cast<uint64_t>(d0) * static_cast<uint64_t>(p.row_bytes) +
+                   static_cast<uint64_t>(n0 - s0 * f.vpr) * 16u;
+    if (w.flags == 0 && in && d0 < static_cast<uint32_t>(p.A))
+      __builtin_nontemporal_store(x, reinterpret_cast<T*>(out + lane16));
+    return;
+  }
   uint32_t d1 = d0 + 1;
-  // uniform: the chunk reaches row s0 + 1 (b - n0 does not wrap, n0 + 64 can at the last chunk)
-  if (b - n0 < 64u && s0 + 1 < static_cast<uint32_t>(p.A)) {
+  if (s0 + 1 < static_cast<uint32_t>(p.A)) {  // uniform: the chunk reaches row s0 + 1
     const int m1 = cell_of<kC>(s0 + 1, w);
     if (m1 != m0) d1 = dest_row<kC>(s0 + 1, m1, w, rc.pos, outp);  // uniform
   }
@@ -381,6 +411,7 @@ __device__ __forceinline__ void stream_fused_items(const GatherArgs& p, const St
   const int M = p.M, A = p.A;
   RawCells<CountT, kC> rc;
   load_cells<CountT, kC, kVec, kInv>(static_cast<const CountT*>(f.counts), M, f, rc);
+  mask_cells<CountT, kC, kVec, kInv>(rc, M);
   order_cells<CountT, kC, kVec, kInv>(rc, reinterpret_cast<CountT*>(s_lds), M);
   InCells<kC> w;
   finish_cells<CountT, kC, true>(rc, A, w);
