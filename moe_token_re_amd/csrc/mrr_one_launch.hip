@@ -313,7 +313,7 @@ __device__ __forceinline__ void stream_fused_tokens(const GatherArgs& p, const S
     uint8_t* out = p.out_tokens + static_cast<uint64_t>(d0) * static_cast<uint64_t>(p.row_bytes) +
                    static_cast<uint64_t>(n0 - s0 * f.vpr) * 16u;
     if (w.flags == 0 && in && d0 < static_cast<uint32_t>(p.A))
-      __builtin_nontemporal_store(x, reinterpret_cast<T*>(out + lane16));
+      store16_through(out, lane16, x);
     return;
   }
   uint32_t d1 = d0 + 1;
@@ -325,7 +325,7 @@ __device__ __forceinline__ void stream_fused_tokens(const GatherArgs& p, const S
   const uint32_t d = second ? d1 : d0;
   const uint32_t col = v - (second ? s0 + 1 : s0) * f.vpr;  // the vector within its row
   if (w.flags == 0 && in && d < static_cast<uint32_t>(p.A))
-    __builtin_nontemporal_store(x, reinterpret_cast<T*>(p.out_tokens + int64_t(d) * p.row_bytes + int64_t(col) * 16));
+    store16_through(p.out_tokens + int64_t(d) * p.row_bytes + int64_t(col) * 16, x);
 }
 
 // The scale rows of output rows [d0, d0 + rows), output row d0 + r taken
