@@ -1,8 +1,10 @@
 // mrr_bench_copy.hip -- the copy-ceiling kernel of the benchmark: a plain
 // streaming copy in the fastest form measured on MI355X for this job: one
 // 64-lane wave per workgroup, each lane moving one 16-byte vector (1 KiB per
-// workgroup), non-temporal loads and stores. Same byte count as the
-// re-routing gather's token rows, no index work.
+// workgroup), non-temporal loads, stores written through the L2 as streaming
+// data (sc1 nt, ~0.5% faster than nt alone, the same store the re-routing
+// kernels use). Same byte count as the re-routing gather's token rows, no
+// index work.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -20,7 +22,7 @@ __global__ __launch_bounds__(kThreads) void copy_kernel(v4u* __restrict__ dst, c
   const size_t i = size_t(blockIdx.x) * kThreads + threadIdx.x;
   // Branch-free load (a clamped index), predicated store.
   const v4u v = __builtin_nontemporal_load(src + (i < n_vec ? i : n_vec - 1));
-  if (i < n_vec) __builtin_nontemporal_store(v, dst + i);
+  if (i < n_vec) asm volatile("global_store_dwordx4 %0, %1, off sc1 nt" ::"v"(dst + i), "v"(v) : "memory");
 }
 
 }  // namespace

@@ -88,6 +88,16 @@ __device__ __forceinline__ void store16_through(void* base, uint32_t off, VecT<1
   asm volatile("global_store_dwordx4 %0, %1, %2 sc1 nt" ::"v"(off), "v"(v), "s"(base) : "memory");
 }
 
+// A streaming store of a V-byte vector: 16-byte vectors written through the
+// L2 as above, narrower ones non-temporal.
+template <int V>
+__device__ __forceinline__ void store_stream(typename VecT<V>::type* p, typename VecT<V>::type v) {
+  if constexpr (V == 16)
+    store16_through(p, v);
+  else
+    __builtin_nontemporal_store(v, p);
+}
+
 struct GatherArgs {
   const uint8_t* tokens;
   uint8_t* out_tokens;

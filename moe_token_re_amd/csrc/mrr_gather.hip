@@ -286,7 +286,7 @@ __device__ __forceinline__ void stream_whole_row_chunk(const GatherArgs& p, cons
   const bool ok = header_valid(p.hdr, p) & (static_cast<unsigned>(s) < static_cast<unsigned>(p.A));
   const int64_t so = ok ? int64_t(s) * p.row_bytes + int64_t(col) * V : 0;
   const T v = __builtin_nontemporal_load(reinterpret_cast<const T*>(p.tokens + so));
-  if (ok) __builtin_nontemporal_store(v, reinterpret_cast<T*>(p.out_tokens + int64_t(d) * p.row_bytes + int64_t(col) * V));
+  if (ok) store_stream<V>(reinterpret_cast<T*>(p.out_tokens + int64_t(d) * p.row_bytes + int64_t(col) * V), v);
 }
 
 // Chunk `chunk` of a row stream: vectors [64 chunk, 64 chunk + 64) of the
@@ -315,7 +315,7 @@ __device__ __forceinline__ void stream_rows(const uint8_t* __restrict__ src, uin
   // Branch-free load (row 0, column 0 when not moving: always valid here).
   const int64_t so = ok ? int64_t(s) * row_bytes + int64_t(col) * V : 0;
   const T v = __builtin_nontemporal_load(reinterpret_cast<const T*>(src + so));
-  if (ok) __builtin_nontemporal_store(v, reinterpret_cast<T*>(dst + (g0 + lane) * V));
+  if (ok) store_stream<V>(reinterpret_cast<T*>(dst + (g0 + lane) * V), v);
 }
 
 // The 16 bytes at byte sh (0..15) of the 32-byte concatenation lo:hi, by
@@ -443,7 +443,7 @@ __device__ __forceinline__ void byte_block(const GatherArgs& p, int64_t o, int64
   }
   if (!ok) return;
   if (o + 16 <= total) {
-    __builtin_nontemporal_store(v, reinterpret_cast<T*>(p.out_tokens + o));
+    store16_through(p.out_tokens + o, v);
   } else {
     const uint32_t wv[4] = {v.x, v.y, v.z, v.w};
     for (int b = 0; b < static_cast<int>(total - o); ++b)
@@ -510,7 +510,7 @@ __device__ __forceinline__ void stream_bytes_chunk(const GatherArgs& p, const St
       const bool ok = hv & (w[0] >= 0) & (int64_t(w[0]) + span <= p.A);
       const int64_t delta = ok ? (int64_t(w[0]) - d_base) * R : -o0;  // not moving: input bytes [0, 1024)
       const T v = run_block(p.tokens, o, delta, static_cast<int>(delta & 15));
-      if (ok) __builtin_nontemporal_store(v, reinterpret_cast<T*>(p.out_tokens + o));
+      if (ok) store16_through(p.out_tokens + o, v);
       return;
     }
     // row within the chunk: at most one boundary for rows of 1 KiB or more; below that,
@@ -535,7 +535,7 @@ __device__ __forceinline__ void stream_bytes_chunk(const GatherArgs& p, const St
       const int64_t delta = ok ? (int64_t(s0) - d_base) * R : -o0;  // not moving: input bytes [0, 1024)
       const int sh = __builtin_amdgcn_readfirstlane(static_cast<int>(delta & 15));
       const T v = run_block(p.tokens, o, delta, sh);
-      if (ok) __builtin_nontemporal_store(v, reinterpret_cast<T*>(p.out_tokens + o));
+      if (ok) store16_through(p.out_tokens + o, v);
       return;
     }
     dd = Ri >= 1024 ? (off >= Ri ? 1 : 0) : div_small(off, g.inv_row);
