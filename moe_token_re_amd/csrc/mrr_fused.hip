@@ -59,8 +59,7 @@ __device__ __forceinline__ void store_round(const RowRound<V>& q, uint8_t* __res
   for (int k = 0; k < kGatherUnroll; ++k) {
     const int32_t d = s_dst[q.r[k]];
     if (q.c[k] >= 0 && static_cast<unsigned>(d) < static_cast<unsigned>(A))
-      __builtin_nontemporal_store(q.v[k],
-                                  reinterpret_cast<T*>(dst + int64_t(d) * row_bytes + int64_t(q.c[k]) * V));
+      store_stream<V>(reinterpret_cast<T*>(dst + int64_t(d) * row_bytes + int64_t(q.c[k]) * V), q.v[k]);
   }
 }
 
@@ -154,7 +153,7 @@ __global__ __launch_bounds__(kGatherThreads) void fused_kernel(GatherArgs p, Fus
   if (kSV > 0 && sc_in) {
     const int32_t d = s_dst[sc_row];
     if (static_cast<unsigned>(d) < static_cast<unsigned>(p.A))
-      __builtin_nontemporal_store(piece, reinterpret_cast<ST*>(p.out_scales + int64_t(d) * Rs + sc_off));
+      store_stream<(kSV > 0 ? kSV : 4)>(reinterpret_cast<ST*>(p.out_scales + int64_t(d) * Rs + sc_off), piece);
   }
   if (tid < rows) {
     const int32_t d = s_dst[tid];

@@ -138,7 +138,7 @@ __device__ __forceinline__ void copy_rows(const uint8_t* __restrict__ src, uint8
     for (int k = 0; k < kGatherUnroll; ++k) {
       const int e = e0 + tid + k * kGatherThreads;
       if (col[k] >= 0 && srow[k] >= 0)
-        __builtin_nontemporal_store(v[k], reinterpret_cast<T*>(dst_chunk + int64_t(e) * V));
+        store_stream<V>(reinterpret_cast<T*>(dst_chunk + int64_t(e) * V), v[k]);
     }
   }
 }
@@ -176,7 +176,7 @@ __device__ __forceinline__ void move_rows(const GatherArgs& p, int row0, int row
   copy_rows<V>(p.tokens, p.out_tokens + int64_t(row0) * p.row_bytes, p.row_bytes, p.vecs_per_row, rows, s_src);
 
   if (kSV > 0 && sc_src >= 0)
-    __builtin_nontemporal_store(piece, reinterpret_cast<ST*>(p.out_scales + int64_t(row0 + sc_row) * Rs + sc_off));
+    store_stream<(kSV > 0 ? kSV : 4)>(reinterpret_cast<ST*>(p.out_scales + int64_t(row0 + sc_row) * Rs + sc_off), piece);
   for (int lr = tid; lr < rows; lr += kGatherThreads) {
     const int32_t s = lr == tid ? my_s : s_src[lr];
     if (s < 0) continue;

@@ -355,7 +355,7 @@ __device__ __forceinline__ void stream_fused_scales(const GatherArgs& p, const S
     }
 #pragma unroll
     for (int k = 0; k < kScaleRound; ++k)
-      if (in[k]) __builtin_nontemporal_store(v[k], reinterpret_cast<T*>(p.out_scales + to[k]));
+      if (in[k]) store_stream<SV>(reinterpret_cast<T*>(p.out_scales + to[k]), v[k]);
   }
 }
 
