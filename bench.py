@@ -271,7 +271,7 @@ class Bench:
         return name, kbytes, b2b_us, pair_us, off
 
     def copy_ceiling(self, lib, k):
-        """The plain 16-byte non-temporal copy kernel and hipMemcpyAsync moving
+        """The plain 16-byte streaming copy kernel and hipMemcpyAsync moving
         the workload's token bytes over the same rotation; the faster rate."""
         torch, w, n, s = self.torch, self.w, self.n_sets, self.stream
         nbytes16 = (w.A * w.token_row_bytes) // 16 * 16
