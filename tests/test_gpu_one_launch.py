@@ -146,3 +146,36 @@ def test_one_launch_bad_counts_write_nothing(kind, ne, direction):
     assert status == _lib.ERROR_BAD_COUNTS, kind
     for o in out:
         assert (o == SENTINEL).all(), kind
+
+
+def exact_case(seed, n, e, a, row_bytes, scale_words, idx_type):
+    """A call of exactly `a` rows over n x e cells (multinomial counts, most
+    cells empty when a is small): int8 token rows of row_bytes, [A] or
+    [A, scale_words] fp32 scales, weights."""
+    rng = np.random.default_rng(seed)
+    counts = rng.multinomial(a, [1.0 / (n * e)] * (n * e)).reshape(n, e).astype(np.int32)
+    tok = rng.integers(0, 256, (a, row_bytes), dtype=np.uint8)
+    shape = (a,) if scale_words == 1 else (a, scale_words)
+    scales = rng.standard_normal(shape, dtype=np.float32)
+    weight = rng.random((a, 1), dtype=np.float32)
+    return workloads.Workload(f"exact_{seed}_{a}", counts, tok, "int8", row_bytes, scales, "float32", weight, 1,
+                              idx_type)
+
+
+# Item waves move 256 output rows each when scale rows are at most 16 bytes
+# (four a lane) and 64 rows otherwise: row counts at and around those
+# boundaries, one row, and rows that are no whole number of KiB.
+EDGE_ROWS = [(1, 1), (255, 1), (256, 1), (257, 1), (513, 1), (1, 8), (63, 8), (64, 8), (65, 8), (129, 8)]
+
+
+@pytest.mark.parametrize("direction", DIRS, ids=DIR_IDS)
+@pytest.mark.parametrize("ne", [(16, 16), (16, 24)], ids=["256_cells", "384_cells"])
+@pytest.mark.parametrize("a,scale_words", EDGE_ROWS, ids=[f"A{a}_s{s}" for a, s in EDGE_ROWS])
+def test_one_launch_item_wave_edges(a, scale_words, ne, direction):
+    row_bytes = 1040 if a % 2 else 1024
+    w = exact_case(600 + a, ne[0], ne[1], a, row_bytes, scale_words, idx_type=a % 2)
+    assert w.A == a
+    assert takes_one_launch(w, direction)
+    out, status = run_hip(w, _dev(), direction=direction)
+    assert status == _lib.SUCCESS, _lib.status_string(status)
+    assert_parity(w, out, run_oracle(w, direction))
