@@ -139,8 +139,9 @@ struct StreamFusedArgs {
   int32_t rpl;         // output rows per lane of an item wave: 4, or 1 for scale rows over 16 bytes
   int32_t idx16;       // permute_token_idx is 16-byte aligned (four rows' indices in one store)
   int32_t w16;         // permute_topk_weight is 16-byte aligned (the same for the weights)
-  uint32_t vpr;        // 16-byte vectors per token row (at least 64)
+  uint32_t vpr;        // 16-byte vectors per token row (at least 2)
   uint32_t vpr_magic;  // ceil(2^32 / vpr): n / vpr by a multiply-high and one correction (n < 2^32)
+  float inv_vpr;       // 1 / vpr
   uint32_t vectors;    // A * vpr: the token vectors of the call
   int32_t minor;       // cells per major index in input order: E forward, N inverse
   int32_t major;       // N forward, E inverse

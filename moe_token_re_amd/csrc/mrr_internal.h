@@ -102,11 +102,14 @@ constexpr int64_t kFusedMaxTokenBytesFewCells = int64_t(28) << 20;
 constexpr int64_t kFusedMaxByteRowBytes = int64_t(4) << 20;
 
 // The one-launch stream kernel (count matrices of at most 512 cells, 4 or 8
-// a lane, token rows of 16-byte vectors and at least 1 KiB): its item waves
+// a lane, token rows of 16-byte vectors and at least 32 bytes): its item waves
 // move 64 scale rows each, so scale rows are limited to this many bytes
 // (larger ones take two kernels).
 constexpr int kStreamFusedMaxCells = 512;
 constexpr int64_t kStreamFusedMaxScaleRow = 4096;
+// Below this many bytes of token rows, rows under 1 KiB stay with the fused
+// kernel where it applies (it measured as fast or faster there).
+constexpr int64_t kStreamFusedSmallRowMinBytes = int64_t(2) << 20;
 
 // Offsets computed in one workgroup's LDS (the single-workgroup offsets
 // kernel, and every workgroup of the fused kernel) use one of two layouts:

@@ -266,12 +266,13 @@ __device__ __forceinline__ uint32_t dest_row(uint32_t s, int m, const InCells<kC
 }
 
 // Token wave c: the 16-byte vectors [64 c, 64 c + 64) of the input token rows
-// taken as one stream (input order, vpr >= 64 vectors a row), one load and
+// taken as one stream (input order, vpr >= 2 vectors a row), one load and
 // store per lane: this chip streams fastest with one-wave workgroups of one
 // load each (two chunks a wave measured slower). The load needs no offsets.
-// The chunk lies in row s0, or reaches into row s0 + 1 when the rows are no
-// whole number of KiB; then the wave also works out where row s0 + 1 goes
-// (the next output row when it is in the same cell).
+// The chunk covers rows s0 .. s_last. When they all lie in one cell (always
+// for a single row), they go to consecutive output rows, so the chunk's 1 KiB
+// lands contiguous from output row d0 on. Otherwise each lane finds its row,
+// and a walk over the cells the chunk touches gives each row its output row.
 template <typename CountT, int kC, bool kVec, bool kInv>
 __device__ __forceinline__ void stream_fused_tokens(const GatherArgs& p, const StreamFusedArgs& f, uint32_t c,
                                                     uint32_t* s_lds) {
@@ -308,24 +309,35 @@ __device__ __forceinline__ void stream_fused_tokens(const GatherArgs& p, const S
   cell_positions<kC>(rc.pos, outp);
   const int m0 = cell_of<kC>(s0, w);
   const uint32_t d0 = dest_row<kC>(s0, m0, w, rc.pos, outp);
-  const uint32_t b = (s0 + 1) * f.vpr;  // the first vector of row s0 + 1 (<= A * vpr, > n0)
-  if (b - n0 >= 64u) {  // uniform (every chunk when the rows are whole KiB): the chunk lies in row s0
+  // the chunk's last row, and its cell
+  const uint32_t n_last = min(n0 + 63u, f.vectors - 1u);
+  const uint32_t ql = __umulhi(n_last, f.vpr_magic);
+  const uint32_t s_last = __builtin_amdgcn_readfirstlane(ql - (ql * f.vpr > n_last ? 1u : 0u));
+  const int m_last = s_last == s0 ? m0 : cell_of<kC>(s_last, w);
+  if (m_last == m0) {  // uniform (every chunk when the rows are whole KiB)
     uint8_t* out = p.out_tokens + static_cast<uint64_t>(d0) * static_cast<uint64_t>(p.row_bytes) +
                    static_cast<uint64_t>(n0 - s0 * f.vpr) * 16u;
-    if (w.flags == 0 && in && d0 < static_cast<uint32_t>(p.A))
+    if (w.flags == 0 && in && d0 + (s_last - s0) < static_cast<uint32_t>(p.A))
       store16_through(out, lane16, x);
     return;
   }
-  uint32_t d1 = d0 + 1;
-  if (s0 + 1 < static_cast<uint32_t>(p.A)) {  // uniform: the chunk reaches row s0 + 1
-    const int m1 = cell_of<kC>(s0 + 1, w);
-    if (m1 != m0) d1 = dest_row<kC>(s0 + 1, m1, w, rc.pos, outp);  // uniform
+  if (w.flags != 0) return;  // uniform: rejected counts
+  // this lane's row: t < 64 + vpr vectors past the start of row s0 (div_small is exact below 2^12)
+  const uint32_t t = v - s0 * f.vpr;
+  const uint32_t r = s0 + (f.vpr >= 64 ? (t >= f.vpr ? 1u : 0u) : static_cast<uint32_t>(div_small(t, f.inv_vpr)));
+  uint32_t cnt[kC];
+#pragma unroll
+  for (int k = 0; k < kC; ++k) cnt[k] = static_cast<uint32_t>(w.c[k]);
+  uint32_t d = 0xffffffffu;  // (stays out of range, so unstored, if no cell held the row)
+  for (int m = m0; m <= m_last; ++m) {  // uniform: the cells of rows s0 .. s_last, in input order
+    const uint32_t n = cell_value<kC>(cnt, m);
+    if (n == 0) continue;
+    const uint32_t st = cell_value<kC>(w.start, m);
+    const uint32_t om = dest_row<kC>(st, m, w, rc.pos, outp);  // the cell's output offset
+    if (r - st < n) d = om + (r - st);
   }
-  const bool second = v >= b;
-  const uint32_t d = second ? d1 : d0;
-  const uint32_t col = v - (second ? s0 + 1 : s0) * f.vpr;  // the vector within its row
-  if (w.flags == 0 && in && d < static_cast<uint32_t>(p.A))
-    store16_through(p.out_tokens + int64_t(d) * p.row_bytes + int64_t(col) * 16, x);
+  if (in && d < static_cast<uint32_t>(p.A))
+    store16_through(p.out_tokens + int64_t(d) * p.row_bytes + int64_t(v - r * f.vpr) * 16, x);
 }
 
 // The scale rows of output rows [d0, d0 + rows), output row d0 + r taken
@@ -593,8 +605,9 @@ mrr_status launch_stream_fused(const Plan& pl, const mrr_args* a, void* ws, hipS
   f.rpl = pl.sf_rows_per_lane;
   f.idx16 = reinterpret_cast<uintptr_t>(g.idx) % 16 == 0 ? 1 : 0;
   f.w16 = reinterpret_cast<uintptr_t>(g.out_weight) % 16 == 0 ? 1 : 0;
-  f.vpr = static_cast<uint32_t>(pl.row_bytes / 16);  // >= 64
+  f.vpr = static_cast<uint32_t>(pl.row_bytes / 16);  // >= 2
   f.vpr_magic = static_cast<uint32_t>(((uint64_t(1) << 32) + f.vpr - 1) / f.vpr);
+  f.inv_vpr = 1.0f / static_cast<float>(f.vpr);
   f.vectors = static_cast<uint32_t>(pl.A * f.vpr);   // < 2^32 (the plan checks)
   f.minor = static_cast<int32_t>(pl.inverse ? pl.N : pl.E);
   f.major = static_cast<int32_t>(pl.inverse ? pl.E : pl.N);

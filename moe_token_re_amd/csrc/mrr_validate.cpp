@@ -65,6 +65,7 @@ struct Tuning {
   bool fused;       // allow the single-kernel path (MRR_FUSED=0 turns it off)
   bool byte_rows;   // rows that are no multiple of 16 bytes stream as aligned 16-byte blocks
   bool stream_fused;  // allow the one-launch stream kernel (MRR_STREAM_FUSED=0 turns it off)
+  int sf_min_row;     // its smallest token row in bytes (MRR_SF_MIN_ROW, at least 32)
   bool log;
   Tuning()
       : rows_per_wg(env_int("MRR_ROWS_PER_WG", 0)),
@@ -74,6 +75,7 @@ struct Tuning {
         fused(env_int("MRR_FUSED", 1) != 0),
         byte_rows(env_int("MRR_BYTE_ROWS", 1) != 0),
         stream_fused(env_int("MRR_STREAM_FUSED", 1) != 0),
+        sf_min_row(std::max(32, env_int("MRR_SF_MIN_ROW", 32))),
         log(env_int("MRR_LOG", 0) != 0) {}
 };
 
@@ -290,16 +292,22 @@ mrr_status make_plan(const mrr_args* a, const void* ws, size_t ws_bytes, Plan* p
   if (q.fused && q.grid > max_launch_grid(kGatherThreads)) q.fused = false;
   // The one-launch stream kernel runs in place of both the fused kernel and
   // the two kernels whenever its shape fits: at most 512 cells, token rows of
-  // 16-byte vectors (both buffers aligned) and at least 1 KiB, scale rows of
-  // at most 4 KiB, A < 2^30 (its exact-sum check), fewer than 2^32 token
-  // vectors in all, and one launch of at most 2^31 workgroups. (16x16 counts with 7168-byte rows, whole call: 1.8 MiB 4.7
+  // 16-byte vectors (both buffers aligned) and at least 32 bytes, scale rows
+  // of at most 4 KiB, A < 2^30 (its exact-sum check), fewer than 2^32 token
+  // vectors in all, and one launch of at most 2^31 workgroups; rows under
+  // 1 KiB leave calls of under 2 MiB of token rows to the fused kernel where
+  // it applies. (16x16 counts with 7168-byte rows, whole call: 1.8 MiB 4.7
   // against 5.7 us for the fused kernel, 27 MiB 11.2 against 14.1, 46 MiB
-  // 17.6 against 21.4; at 112 MiB 37 against 41 us for the two kernels.)
+  // 17.6 against 21.4; at 112 MiB 37 against 41 us for the two kernels.
+  // 512-byte rows: 1 MiB 5.34 against 5.37, 16 MiB 8.33 against 10.73 (fused),
+  // 131 MiB 43.5 against 50.0 (two kernels); 32-byte rows at 64 MiB 32.3
+  // against 45.6; the 42-row tiny call 4.64 against 3.73 for the fused kernel.)
   q.stream_fused = false;
   q.sf_item_waves = q.sf_grid = 0;
   q.sf_rows_per_lane = 1;
   q.sf_cells_per_lane = M > 256 ? 8 : 4;
-  if (tuning().stream_fused && q.A > 0 && M <= kStreamFusedMaxCells && q.token_vec == 16 && q.row_bytes >= 1024 &&
+  if (tuning().stream_fused && q.A > 0 && M <= kStreamFusedMaxCells && q.token_vec == 16 &&
+      q.row_bytes >= tuning().sf_min_row &&
       q.scale_row_bytes <= kStreamFusedMaxScaleRow && q.A < (int64_t(1) << 30) &&
       q.A * (q.row_bytes / 16) < (int64_t(1) << 32)) {
     // item waves of 256 output rows (64 for scale rows of more than 16 bytes,
@@ -307,7 +315,8 @@ mrr_status make_plan(const mrr_args* a, const void* ws, size_t ws_bytes, Plan* p
     q.sf_rows_per_lane = q.scale_row_bytes > 16 ? 1 : 4;
     const int64_t waves = (q.A + 64 * q.sf_rows_per_lane - 1) / (64 * q.sf_rows_per_lane);
     const int64_t grid = waves + (q.A * (q.row_bytes / 16) + 63) / 64;
-    if (grid < kMaxStreamGrid && grid <= max_launch_grid(64)) {
+    const bool small_fused = q.fused && q.row_bytes < 1024 && q.A * q.row_bytes < kStreamFusedSmallRowMinBytes;
+    if (grid < kMaxStreamGrid && grid <= max_launch_grid(64) && !small_fused) {
       q.stream_fused = true;
       q.fused = false;
       q.sf_item_waves = waves;

@@ -276,19 +276,43 @@ def test_plan_size_classes():
         st, info = describe(valid_args(A=a_rows, H=7184, N=16, E=16, tok=_lib.I8))
         assert st == _lib.SUCCESS and info.fused == 2, a_rows
         assert info.one_launch_workgroups == -(-a_rows // 256) + -(-a_rows * 449 // 64)
-    # rows under 1 KiB (1008 bytes): the fused kernel up to 28 MiB of token rows with at most 64 cells,
-    # 48 MiB with at most 256, else offsets + gather
-    below28, above28, above48 = 28 * mib // 1008 - 1, 28 * mib // 1008 + 1, 48 * mib // 1008 + 1
-    for n, e in [(8, 8), (4, 4), (1, 64)]:
-        st, info = describe(valid_args(A=below28, H=1008, N=n, E=e, tok=_lib.I8))
+    # rows of 16-byte vectors under 1 KiB (1008 bytes): the fused kernel below 2 MiB of token rows where
+    # it applies (at most 256 cells), the one-launch kernel from there on, at any size
+    below2, at2 = 2 * mib // 1008 - 1, 2 * mib // 1008 + 1
+    for n, e in [(8, 8), (4, 4), (1, 64), (16, 16)]:
+        st, info = describe(valid_args(A=below2, H=1008, N=n, E=e, tok=_lib.I8))
         assert st == _lib.SUCCESS and info.fused == 1, (n, e)
-        st, info = describe(valid_args(A=above28, H=1008, N=n, E=e, tok=_lib.I8))
+        for a_rows in (at2, 100 * mib // 1008):
+            st, info = describe(valid_args(A=a_rows, H=1008, N=n, E=e, tok=_lib.I8))
+            assert st == _lib.SUCCESS and info.fused == 2, (n, e, a_rows)
+            assert info.one_launch_workgroups == -(-a_rows // 256) + -(-a_rows * 63 // 64)
+    # 257..512 cells (no fused kernel there): the one-launch kernel at every size
+    for a_rows in (1, below2, at2):
+        st, info = describe(valid_args(A=a_rows, H=1008, N=16, E=24, tok=_lib.I8))
+        assert st == _lib.SUCCESS and info.fused == 2, a_rows
+    # 32-byte rows (two vectors): the one-launch kernel from 2 MiB; 16-byte rows never
+    st, info = describe(valid_args(A=3 * mib // 32, H=32, N=16, E=16, tok=_lib.I8))
+    assert st == _lib.SUCCESS and info.fused == 2 and info.one_launch_workgroups == -(-3 * mib // 32 // 256) + \
+        -(-3 * mib // 32 * 2 // 64)
+    st, info = describe(valid_args(A=3 * mib // 16, H=16, N=16, E=16, tok=_lib.I8))
+    assert st == _lib.SUCCESS and info.fused == 1
+    # 16-byte rows (never the one-launch kernel): the fused kernel up to 28 MiB of token rows with at most
+    # 64 cells, 48 MiB with at most 256, else offsets + gather
+    below28, above28, above48 = 28 * mib // 16 - 1, 28 * mib // 16 + 1, 48 * mib // 16 + 1
+    for n, e in [(8, 8), (4, 4), (1, 64)]:
+        st, info = describe(valid_args(A=below28, H=16, N=n, E=e, tok=_lib.I8))
+        assert st == _lib.SUCCESS and info.fused == 1, (n, e)
+        st, info = describe(valid_args(A=above28, H=16, N=n, E=e, tok=_lib.I8))
         assert st == _lib.SUCCESS and info.fused == 0 and info.gather_kernel == 1, (n, e)
         assert info.one_launch_workgroups == 0 and info.offsets_workgroups == -(-above28 // 256)
-    st, info = describe(valid_args(A=above28, H=1008, N=16, E=16, tok=_lib.I8))
+    st, info = describe(valid_args(A=above28, H=16, N=16, E=16, tok=_lib.I8))
     assert st == _lib.SUCCESS and info.fused == 1
-    st, info = describe(valid_args(A=above48, H=1008, N=16, E=16, tok=_lib.I8))
+    st, info = describe(valid_args(A=above48, H=16, N=16, E=16, tok=_lib.I8))
     assert st == _lib.SUCCESS and info.fused == 0 and info.offsets_workgroups == -(-above48 // 256)
+    # rows that are no multiple of 16 bytes (1000 bytes): the fused kernel below 4 MiB, else offsets + gather
+    for a_rows, fused in ((4 * mib // 1000 - 1, 1), (4 * mib // 1000 + 1, 0)):
+        st, info = describe(valid_args(A=a_rows, H=1000, N=16, E=16, tok=_lib.I8))
+        assert st == _lib.SUCCESS and info.fused == fused, a_rows
     # whole-KiB rows but not the one-launch kernel's other limits (above 48 MiB: offsets + gather)
     above48 = 48 * mib // 7168 + 1
     a = valid_args(A=above48, H=7168, N=16, E=16, tok=_lib.I8)

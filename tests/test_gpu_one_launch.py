@@ -179,3 +179,67 @@ def test_one_launch_item_wave_edges(a, scale_words, ne, direction):
     out, status = run_hip(w, _dev(), direction=direction)
     assert status == _lib.SUCCESS, _lib.status_string(status)
     assert_parity(w, out, run_oracle(w, direction))
+
+
+def mixed_case(seed, n, e, row_bytes, target_mib, tokens_dtype="int8", small=(0, 4), **kw):
+    """Counts mostly small (so that a 1 KiB chunk of short rows spans several
+    cells, empty ones among them) with one large cell that brings the token
+    rows to about target_mib MiB."""
+    rng = np.random.default_rng(seed)
+    bits = workloads.TOKEN_DTYPES[tokens_dtype][0]
+    h = row_bytes * 8 // bits
+    w = workloads.random_case(seed, n, e, h, tokens_dtype=tokens_dtype, count_range=small, **kw)
+    counts = w.counts.copy()
+    want = int(target_mib * MIB) // row_bytes
+    big = int(rng.integers(0, n * e))
+    counts.reshape(-1)[big] += max(0, want - int(counts.sum()))
+    a = int(counts.sum())
+    tok = rng.integers(0, 256, (a, row_bytes), dtype=np.uint8).view(w.tokens.dtype).reshape(a, -1)
+    sc = None
+    if w.scales is not None:
+        sc = rng.integers(0, 256, (a,) + w.scales.shape[1:] + (w.scales.dtype.itemsize,), dtype=np.uint8)
+        sc = sc.view(w.scales.dtype).reshape((a,) + w.scales.shape[1:])
+    wt = rng.random((a, 1), dtype=np.float32) if w.weight is not None else None
+    return workloads.Workload(f"mixed_{seed}", counts, tok, tokens_dtype, h, sc, w.scales_dtype, wt, w.etn_type,
+                              w.idx_type)
+
+
+# Token rows of 16-byte vectors under 1 KiB: a chunk spans several rows, often
+# of several cells. Calls of at least 2 MiB of token rows (the fused kernel
+# takes smaller ones where it applies), or with more than 256 cells.
+SMALL_ROWS = {
+    "16x16_32B_mixed": dict(seed=700, n=16, e=16, row_bytes=32, target_mib=3),
+    "16x16_48B_mixed_w_scatter": dict(seed=701, n=16, e=16, row_bytes=48, target_mib=3, weight=True, idx_type=1,
+                                      scales="a"),
+    "5x7_64B_mixed_as3": dict(seed=702, n=5, e=7, row_bytes=64, target_mib=4, scales="as", S=3),
+    "16x24_128B_mixed_e8m0": dict(seed=703, n=16, e=24, row_bytes=128, target_mib=1, tokens_dtype="float8_e4m3fn",
+                                  scales="e8m0"),
+    "64x8_256B_mixed_i64_cumsum": dict(seed=704, n=64, e=8, row_bytes=256, target_mib=2, tokens_dtype="bfloat16",
+                                       counts_dtype=np.int64, etn_type=0, weight=True),
+    "1x1_512B": dict(seed=705, n=1, e=1, row_bytes=512, target_mib=3, small=(0, 1)),
+    "32x8_1008B_mixed_w": dict(seed=706, n=32, e=8, row_bytes=1008, target_mib=6, weight=True, scales="a"),
+    "13x23_80B_mixed_i64": dict(seed=707, n=13, e=23, row_bytes=80, target_mib=0.5, counts_dtype=np.int64,
+                                small=(0, 3)),
+}
+
+
+@pytest.mark.parametrize("direction", DIRS, ids=DIR_IDS)
+@pytest.mark.parametrize("name", list(SMALL_ROWS))
+def test_one_launch_small_rows(name, direction):
+    w = mixed_case(**SMALL_ROWS[name])
+    assert takes_one_launch(w, direction), name
+    out, status = run_hip(w, _dev(), direction=direction)
+    assert status == _lib.SUCCESS, _lib.status_string(status)
+    assert_parity(w, out, run_oracle(w, direction))
+
+
+@pytest.mark.parametrize("direction", DIRS, ids=DIR_IDS)
+def test_small_rows_below_2mib_stay_fused(direction):
+    w = mixed_case(708, 16, 16, 256, 1)
+    dev = _dev()
+    t = workloads.torch_inputs(w, dev)
+    call, _ = api.make_call(t["tokens"], t["counts"], tokens_dtype=t["tokens_dtype"], direction=direction)
+    assert call.plan()["fused"] == 1
+    out, status = run_hip(w, dev, direction=direction)
+    assert status == _lib.SUCCESS
+    assert_parity(w, out, run_oracle(w, direction))
