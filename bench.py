@@ -2,7 +2,7 @@
 
 A step is one whole call of the operator (the one-launch stream kernel for
 count matrices of at most 512 cells and token rows of 16-byte vectors from
-1 KiB, the fused kernel for small calls, else offsets kernel + gather
+32 bytes, the fused kernel for small calls, else offsets kernel + gather
 kernel) on one batch of synthetic input already resident in HBM. The headline workload is the shape of the pages'
 single-operator example: A=16384 tokens of H=7168 int8 values, N=E=16, one
 huge segment, [A] fp32 scales (moe_token_re_amd/workloads.py has the recipe).

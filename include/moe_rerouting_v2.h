@@ -178,10 +178,11 @@ typedef struct mrr_plan_info {
                                     each recompute the offsets of the (small) count matrix in LDS
                                     or registers (small calls); 2 = one kernel of 64-lane
                                     workgroups (count matrices of at most 512 cells, token rows of
-                                    16-byte vectors and at least 1 KiB): item waves of 256 output
+                                    16-byte vectors and at least 32 bytes; rows under 1 KiB from 2
+                                    MiB of token rows where 1 applies): item waves of 256 output
                                     rows (64 with scale rows over 16 bytes), then one wave per
-                                    1 KiB of the input token rows, each
-                                    computing the offsets it needs from the counts; 0 = the offsets kernel, then the gather
+                                    1 KiB of the input token rows, each computing the offsets it
+                                    needs from the counts; 0 = the offsets kernel, then the gather
                                     kernel (the two-phase entry points always do that) */
   int32_t token_vec_bytes;       /* bytes per load/store of the token copy: 16, 8, 4, 2 or 1
                                     (16 also for rows that are no multiple of 16 bytes when the

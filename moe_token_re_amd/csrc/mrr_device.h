@@ -24,7 +24,7 @@
 //   mrr_fused.hip    the whole call in one launch for small count matrices;
 //   mrr_one_launch.hip  the whole call in one launch of one-wave workgroups
 //                    for count matrices of at most 512 cells and token rows
-//                    of 16-byte vectors from 1 KiB, at any size;
+//                    of 16-byte vectors from 32 bytes, at any size;
 //   mrr_entry.hip    the C entry points.
 // This header holds the workgroup and wave scans, the count checks and the
 // workspace header, the offsets of a count matrix in a workgroup's LDS (one
@@ -129,8 +129,8 @@ struct FusedArgs {
   int32_t cumsum;
 };
 
-// The one-launch stream kernel's own arguments (count matrices of at most 256
-// cells, token rows of whole 16-byte vectors, at least 1 KiB).
+// The one-launch stream kernel's own arguments (count matrices of at most 512
+// cells, token rows of whole 16-byte vectors, at least 32 bytes).
 struct StreamFusedArgs {
   const void* counts;
   void* etn;

@@ -2,11 +2,11 @@
 // "CANN ops-transformer MoeReRoutingV2": the offsets and moves of "计算公式",
 // permute_token_idx and expert_token_num of "参数说明") in one launch of
 // 64-lane workgroups, for count matrices of at most 512 cells, token rows of
-// 16-byte vectors and at least 1 KiB, and scale rows of at most 4 KiB, at any
-// size. Workgroups [0, item_waves) move the per-row items and scale rows of
-// 64 rpl output rows each; every later workgroup moves one 1 KiB chunk of the
-// input token rows, in input order, so that its token load goes out at once
-// (beside the count load); it then works out where its row (or two rows) go
+// 16-byte vectors and at least 32 bytes, and scale rows of at most 4 KiB, at
+// any size. Workgroups [0, item_waves) move the per-row items and scale rows
+// of 64 rpl output rows each; every later workgroup moves one 1 KiB chunk of
+// the input token rows, in input order, so that its token load goes out at
+// once (beside the count load); it then works out where the chunk's rows go
 // from the counts while the load is in flight. Every wave checks the counts
 // itself and writes nothing when they are rejected; workgroup 0 writes
 // expert_token_num and the status. A lane holds kC cells of the matrix: 4 up
@@ -314,7 +314,7 @@ __device__ __forceinline__ void stream_fused_tokens(const GatherArgs& p, const S
   const uint32_t ql = __umulhi(n_last, f.vpr_magic);
   const uint32_t s_last = __builtin_amdgcn_readfirstlane(ql - (ql * f.vpr > n_last ? 1u : 0u));
   const int m_last = s_last == s0 ? m0 : cell_of<kC>(s_last, w);
-  if (m_last == m0) {  // uniform (every chunk when the rows are whole KiB)
+  if (m_last == m0) {  // uniform (every chunk when the rows are whole KiB; most of them otherwise)
     uint8_t* out = p.out_tokens + static_cast<uint64_t>(d0) * static_cast<uint64_t>(p.row_bytes) +
                    static_cast<uint64_t>(n0 - s0 * f.vpr) * 16u;
     if (w.flags == 0 && in && d0 + (s_last - s0) < static_cast<uint32_t>(p.A))

@@ -1,18 +1,20 @@
 """Parity of the one-launch stream kernel with the CPU oracle, byte for byte.
 
 moe_rerouting_v2 takes that kernel for count matrices of at most 512 cells,
-token rows of 16-byte vectors and at least 1 KiB, and scale rows of at most
-4 KiB, at any size (every case below first checks, through the plan, that it
-does): item waves of 64 or 256 output rows, then one wave per KiB of the
+token rows of 16-byte vectors and at least 32 bytes, and scale rows of at
+most 4 KiB, at any size (rows under 1 KiB from 2 MiB of token rows when the
+fused kernel applies; every case below first checks, through the plan, that
+it does): item waves of 64 or 256 output rows, then one wave per KiB of the
 input token rows, each wave computing the offsets it needs from the counts.
 Cases cover both directions, int32 and int64 counts, empty cells, one rank or
 one expert, count matrices of 8, 35, 64 and 256 cells (four a lane) and of
 299, 300, 323, 384 and 512 cells (eight a lane, among them counts in 16-byte
 groups that end half-way through a lane and matrices of no whole number of
 such groups), both index forms and expert_token_num modes, weights, scale
-rows of 4 bytes, 12 bytes, e8m0 and 4000 bytes, and rows that are no whole
+rows of 4 bytes, 12 bytes, e8m0 and 4000 bytes, rows that are no whole
 number of KiB (a wave's KiB then reaches into the next row, often of another
-cell).
+cell), and rows of 32 to 1008 bytes (a wave's KiB spans several rows, often of
+several cells, empty ones among them).
 Rejected counts (negative, a wrong sum, a count above INT32_MAX, int32
 counts whose sum wraps to A modulo 2^32) leave every output untouched."""
 import numpy as np
