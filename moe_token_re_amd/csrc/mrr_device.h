@@ -141,12 +141,12 @@ struct StreamFusedArgs {
   int32_t w16;         // permute_topk_weight is 16-byte aligned (the same for the weights)
   uint32_t vpr;        // 16-byte vectors per token row (at least 2)
   uint32_t vpr_magic;  // ceil(2^32 / vpr): n / vpr by a multiply-high and one correction (n < 2^32)
-  float inv_vpr;       // 1 / vpr
   uint32_t vectors;    // A * vpr: the token vectors of the call
   int32_t minor;       // cells per major index in input order: E forward, N inverse
   int32_t major;       // N forward, E inverse
   float inv_minor;     // 1 / minor
   float inv_spr;       // 1 / (scale vectors per row), when there are scales
+  float inv_vpr;       // 1 / vpr
   // The output-order position of each input-order cell: it depends on N, E
   // and the direction alone, so the host computes it once instead of every
   // wave. With 4 cells a lane (at most 256 cells), cell m = 4 l + k in byte k

@@ -309,10 +309,13 @@ __device__ __forceinline__ void stream_fused_tokens(const GatherArgs& p, const S
   cell_positions<kC>(rc.pos, outp);
   const int m0 = cell_of<kC>(s0, w);
   const uint32_t d0 = dest_row<kC>(s0, m0, w, rc.pos, outp);
-  // the chunk's last row, and its cell
-  const uint32_t n_last = min(n0 + 63u, f.vectors - 1u);
-  const uint32_t ql = __umulhi(n_last, f.vpr_magic);
-  const uint32_t s_last = __builtin_amdgcn_readfirstlane(ql - (ql * f.vpr > n_last ? 1u : 0u));
+  // the chunk's last row (s0 when the rows are whole KiB), and its cell
+  uint32_t s_last = s0;
+  if (f.vpr % 64u != 0) {  // uniform
+    const uint32_t n_last = min(n0 + 63u, f.vectors - 1u);
+    const uint32_t ql = __umulhi(n_last, f.vpr_magic);
+    s_last = __builtin_amdgcn_readfirstlane(ql - (ql * f.vpr > n_last ? 1u : 0u));
+  }
   const int m_last = s_last == s0 ? m0 : cell_of<kC>(s_last, w);
   if (m_last == m0) {  // uniform (every chunk when the rows are whole KiB; most of them otherwise)
     uint8_t* out = p.out_tokens + static_cast<uint64_t>(d0) * static_cast<uint64_t>(p.row_bytes) +
