@@ -102,7 +102,8 @@ constexpr int64_t kFusedMaxTokenBytesFewCells = int64_t(28) << 20;
 constexpr int64_t kFusedMaxByteRowBytes = int64_t(4) << 20;
 
 // The one-launch stream kernel (count matrices of at most 512 cells, 4 or 8
-// a lane, token rows of 16-byte vectors and at least 32 bytes): its item waves
+// a lane, token rows of 16-byte vectors and at least 32 bytes, or rows of at
+// least 17 bytes that are no multiple of 64 in its byte form): its item waves
 // move 64 scale rows each, so scale rows are limited to this many bytes
 // (larger ones take two kernels).
 constexpr int kStreamFusedMaxCells = 512;
@@ -110,6 +111,9 @@ constexpr int64_t kStreamFusedMaxScaleRow = 4096;
 // Below this many bytes of token rows, rows under 1 KiB stay with the fused
 // kernel where it applies (it measured as fast or faster there).
 constexpr int64_t kStreamFusedSmallRowMinBytes = int64_t(2) << 20;
+// The same for byte-form rows under 512 bytes (its slow path walks the cells
+// of a wave one by one): the fused kernel below this many bytes.
+constexpr int64_t kStreamFusedSmallByteRowMinBytes = int64_t(256) << 10;
 
 // Offsets computed in one workgroup's LDS (the single-workgroup offsets
 // kernel, and every workgroup of the fused kernel) use one of two layouts:
@@ -159,6 +163,7 @@ struct Plan {
   int sf_rows_per_lane;     // output rows per lane of an item wave: 4, or 1 for scale rows over 16 bytes
   int sf_cells_per_lane;    // cells of the count matrix per lane: 4 (at most 256 cells) or 8 (at most 512)
   int64_t sf_grid;          // its workgroups: item waves + ceil(A * R / 1024)
+  bool sf_bytes;            // its byte form: rows that are no multiple of 64 bytes as one byte stream
   int rows_per_wg;
   int64_t grid;             // gather workgroups
   bool stream;              // the gather kernel is the stream kernel: 64-lane workgroups, one chunk of

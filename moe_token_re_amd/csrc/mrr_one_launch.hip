@@ -343,6 +343,156 @@ __device__ __forceinline__ void stream_fused_tokens(const GatherArgs& p, const S
     store16_through(p.out_tokens + int64_t(d) * p.row_bytes + int64_t(v - r * f.vpr) * 16, x);
 }
 
+// Bytes [0, n) of v (n <= 16) to dst, one byte store each: the output
+// blocks that hold bytes of two cells, whose other bytes another wave writes.
+__device__ __forceinline__ void store_bytes(uint8_t* dst, const VecT<16>::type& v, uint32_t n) {
+  const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (uint32_t k = 0; k < 16; ++k)
+    if (k < n) dst[k] = static_cast<uint8_t>(wd[k >> 2] >> (8 * (k & 3)));
+}
+
+// Token wave c for token rows that are no multiple of 64 bytes (R >= 17, both
+// token buffers 16-byte aligned, A R < 2^31): the rows taken as one byte
+// stream, the wave owns the bytes [base, base + 1 KiB), base = 1024 c, and
+// loads the 68 aligned 16-byte blocks from base (64 and then 4 more, before
+// the offsets, as above). A cell's rows are one byte range on both sides,
+// moved by delta = (output row - input row) R bytes. Stores are grouped by
+// aligned 64-byte segments of the output: every block of a cell in a segment
+// is written by the wave that owns the first of the cell's input bytes in that
+// segment, so no two waves write parts of one segment except where two cells
+// meet in the output. (This chip streams a permuted copy fastest when each
+// wave writes a whole 1 KiB: waves whose 1 KiB of output starts at 16 bytes
+// past a 64-byte boundary ran 13-22% slower, at 64 bytes past it 1-3%, and
+// waves of fewer bytes slower still: 960-byte waves 17%, under a permutation
+// of 256 cells.) An aligned output block whose bytes all come from one cell
+// is input bytes [x, x + 16), x = 16 o - delta, the blocks (x - base) / 16 and
+// the next funnel-shifted by sh = -delta mod 16: the lanes read them from the
+// blocks staged in LDS. With the wave inside one cell it writes the 1 KiB of
+// output from the first segment whose input starts at or after base, block j
+// by lane j. A cell's first block, when it also holds bytes of the output
+// row before (its head), and its last, when it holds bytes of the row after
+// (its tail), are written byte by byte; the other cell's wave writes the rest
+// of them.
+constexpr int kByteBlocks = 68;  // blocks staged per wave: a segment starting at byte 1023 ends before 1088
+
+// Stages this wave's blocks in LDS (after the values u, v, b that the stores
+// need are computed: the empty statement takes them and hands x on, so that
+// the compiler computes them before it waits for the token loads).
+__device__ __forceinline__ void stage_blocks(VecT<16>::type* s_blk, VecT<16>::type& x, VecT<16>::type& xb,
+                                             uint32_t u, uint32_t v, bool b) {
+  asm volatile("" : "+v"(x.x), "+v"(x.y), "+v"(x.z), "+v"(x.w), "+v"(xb.x), "+v"(xb.y), "+v"(xb.z), "+v"(xb.w)
+               : "s"(u), "v"(v), "v"(static_cast<uint32_t>(b)));
+  const int lane = threadIdx.x & 63;
+  s_blk[lane] = x;
+  if (lane < kByteBlocks - 64) s_blk[64 + lane] = xb;
+  __builtin_amdgcn_wave_barrier();
+}
+
+template <typename CountT, int kC, bool kVec, bool kInv>
+__device__ __forceinline__ void stream_fused_bytes(const GatherArgs& p, const StreamFusedArgs& f, uint32_t c,
+                                                   uint32_t* s_lds) {
+  using T = VecT<16>::type;
+  const int lane = threadIdx.x & 63;
+  const uint32_t base = c * 1024u;  // < A R < 2^31
+  const uint32_t tb = f.tbytes, rb = f.rbytes;
+  const uint32_t lane16 = static_cast<uint32_t>(lane) * 16u;
+  RawCells<CountT, kC> rc;
+  load_cells<CountT, kC, kVec, kInv>(static_cast<const CountT*>(f.counts), p.M, f, rc);
+  // Only blocks that hold bytes of the stream are loaded (a lane past the end
+  // reads the chunk's first block): such a block never crosses a page. Lane l
+  // also loads block 64 + l % 4, the next wave's first bytes, with a plain
+  // load, which the cache then often serves (16x16 counts, 7169-byte rows,
+  // 112 MiB: 40.2 us per call against 42.3 with a non-temporal load and 39.1
+  // with no such load at all, wrong results).
+  const uint8_t* tok = p.tokens + base;
+  const uint32_t lb = 1024u + 16u * static_cast<uint32_t>(lane & 3);
+  T x = __builtin_nontemporal_load(reinterpret_cast<const T*>(tok + (base + lane16 < tb ? lane16 : 0u)));
+  T xb = *reinterpret_cast<const T*>(tok + (base + lb < tb ? lb : 0u));
+  // as in stream_fused_tokens: the loads stay ahead of the offsets arithmetic
+  asm volatile("" ::"s"(p.tokens) : "memory");
+#pragma unroll
+  for (int k = 0; k < kC; ++k) asm volatile("" : "+v"(rc.r[k]));
+#pragma unroll
+  for (int j = 0; j < PosFmt<kC>::kWords; ++j) asm volatile("" : "+v"(rc.pos[j]));
+  mask_cells<CountT, kC, kVec, kInv>(rc, p.M);
+  order_cells<CountT, kC, kVec, kInv>(rc, reinterpret_cast<CountT*>(s_lds), p.M);
+  InCells<kC> w;
+  finish_cells<CountT, kC, false>(rc, p.A, w);
+  if (w.flags != 0) return;  // uniform: rejected counts
+  uint32_t outp[kC];
+  cell_positions<kC>(rc.pos, outp);
+  T* s_blk = reinterpret_cast<T*>(s_lds);  // the counts in LDS (order_cells) are in registers by now
+  const uint32_t s0 = __builtin_amdgcn_readfirstlane(div_magic(base, rb, f.rb_magic));
+  const int m0 = cell_of<kC>(s0, w);
+  const uint32_t d0 = dest_row<kC>(s0, m0, w, rc.pos, outp);
+  // Fast path: the cell of row s0 holds the input of the 1 KiB of output from
+  // the first segment whose input starts at base + sh64 (sh64 = -delta mod
+  // 64), [base + sh64, base + sh64 + 1024), and starts before base (or sh64
+  // == 0: no head segment).
+  const uint32_t delta = (d0 - s0) * rb;  // mod 2^32: output byte = input byte + delta
+  const uint32_t sh64 = (0u - delta) & 63u;
+  const uint32_t reach = base + sh64 + 1024u;
+  bool fast = false;
+  if (reach <= tb) {  // uniform
+    const uint32_t s_e = __builtin_amdgcn_readfirstlane(div_magic(reach - 1u, rb, f.rb_magic));
+    fast = s_e == s0 || cell_of<kC>(s_e, w) == m0;
+    if (fast && sh64 != 0 && s0 * rb == base) fast = cell_value<kC>(w.start, m0) != s0;
+  }
+  if (fast) {
+    const uint32_t o = base + sh64 + delta + lane16;  // 64-byte aligned from lane 0
+    const bool ok = o <= tb - 16u;
+    stage_blocks(s_blk, x, xb, sh64, o, ok);
+    const int v = static_cast<int>(sh64 >> 4) + lane;
+    const T y = funnel16_uniform(s_blk[v], s_blk[v + 1], static_cast<int>(sh64 & 15u));
+    if (ok) store16_through(p.out_tokens + o, y);
+    return;
+  }
+  // Otherwise each cell the owned bytes touch in turn (rows s0 .. s_last), for
+  // the blocks of lanes v = lane and v = 64 + lane (lanes 0..3).
+  const uint32_t own_end = min(base + 1024u, tb);
+  const uint32_t s_last = __builtin_amdgcn_readfirstlane(div_magic(own_end - 1u, rb, f.rb_magic));
+  const int m_last = s_last == s0 ? m0 : cell_of<kC>(s_last, w);
+  uint32_t cnt[kC];
+#pragma unroll
+  for (int k = 0; k < kC; ++k) cnt[k] = static_cast<uint32_t>(w.c[k]);
+  stage_blocks(s_blk, x, xb, s_last, own_end, true);
+  for (int m = m0; m <= m_last; ++m) {  // uniform
+    const uint32_t n = cell_value<kC>(cnt, m);
+    if (n == 0) continue;
+    const uint32_t st = cell_value<kC>(w.start, m);
+    const uint32_t om = dest_row<kC>(st, m, w, rc.pos, outp);
+    if (om + n > static_cast<uint32_t>(p.A)) continue;  // (valid counts keep every cell in range)
+    const uint32_t cs = st * rb, ce = cs + n * rb;  // the cell's input bytes
+    const uint32_t dl = (om - st) * rb;
+    const uint32_t shm = (0u - dl) & 15u;
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const int v = lane + 64 * pass;
+      if (v >= kByteBlocks) break;
+      const uint32_t xl = base + shm + 16u * static_cast<uint32_t>(v);  // this block's first input byte
+      // the first of the cell's input bytes in the block's segment (signed:
+      // the segment may start before byte 0; every byte offset is below 2^31)
+      const int32_t xf =
+          max(static_cast<int32_t>(xl) - static_cast<int32_t>((xl + dl) & 63u), static_cast<int32_t>(cs));
+      if (xl >= cs && xl < ce && xf >= static_cast<int32_t>(base) && xf < static_cast<int32_t>(own_end)) {
+        const T y = funnel16_uniform(s_blk[v], s_blk[v + 1], static_cast<int>(shm));
+        if (xl + 16u <= ce)
+          store16_through(p.out_tokens + (xl + dl), y);
+        else
+          store_bytes(p.out_tokens + (xl + dl), y, ce - xl);  // the tail block
+      }
+    }
+    if (cs >= base && cs < own_end && ((cs + dl) & 15u) != 0) {  // uniform: the head block
+      const uint32_t at = cs - base;
+      if (static_cast<uint32_t>(lane) == at >> 4) {
+        const T z = funnel16(s_blk[lane], s_blk[lane + 1], static_cast<int>(at & 15u));  // input [cs, cs + 16)
+        store_bytes(p.out_tokens + (cs + dl), z, min(16u - ((cs + dl) & 15u), ce - cs));
+      }
+    }
+  }
+}
+
 // The scale rows of output rows [d0, d0 + rows), output row d0 + r taken
 // from input row s_src[r] (LDS); kScaleRound vectors per lane are loaded
 // before they are stored.
@@ -540,60 +690,69 @@ __device__ __forceinline__ void stream_fused_items(const GatherArgs& p, const St
   }
 }
 
-template <bool kScatter, bool kWeight, typename CountT, int kC, bool kVec, bool kInv>
+// kBytes: token rows that are no multiple of 16 bytes (stream_fused_bytes).
+template <bool kScatter, bool kWeight, typename CountT, int kC, bool kVec, bool kInv, bool kBytes>
 __global__ __launch_bounds__(64) void stream_fused_kernel(GatherArgs p, StreamFusedArgs f) {
   __shared__ uint32_t s_lds[stream_fused_lds_words<kC>()];
   const int b = static_cast<int>(blockIdx.x);
   // The scalars a token wave needs before its loads, fetched together with the
   // first kernel arguments (the compiler would fetch them one after the
   // other inside the branch, each a scalar-cache round trip).
-  asm volatile("" ::"s"(p.tokens), "s"(f.counts), "s"(f.vpr), "s"(f.vpr_magic), "s"(f.vectors), "s"(p.M));
+  if constexpr (kBytes)
+    asm volatile("" ::"s"(p.tokens), "s"(f.counts), "s"(f.tbytes), "s"(f.rbytes), "s"(f.rb_magic), "s"(p.M));
+  else
+    asm volatile("" ::"s"(p.tokens), "s"(f.counts), "s"(f.vpr), "s"(f.vpr_magic), "s"(f.vectors), "s"(p.M));
   if (b < f.item_waves) {  // uniform
     stream_fused_items<kScatter, kWeight, CountT, kC, kVec, kInv>(p, f, b, s_lds);
     return;
   }
-  stream_fused_tokens<CountT, kC, kVec, kInv>(p, f, static_cast<uint32_t>(b - f.item_waves), s_lds);
+  if constexpr (kBytes)
+    stream_fused_bytes<CountT, kC, kVec, kInv>(p, f, static_cast<uint32_t>(b - f.item_waves), s_lds);
+  else
+    stream_fused_tokens<CountT, kC, kVec, kInv>(p, f, static_cast<uint32_t>(b - f.item_waves), s_lds);
 }
 
-template <typename CountT, int kC, bool kVec, bool kInv>
+template <typename CountT, int kC, bool kVec, bool kInv, bool kBytes>
 void launch_stream_fused_c(const Plan& pl, const GatherArgs& g, const StreamFusedArgs& f, unsigned grid,
                            hipStream_t stream) {
   const dim3 block(64);
   if (pl.scatter) {
     if (pl.has_weight)
-      hipLaunchKernelGGL((stream_fused_kernel<true, true, CountT, kC, kVec, kInv>), dim3(grid), block, 0, stream, g,
-                         f);
+      hipLaunchKernelGGL((stream_fused_kernel<true, true, CountT, kC, kVec, kInv, kBytes>), dim3(grid), block, 0,
+                         stream, g, f);
     else
-      hipLaunchKernelGGL((stream_fused_kernel<true, false, CountT, kC, kVec, kInv>), dim3(grid), block, 0, stream, g,
-                         f);
+      hipLaunchKernelGGL((stream_fused_kernel<true, false, CountT, kC, kVec, kInv, kBytes>), dim3(grid), block, 0,
+                         stream, g, f);
   } else {
     if (pl.has_weight)
-      hipLaunchKernelGGL((stream_fused_kernel<false, true, CountT, kC, kVec, kInv>), dim3(grid), block, 0, stream, g,
-                         f);
+      hipLaunchKernelGGL((stream_fused_kernel<false, true, CountT, kC, kVec, kInv, kBytes>), dim3(grid), block, 0,
+                         stream, g, f);
     else
-      hipLaunchKernelGGL((stream_fused_kernel<false, false, CountT, kC, kVec, kInv>), dim3(grid), block, 0, stream,
-                         g, f);
+      hipLaunchKernelGGL((stream_fused_kernel<false, false, CountT, kC, kVec, kInv, kBytes>), dim3(grid), block, 0,
+                         stream, g, f);
   }
 }
 
-template <typename CountT, int kC>
+template <typename CountT, int kC, bool kBytes>
 void launch_stream_fused_v(const Plan& pl, const GatherArgs& g, const StreamFusedArgs& f, unsigned grid, bool vec,
                            hipStream_t stream) {
   if (vec)
-    pl.inverse ? launch_stream_fused_c<CountT, kC, true, true>(pl, g, f, grid, stream)
-               : launch_stream_fused_c<CountT, kC, true, false>(pl, g, f, grid, stream);
+    pl.inverse ? launch_stream_fused_c<CountT, kC, true, true, kBytes>(pl, g, f, grid, stream)
+               : launch_stream_fused_c<CountT, kC, true, false, kBytes>(pl, g, f, grid, stream);
   else
-    pl.inverse ? launch_stream_fused_c<CountT, kC, false, true>(pl, g, f, grid, stream)
-               : launch_stream_fused_c<CountT, kC, false, false>(pl, g, f, grid, stream);
+    pl.inverse ? launch_stream_fused_c<CountT, kC, false, true, kBytes>(pl, g, f, grid, stream)
+               : launch_stream_fused_c<CountT, kC, false, false, kBytes>(pl, g, f, grid, stream);
 }
 
 template <typename CountT>
 void launch_stream_fused_t(const Plan& pl, const GatherArgs& g, const StreamFusedArgs& f, unsigned grid, bool vec,
                            hipStream_t stream) {
-  if (pl.sf_cells_per_lane == 8)
-    launch_stream_fused_v<CountT, 8>(pl, g, f, grid, vec, stream);
+  if (pl.sf_bytes)
+    pl.sf_cells_per_lane == 8 ? launch_stream_fused_v<CountT, 8, true>(pl, g, f, grid, vec, stream)
+                              : launch_stream_fused_v<CountT, 4, true>(pl, g, f, grid, vec, stream);
   else
-    launch_stream_fused_v<CountT, 4>(pl, g, f, grid, vec, stream);
+    pl.sf_cells_per_lane == 8 ? launch_stream_fused_v<CountT, 8, false>(pl, g, f, grid, vec, stream)
+                              : launch_stream_fused_v<CountT, 4, false>(pl, g, f, grid, vec, stream);
 }
 
 }  // namespace
@@ -608,10 +767,16 @@ mrr_status launch_stream_fused(const Plan& pl, const mrr_args* a, void* ws, hipS
   f.rpl = pl.sf_rows_per_lane;
   f.idx16 = reinterpret_cast<uintptr_t>(g.idx) % 16 == 0 ? 1 : 0;
   f.w16 = reinterpret_cast<uintptr_t>(g.out_weight) % 16 == 0 ? 1 : 0;
-  f.vpr = static_cast<uint32_t>(pl.row_bytes / 16);  // >= 2
-  f.vpr_magic = static_cast<uint32_t>(((uint64_t(1) << 32) + f.vpr - 1) / f.vpr);
-  f.inv_vpr = 1.0f / static_cast<float>(f.vpr);
-  f.vectors = static_cast<uint32_t>(pl.A * f.vpr);   // < 2^32 (the plan checks)
+  if (pl.sf_bytes) {
+    f.rbytes = static_cast<uint32_t>(pl.row_bytes);  // in [17, 2^16), no multiple of 16
+    f.rb_magic = static_cast<uint32_t>(((uint64_t(1) << 32) + f.rbytes - 1) / f.rbytes);
+    f.tbytes = static_cast<uint32_t>(pl.A * pl.row_bytes);  // < 2^31 (the plan checks)
+  } else {
+    f.vpr = static_cast<uint32_t>(pl.row_bytes / 16);  // >= 2
+    f.vpr_magic = static_cast<uint32_t>(((uint64_t(1) << 32) + f.vpr - 1) / f.vpr);
+    f.inv_vpr = 1.0f / static_cast<float>(f.vpr);
+    f.vectors = static_cast<uint32_t>(pl.A * f.vpr);   // < 2^32 (the plan checks)
+  }
   f.minor = static_cast<int32_t>(pl.inverse ? pl.N : pl.E);
   f.major = static_cast<int32_t>(pl.inverse ? pl.E : pl.N);
   f.inv_minor = 1.0f / static_cast<float>(f.minor);

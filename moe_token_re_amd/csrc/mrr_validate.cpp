@@ -65,7 +65,11 @@ struct Tuning {
   bool fused;       // allow the single-kernel path (MRR_FUSED=0 turns it off)
   bool byte_rows;   // rows that are no multiple of 16 bytes stream as aligned 16-byte blocks
   bool stream_fused;  // allow the one-launch stream kernel (MRR_STREAM_FUSED=0 turns it off)
+  int sf_bytes;       // its byte form: 0 off, 1 rows that are no multiple of 16 bytes, 2 (default) also
+                      // rows of 16-byte vectors that are no multiple of 64 bytes (MRR_SF_BYTES)
+  int sf_bytes16_min; // the shortest such row of 16-byte vectors it takes (MRR_SF_BYTES16_MIN)
   int sf_min_row;     // its smallest token row in bytes (MRR_SF_MIN_ROW, at least 32)
+  int64_t sf_small;   // rows under 1 KiB: token bytes below which the fused kernel stays (MRR_SF_SMALL_KIB)
   bool log;
   Tuning()
       : rows_per_wg(env_int("MRR_ROWS_PER_WG", 0)),
@@ -75,7 +79,10 @@ struct Tuning {
         fused(env_int("MRR_FUSED", 1) != 0),
         byte_rows(env_int("MRR_BYTE_ROWS", 1) != 0),
         stream_fused(env_int("MRR_STREAM_FUSED", 1) != 0),
+        sf_bytes(env_int("MRR_SF_BYTES", 2)),
+        sf_bytes16_min(env_int("MRR_SF_BYTES16_MIN", 1000)),
         sf_min_row(std::max(32, env_int("MRR_SF_MIN_ROW", 32))),
+        sf_small(int64_t(1024) * env_int("MRR_SF_SMALL_KIB", static_cast<int>(mrr::kStreamFusedSmallRowMinBytes >> 10))),
         log(env_int("MRR_LOG", 0) != 0) {}
 };
 
@@ -302,22 +309,56 @@ mrr_status make_plan(const mrr_args* a, const void* ws, size_t ws_bytes, Plan* p
   // 512-byte rows: 1 MiB 5.34 against 5.37, 16 MiB 8.33 against 10.73 (fused),
   // 131 MiB 43.5 against 50.0 (two kernels); 32-byte rows at 64 MiB 32.3
   // against 45.6; the 42-row tiny call 4.64 against 3.73 for the fused kernel.)
+  // Rows that are no multiple of 16 bytes, and rows of 16-byte vectors from
+  // 1000 bytes that are no multiple of 64, take the kernel's byte form: at
+  // least 17 bytes and below 2^16 (its row division), both token buffers
+  // 16-byte aligned, and fewer than 2^31 token bytes (32-bit byte offsets).
+  // (Its waves write whole 64-byte pieces of the output where 16-byte vectors
+  // of such rows would write parts of them from two waves. 16x16 counts,
+  // whole call: 7184-byte rows, 112 MiB, 40.0 against 44.8 us; 1040-byte rows,
+  // 64 MiB, 24.5 against 25.9; 1008-byte rows 24.6 against 25.9; below 1000
+  // bytes the 16-byte vectors measured faster (720-byte rows 14.3 against
+  // 14.7, 32-byte rows 18.1 against 18.9). Against the two kernels, rows that
+  // are no multiple of 16 bytes: 7169-byte rows 40.5 against 46.0 us, 1000
+  // bytes 25.0 against 28.8, 158 bytes (16 MiB) 10.0 against 13.2, 42 bytes
+  // (32 MiB) 18.7 against 26.0.)
   q.stream_fused = false;
+  q.sf_bytes = false;
   q.sf_item_waves = q.sf_grid = 0;
   q.sf_rows_per_lane = 1;
   q.sf_cells_per_lane = M > 256 ? 8 : 4;
-  if (tuning().stream_fused && q.A > 0 && M <= kStreamFusedMaxCells && q.token_vec == 16 &&
-      q.row_bytes >= tuning().sf_min_row &&
-      q.scale_row_bytes <= kStreamFusedMaxScaleRow && q.A < (int64_t(1) << 30) &&
-      q.A * (q.row_bytes / 16) < (int64_t(1) << 32)) {
+  const bool sf_vec_rows = q.token_vec == 16 && q.row_bytes >= tuning().sf_min_row &&
+                           q.A * (q.row_bytes / 16) < (int64_t(1) << 32);
+  const bool sf_byte_rows = (q.row_bytes % 16 != 0 ? tuning().sf_bytes >= 1
+                                                   : tuning().sf_bytes >= 2 && q.row_bytes % 64 != 0 &&
+                                                         q.row_bytes >= tuning().sf_bytes16_min) &&
+                            q.row_bytes >= 17 &&
+                            q.row_bytes < 65536 && aligned(a->tokens, 16) && aligned(a->permute_tokens, 16) &&
+                            q.A * q.row_bytes < (int64_t(1) << 31);
+  if (tuning().stream_fused && q.A > 0 && M <= kStreamFusedMaxCells && (sf_vec_rows || sf_byte_rows) &&
+      q.scale_row_bytes <= kStreamFusedMaxScaleRow && q.A < (int64_t(1) << 30)) {
     // item waves of 256 output rows (64 for scale rows of more than 16 bytes,
     // so that more waves carry their traffic)
     q.sf_rows_per_lane = q.scale_row_bytes > 16 ? 1 : 4;
     const int64_t waves = (q.A + 64 * q.sf_rows_per_lane - 1) / (64 * q.sf_rows_per_lane);
-    const int64_t grid = waves + (q.A * (q.row_bytes / 16) + 63) / 64;
-    const bool small_fused = q.fused && q.row_bytes < 1024 && q.A * q.row_bytes < kStreamFusedSmallRowMinBytes;
+    // token waves: 1 KiB of the rows each
+    const int64_t grid = waves + (q.A * q.row_bytes + 1023) / 1024;
+    // Small calls of short rows stay with the fused kernel where it applies:
+    // rows of 16-byte vectors under 1 KiB below 2 MiB of rows, rows that are
+    // no multiple of 16 bytes (the fused kernel moves them in narrower
+    // vectors) under 512 bytes below 256 KiB (there a wave's KiB spans
+    // several cells and walks them one by one). (158-byte rows, 16x16 counts:
+    // 0.11 MiB 8.5 against 6.7 us for the fused kernel, 0.23 MiB 5.5-6.4
+    // against 6.2, 0.47 MiB 4.9-5.8 against 6.3; 1000-byte rows: 0.24 MiB 4.3
+    // against 6.8, 0.5 MiB 4.6 against 6.9; 1001-byte rows, 4x4 counts, 15
+    // rows: 4.1 against 6.1.)
+    const bool small_fused =
+        q.fused && (q.row_bytes % 16 != 0
+                        ? q.row_bytes < 512 && q.A * q.row_bytes < kStreamFusedSmallByteRowMinBytes
+                        : q.row_bytes < 1024 && q.A * q.row_bytes < tuning().sf_small);
     if (grid < kMaxStreamGrid && grid <= max_launch_grid(64) && !small_fused) {
       q.stream_fused = true;
+      q.sf_bytes = sf_byte_rows;
       q.fused = false;
       q.sf_item_waves = waves;
       q.sf_grid = grid;
@@ -354,7 +395,7 @@ extern "C" mrr_status mrr_describe_plan(const mrr_args* args, const void* worksp
   const mrr_status st = mrr::make_plan(args, workspace, workspace_bytes, &plan);
   if (st != MRR_SUCCESS) return st;
   info->fused = plan.fused ? 1 : plan.stream_fused ? 2 : 0;
-  info->token_vec_bytes = plan.byte_rows && !plan.fused ? 16 : plan.token_vec;
+  info->token_vec_bytes = (plan.byte_rows || plan.sf_bytes) && !plan.fused ? 16 : plan.token_vec;
   info->scale_vec_bytes = plan.scale_row_bytes > 0 ? plan.scale_vec : 0;
   info->rows_per_workgroup = plan.rows_per_wg;
   info->threads_per_workgroup = plan.fused || !plan.stream ? mrr::kGatherThreads : 64;

@@ -233,15 +233,30 @@ def test_describe_plan():
     a = valid_args(tok=_lib.F16, H=79)
     st, info = describe(a)
     assert st == _lib.SUCCESS and info.token_vec_bytes == 2 and info.token_row_bytes == 158
-    # ...and stream as aligned 16-byte blocks of the output in the stream gather: 1 KiB chunks of
-    # the 158-byte rows, and 256-row chunks of the items with their 4-byte scale rows
+    # ...and take the one-launch kernel's byte form from 2 MiB of rows: 1024 item waves, then one
+    # wave per KiB of the 158-byte rows taken as one stream.
+    # In two phases they stream as aligned 16-byte blocks of the output in the stream gather: 1 KiB
+    # chunks of the rows, and 256-row chunks of the items with their 4-byte scale rows
     st, info = describe(valid_args(tok=_lib.F16, H=79, A=262144, N=16, E=16))
-    assert st == _lib.SUCCESS and info.gather_kernel == 1 and info.token_vec_bytes == 16
+    assert st == _lib.SUCCESS and info.fused == 2 and info.token_vec_bytes == 16
+    assert info.one_launch_workgroups == 262144 // 256 + (262144 * 158 + 1023) // 1024
+    assert info.gather_kernel == 1
     assert info.gather_workgroups == (262144 * 158 + 1023) // 1024 + 262144 // 256
-    # rows under 147 bytes: the same 1 KiB chunks (their row-map words loaded one per lane)
+    # rows under 147 bytes: the same (in two phases the same 1 KiB chunks, their row-map words
+    # loaded one per lane)
     st, info = describe(valid_args(tok=_lib.F16, H=63, A=65536, N=16, E=16))
-    assert st == _lib.SUCCESS and info.gather_kernel == 1 and info.fused == 0
+    assert st == _lib.SUCCESS and info.gather_kernel == 1 and info.fused == 2
+    assert info.one_launch_workgroups == 65536 // 256 + (65536 * 126 + 1023) // 1024
     assert info.gather_workgroups == (65536 * 126 + 1023) // 1024 + 65536 // 256
+    # the byte form wants both token buffers 16-byte aligned and fewer than 2^31 token bytes
+    a = valid_args(tok=_lib.F16, H=79, A=262144, N=16, E=16)
+    a.tokens = BASE["tokens"] + 2
+    st, info = describe(a)
+    assert st == _lib.SUCCESS and info.fused != 2
+    st, info = describe(valid_args(tok=_lib.I8, H=8191, A=262144, N=16, E=16))
+    assert st == _lib.SUCCESS and info.fused == 2
+    st, info = describe(valid_args(tok=_lib.I8, H=8193, A=262144, N=16, E=16))
+    assert st == _lib.SUCCESS and info.fused == 0
     # scale rows of more than 16 bytes keep chunks of their own (e8m0 [A, 112, 2]: 224 bytes a row)
     st, info = describe(valid_args(A=32768, H=7168, N=32, E=8, tok=_lib.F8_E4M3FN, scales="e8m0"))
     assert st == _lib.SUCCESS and info.gather_kernel == 1
@@ -309,10 +324,19 @@ def test_plan_size_classes():
     assert st == _lib.SUCCESS and info.fused == 1
     st, info = describe(valid_args(A=above48, H=16, N=16, E=16, tok=_lib.I8))
     assert st == _lib.SUCCESS and info.fused == 0 and info.offsets_workgroups == -(-above48 // 256)
-    # rows that are no multiple of 16 bytes (1000 bytes): the fused kernel below 4 MiB, else offsets + gather
-    for a_rows, fused in ((4 * mib // 1000 - 1, 1), (4 * mib // 1000 + 1, 0)):
+    # rows that are no multiple of 16 bytes take the one-launch kernel's byte form (one wave per KiB):
+    # from 512 bytes (1000 here) at any size, shorter ones (158 bytes) from 256 KiB of rows, the fused
+    # kernel below that; with more than 512 cells offsets + gather
+    for a_rows in (1, 42, 2 * mib // 1000 - 1, 2 * mib // 1000 + 1, 100 * mib // 1000):
         st, info = describe(valid_args(A=a_rows, H=1000, N=16, E=16, tok=_lib.I8))
+        assert st == _lib.SUCCESS and info.fused == 2, a_rows
+        assert info.one_launch_workgroups == -(-a_rows // 256) + -(-a_rows * 1000 // 1024)
+    for a_rows, fused in ((256 * 1024 // 158 - 1, 1), (256 * 1024 // 158 + 1, 2), (16 * mib // 158, 2)):
+        st, info = describe(valid_args(A=a_rows, H=79, N=16, E=16, tok=_lib.F16))
         assert st == _lib.SUCCESS and info.fused == fused, a_rows
+    for a_rows in (2 * mib // 1000 + 1, 100 * mib // 1000):
+        st, info = describe(valid_args(A=a_rows, H=1000, N=16, E=40, tok=_lib.I8))
+        assert st == _lib.SUCCESS and info.fused == 0 and info.gather_kernel == 1, a_rows
     # whole-KiB rows but not the one-launch kernel's other limits (above 48 MiB: offsets + gather)
     above48 = 48 * mib // 7168 + 1
     a = valid_args(A=above48, H=7168, N=16, E=16, tok=_lib.I8)

@@ -1,11 +1,15 @@
 """Parity of the one-launch stream kernel with the CPU oracle, byte for byte.
 
 moe_rerouting_v2 takes that kernel for count matrices of at most 512 cells,
-token rows of 16-byte vectors and at least 32 bytes, and scale rows of at
-most 4 KiB, at any size (rows under 1 KiB from 2 MiB of token rows when the
-fused kernel applies; every case below first checks, through the plan, that
-it does): item waves of 64 or 256 output rows, then one wave per KiB of the
-input token rows, each wave computing the offsets it needs from the counts.
+token rows of 16-byte vectors and at least 32 bytes or of any length from 17
+bytes, and scale rows of at most 4 KiB, at any size (short rows only from 2
+MiB or 256 KiB of token rows when the fused kernel applies; every case below
+first checks, through the plan, that it does): item waves of 64 or 256 output
+rows, then one wave per KiB of the input token rows, each wave computing the
+offsets it needs from the counts. Rows that are no multiple of 16 bytes, and
+rows of 16-byte vectors from 1000 bytes that are no multiple of 64, take its
+byte form (the rows as one byte stream, stores grouped by 64-byte pieces of
+the output).
 Cases cover both directions, int32 and int64 counts, empty cells, one rank or
 one expert, count matrices of 8, 35, 64 and 256 cells (four a lane) and of
 299, 300, 323, 384 and 512 cells (eight a lane, among them counts in 16-byte
@@ -245,3 +249,122 @@ def test_small_rows_below_2mib_stay_fused(direction):
     out, status = run_hip(w, dev, direction=direction)
     assert status == _lib.SUCCESS
     assert_parity(w, out, run_oracle(w, direction))
+
+
+# Token rows that are no multiple of 16 bytes (the kernel's byte form): the
+# rows as one byte stream, 960 bytes a wave, stores grouped by 64-byte
+# segments of the output; a cell's output bytes start and end inside 16-byte
+# blocks shared with the cells next to it in the output, whose waves write the
+# other bytes. Mostly small cells (a wave's bytes span several cells, empty
+# ones among them) with one large cell, as above.
+BYTE_ROWS = {
+    "16x16_158B_f16_w": dict(seed=720, n=16, e=16, row_bytes=158, target_mib=4, tokens_dtype="float16",
+                             weight=True),
+    "16x16_17B_i64_scatter": dict(seed=721, n=16, e=16, row_bytes=17, target_mib=3, counts_dtype=np.int64,
+                                  idx_type=1),
+    "5x7_42B_bf16_as3": dict(seed=722, n=5, e=7, row_bytes=42, target_mib=3, tokens_dtype="bfloat16", scales="as",
+                             S=3),
+    "16x24_1000B_fp8_e8m0": dict(seed=723, n=16, e=24, row_bytes=1000, target_mib=3, tokens_dtype="float8_e4m3fn",
+                                 scales="e8m0"),
+    "1x1_1025B_fp4": dict(seed=724, n=1, e=1, row_bytes=1025, target_mib=3, tokens_dtype="float4_e2m1fn_x2",
+                          small=(0, 1)),
+    "32x16_4097B_w_cumsum": dict(seed=725, n=32, e=16, row_bytes=4097, target_mib=8, weight=True, etn_type=0),
+    "64x8_90B_f16_zeros": dict(seed=726, n=64, e=8, row_bytes=90, target_mib=2.5, tokens_dtype="float16",
+                               small=(0, 2)),
+    "16x16_7169B_a": dict(seed=727, n=16, e=16, row_bytes=7169, target_mib=24, scales="a"),
+    "13x23_1009B_i64_as2": dict(seed=728, n=13, e=23, row_bytes=1009, target_mib=6, counts_dtype=np.int64,
+                                scales="as", S=2),
+    "8x8_30B_f16_cells_to_40": dict(seed=729, n=8, e=8, row_bytes=30, target_mib=2.5, tokens_dtype="float16",
+                                    small=(0, 40)),
+}
+
+
+@pytest.mark.parametrize("direction", DIRS, ids=DIR_IDS)
+@pytest.mark.parametrize("name", list(BYTE_ROWS))
+def test_one_launch_byte_rows(name, direction):
+    w = mixed_case(**BYTE_ROWS[name])
+    assert w.tokens.nbytes // w.A % 16 != 0
+    assert takes_one_launch(w, direction), name
+    out, status = run_hip(w, _dev(), direction=direction)
+    assert status == _lib.SUCCESS, _lib.status_string(status)
+    assert_parity(w, out, run_oracle(w, direction))
+
+
+# Balanced counts (cells of hundreds of rows: most waves lie inside one cell).
+BYTE_SIZED = {
+    "16x16_f16_H79": dict(seed=730, n=16, e=16, h=79, tokens_dtype="float16", target_mib=40, weight=True),
+    "16x32_int8_H1001_zeros": dict(seed=731, n=16, e=32, h=1001, tokens_dtype="int8", zero_cells=True,
+                                   target_mib=16, scales="a"),
+    "24x16_bf16_H21_i64_scatter": dict(seed=732, n=24, e=16, h=21, tokens_dtype="bfloat16", counts_dtype=np.int64,
+                                       idx_type=1, target_mib=4),
+    "4x4_fp4_H4098_e8m0_cumsum": dict(seed=733, n=4, e=4, h=4098, tokens_dtype="float4_e2m1fn_x2",
+                                      scales="e8m0", etn_type=0, target_mib=12),
+    # rows of 16-byte vectors that are no multiple of 64 bytes (the byte form from 1000 bytes)
+    "16x16_int8_H7184_w": dict(seed=735, n=16, e=16, h=7184, tokens_dtype="int8", weight=True, target_mib=24),
+    "24x16_bf16_H504_i64": dict(seed=736, n=24, e=16, h=504, tokens_dtype="bfloat16", counts_dtype=np.int64,
+                                target_mib=8, scales="a"),
+}
+
+
+@pytest.mark.parametrize("direction", DIRS, ids=DIR_IDS)
+@pytest.mark.parametrize("name", list(BYTE_SIZED))
+def test_one_launch_byte_rows_balanced(name, direction):
+    w = sized_case(**BYTE_SIZED[name])
+    assert w.tokens.nbytes // w.A % 64 != 0
+    assert takes_one_launch(w, direction), name
+    out, status = run_hip(w, _dev(), direction=direction)
+    assert status == _lib.SUCCESS, _lib.status_string(status)
+    assert_parity(w, out, run_oracle(w, direction))
+
+
+# A few rows of 1 KiB or more (no fused kernel there): the last wave's bytes
+# end inside a block, and with one row a wave's bytes lie in one or two rows.
+BYTE_EDGES = [(1, 1025), (2, 1025), (3, 1031), (7, 2047), (63, 1100), (64, 1111), (65, 1033), (256, 1039),
+              (257, 1201)]
+
+
+@pytest.mark.parametrize("direction", DIRS, ids=DIR_IDS)
+@pytest.mark.parametrize("ne", [(16, 16), (16, 24)], ids=["256_cells", "384_cells"])
+@pytest.mark.parametrize("a,row_bytes", BYTE_EDGES, ids=[f"A{a}_R{r}" for a, r in BYTE_EDGES])
+def test_one_launch_byte_rows_edges(a, row_bytes, ne, direction):
+    w = exact_case(650 + a, ne[0], ne[1], a, row_bytes, 1 + 7 * (a % 2), idx_type=a % 2)
+    assert w.A == a
+    assert takes_one_launch(w, direction)
+    out, status = run_hip(w, _dev(), direction=direction)
+    assert status == _lib.SUCCESS, _lib.status_string(status)
+    assert_parity(w, out, run_oracle(w, direction))
+
+
+@pytest.mark.parametrize("direction", DIRS, ids=DIR_IDS)
+def test_one_launch_byte_rows_equal_two_phases(direction):
+    """The byte form against the two phases' byte stream (the run copy)."""
+    w = sized_case(734, 16, 16, 79, "float16", target_mib=20, weight=True, scales="a", idx_type=1)
+    assert takes_one_launch(w, direction)
+    whole, st1 = run_hip(w, _dev(), direction=direction)
+    parts, st2 = run_hip(w, _dev(), phases=True, direction=direction)
+    assert st1 == st2 == _lib.SUCCESS
+    for x, y in zip(whole, parts):
+        assert np.array_equal(x, y)
+
+
+@pytest.mark.parametrize("direction", DIRS, ids=DIR_IDS)
+@pytest.mark.parametrize("kind", ["negative", "sum_high"])
+def test_one_launch_byte_rows_bad_counts_write_nothing(kind, direction):
+    rng = np.random.default_rng(78)
+    counts = rng.integers(180, 220, (16, 16)).astype(np.int32)
+    a = int(counts.sum())
+    if kind == "negative":
+        counts[1, 1] = -counts[1, 1]
+        counts[2, 2] += 2 * abs(int(counts[1, 1]))
+    else:
+        counts[0, 0] += 1
+    row = 1001
+    tok = rng.integers(0, 256, (a, row), dtype=np.uint8)
+    w = workloads.Workload(f"bad_bytes_{kind}", counts, tok, "int8", row,
+                           rng.standard_normal(a, dtype=np.float32), "float32",
+                           rng.random((a, 1), dtype=np.float32), 1, 0)
+    assert takes_one_launch(w, direction)
+    out, status = run_hip(w, _dev(), direction=direction)
+    assert status == _lib.ERROR_BAD_COUNTS, kind
+    for o in out:
+        assert (o == SENTINEL).all(), kind
