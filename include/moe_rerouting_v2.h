@@ -178,15 +178,18 @@ typedef struct mrr_plan_info {
                                     each recompute the offsets of the (small) count matrix in LDS
                                     or registers (small calls); 2 = one kernel of 64-lane
                                     workgroups (count matrices of at most 512 cells, token rows of
-                                    16-byte vectors and at least 32 bytes; rows under 1 KiB from 2
-                                    MiB of token rows where 1 applies): item waves of 256 output
-                                    rows (64 with scale rows over 16 bytes), then one wave per
-                                    1 KiB of the input token rows, each computing the offsets it
-                                    needs from the counts; 0 = the offsets kernel, then the gather
-                                    kernel (the two-phase entry points always do that) */
+                                    16-byte vectors and at least 32 bytes, or of 17 bytes or more
+                                    that are no multiple of 16 with both token buffers 16-byte
+                                    aligned; short rows only from 2 MiB or 256 KiB of token rows
+                                    where 1 applies): item waves of 256 output rows (64 with scale
+                                    rows over 16 bytes), then one wave per 1 KiB of the input token
+                                    rows, each computing the offsets it needs from the counts; 0 =
+                                    the offsets kernel, then the gather kernel (the two-phase entry
+                                    points always do that) */
   int32_t token_vec_bytes;       /* bytes per load/store of the token copy: 16, 8, 4, 2 or 1
                                     (16 also for rows that are no multiple of 16 bytes when the
-                                    stream gather moves them as aligned 16-byte output blocks) */
+                                    one-launch kernel or the stream gather moves them as aligned
+                                    16-byte output blocks) */
   int32_t scale_vec_bytes;       /* the same for scale rows; 0 without scales */
   int32_t rows_per_workgroup;    /* adjacent rows per workgroup: input rows of the fused kernel,
                                     output rows of the row-workgroup gather */

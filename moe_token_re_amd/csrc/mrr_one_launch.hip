@@ -2,15 +2,15 @@
 // "CANN ops-transformer MoeReRoutingV2": the offsets and moves of "计算公式",
 // permute_token_idx and expert_token_num of "参数说明") in one launch of
 // 64-lane workgroups, for count matrices of at most 512 cells, token rows of
-// 16-byte vectors and at least 32 bytes, and scale rows of at most 4 KiB, at
-// any size. Workgroups [0, item_waves) move the per-row items and scale rows
-// of 64 rpl output rows each; every later workgroup moves one 1 KiB chunk of
-// the input token rows, in input order, so that its token load goes out at
-// once (beside the count load); it then works out where the chunk's rows go
-// from the counts while the load is in flight. Every wave checks the counts
-// itself and writes nothing when they are rejected; workgroup 0 writes
-// expert_token_num and the status. A lane holds kC cells of the matrix: 4 up
-// to 256 cells, 8 up to 512.
+// 16-byte vectors and at least 32 bytes (or, in the byte form, of any length
+// from 17 bytes), and scale rows of at most 4 KiB, at any size. Workgroups
+// [0, item_waves) move the per-row items and scale rows of 64 rpl output rows
+// each; every later workgroup moves one 1 KiB chunk of the input token rows,
+// in input order, so that its token load goes out at once (beside the count
+// load); it then works out where the chunk's rows go from the counts while
+// the load is in flight. Every wave checks the counts itself and writes
+// nothing when they are rejected; workgroup 0 writes expert_token_num and the
+// status. A lane holds kC cells of the matrix: 4 up to 256 cells, 8 up to 512.
 #include "mrr_device.h"
 
 namespace mrr {
@@ -389,6 +389,21 @@ __device__ __forceinline__ void stage_blocks(VecT<16>::type* s_blk, VecT<16>::ty
   __builtin_amdgcn_wave_barrier();
 }
 
+// The 16 staged bytes from byte k of the wave's stream (k + 16 within the
+// staged blocks or the word after them): five words from LDS, then byte
+// funnel shifts (no branch on the shift).
+__device__ __forceinline__ VecT<16>::type staged16(const VecT<16>::type* s_blk, uint32_t k) {
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(s_blk) + (k >> 2);
+  const uint32_t r = k & 3u;
+  const uint32_t w0 = w[0], w1 = w[1], w2 = w[2], w3 = w[3], w4 = w[4];
+  VecT<16>::type o;
+  o.x = __builtin_amdgcn_alignbyte(w1, w0, r);
+  o.y = __builtin_amdgcn_alignbyte(w2, w1, r);
+  o.z = __builtin_amdgcn_alignbyte(w3, w2, r);
+  o.w = __builtin_amdgcn_alignbyte(w4, w3, r);
+  return o;
+}
+
 template <typename CountT, int kC, bool kVec, bool kInv>
 __device__ __forceinline__ void stream_fused_bytes(const GatherArgs& p, const StreamFusedArgs& f, uint32_t c,
                                                    uint32_t* s_lds) {
@@ -401,13 +416,14 @@ __device__ __forceinline__ void stream_fused_bytes(const GatherArgs& p, const St
   load_cells<CountT, kC, kVec, kInv>(static_cast<const CountT*>(f.counts), p.M, f, rc);
   // Only blocks that hold bytes of the stream are loaded (a lane past the end
   // reads the chunk's first block): such a block never crosses a page. Lane l
-  // also loads block 64 + l % 4, the next wave's first bytes, with a plain
-  // load, which the cache then often serves (16x16 counts, 7169-byte rows,
-  // 112 MiB: 40.2 us per call against 42.3 with a non-temporal load and 39.1
-  // with no such load at all, wrong results).
+  // also loads block 64 + l % 4, the next wave's first bytes. Plain loads,
+  // which the cache then often serves to the other wave (16x16 counts,
+  // 7169-byte rows, 112 MiB: 40.2 us per call against 42.3 with
+  // non-temporal loads, 39.1 with no extra load at all (wrong results); both
+  // loads plain 39.9).
   const uint8_t* tok = p.tokens + base;
   const uint32_t lb = 1024u + 16u * static_cast<uint32_t>(lane & 3);
-  T x = __builtin_nontemporal_load(reinterpret_cast<const T*>(tok + (base + lane16 < tb ? lane16 : 0u)));
+  T x = *reinterpret_cast<const T*>(tok + (base + lane16 < tb ? lane16 : 0u));
   T xb = *reinterpret_cast<const T*>(tok + (base + lb < tb ? lb : 0u));
   // as in stream_fused_tokens: the loads stay ahead of the offsets arithmetic
   asm volatile("" ::"s"(p.tokens) : "memory");
@@ -443,8 +459,7 @@ __device__ __forceinline__ void stream_fused_bytes(const GatherArgs& p, const St
     const uint32_t o = base + sh64 + delta + lane16;  // 64-byte aligned from lane 0
     const bool ok = o <= tb - 16u;
     stage_blocks(s_blk, x, xb, sh64, o, ok);
-    const int v = static_cast<int>(sh64 >> 4) + lane;
-    const T y = funnel16_uniform(s_blk[v], s_blk[v + 1], static_cast<int>(sh64 & 15u));
+    const T y = staged16(s_blk, 16u * static_cast<uint32_t>(lane) + sh64);
     if (ok) store16_through(p.out_tokens + o, y);
     return;
   }
@@ -476,7 +491,7 @@ __device__ __forceinline__ void stream_fused_bytes(const GatherArgs& p, const St
       const int32_t xf =
           max(static_cast<int32_t>(xl) - static_cast<int32_t>((xl + dl) & 63u), static_cast<int32_t>(cs));
       if (xl >= cs && xl < ce && xf >= static_cast<int32_t>(base) && xf < static_cast<int32_t>(own_end)) {
-        const T y = funnel16_uniform(s_blk[v], s_blk[v + 1], static_cast<int>(shm));
+        const T y = staged16(s_blk, xl - base);
         if (xl + 16u <= ce)
           store16_through(p.out_tokens + (xl + dl), y);
         else
@@ -486,7 +501,7 @@ __device__ __forceinline__ void stream_fused_bytes(const GatherArgs& p, const St
     if (cs >= base && cs < own_end && ((cs + dl) & 15u) != 0) {  // uniform: the head block
       const uint32_t at = cs - base;
       if (static_cast<uint32_t>(lane) == at >> 4) {
-        const T z = funnel16(s_blk[lane], s_blk[lane + 1], static_cast<int>(at & 15u));  // input [cs, cs + 16)
+        const T z = staged16(s_blk, at);  // input bytes [cs, cs + 16)
         store_bytes(p.out_tokens + (cs + dl), z, min(16u - ((cs + dl) & 15u), ce - cs));
       }
     }
