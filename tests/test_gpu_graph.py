@@ -20,10 +20,12 @@ def _host_bytes(outs):
 
 @pytest.mark.parametrize("direction", [_lib.FORWARD, _lib.INVERSE], ids=["forward", "inverse"])
 # (N, E, H, counts, the plan's launch): the fused kernel, the two kernels, and
-# the one-launch stream kernel (50 MiB of 1 KiB bf16 rows; 384 cells: eight a lane)
+# the one-launch stream kernel (50 MiB of 1 KiB bf16 rows; 384 cells: eight a
+# lane; 158-byte rows: its byte form)
 @pytest.mark.parametrize("n,e,h,count_range,fused", [(4, 3, 256, (0, 6), 1), (40, 30, 256, (0, 6), 0),
-                                                     (16, 16, 512, (180, 221), 2), (16, 24, 512, (60, 100), 2)],
-                         ids=["fused", "two_kernel", "one_launch", "one_launch_384"])
+                                                     (16, 16, 512, (180, 221), 2), (16, 24, 512, (60, 100), 2),
+                                                     (16, 16, 79, (180, 221), 2)],
+                         ids=["fused", "two_kernel", "one_launch", "one_launch_384", "one_launch_bytes"])
 def test_graph_replays_match_oracle(n, e, h, count_range, fused, direction):
     dev = _dev()
     base = workloads.random_case(71, n, e, h, tokens_dtype="bfloat16", count_range=count_range, scales="as", S=3,

@@ -2,12 +2,14 @@
 (no workspace argument: the library's static device scratch), against
 moe_rerouting_v2 with a workspace of its own, through the C ABI on the GPU.
 
-Six calls go out back to back on one stream, each with a smaller input than
+Seven calls go out back to back on one stream, each with a smaller input than
 the one before, so each finds the scratch holding the previous call's header
 and row map: a 2-million-row call that fills the scratch nearly to its limit,
 the 256 x 64 banded shape, two calls of the one-launch kernel (384 and 256
-cells), a 32 x 32 call with 158-byte rows, and the single-kernel tiny call. Every output byte must equal the existing entry
-point's on the same inputs (and the oracle's)."""
+cells), a 32 x 32 call with 158-byte rows, a 16 x 16 call with 158-byte rows
+(the one-launch kernel's byte form), and the single-kernel tiny call. Every
+output byte must equal the existing entry point's on the same inputs (and the
+oracle's)."""
 import numpy as np
 import pytest
 import torch
@@ -31,6 +33,8 @@ def _cases():
                               idx_type=1, counts_dtype=np.int64),
         workloads.random_case(72, 32, 32, 79, tokens_dtype="float16", count_range=(0, 20), scales="e8m0",
                               idx_type=1, etn_type=0),
+        workloads.random_case(75, 16, 16, 79, tokens_dtype="float16", count_range=(15, 25), scales="a",
+                              weight=True),
         workloads.make("tiny"),
     ]
 
