@@ -318,6 +318,58 @@ __device__ __forceinline__ void stream_rows(const uint8_t* __restrict__ src, uin
   if (ok) store_stream<V>(reinterpret_cast<T*>(dst + (g0 + lane) * V), v);
 }
 
+// The 16 bytes at byte sh (0..15) of the 32-byte concatenation lo:hi, by
+// byte funnel shifts (cheapest when sh is the same in every lane).
+__device__ __forceinline__ VecT<16>::type funnel16(const VecT<16>::type& lo, const VecT<16>::type& hi, int sh) {
+  const uint32_t wd[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  const int q = sh >> 2;
+  const uint32_t r = static_cast<uint32_t>(sh & 3);
+  uint32_t x[5];  // wd[q .. q + 4]
+#pragma unroll
+  for (int i = 0; i < 5; ++i) x[i] = q == 0 ? wd[i] : q == 1 ? wd[i + 1] : q == 2 ? wd[i + 2] : wd[i + 3];
+  VecT<16>::type out;
+  out.x = __builtin_amdgcn_alignbyte(x[1], x[0], r);
+  out.y = __builtin_amdgcn_alignbyte(x[2], x[1], r);
+  out.z = __builtin_amdgcn_alignbyte(x[3], x[2], r);
+  out.w = __builtin_amdgcn_alignbyte(x[4], x[3], r);
+  return out;
+}
+
+// funnel16 for a shift that is the same in every lane: a branch on q = sh / 4
+// picks the four byte-aligned word pairs.
+__device__ __forceinline__ VecT<16>::type funnel16_uniform(const VecT<16>::type& lo, const VecT<16>::type& hi,
+                                                           int sh) {
+  const uint32_t r = static_cast<uint32_t>(sh & 3);
+  VecT<16>::type o;
+  switch (sh >> 2) {
+    case 0:
+      o.x = __builtin_amdgcn_alignbyte(lo.y, lo.x, r);
+      o.y = __builtin_amdgcn_alignbyte(lo.z, lo.y, r);
+      o.z = __builtin_amdgcn_alignbyte(lo.w, lo.z, r);
+      o.w = __builtin_amdgcn_alignbyte(hi.x, lo.w, r);
+      break;
+    case 1:
+      o.x = __builtin_amdgcn_alignbyte(lo.z, lo.y, r);
+      o.y = __builtin_amdgcn_alignbyte(lo.w, lo.z, r);
+      o.z = __builtin_amdgcn_alignbyte(hi.x, lo.w, r);
+      o.w = __builtin_amdgcn_alignbyte(hi.y, hi.x, r);
+      break;
+    case 2:
+      o.x = __builtin_amdgcn_alignbyte(lo.w, lo.z, r);
+      o.y = __builtin_amdgcn_alignbyte(hi.x, lo.w, r);
+      o.z = __builtin_amdgcn_alignbyte(hi.y, hi.x, r);
+      o.w = __builtin_amdgcn_alignbyte(hi.z, hi.y, r);
+      break;
+    default:
+      o.x = __builtin_amdgcn_alignbyte(hi.x, lo.w, r);
+      o.y = __builtin_amdgcn_alignbyte(hi.y, hi.x, r);
+      o.z = __builtin_amdgcn_alignbyte(hi.z, hi.y, r);
+      o.w = __builtin_amdgcn_alignbyte(hi.w, hi.z, r);
+      break;
+  }
+  return o;
+}
+
 // Bytes [w, w + 16) of `base`, of which [n0, n1) are needed (w <= n0 < n1 <=
 // w + 16): two aligned 16-byte loads, each of a block that holds a needed
 // byte (a block with none takes the other's address, so no load leaves the
