@@ -368,3 +368,19 @@ def test_one_launch_byte_rows_bad_counts_write_nothing(kind, direction):
     assert status == _lib.ERROR_BAD_COUNTS, kind
     for o in out:
         assert (o == SENTINEL).all(), kind
+
+
+# Short rows in small calls with more than 256 cells (no fused kernel there):
+# a wave's KiB spans many rows, most cells hold a row or none.
+SMALL_BYTE_CALLS = [(1, 17), (5, 30), (100, 42), (1000, 158), (3000, 63)]
+
+
+@pytest.mark.parametrize("direction", DIRS, ids=DIR_IDS)
+@pytest.mark.parametrize("a,row_bytes", SMALL_BYTE_CALLS, ids=[f"A{a}_R{r}" for a, r in SMALL_BYTE_CALLS])
+def test_one_launch_byte_rows_small_calls(a, row_bytes, direction):
+    w = exact_case(680 + a, 16, 24, a, row_bytes, 1 + 2 * (a % 2), idx_type=a % 2)
+    assert w.A == a
+    assert takes_one_launch(w, direction)
+    out, status = run_hip(w, _dev(), direction=direction)
+    assert status == _lib.SUCCESS, _lib.status_string(status)
+    assert_parity(w, out, run_oracle(w, direction))
