@@ -46,13 +46,30 @@ struct RawCells {
   uint32_t pos[PosFmt<kC>::kWords];  // this lane's words of the output-position table
 };
 
-template <typename CountT, int kC, bool kVec, bool kInv>
+// kCalc (eight cells a lane, the minor dimension a multiple of 8): the
+// lane's words of the position table computed instead of loaded. Its eight
+// cells m = 8 lane + k then share one major index a = 8 lane / minor, and
+// cell m's position is (8 lane - a minor + k) major + a (0 past the matrix).
+template <typename CountT, int kC, bool kVec, bool kInv, bool kCalc>
 __device__ __forceinline__ void load_cells(const CountT* __restrict__ counts, int M, const StreamFusedArgs& f,
                                            RawCells<CountT, kC>& rc) {
   using PF = PosFmt<kC>;
   const int lane = threadIdx.x & 63;
+  if constexpr (kCalc) {
+    static_assert(kC == 8, "computed positions: eight cells a lane");
+    const int m0 = kC * lane;
+    const int a = div_small(m0, f.inv_minor);
+    const uint32_t b0 = static_cast<uint32_t>(m0 - a * f.minor);
 #pragma unroll
-  for (int j = 0; j < PF::kWords; ++j) rc.pos[j] = f.outpos[PF::kWords * lane + j];
+    for (int j = 0; j < PF::kWords; ++j) {
+      const uint32_t lo = m0 + 2 * j < M ? (b0 + 2 * j) * f.major + a : 0u;
+      const uint32_t hi = m0 + 2 * j + 1 < M ? (b0 + 2 * j + 1) * f.major + a : 0u;
+      rc.pos[j] = lo | (hi << 16);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < PF::kWords; ++j) rc.pos[j] = f.outpos[PF::kWords * lane + j];
+  }
   if (kVec) {
 #pragma unroll
     for (int g = 0; g < kC / 4; ++g) {
@@ -273,7 +290,7 @@ __device__ __forceinline__ uint32_t dest_row(uint32_t s, int m, const InCells<kC
 // for a single row), they go to consecutive output rows, so the chunk's 1 KiB
 // lands contiguous from output row d0 on. Otherwise each lane finds its row,
 // and a walk over the cells the chunk touches gives each row its output row.
-template <typename CountT, int kC, bool kVec, bool kInv>
+template <typename CountT, int kC, bool kVec, bool kInv, bool kCalc>
 __device__ __forceinline__ void stream_fused_tokens(const GatherArgs& p, const StreamFusedArgs& f, uint32_t c,
                                                     uint32_t* s_lds) {
   using T = VecT<16>::type;
@@ -286,7 +303,7 @@ __device__ __forceinline__ void stream_fused_tokens(const GatherArgs& p, const S
   const bool in = v < f.vectors;  // the last chunk may be partial
   const uint32_t lane16 = static_cast<uint32_t>(lane) * 16u;
   RawCells<CountT, kC> rc;
-  load_cells<CountT, kC, kVec, kInv>(static_cast<const CountT*>(f.counts), p.M, f, rc);
+  load_cells<CountT, kC, kVec, kInv, kCalc>(static_cast<const CountT*>(f.counts), p.M, f, rc);
   // a uniform base and a 32-bit lane offset (a lane past the end reads the chunk's first vector)
   const uint8_t* tok = p.tokens + static_cast<uint64_t>(n0) * 16u;
   const T x = __builtin_nontemporal_load(reinterpret_cast<const T*>(tok + (in ? lane16 : 0u)));
@@ -404,7 +421,7 @@ __device__ __forceinline__ VecT<16>::type staged16(const VecT<16>::type* s_blk, 
   return o;
 }
 
-template <typename CountT, int kC, bool kVec, bool kInv>
+template <typename CountT, int kC, bool kVec, bool kInv, bool kCalc>
 __device__ __forceinline__ void stream_fused_bytes(const GatherArgs& p, const StreamFusedArgs& f, uint32_t c,
                                                    uint32_t* s_lds) {
   using T = VecT<16>::type;
@@ -413,7 +430,7 @@ __device__ __forceinline__ void stream_fused_bytes(const GatherArgs& p, const St
   const uint32_t tb = f.tbytes, rb = f.rbytes;
   const uint32_t lane16 = static_cast<uint32_t>(lane) * 16u;
   RawCells<CountT, kC> rc;
-  load_cells<CountT, kC, kVec, kInv>(static_cast<const CountT*>(f.counts), p.M, f, rc);
+  load_cells<CountT, kC, kVec, kInv, kCalc>(static_cast<const CountT*>(f.counts), p.M, f, rc);
   // Only blocks that hold bytes of the stream are loaded (a lane past the end
   // reads the chunk's first block): such a block never crosses a page. Lane l
   // also loads block 64 + l % 4, the next wave's first bytes. Plain loads,
@@ -576,7 +593,7 @@ constexpr int stream_fused_lds_words() {
 // of 7 KiB, 256 item waves at the head of the grid cost ~1 us per call, 128
 // ~0.1); one where they are larger, so that more waves carry the scale
 // traffic.
-template <bool kScatter, bool kWeight, typename CountT, int kC, bool kVec, bool kInv>
+template <bool kScatter, bool kWeight, typename CountT, int kC, bool kVec, bool kInv, bool kCalc>
 __device__ __forceinline__ void stream_fused_items(const GatherArgs& p, const StreamFusedArgs& f, int iw,
                                                    uint32_t* s_lds) {
   // By output position: the count, overwritten by the output offset (each
@@ -590,7 +607,7 @@ __device__ __forceinline__ void stream_fused_items(const GatherArgs& p, const St
   const int lane = threadIdx.x & 63;
   const int M = p.M, A = p.A;
   RawCells<CountT, kC> rc;
-  load_cells<CountT, kC, kVec, kInv>(static_cast<const CountT*>(f.counts), M, f, rc);
+  load_cells<CountT, kC, kVec, kInv, kCalc>(static_cast<const CountT*>(f.counts), M, f, rc);
   mask_cells<CountT, kC, kVec, kInv>(rc, M);
   order_cells<CountT, kC, kVec, kInv>(rc, reinterpret_cast<CountT*>(s_lds), M);
   InCells<kC> w;
@@ -706,7 +723,7 @@ __device__ __forceinline__ void stream_fused_items(const GatherArgs& p, const St
 }
 
 // kBytes: token rows that are no multiple of 16 bytes (stream_fused_bytes).
-template <bool kScatter, bool kWeight, typename CountT, int kC, bool kVec, bool kInv, bool kBytes>
+template <bool kScatter, bool kWeight, typename CountT, int kC, bool kVec, bool kInv, bool kBytes, bool kCalc>
 __global__ __launch_bounds__(64) void stream_fused_kernel(GatherArgs p, StreamFusedArgs f) {
   __shared__ uint32_t s_lds[stream_fused_lds_words<kC>()];
   const int b = static_cast<int>(blockIdx.x);
@@ -718,56 +735,67 @@ __global__ __launch_bounds__(64) void stream_fused_kernel(GatherArgs p, StreamFu
   else
     asm volatile("" ::"s"(p.tokens), "s"(f.counts), "s"(f.vpr), "s"(f.vpr_magic), "s"(f.vectors), "s"(p.M));
   if (b < f.item_waves) {  // uniform
-    stream_fused_items<kScatter, kWeight, CountT, kC, kVec, kInv>(p, f, b, s_lds);
+    stream_fused_items<kScatter, kWeight, CountT, kC, kVec, kInv, kCalc>(p, f, b, s_lds);
     return;
   }
   if constexpr (kBytes)
-    stream_fused_bytes<CountT, kC, kVec, kInv>(p, f, static_cast<uint32_t>(b - f.item_waves), s_lds);
+    stream_fused_bytes<CountT, kC, kVec, kInv, kCalc>(p, f, static_cast<uint32_t>(b - f.item_waves), s_lds);
   else
-    stream_fused_tokens<CountT, kC, kVec, kInv>(p, f, static_cast<uint32_t>(b - f.item_waves), s_lds);
+    stream_fused_tokens<CountT, kC, kVec, kInv, kCalc>(p, f, static_cast<uint32_t>(b - f.item_waves), s_lds);
 }
 
-template <typename CountT, int kC, bool kVec, bool kInv, bool kBytes>
+template <typename CountT, int kC, bool kVec, bool kInv, bool kBytes, bool kCalc>
 void launch_stream_fused_c(const Plan& pl, const GatherArgs& g, const StreamFusedArgs& f, unsigned grid,
                            hipStream_t stream) {
   const dim3 block(64);
   if (pl.scatter) {
     if (pl.has_weight)
-      hipLaunchKernelGGL((stream_fused_kernel<true, true, CountT, kC, kVec, kInv, kBytes>), dim3(grid), block, 0,
-                         stream, g, f);
+      hipLaunchKernelGGL((stream_fused_kernel<true, true, CountT, kC, kVec, kInv, kBytes, kCalc>), dim3(grid), block,
+                         0, stream, g, f);
     else
-      hipLaunchKernelGGL((stream_fused_kernel<true, false, CountT, kC, kVec, kInv, kBytes>), dim3(grid), block, 0,
-                         stream, g, f);
+      hipLaunchKernelGGL((stream_fused_kernel<true, false, CountT, kC, kVec, kInv, kBytes, kCalc>), dim3(grid), block,
+                         0, stream, g, f);
   } else {
     if (pl.has_weight)
-      hipLaunchKernelGGL((stream_fused_kernel<false, true, CountT, kC, kVec, kInv, kBytes>), dim3(grid), block, 0,
-                         stream, g, f);
+      hipLaunchKernelGGL((stream_fused_kernel<false, true, CountT, kC, kVec, kInv, kBytes, kCalc>), dim3(grid), block,
+                         0, stream, g, f);
     else
-      hipLaunchKernelGGL((stream_fused_kernel<false, false, CountT, kC, kVec, kInv, kBytes>), dim3(grid), block, 0,
-                         stream, g, f);
+      hipLaunchKernelGGL((stream_fused_kernel<false, false, CountT, kC, kVec, kInv, kBytes, kCalc>), dim3(grid),
+                         block, 0, stream, g, f);
   }
 }
 
-template <typename CountT, int kC, bool kBytes>
+template <typename CountT, int kC, bool kBytes, bool kCalc>
 void launch_stream_fused_v(const Plan& pl, const GatherArgs& g, const StreamFusedArgs& f, unsigned grid, bool vec,
                            hipStream_t stream) {
   if (vec)
-    pl.inverse ? launch_stream_fused_c<CountT, kC, true, true, kBytes>(pl, g, f, grid, stream)
-               : launch_stream_fused_c<CountT, kC, true, false, kBytes>(pl, g, f, grid, stream);
+    pl.inverse ? launch_stream_fused_c<CountT, kC, true, true, kBytes, kCalc>(pl, g, f, grid, stream)
+               : launch_stream_fused_c<CountT, kC, true, false, kBytes, kCalc>(pl, g, f, grid, stream);
   else
-    pl.inverse ? launch_stream_fused_c<CountT, kC, false, true, kBytes>(pl, g, f, grid, stream)
-               : launch_stream_fused_c<CountT, kC, false, false, kBytes>(pl, g, f, grid, stream);
+    pl.inverse ? launch_stream_fused_c<CountT, kC, false, true, kBytes, kCalc>(pl, g, f, grid, stream)
+               : launch_stream_fused_c<CountT, kC, false, false, kBytes, kCalc>(pl, g, f, grid, stream);
+}
+
+// Four cells a lane up to 256 cells; eight up to 512, their output positions
+// computed where the minor dimension is a multiple of 8, else from the table.
+template <typename CountT, bool kBytes>
+void launch_stream_fused_b(const Plan& pl, const GatherArgs& g, const StreamFusedArgs& f, unsigned grid, bool vec,
+                           hipStream_t stream) {
+  if (pl.sf_cells_per_lane != 8)
+    launch_stream_fused_v<CountT, 4, kBytes, false>(pl, g, f, grid, vec, stream);
+  else if (f.minor % 8 == 0)
+    launch_stream_fused_v<CountT, 8, kBytes, true>(pl, g, f, grid, vec, stream);
+  else
+    launch_stream_fused_v<CountT, 8, kBytes, false>(pl, g, f, grid, vec, stream);
 }
 
 template <typename CountT>
 void launch_stream_fused_t(const Plan& pl, const GatherArgs& g, const StreamFusedArgs& f, unsigned grid, bool vec,
                            hipStream_t stream) {
   if (pl.sf_bytes)
-    pl.sf_cells_per_lane == 8 ? launch_stream_fused_v<CountT, 8, true>(pl, g, f, grid, vec, stream)
-                              : launch_stream_fused_v<CountT, 4, true>(pl, g, f, grid, vec, stream);
+    launch_stream_fused_b<CountT, true>(pl, g, f, grid, vec, stream);
   else
-    pl.sf_cells_per_lane == 8 ? launch_stream_fused_v<CountT, 8, false>(pl, g, f, grid, vec, stream)
-                              : launch_stream_fused_v<CountT, 4, false>(pl, g, f, grid, vec, stream);
+    launch_stream_fused_b<CountT, false>(pl, g, f, grid, vec, stream);
 }
 
 }  // namespace
