@@ -406,9 +406,10 @@ __device__ __forceinline__ void stage_blocks(VecT<16>::type* s_blk, VecT<16>::ty
   __builtin_amdgcn_wave_barrier();
 }
 
-// The 16 staged bytes from byte k of the wave's stream (k + 16 within the
-// staged blocks or the word after them): five words from LDS, then byte
-// funnel shifts (no branch on the shift).
+// The 16 staged bytes from byte k of the wave's stream: five words from LDS
+// from word k / 4 on, then byte funnel shifts (no branch on the shift). For a
+// tail block near the end of the staged bytes the last words lie past them,
+// inside the LDS array; their bytes are never stored.
 __device__ __forceinline__ VecT<16>::type staged16(const VecT<16>::type* s_blk, uint32_t k) {
   const uint32_t* w = reinterpret_cast<const uint32_t*>(s_blk) + (k >> 2);
   const uint32_t r = k & 3u;
